@@ -1,0 +1,113 @@
+"""Pins of the oracle's MoE layer: a dense brute force over all experts under
+a routing mask (different loop order), k = E, x = 0, and a closed-form layer."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def _dense_experts(shape, seed=0, layer=0):
+    lay = synth.mxfp4_layer(seed, layer, shape)
+    deq = {}
+    for name in ("gate", "up", "down"):
+        codes, scales = lay[name]
+        deq[name] = np.stack([oracle.mxfp4_dequant(codes[e], scales[e]) for e in range(shape.E + 1)])
+    return deq
+
+
+def _brute_force(x, ids, w, deq, n_exp):
+    """Sum over every routed expert, masked by a dense [M][E] weight matrix,
+    tokens batched per expert; the shared expert added last."""
+    m_tokens = x.shape[0]
+    dense_w = np.zeros((m_tokens, n_exp))
+    for m in range(m_tokens):
+        for j in range(ids.shape[1]):
+            dense_w[m, ids[m, j]] += w[m, j]
+    y = np.zeros_like(x)
+    for e in list(range(n_exp)) + [n_exp]:
+        g = x @ deq["gate"][e].T           # [M][I]
+        u = x @ deq["up"][e].T
+        h = g * (1.0 / (1.0 + np.exp(-g))) * u
+        out = h @ deq["down"][e].T         # [M][H]
+        coef = np.ones(m_tokens) if e == n_exp else dense_w[:, e]
+        y += coef[:, None] * out
+    return y
+
+
+@pytest.mark.parametrize("m_tokens", [1, 3, 4])
+def test_moe_matches_dense_brute_force(m_tokens):
+    shape = synth.TINY
+    deq = _dense_experts(shape)
+    wl = synth.Workload("t", shape, m_tokens, router_matrix=True)
+    xb, lg = synth.moe_inputs(wl)
+    x = synth.bf16_values(xb).astype(np.float64)
+    ids, w = oracle.route_topk(lg, shape.k)
+    y = oracle.moe_layer(x, ids, w, lambda e: (deq["gate"][e], deq["up"][e], deq["down"][e]),
+                         (deq["gate"][shape.E], deq["up"][shape.E], deq["down"][shape.E]))
+    ref = _brute_force(x, ids, w, deq, shape.E)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_moe_k_equals_e_is_dense_softmax_mixture():
+    shape = synth.TINY
+    deq = _dense_experts(shape)
+    xb, lg = synth.moe_inputs(synth.Workload("t", shape, 2, router_matrix=True))
+    x = synth.bf16_values(xb).astype(np.float64)
+    ids, w = oracle.route_topk(lg, shape.E)
+    y = oracle.moe_layer(x, ids, w, lambda e: (deq["gate"][e], deq["up"][e], deq["down"][e]),
+                         (deq["gate"][shape.E], deq["up"][shape.E], deq["down"][shape.E]))
+    p = np.exp(lg.astype(np.float64) - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    ref = np.zeros_like(x)
+    for e in range(shape.E + 1):
+        g = x @ deq["gate"][e].T
+        u = x @ deq["up"][e].T
+        out = (g / (1 + np.exp(-g)) * u) @ deq["down"][e].T
+        ref += (p[:, e:e + 1] if e < shape.E else 1.0) * out
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_moe_zero_input_gives_zero():
+    shape = synth.TINY
+    deq = _dense_experts(shape)
+    x = np.zeros((1, shape.H))
+    ids = np.array([[3, 9]])
+    w = np.array([[0.7, 0.3]])
+    y = oracle.moe_layer(x, ids, w, lambda e: (deq["gate"][e], deq["up"][e], deq["down"][e]),
+                         (deq["gate"][shape.E], deq["up"][shape.E], deq["down"][shape.E]))
+    assert (y == 0).all()
+
+
+def test_moe_closed_form_constant_layer():
+    # H = 64, I = 32, two routed experts + shared, k = 1.  Expert 0 codes all
+    # 0x22 (every element 1.0), expert 1 all 0x44 (2.0), shared 0x22 with scale
+    # 2^-1.  x = 1/64 everywhere.  Token routes to expert 1 with weight 1.
+    H, I = 64, 32
+    def const(byte, scale_code, n, k):
+        return oracle.mxfp4_dequant(np.full((n, k // 2), byte, np.uint8),
+                                    np.full((n, k // 32), scale_code, np.uint8))
+    experts = {0: tuple(const(0x22, 127, *s) for s in ((I, H), (I, H), (H, I))),
+               1: tuple(const(0x44, 127, *s) for s in ((I, H), (I, H), (H, I)))}
+    shared = tuple(const(0x22, 126, *s) for s in ((I, H), (I, H), (H, I)))
+    x = np.full((1, H), 1.0 / 64)
+    ids, w = oracle.route_topk(np.float32([[0.0, 1.0]]), 1)
+    assert ids.tolist() == [[1]] and w.tolist() == [[1.0]]
+    y = oracle.moe_layer(x, ids, w, lambda e: experts[e], shared)
+    # expert 1: g = u = 64 * 2 / 64 = 2, h = silu(2) * 2, y_n = 32 * 2 * h
+    h1 = 2.0 / (1.0 + math.exp(-2.0)) * 2.0
+    # shared: g = u = 64 * 0.5 / 64 = 0.5, h = silu(0.5) * 0.5, y_n = 32 * 0.5 * h
+    hs = 0.5 / (1.0 + math.exp(-0.5)) * 0.5
+    want = 64.0 * h1 + 16.0 * hs
+    assert abs(want - 227.9738892871453) < 1e-12
+    np.testing.assert_allclose(y[0], want, rtol=1e-15)
+
+
+def test_rmsnorm_hand_worked():
+    r = np.array([[3.0, -4.0, 0.0, 0.0]])     # mean square 25/4, rms 2.5
+    np.testing.assert_allclose(oracle.rmsnorm(r, eps=0.0), [[1.2, -1.6, 0.0, 0.0]], rtol=1e-15)
+    r2 = np.random.default_rng(1).standard_normal((2, 64))
+    np.testing.assert_allclose(oracle.rmsnorm(r2 * 7.0, eps=0.0), oracle.rmsnorm(r2, eps=0.0), rtol=1e-13)
