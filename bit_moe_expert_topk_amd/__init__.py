@@ -1,0 +1,240 @@
+"""libmoedec Python binding: batch-1 MoE decode (top-k routing, MXFP4 routed +
+shared SwiGLU experts, M = 1..4 tokens) and an online-FP8 LM head on gfx950.
+
+Thin torch-tensor wrappers over the C ABI in include/moedec.h: they check
+dtypes/devices, allocate outputs with torch when none are given, and pass raw
+pointers plus torch's current HIP stream.  All computation happens in the
+library's HIP kernels; there is no CPU fallback.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (Dispatch, LMHeadFP8Desc, MoEWeights, MXFP4Sizes, MAX_E, MAX_K, MAX_M,
+                   MAX_SLOTS, MOE_MAGIC, LMHEAD_MAGIC, FMT_E4M3FN_ROWSCALE_F32)
+
+lib = _lib.lib
+LIB_PATH = _lib.LIB_PATH
+DISPATCH_BYTES = ctypes.sizeof(Dispatch)
+
+
+class MoedecError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"libmoedec status {status}: {message}")
+        self.status = status
+
+
+def _check(status):
+    if status != 0:
+        msg = lib.moedec_status_string(status).decode()
+        detail = lib.moedec_last_error().decode()
+        raise MoedecError(status, f"{msg}: {detail}")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+# --------------------------------------------------------------------------
+# Routing
+
+def route_topk(logits, k, ids=None, weights=None, dispatch=None):
+    """Top-k routing of [M][E] float32 logits -> (ids [M][k] int32,
+    weights [M][k] float32, dispatch uint8[DISPATCH_BYTES])."""
+    _need(logits, torch.float32, "logits", 2)
+    m_tokens, n_exp = logits.shape
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((m_tokens, k), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((m_tokens, k), dtype=torch.float32, device=dev)
+    if dispatch is None:
+        dispatch = torch.empty(DISPATCH_BYTES, dtype=torch.uint8, device=dev)
+    _check(lib.moe_route_topk(_ptr(logits), m_tokens, n_exp, k, _ptr(ids), _ptr(weights),
+                              _ptr(dispatch), _stream(logits)))
+    return ids, weights, dispatch
+
+
+def decode_dispatch(dispatch):
+    """Host copy of a device dispatch table as a dict of python/numpy values."""
+    import numpy as np
+    raw = bytes(dispatch.detach().cpu().numpy().tobytes())
+    d = Dispatch.from_buffer_copy(raw)
+    n = d.n_slots
+    return {
+        "n_slots": n,
+        "M": d.M,
+        "expert": np.array(d.expert[:n], dtype=np.int32),
+        "token_mask": np.array(d.token_mask[:n], dtype=np.uint32),
+        "weight": np.array([list(d.weight[i]) for i in range(n)], dtype=np.float32),
+        "raw": d,
+    }
+
+
+# --------------------------------------------------------------------------
+# MXFP4 experts
+
+def packed_sizes(H, I):
+    out = MXFP4Sizes()
+    _check(lib.moedec_mxfp4_packed_sizes(H, I, ctypes.byref(out)))
+    return out
+
+
+def pack_gateup(gate_codes, gate_scales, up_codes, up_scales, out_codes=None, out_scales=None):
+    """Pack canonical gate/up MXFP4 matrices [n][I][H/2], [n][I][H/32]."""
+    for t, n in ((gate_codes, "gate_codes"), (gate_scales, "gate_scales"),
+                 (up_codes, "up_codes"), (up_scales, "up_scales")):
+        _need(t, torch.uint8, n, 3)
+    n_exp, I, half_h = gate_codes.shape
+    H = 2 * half_h
+    sz = packed_sizes(H, I)
+    if out_codes is None:
+        out_codes = torch.empty(n_exp * sz.gu_codes, dtype=torch.uint8, device=gate_codes.device)
+    if out_scales is None:
+        out_scales = torch.empty(n_exp * sz.gu_scales, dtype=torch.uint8, device=gate_codes.device)
+    _check(lib.moe_pack_gateup_mxfp4(_ptr(gate_codes), _ptr(gate_scales), _ptr(up_codes),
+                                     _ptr(up_scales), n_exp, H, I, _ptr(out_codes),
+                                     _ptr(out_scales), _stream(gate_codes)))
+    return out_codes, out_scales
+
+
+def pack_down(down_codes, down_scales, out_codes=None, out_scales=None):
+    """Pack canonical down MXFP4 matrices [n][H][I/2], [n][H][I/32]."""
+    _need(down_codes, torch.uint8, "down_codes", 3)
+    _need(down_scales, torch.uint8, "down_scales", 3)
+    n_exp, H, half_i = down_codes.shape
+    I = 2 * half_i
+    sz = packed_sizes(H, I)
+    if out_codes is None:
+        out_codes = torch.empty(n_exp * sz.dn_codes, dtype=torch.uint8, device=down_codes.device)
+    if out_scales is None:
+        out_scales = torch.empty(n_exp * sz.dn_scales, dtype=torch.uint8, device=down_codes.device)
+    _check(lib.moe_pack_down_mxfp4(_ptr(down_codes), _ptr(down_scales), n_exp, H, I,
+                                   _ptr(out_codes), _ptr(out_scales), _stream(down_codes)))
+    return out_codes, out_scales
+
+
+class MoELayerWeights:
+    """Packed MXFP4 weights of one MoE layer: E routed experts + 1 shared.
+
+    The four packed arrays hold E+1 consecutive experts; the last one is the
+    shared expert.  Tensors are kept alive by this object.
+    """
+
+    def __init__(self, E, H, I, gu_codes, gu_scales, dn_codes, dn_scales):
+        self.E, self.H, self.I = E, H, I
+        self.sizes = packed_sizes(H, I)
+        sz = self.sizes
+        for t, per in ((gu_codes, sz.gu_codes), (gu_scales, sz.gu_scales),
+                       (dn_codes, sz.dn_codes), (dn_scales, sz.dn_scales)):
+            _need(t, torch.uint8, "packed weights")
+            if t.numel() < (E + 1) * per:
+                raise ValueError(f"packed array has {t.numel()} bytes, need {(E + 1) * per}")
+        self.gu_codes, self.gu_scales = gu_codes, gu_scales
+        self.dn_codes, self.dn_scales = dn_codes, dn_scales
+        base = lambda t: t.data_ptr()
+        self.desc = MoEWeights(
+            MOE_MAGIC, E, H, I,
+            base(gu_codes), base(gu_scales), base(dn_codes), base(dn_scales),
+            base(gu_codes) + E * sz.gu_codes, base(gu_scales) + E * sz.gu_scales,
+            base(dn_codes) + E * sz.dn_codes, base(dn_scales) + E * sz.dn_scales)
+
+    @classmethod
+    def from_canonical(cls, gate, up, down, E):
+        """gate/up/down: (codes, scales) uint8 device tensors with E+1 experts
+        stacked on dim 0 (index E = shared expert)."""
+        gu_c, gu_s = pack_gateup(gate[0], gate[1], up[0], up[1])
+        dn_c, dn_s = pack_down(down[0], down[1])
+        H = 2 * gate[0].shape[2]
+        I = gate[0].shape[1]
+        return cls(E, H, I, gu_c, gu_s, dn_c, dn_s)
+
+
+def ffn_workspace_bytes(M, k_max, H, I):
+    return lib.moe_ffn_workspace_bytes(M, k_max, H, I)
+
+
+def make_ffn_workspace(M, k_max, H, I, device):
+    """Zero-filled workspace for expert_ffn (zero fill is required once)."""
+    n = ffn_workspace_bytes(M, k_max, H, I)
+    if n == 0:
+        raise ValueError("unsupported workspace shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def expert_ffn(weights, x, dispatch, k_max, workspace, y=None, y_f32=None, want_f32=True):
+    """Routed + shared expert FFN.  x: [M][H] bfloat16.  Returns (y bf16, y_f32 or None)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(dispatch, torch.uint8, "dispatch", 1)
+    _need(workspace, torch.uint8, "workspace", 1)
+    m_tokens, hidden = x.shape
+    if y is None:
+        y = torch.empty((m_tokens, hidden), dtype=torch.bfloat16, device=x.device)
+    if y_f32 is None and want_f32:
+        y_f32 = torch.empty((m_tokens, hidden), dtype=torch.float32, device=x.device)
+    _check(lib.moe_expert_ffn_mxfp4(ctypes.byref(weights.desc), _ptr(x), m_tokens, _ptr(dispatch),
+                                    k_max, _ptr(y), _ptr(y_f32), _ptr(workspace),
+                                    workspace.numel(), _stream(x)))
+    return y, y_f32
+
+
+# --------------------------------------------------------------------------
+# LM head
+
+class LMHeadFP8:
+    """An FP8 LM head: E4M3 codes [V][H] + float32 row scales [V], carried
+    with a typed descriptor so the codes cannot be consumed as bf16."""
+
+    def __init__(self, codes, row_scale, desc):
+        self.codes, self.row_scale, self.desc = codes, row_scale, desc
+        self.V, self.H = codes.shape
+
+
+def lmhead_quant_fp8(w_bf16):
+    _need(w_bf16, torch.bfloat16, "w_bf16", 2)
+    V, H = w_bf16.shape
+    codes = torch.empty((V, H), dtype=torch.uint8, device=w_bf16.device)
+    row_scale = torch.empty(V, dtype=torch.float32, device=w_bf16.device)
+    desc = LMHeadFP8Desc()
+    _check(lib.lmhead_quant_fp8(_ptr(w_bf16), V, H, _ptr(codes), _ptr(row_scale),
+                                ctypes.byref(desc), _stream(w_bf16)))
+    return LMHeadFP8(codes, row_scale, desc)
+
+
+def lmhead_gemv_fp8(head, x, out=None):
+    _need(x, torch.bfloat16, "x", 2)
+    m_tokens = x.shape[0]
+    if out is None:
+        out = torch.empty((m_tokens, head.V), dtype=torch.float32, device=x.device)
+    _check(lib.lmhead_gemv_fp8(ctypes.byref(head.desc), _ptr(x), m_tokens, _ptr(out), _stream(x)))
+    return out
+
+
+def lmhead_gemv_bf16(w_bf16, x, out=None):
+    _need(w_bf16, torch.bfloat16, "w_bf16", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    V, H = w_bf16.shape
+    m_tokens = x.shape[0]
+    if out is None:
+        out = torch.empty((m_tokens, V), dtype=torch.float32, device=x.device)
+    _check(lib.lmhead_gemv_bf16(_ptr(w_bf16), V, H, _ptr(x), m_tokens, _ptr(out), _stream(x)))
+    return out

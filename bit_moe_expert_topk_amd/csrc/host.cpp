@@ -1,0 +1,254 @@
+// C ABI of libmoedec: argument checks, the gfx950 device check, launches.
+// Nothing here allocates device memory or synchronises a stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+#include "moedec.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device verdict: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(MOEDEC_ERR_DEVICE, "no current HIP device");
+    int v = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(MOEDEC_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+        v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_ok[dev].store(v, std::memory_order_relaxed);
+    }
+    if (v != 1) return fail(MOEDEC_ERR_DEVICE, "device %d is not gfx950", dev);
+    return MOEDEC_OK;
+}
+
+int launched(hipError_t err, const char* what) {
+    if (err != hipSuccess)
+        return fail(MOEDEC_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(err));
+    g_last_error[0] = '\0';
+    return MOEDEC_OK;
+}
+
+int check_mxfp4_shape(int H, int I) {
+    if (H < 64 || H > 16384 || H % 64 != 0)
+        return fail(MOEDEC_ERR_SHAPE, "H=%d: need 64 <= H <= 16384 and H %% 64 == 0", H);
+    if (I < 32 || I > 16384 || I % 32 != 0)
+        return fail(MOEDEC_ERR_SHAPE, "I=%d: need 32 <= I <= 16384 and I %% 32 == 0", I);
+    return MOEDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moedec_abi_version(void) { return MOEDEC_ABI_VERSION; }
+
+const char* moedec_status_string(int status) {
+    switch (status) {
+        case MOEDEC_OK: return "ok";
+        case MOEDEC_ERR_NULL: return "null pointer";
+        case MOEDEC_ERR_ALIGN: return "misaligned pointer";
+        case MOEDEC_ERR_SHAPE: return "unsupported shape";
+        case MOEDEC_ERR_FORMAT: return "descriptor format mismatch";
+        case MOEDEC_ERR_WORKSPACE: return "workspace too small";
+        case MOEDEC_ERR_LAUNCH: return "kernel launch failed";
+        case MOEDEC_ERR_DEVICE: return "device is not gfx950";
+        default: return "unknown status";
+    }
+}
+
+const char* moedec_last_error(void) { return g_last_error; }
+
+int moe_route_topk(const float* logits, int M, int E, int k, int32_t* topk_ids, float* topk_w,
+                   moedec_dispatch* dispatch, moedec_stream_t stream) {
+    if (!logits) return fail(MOEDEC_ERR_NULL, "logits is NULL");
+    if (!topk_ids && !topk_w && !dispatch)
+        return fail(MOEDEC_ERR_NULL, "no output given (topk_ids, topk_w and dispatch all NULL)");
+    if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
+    if (E < 1 || E > MOEDEC_MAX_E) return fail(MOEDEC_ERR_SHAPE, "E=%d not in 1..%d", E, MOEDEC_MAX_E);
+    if (k < 1 || k > E || k > MOEDEC_MAX_K)
+        return fail(MOEDEC_ERR_SHAPE, "k=%d not in 1..min(E, %d)", k, MOEDEC_MAX_K);
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+        return fail(MOEDEC_ERR_ALIGN, "logits/topk_ids/topk_w must be 4-byte aligned");
+    if (!aligned(dispatch, 16)) return fail(MOEDEC_ERR_ALIGN, "dispatch must be 16-byte aligned");
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_route_topk(logits, M, E, k, topk_ids, topk_w, dispatch,
+                                              static_cast<hipStream_t>(stream)),
+                    "moe_route_topk");
+}
+
+int moedec_mxfp4_packed_sizes(int H, int I, moedec_mxfp4_sizes* out) {
+    if (!out) return fail(MOEDEC_ERR_NULL, "out is NULL");
+    if (int st = check_mxfp4_shape(H, I)) return st;
+    const size_t kbh4 = (size_t)(H / 32 + 3) / 4, kbi4 = (size_t)(I / 32 + 3) / 4;
+    out->gu_codes = (size_t)I * H;
+    out->gu_scales = (size_t)(I / 32) * kbh4 * 256;
+    out->dn_codes = (size_t)H * I / 2;
+    out->dn_scales = (size_t)(H / 64) * kbi4 * 256;
+    g_last_error[0] = '\0';
+    return MOEDEC_OK;
+}
+
+int moe_pack_gateup_mxfp4(const uint8_t* gate_codes, const uint8_t* gate_scales,
+                          const uint8_t* up_codes, const uint8_t* up_scales, int n_experts, int H,
+                          int I, uint8_t* gu_codes, uint8_t* gu_scales, moedec_stream_t stream) {
+    if (!gate_codes || !gate_scales || !up_codes || !up_scales || !gu_codes || !gu_scales)
+        return fail(MOEDEC_ERR_NULL, "a pack pointer is NULL");
+    if (n_experts < 1 || n_experts > MOEDEC_MAX_E + 1)
+        return fail(MOEDEC_ERR_SHAPE, "n_experts=%d not in 1..%d", n_experts, MOEDEC_MAX_E + 1);
+    if (int st = check_mxfp4_shape(H, I)) return st;
+    if (!aligned(gate_codes, 16) || !aligned(up_codes, 16) || !aligned(gu_codes, 16))
+        return fail(MOEDEC_ERR_ALIGN, "code arrays must be 16-byte aligned");
+    if (!aligned(gu_scales, 4)) return fail(MOEDEC_ERR_ALIGN, "packed scales must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_pack_gateup(gate_codes, gate_scales, up_codes, up_scales,
+                                               n_experts, H, I, gu_codes, gu_scales,
+                                               static_cast<hipStream_t>(stream)),
+                    "moe_pack_gateup_mxfp4");
+}
+
+int moe_pack_down_mxfp4(const uint8_t* down_codes, const uint8_t* down_scales, int n_experts,
+                        int H, int I, uint8_t* dn_codes, uint8_t* dn_scales,
+                        moedec_stream_t stream) {
+    if (!down_codes || !down_scales || !dn_codes || !dn_scales)
+        return fail(MOEDEC_ERR_NULL, "a pack pointer is NULL");
+    if (n_experts < 1 || n_experts > MOEDEC_MAX_E + 1)
+        return fail(MOEDEC_ERR_SHAPE, "n_experts=%d not in 1..%d", n_experts, MOEDEC_MAX_E + 1);
+    if (int st = check_mxfp4_shape(H, I)) return st;
+    if (!aligned(down_codes, 16) || !aligned(dn_codes, 16))
+        return fail(MOEDEC_ERR_ALIGN, "code arrays must be 16-byte aligned");
+    if (!aligned(dn_scales, 4)) return fail(MOEDEC_ERR_ALIGN, "packed scales must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_pack_down(down_codes, down_scales, n_experts, H, I, dn_codes,
+                                             dn_scales, static_cast<hipStream_t>(stream)),
+                    "moe_pack_down_mxfp4");
+}
+
+size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I) {
+    if (M < 1 || M > MOEDEC_MAX_M || k_max < 1 || k_max > MOEDEC_MAX_K || H < 64 || H % 64 ||
+        I < 32 || I % 32)
+        return 0;
+    return moedec::ffn_layout(M, k_max, H, I).total;
+}
+
+int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, int M,
+                         const moedec_dispatch* dispatch, int k_max, uint16_t* y_bf16, float* y_f32,
+                         void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+    if (!w) return fail(MOEDEC_ERR_NULL, "weights descriptor is NULL");
+    if (w->magic != MOEDEC_MOE_MAGIC)
+        return fail(MOEDEC_ERR_FORMAT, "weights descriptor magic 0x%08x != 0x%08x", w->magic,
+                    MOEDEC_MOE_MAGIC);
+    if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales || !w->sh_gu_codes ||
+        !w->sh_gu_scales || !w->sh_dn_codes || !w->sh_dn_scales)
+        return fail(MOEDEC_ERR_NULL, "a weight pointer is NULL");
+    if (!x_bf16 || !dispatch || !y_bf16 || !workspace)
+        return fail(MOEDEC_ERR_NULL, "x, dispatch, y_bf16 or workspace is NULL");
+    if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
+    if (k_max < 1 || k_max > MOEDEC_MAX_K || k_max > w->E)
+        return fail(MOEDEC_ERR_SHAPE, "k_max=%d not in 1..min(E, %d)", k_max, MOEDEC_MAX_K);
+    if (w->E < 1 || w->E > MOEDEC_MAX_E) return fail(MOEDEC_ERR_SHAPE, "E=%d not in 1..%d", w->E, MOEDEC_MAX_E);
+    if (int st = check_mxfp4_shape(w->H, w->I)) return st;
+    if (!aligned(w->gu_codes, 16) || !aligned(w->dn_codes, 16) || !aligned(w->sh_gu_codes, 16) ||
+        !aligned(w->sh_dn_codes, 16))
+        return fail(MOEDEC_ERR_ALIGN, "packed code arrays must be 16-byte aligned");
+    if (!aligned(w->gu_scales, 4) || !aligned(w->dn_scales, 4) || !aligned(w->sh_gu_scales, 4) ||
+        !aligned(w->sh_dn_scales, 4))
+        return fail(MOEDEC_ERR_ALIGN, "packed scale arrays must be 4-byte aligned");
+    if (!aligned(x_bf16, 4) || !aligned(y_bf16, 4) || !aligned(y_f32, 4))
+        return fail(MOEDEC_ERR_ALIGN, "x, y_bf16 and y_f32 must be 4-byte aligned");
+    if (!aligned(dispatch, 16) || !aligned(workspace, 16))
+        return fail(MOEDEC_ERR_ALIGN, "dispatch and workspace must be 16-byte aligned");
+    const size_t need = moedec::ffn_layout(M, k_max, w->H, w->I).total;
+    if (workspace_bytes < need)
+        return fail(MOEDEC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_expert_ffn(*w, x_bf16, M, dispatch, k_max, y_bf16, y_f32,
+                                              workspace, static_cast<hipStream_t>(stream)),
+                    "moe_expert_ffn_mxfp4");
+}
+
+int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H, uint8_t* codes, float* row_scale,
+                     moedec_lmhead_fp8* out_desc, moedec_stream_t stream) {
+    if (!w_bf16 || !codes || !row_scale) return fail(MOEDEC_ERR_NULL, "w, codes or row_scale is NULL");
+    if (V < 1) return fail(MOEDEC_ERR_SHAPE, "V=%d < 1", V);
+    if (H < 16 || H > 8192 || H % 16)
+        return fail(MOEDEC_ERR_SHAPE, "H=%d: need 16 <= H <= 8192 and H %% 16 == 0", H);
+    if (!aligned(w_bf16, 16) || !aligned(codes, 16) || !aligned(row_scale, 4))
+        return fail(MOEDEC_ERR_ALIGN, "w and codes must be 16-byte aligned, row_scale 4-byte");
+    if (int st = check_device()) return st;
+    const int st = launched(moedec::launch_lmhead_quant(w_bf16, V, H, codes, row_scale,
+                                                        static_cast<hipStream_t>(stream)),
+                            "lmhead_quant_fp8");
+    if (st == MOEDEC_OK && out_desc) {
+        out_desc->magic = MOEDEC_LMHEAD_MAGIC;
+        out_desc->format = MOEDEC_FMT_E4M3FN_ROWSCALE_F32;
+        out_desc->V = V;
+        out_desc->H = H;
+        out_desc->codes = codes;
+        out_desc->row_scale = row_scale;
+    }
+    return st;
+}
+
+int lmhead_gemv_fp8(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M, float* logits,
+                    moedec_stream_t stream) {
+    if (!head) return fail(MOEDEC_ERR_NULL, "head descriptor is NULL");
+    if (head->magic != MOEDEC_LMHEAD_MAGIC)
+        return fail(MOEDEC_ERR_FORMAT, "head magic 0x%08x is not an FP8 LM-head descriptor",
+                    head->magic);
+    if (head->format != MOEDEC_FMT_E4M3FN_ROWSCALE_F32)
+        return fail(MOEDEC_ERR_FORMAT, "head format %u is not E4M3 with per-row float32 scales",
+                    head->format);
+    if (!head->codes || !head->row_scale || !x_bf16 || !logits)
+        return fail(MOEDEC_ERR_NULL, "codes, row_scale, x or logits is NULL");
+    if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
+    if (head->V < 1) return fail(MOEDEC_ERR_SHAPE, "V=%d < 1", head->V);
+    if (head->H < 16 || head->H > 4096 || head->H % 16)
+        return fail(MOEDEC_ERR_SHAPE, "H=%d: need 16 <= H <= 4096 and H %% 16 == 0", head->H);
+    if (!aligned(head->codes, 16) || !aligned(head->row_scale, 4) || !aligned(x_bf16, 4) ||
+        !aligned(logits, 4))
+        return fail(MOEDEC_ERR_ALIGN, "codes 16-byte, row_scale/x/logits 4-byte alignment needed");
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_gemv_fp8(head->codes, head->row_scale, head->V, head->H, x_bf16,
+                                            M, logits, static_cast<hipStream_t>(stream)),
+                    "lmhead_gemv_fp8");
+}
+
+int lmhead_gemv_bf16(const uint16_t* w_bf16, int V, int H, const uint16_t* x_bf16, int M,
+                     float* logits, moedec_stream_t stream) {
+    if (!w_bf16 || !x_bf16 || !logits) return fail(MOEDEC_ERR_NULL, "w, x or logits is NULL");
+    if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
+    if (V < 1) return fail(MOEDEC_ERR_SHAPE, "V=%d < 1", V);
+    if (H < 8 || H > 4096 || H % 8)
+        return fail(MOEDEC_ERR_SHAPE, "H=%d: need 8 <= H <= 4096 and H %% 8 == 0", H);
+    if (!aligned(w_bf16, 16) || !aligned(x_bf16, 4) || !aligned(logits, 4))
+        return fail(MOEDEC_ERR_ALIGN, "w 16-byte, x/logits 4-byte alignment needed");
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_gemv_bf16(w_bf16, V, H, x_bf16, M, logits,
+                                             static_cast<hipStream_t>(stream)),
+                    "lmhead_gemv_bf16");
+}
+
+}  // extern "C"

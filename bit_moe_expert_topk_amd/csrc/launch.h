@@ -1,0 +1,39 @@
+// Internal launch functions (C++), called by the C ABI layer after argument
+// checks.  Each returns the hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moedec.h"
+
+namespace moedec {
+
+hipError_t launch_route_topk(const float* logits, int M, int E, int k, int32_t* ids, float* w,
+                             moedec_dispatch* disp, hipStream_t s);
+
+hipError_t launch_pack_gateup(const uint8_t* gc, const uint8_t* gs, const uint8_t* uc,
+                              const uint8_t* us, int n_exp, int H, int I, uint8_t* oc,
+                              uint8_t* os, hipStream_t s);
+hipError_t launch_pack_down(const uint8_t* dc, const uint8_t* ds, int n_exp, int H, int I,
+                            uint8_t* oc, uint8_t* os, hipStream_t s);
+
+struct FfnLayout {
+    size_t h_off, part_off, ticket_off, total;
+    int max_slots;
+};
+FfnLayout ffn_layout(int M, int k_max, int H, int I);
+
+hipError_t launch_expert_ffn(const moedec_moe_weights& w, const uint16_t* x, int M,
+                             const moedec_dispatch* disp, int k_max, uint16_t* y_bf16,
+                             float* y_f32, void* ws, hipStream_t s);
+
+hipError_t launch_lmhead_quant(const uint16_t* w, int V, int H, uint8_t* codes, float* rs,
+                               hipStream_t s);
+hipError_t launch_gemv_fp8(const uint8_t* codes, const float* rs, int V, int H,
+                           const uint16_t* x, int M, float* logits, hipStream_t s);
+hipError_t launch_gemv_bf16(const uint16_t* w, int V, int H, const uint16_t* x, int M,
+                            float* logits, hipStream_t s);
+
+}  // namespace moedec

@@ -1,0 +1,229 @@
+/*
+ * moedec.h -- C ABI of libmoedec: batch-1 MoE decode with MXFP4 experts and
+ * an FP8 LM head, hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * Sources cited below
+ *   [news] yoususu.cn/post/959 -- news article on NVIDIA's software-only DGX
+ *          Spark decode speed-up (section "where the speed comes from").
+ *   [ic]   ic.work article on DGX Spark running Ling-3.0-flash (section "three
+ *          scalpels": 512 routed + 1 shared expert, MXFP4 routed experts,
+ *          157K vocabulary).
+ *   [card] ai.cheesepanini.fun knowledge card "three ways to boost MoE
+ *          inference on DGX Spark" (background; method points #1 MoE kernel,
+ *          #2 FP8 LM head, #3 4-token verify window).
+ *   [MX]   OCP Microscaling Formats (MX) v1.0; [OFP8] OCP 8-bit Floating
+ *          Point rev 1.0.
+ *
+ * Conventions for every call
+ *   - All pointers are DEVICE pointers unless marked "host".  The caller owns
+ *     every buffer; the library never allocates, frees or synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = null stream) and the
+ *     call returns without waiting.  The return value reports host-side
+ *     argument checks and launch errors only; a fault inside a kernel shows
+ *     up at the caller's next synchronisation.
+ *   - On a non-zero return nothing was enqueued, and moedec_last_error()
+ *     holds a message for the calling thread.
+ *   - bf16 values are passed as uint16 bit patterns.
+ *   - The library holds no state between calls other than a per-device
+ *     check that the device is gfx950; calls are thread-safe.  Calls that
+ *     share one workspace must be ordered (same stream or synchronised).
+ */
+#ifndef MOEDEC_H
+#define MOEDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEDEC_ABI_VERSION 1
+
+typedef void* moedec_stream_t;
+
+/* Status codes. */
+#define MOEDEC_OK             0
+#define MOEDEC_ERR_NULL      -1   /* a required pointer is NULL */
+#define MOEDEC_ERR_ALIGN     -2   /* a pointer is not aligned as documented */
+#define MOEDEC_ERR_SHAPE     -3   /* a size is outside the supported range */
+#define MOEDEC_ERR_FORMAT    -4   /* a descriptor's magic/format tag is wrong */
+#define MOEDEC_ERR_WORKSPACE -5   /* workspace smaller than required */
+#define MOEDEC_ERR_LAUNCH    -6   /* the HIP runtime rejected a launch */
+#define MOEDEC_ERR_DEVICE    -7   /* the current device is not a gfx950 GPU */
+
+/* Limits. */
+#define MOEDEC_MAX_M      4       /* tokens per call: 1, or the 4-token verify window [card #3] */
+#define MOEDEC_MAX_K      32      /* experts chosen per token */
+#define MOEDEC_MAX_E      1024    /* routed experts per layer */
+#define MOEDEC_MAX_SLOTS  (MOEDEC_MAX_M * MOEDEC_MAX_K + 1)
+
+int moedec_abi_version(void);
+const char* moedec_status_string(int status);   /* static text, never NULL */
+const char* moedec_last_error(void);            /* thread-local; "" when none */
+
+/* ------------------------------------------------------------------------
+ * Routing.  [card background; news: 8 of 512 routed experts per token;
+ * card #3: a 4-token verify touches up to 32 experts]
+ *
+ * Per token m: the k experts with the largest float32 logits, ordered by
+ * (logit descending, expert index ascending), +0.0 and -0.0 equal; weights
+ * are the softmax over all E logits renormalised over the k chosen ones.
+ * The dispatch table groups the tokens by expert so that each active expert's
+ * weights are read once per call whatever the number of tokens using it.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t  n_slots;                              /* distinct routed experts + 1 */
+    int32_t  M;                                    /* tokens */
+    int32_t  expert[MOEDEC_MAX_SLOTS];             /* ascending ids, then E (= shared) */
+    uint32_t token_mask[MOEDEC_MAX_SLOTS];         /* bit m: token m uses the slot */
+    float    weight[MOEDEC_MAX_SLOTS][MOEDEC_MAX_M]; /* 0 where the token does not */
+} moedec_dispatch;                                 /* entries >= n_slots are zero */
+
+/*
+ * logits     [M][E] float32, 4-byte aligned, finite (NaN is outside the domain)
+ * topk_ids   [M][k] int32   (may be NULL)
+ * topk_w     [M][k] float32 (may be NULL)
+ * dispatch   one moedec_dispatch in device memory (may be NULL; at least one
+ *            of the three outputs must be given), 16-byte aligned
+ * 1 <= M <= 4, 1 <= E <= 1024, 1 <= k <= min(E, 32).
+ */
+int moe_route_topk(const float* logits, int M, int E, int k,
+                   int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
+                   moedec_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MXFP4 expert weights.  [ic three scalpels: routed experts are MXFP4;
+ * MX §5: 32 E2M1 codes share one E8M0 scale]
+ *
+ * Canonical layout of an N x K MXFP4 matrix: codes [N][K/2] bytes, low nibble
+ * = even k; scales [N][K/32] bytes.  Experts are stacked along a leading axis.
+ *
+ * The FFN kernel reads a packed layout in which one 64-lane wave fetches one
+ * contiguous 1 KiB chunk per step:
+ *   gate/up, per expert, KB = H/32 blocks, KB4 = ceil(KB/4), I/32 row groups:
+ *     codes  [I/32][KB][64][16]: lane l < 32 holds gate row 32r+l, lane l >= 32
+ *            up row 32r+l-32, the 16 code bytes of block q
+ *     scales [I/32][KB4][64][4]: byte b of lane l's word p = scale of block 4p+b
+ *            (0 beyond KB)
+ *   down, per expert, KB = I/32, KB4 = ceil(KB/4), H/64 row groups:
+ *     codes  [H/64][KB][64][16]: lane l holds row 64g+l
+ *     scales [H/64][KB4][64][4]
+ * The packing is a byte permutation (plus zero padding of scales); it is done
+ * once, by the two calls below.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    size_t gu_codes, gu_scales, dn_codes, dn_scales;   /* bytes per expert */
+} moedec_mxfp4_sizes;
+
+/* Per-expert packed sizes; returns MOEDEC_ERR_SHAPE unless H % 64 == 0,
+ * I % 32 == 0, 64 <= H <= 16384, 32 <= I <= 16384.  `out` is host memory. */
+int moedec_mxfp4_packed_sizes(int H, int I, moedec_mxfp4_sizes* out);
+
+/* gate, up: canonical [n_experts][I][H/2] codes, [n_experts][I][H/32] scales.
+ * Output: n_experts consecutive packed experts.  Codes pointers 16-byte
+ * aligned, scale outputs 4-byte aligned. */
+int moe_pack_gateup_mxfp4(const uint8_t* gate_codes, const uint8_t* gate_scales,
+                          const uint8_t* up_codes, const uint8_t* up_scales,
+                          int n_experts, int H, int I,
+                          uint8_t* gu_codes, uint8_t* gu_scales, moedec_stream_t stream);
+
+/* down: canonical [n_experts][H][I/2] codes, [n_experts][H][I/32] scales. */
+int moe_pack_down_mxfp4(const uint8_t* down_codes, const uint8_t* down_scales,
+                        int n_experts, int H, int I,
+                        uint8_t* dn_codes, uint8_t* dn_scales, moedec_stream_t stream);
+
+#define MOEDEC_MOE_MAGIC 0x4D4F4534u   /* "MOE4" */
+
+/* Packed weights of one MoE layer.  Routed expert e starts at e * (per-expert
+ * size) in each routed array; the shared expert has its own pointers. */
+typedef struct {
+    uint32_t magic;                    /* MOEDEC_MOE_MAGIC */
+    int32_t  E, H, I;
+    const uint8_t* gu_codes;           /* [E] packed gate/up codes (16-byte aligned) */
+    const uint8_t* gu_scales;          /* [E] packed gate/up scales (4-byte aligned) */
+    const uint8_t* dn_codes;           /* [E] packed down codes */
+    const uint8_t* dn_scales;          /* [E] packed down scales */
+    const uint8_t* sh_gu_codes;        /* shared expert, same per-expert layout */
+    const uint8_t* sh_gu_scales;
+    const uint8_t* sh_dn_codes;
+    const uint8_t* sh_dn_scales;
+} moedec_moe_weights;                  /* host struct (pointers inside are device) */
+
+/* ------------------------------------------------------------------------
+ * Routed + shared SwiGLU expert FFN.  [card #1: MXFP4 MoE kernel, expert
+ * intermediate 768; ic three scalpels: 512 routed + 1 shared expert]
+ *
+ * For each token m: y[m] = sum over slots s using m of
+ *     weight[s][m] * W_down[e] (silu(W_gate[e] x[m]) * (W_up[e] x[m]))
+ * (the shared slot has weight 1), E2M1 x E8M0 weights, bf16 x, float32
+ * accumulation, h kept in float32, y rounded once to bf16 (nearest even).
+ *
+ * w           host pointer to the layer's packed weights
+ * x_bf16      [M][H] bf16, 4-byte aligned
+ * dispatch    from moe_route_topk for the same M (and k <= k_max)
+ * k_max       the k used for routing (sizes the launch; 1..32)
+ * y_bf16      [M][H] bf16 output, 4-byte aligned
+ * y_f32       [M][H] float32 output or NULL
+ * workspace   >= moe_ffn_workspace_bytes(M, k_max, H, I) bytes, 16-byte
+ *             aligned, ZERO-FILLED ONCE before its first use; every call
+ *             leaves it ready for the next.  Calls sharing it must not overlap.
+ * Values outside the formats' domain (E8M0 code 0 or 255, NaN) give
+ * undefined results.
+ */
+size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I);
+
+int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, int M,
+                         const moedec_dispatch* dispatch, int k_max,
+                         uint16_t* y_bf16, float* y_f32,
+                         void* workspace, size_t workspace_bytes,
+                         moedec_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * LM head with online FP8 weights.  [news where the speed comes from; card
+ * #2: the 157,184 x 2,560 vocabulary projection is read whole for every
+ * token; a dynamic FP8 config applied when the head is built halves that
+ * read; the draft must share the whole head object, not the raw weight
+ * tensor, or FP8 bytes get read as bf16 -- hence the typed descriptor]
+ * ---------------------------------------------------------------------- */
+#define MOEDEC_LMHEAD_MAGIC 0x4C4D4838u         /* "LMH8" */
+#define MOEDEC_FMT_E4M3FN_ROWSCALE_F32 1u       /* OCP E4M3, one float32 scale per row */
+
+typedef struct {
+    uint32_t magic;                    /* MOEDEC_LMHEAD_MAGIC */
+    uint32_t format;                   /* MOEDEC_FMT_E4M3FN_ROWSCALE_F32 */
+    int32_t  V, H;
+    const uint8_t* codes;              /* [V][H] E4M3 codes, row-major, 16-byte aligned */
+    const float* row_scale;            /* [V] */
+} moedec_lmhead_fp8;                   /* host struct (pointers inside are device) */
+
+/*
+ * Quantise once: a_v = max|W[v,:]|, s_v = a_v / 448 (float32 division, 1 when
+ * a_v = 0), codes = E4M3 nearest-even, saturating to +-448, of W / s_v
+ * (float32 division).  w_bf16 [V][H] 16-byte aligned; codes [V][H] 16-byte
+ * aligned; row_scale [V].  out_desc (host, may be NULL) is filled to describe
+ * codes/row_scale.  1 <= V, 16 <= H <= 8192, H % 16 == 0.
+ */
+int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H,
+                     uint8_t* codes, float* row_scale,
+                     moedec_lmhead_fp8* out_desc, moedec_stream_t stream);
+
+/*
+ * logits[m][v] = s_v * sum_k x[m][k] * e4m3(codes[v][k]), float32 accumulation.
+ * head (host) must carry the LM-head magic and the E4M3 format tag, else
+ * MOEDEC_ERR_FORMAT.  x_bf16 [M][H] 4-byte aligned; logits [M][V] float32.
+ * 1 <= M <= 4, H % 16 == 0, H <= 4096.
+ */
+int lmhead_gemv_fp8(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M,
+                    float* logits, moedec_stream_t stream);
+
+/* Comparator: logits = W x with bf16 W [V][H] (16-byte aligned), float32
+ * accumulation.  1 <= M <= 4, H % 8 == 0, H <= 4096. */
+int lmhead_gemv_bf16(const uint16_t* w_bf16, int V, int H, const uint16_t* x_bf16, int M,
+                     float* logits, moedec_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEDEC_H */

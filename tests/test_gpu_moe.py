@@ -1,0 +1,252 @@
+"""GPU parity of routing, MXFP4 packing and the routed + shared expert FFN
+against the float64 oracle, through the C ABI (via the ctypes binding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (W_ATOL, bf16_tensor, bits_of, check_acc, check_bf16, dense_expert,
+                         oracle_layer, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_moe_expert_topk_amd as m
+    return m
+
+
+# ---------------------------------------------------------------- routing
+
+def _check_route(m, logits, k):
+    say("route", logits.shape, "k", k)
+    ids, w, disp = m.route_topk(torch.from_numpy(logits).cuda(), k)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.max(np.abs(w.cpu().numpy() - ref_w)) <= W_ATOL
+    d = m.decode_dispatch(disp)
+    experts, masks, weights = oracle.dispatch_table(ref_ids, ref_w, logits.shape[1])
+    assert d["n_slots"] == len(experts) and d["M"] == logits.shape[0]
+    np.testing.assert_array_equal(d["expert"], experts)
+    np.testing.assert_array_equal(d["token_mask"], masks)
+    assert np.max(np.abs(d["weight"][:, :logits.shape[0]] - weights)) <= W_ATOL
+    raw = d["raw"]
+    for s in range(d["n_slots"], m.MAX_SLOTS):          # unused entries are zero
+        assert raw.expert[s] == 0 and raw.token_mask[s] == 0
+    return ids, w, disp
+
+
+@pytest.mark.parametrize("name", ["tiny_m1", "ling_m1", "ling_m4"])
+def test_route_workloads(m, name):
+    wl = synth.WORKLOADS[name]
+    _, lg = synth.moe_inputs(wl)
+    _check_route(m, lg, wl.shape.k)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_route_ling_m4_seeds(m, seed):
+    _check_route(m, synth.logits_f32(seed, 7, 4, 512), 8)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_route_tie_heavy(m, seed):
+    rng = np.random.default_rng(100 + seed)
+    lg = rng.choice(np.float32([-1.0, 0.0, -0.0, 1.0, 0.5]), size=(4, 512))
+    for k in (1, 8, 32):
+        _check_route(m, lg, k)
+
+
+def test_route_all_equal_and_signed_zeros(m):
+    lg = np.zeros((4, 64), np.float32)
+    lg[1] = -0.0
+    lg[2, ::2] = -0.0
+    _check_route(m, lg, 16)
+
+
+@pytest.mark.parametrize("M,E,k", [(1, 1, 1), (2, 16, 16), (3, 100, 7), (4, 1024, 32), (4, 1000, 32),
+                                   (1, 65, 1), (4, 512, 1)])
+def test_route_shapes(m, M, E, k):
+    lg = synth.logits_f32(3, E, M, E) * np.float32(4.0)
+    _check_route(m, lg, k)
+
+
+# ---------------------------------------------------------------- packing
+
+def np_pack_gateup(gc, gs, uc, us):
+    n, I, hh = gc.shape
+    KB = 2 * hh // 32
+    KB4 = (KB + 3) // 4
+    codes = np.empty((n, I // 32, KB, 64, 16), np.uint8)
+    codes[:, :, :, :32] = gc.reshape(n, I // 32, 32, KB, 16).transpose(0, 1, 3, 2, 4)
+    codes[:, :, :, 32:] = uc.reshape(n, I // 32, 32, KB, 16).transpose(0, 1, 3, 2, 4)
+    scales = np.zeros((n, I // 32, KB4, 64, 4), np.uint8)
+    for half, src in ((0, gs), (1, us)):
+        pad = np.zeros((n, I, 4 * KB4), np.uint8)
+        pad[:, :, :KB] = src
+        scales[:, :, :, 32 * half:32 * half + 32] = pad.reshape(n, I // 32, 32, KB4, 4).transpose(0, 1, 3, 2, 4)
+    return codes.reshape(-1), scales.reshape(-1)
+
+
+def np_pack_down(dc, ds):
+    n, H, hi = dc.shape
+    KB = 2 * hi // 32
+    KB4 = (KB + 3) // 4
+    codes = dc.reshape(n, H // 64, 64, KB, 16).transpose(0, 1, 3, 2, 4)
+    pad = np.zeros((n, H, 4 * KB4), np.uint8)
+    pad[:, :, :KB] = ds
+    scales = pad.reshape(n, H // 64, 64, KB4, 4).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(codes).reshape(-1), np.ascontiguousarray(scales).reshape(-1)
+
+
+@pytest.mark.parametrize("H,I,E", [(256, 64, 4), (192, 96, 3), (2560, 768, 2)])
+def test_pack_is_the_documented_permutation(m, H, I, E):
+    say("pack", H, I, E)
+    shape = synth.MoEShape(H=H, I=I, E=E, k=1, scale_lo=110, scale_hi=140)
+    lay = synth.mxfp4_layer(5, 0, shape)
+    dev = {n: tuple(torch.from_numpy(a).cuda() for a in lay[n]) for n in lay}
+    gu_c, gu_s = m.pack_gateup(dev["gate"][0], dev["gate"][1], dev["up"][0], dev["up"][1])
+    dn_c, dn_s = m.pack_down(dev["down"][0], dev["down"][1])
+    torch.cuda.synchronize()
+    ec, es = np_pack_gateup(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1])
+    np.testing.assert_array_equal(gu_c.cpu().numpy(), ec)
+    np.testing.assert_array_equal(gu_s.cpu().numpy(), es)
+    dc, ds = np_pack_down(lay["down"][0], lay["down"][1])
+    np.testing.assert_array_equal(dn_c.cpu().numpy(), dc)
+    np.testing.assert_array_equal(dn_s.cpu().numpy(), ds)
+
+
+def test_device_generator_matches_host_twin(m):
+    import synth.device as sd
+    say("synth device twin")
+    shape = synth.LING
+    lay = sd.canonical_layer(0, 3, shape, "cuda", n_experts=shape.E + 1)
+    torch.cuda.synchronize()
+    for e in (0, 17, 511, 512):
+        host = synth.mxfp4_expert(0, 3, e, shape)
+        for name in ("gate", "up", "down"):
+            np.testing.assert_array_equal(lay[name][0][e].cpu().numpy(), host[name][0])
+            np.testing.assert_array_equal(lay[name][1][e].cpu().numpy(), host[name][1])
+
+
+# ---------------------------------------------------------------- FFN
+
+def _host_layer_case(m, shape, M, seed=0, layer=0, logits=None, x_bits=None, k=None):
+    k = shape.k if k is None else k
+    lay = synth.mxfp4_layer(seed, layer, shape)
+    dev = {n: tuple(torch.from_numpy(a).cuda() for a in lay[n]) for n in lay}
+    W = m.MoELayerWeights.from_canonical(dev["gate"], dev["up"], dev["down"], shape.E)
+    if x_bits is None:
+        x_bits = synth.activations_bf16(seed, layer, M, shape.H)
+    if logits is None:
+        logits = synth.router_logits_f32(seed, x_bits, shape.E)
+    dense = {e: dense_expert(lay, e) for e in range(shape.E + 1)}
+    return W, x_bits, logits, (lambda e: dense[e]), dense[shape.E], k
+
+
+def _run_ffn(m, W, x_bits, logits, k, ws=None):
+    x = bf16_tensor(x_bits)
+    ids, w, disp = m.route_topk(torch.from_numpy(logits).cuda(), k)
+    if ws is None:
+        ws = m.make_ffn_workspace(x.shape[0], k, W.H, W.I, "cuda")
+    y, y32 = m.expert_ffn(W, x, disp, k, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), bits_of(y), y32.cpu().numpy(), disp
+
+
+def _check_case(m, W, x_bits, logits, k, expert_fn, shared, what):
+    say(what)
+    ids, yb, y32, _ = _run_ffn(m, W, x_bits, logits, k)
+    ref_ids, _, ref_y = oracle_layer(x_bits, logits, k, expert_fn, shared)
+    np.testing.assert_array_equal(ids, ref_ids)
+    check_acc(y32, ref_y, what)
+    check_bf16(yb, y32, ref_y, what)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_ffn_tiny(m, M):
+    W, xb, lg, ef, sh, k = _host_layer_case(m, synth.TINY, M)
+    _check_case(m, W, xb, lg, k, ef, sh, f"tiny M={M}")
+
+
+def test_ffn_tiny_k_equals_e(m):
+    W, xb, lg, ef, sh, _ = _host_layer_case(m, synth.TINY, 4)
+    _check_case(m, W, xb, lg, synth.TINY.E, ef, sh, "tiny M=4 k=E")
+
+
+def test_ffn_tiny_k1(m):
+    W, xb, lg, ef, sh, _ = _host_layer_case(m, synth.TINY, 3)
+    _check_case(m, W, xb, lg, 1, ef, sh, "tiny M=3 k=1")
+
+
+@pytest.mark.parametrize("H,I,E,k,M", [(192, 96, 8, 3, 2), (320, 160, 5, 2, 4), (64, 32, 3, 3, 1)])
+def test_ffn_ragged_block_counts(m, H, I, E, k, M):
+    """Block counts that are not multiples of 4 exercise the scale padding."""
+    shape = synth.MoEShape(H=H, I=I, E=E, k=k, scale_lo=119, scale_hi=123)
+    W, xb, lg, ef, sh, k = _host_layer_case(m, shape, M, seed=2)
+    _check_case(m, W, xb, lg, k, ef, sh, f"ragged H={H} I={I} E={E} k={k} M={M}")
+
+
+def test_ffn_zero_input_is_exact_zero(m):
+    W, _, lg, _, _, k = _host_layer_case(m, synth.TINY, 2)
+    xb = np.zeros((2, synth.TINY.H), np.uint16)
+    _, yb, y32, _ = _run_ffn(m, W, xb, lg, k)
+    assert (y32 == 0).all() and (yb == 0).all()
+
+
+def test_ffn_workspace_reuse_is_deterministic(m):
+    """Back-to-back calls on one workspace (the tickets reset themselves),
+    with a different M in between, give bit-identical results."""
+    say("workspace reuse")
+    W, xb, lg, ef, sh, k = _host_layer_case(m, synth.TINY, 4)
+    ws = m.make_ffn_workspace(4, k, W.H, W.I, "cuda")
+    a = _run_ffn(m, W, xb, lg, k, ws)
+    _run_ffn(m, W, xb[:1], lg[:1], k, ws)
+    b = _run_ffn(m, W, xb, lg, k, ws)
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(a[2], b[2])
+
+
+@pytest.fixture(scope="module")
+def ling_layer(m):
+    import synth.device as sd
+    say("generate Ling layer on device")
+    lay = sd.canonical_layer(0, 0, synth.LING, "cuda")
+    W = m.MoELayerWeights.from_canonical(lay["gate"], lay["up"], lay["down"], synth.LING.E)
+    torch.cuda.synchronize()
+    del lay
+    return W
+
+
+def _ling_expert(e, cache={}):
+    if e not in cache:
+        cache[e] = dense_expert({n: (c[None], s[None]) for n, (c, s) in
+                                 synth.mxfp4_expert(0, 0, e, synth.LING).items()}, 0)
+    return cache[e]
+
+
+@pytest.mark.parametrize("name", ["ling_m1", "ling_m4"])
+def test_ffn_ling(m, ling_layer, name):
+    wl = synth.WORKLOADS[name]
+    xb, lg = synth.moe_inputs(wl)
+    _check_case(m, ling_layer, xb, lg, 8, _ling_expert, _ling_expert(synth.LING.E), name)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_ffn_ling_m4_more_seeds(m, ling_layer, seed):
+    xb = synth.activations_bf16(seed, 0, 4, synth.LING.H)
+    lg = synth.logits_f32(seed, 0, 4, synth.LING.E)
+    _check_case(m, ling_layer, xb, lg, 8, _ling_expert, _ling_expert(synth.LING.E), f"ling M=4 seed {seed}")
+
+
+def test_ffn_ling_shared_tokens_overlap(m, ling_layer):
+    """Four tokens routed to the same 8 experts: each expert serves all four."""
+    xb = synth.activations_bf16(9, 0, 4, synth.LING.H)
+    lg = np.repeat(synth.logits_f32(9, 0, 1, synth.LING.E), 4, axis=0)
+    lg[1:, :] += np.float32(0.0)
+    _check_case(m, ling_layer, xb, lg, 8, _ling_expert, _ling_expert(synth.LING.E), "ling M=4 same experts")
