@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of libmoedec on one MI355X: batch-1 MoE decode and the FP8 LM head.
 
-One step is one Ling-shaped MoE layer at M = 1: moe_route_topk (top-8 of 512,
-softmax renormalised over the 8) then moe_expert_ffn_mxfp4 (8 routed + 1 shared
-SwiGLU experts, MXFP4 weights, bf16 activations).  The steps cycle through
+One step is one Ling-shaped MoE layer at M = 1: top-8-of-512 routing (softmax
+renormalised over the 8) and the 8 routed + 1 shared SwiGLU experts (MXFP4
+weights, bf16 activations), run by moe_layer_mxfp4 as one kernel launch.  The steps cycle through
 --layers distinct layers, each with its own 513 experts resident in HBM
 (42 layers = 67.5 GB), so the 256 MB Infinity Cache cannot serve a repeated
 expert.  Steps are captured into one HIP graph and replayed; HIP events on the
@@ -11,7 +11,8 @@ replay stream time exactly K steps.
 
 Reported next to the headline (M = 1) figure, each measured the same way:
   * the same layers in the 4-token verify window (M = 4);
-  * the FFN call alone (the dominant kernel), for the roofline entry;
+  * the two-call path (moe_route_topk, then moe_expert_ffn_mxfp4), and the
+    FFN call alone on precomputed dispatch tables;
   * the LM head 157,184 x 2,560: one-off FP8 quantisation, FP8 GEMV at M = 1
     and 4, and the bf16 GEMV comparator;
   * the CPU oracle on a bounded sample of the same layers (cpu_baseline).
@@ -119,6 +120,9 @@ def capture(torch, fn):
 # MoE layer measurements
 
 def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
+    """Time K layer steps three ways: the fused layer call (routing + FFN in
+    one launch; the headline), the two-call path (moe_route_topk then
+    moe_expert_ffn_mxfp4) and the FFN call alone on precomputed tables."""
     n_layers = len(layers)
     shape = synth.LING
     k = shape.k
@@ -129,7 +133,11 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
     ys = [torch.empty((M, shape.H), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
     ws = m.make_ffn_workspace(M, k, shape.H, shape.I, dev)
 
-    def layer_step(i):
+    def fused_step(i):
+        L = i % n_layers
+        m.moe_layer(layers[L], xs[L], lgs[L], k, ws, y=ys[L], want_f32=False)
+
+    def two_call_step(i):
         L = i % n_layers
         m.route_topk(lgs[L], k, ids=ids, weights=wts, dispatch=disp[L])
         m.expert_ffn(layers[L], xs[L], disp[L], k, ws, y=ys[L], want_f32=False)
@@ -138,9 +146,10 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
         L = i % n_layers
         m.expert_ffn(layers[L], xs[L], disp[L], k, ws, y=ys[L], want_f32=False)
 
-    # one eager pass: fills every layer's dispatch table, checks the calls work
+    # one eager pass of each path: fills every layer's dispatch table, checks the calls work
     for i in range(n_layers):
-        layer_step(i)
+        two_call_step(i)
+        fused_step(i)
     torch.cuda.synchronize()
     n_slots = [m.decode_dispatch(d)["n_slots"] for d in disp]
     act_bytes = M * shape.E * 4 + 2 * M * shape.H * 2          # logits + x + y (bf16)
@@ -149,16 +158,19 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
     step_bytes = sum(bytes_per_layer[i % n_layers] for i in range(steps)) / steps
 
     t = Timer(torch)
-    g_warm = capture(torch, lambda: [layer_step(i) for i in range(warmup)]) if warmup else None
-    g_main = capture(torch, lambda: [layer_step(i) for i in range(steps)])
+    g_warm = capture(torch, lambda: [fused_step(i) for i in range(warmup)]) if warmup else None
+    g_main = capture(torch, lambda: [fused_step(i) for i in range(steps)])
+    g_two = capture(torch, lambda: [two_call_step(i) for i in range(steps)])
     g_ffn = capture(torch, lambda: [ffn_only(i) for i in range(steps)])
     if g_warm is not None:
         g_warm.replay()
+    g_two.replay()
     g_ffn.replay()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ms = t.run(g_main.replay)
     wall1 = time.perf_counter()
+    ms_two = t.run(g_two.replay)
     ms_ffn = t.run(g_ffn.replay)
     ffn_bytes = step_bytes - M * shape.E * 4                   # no logits read
     res = {
@@ -170,6 +182,8 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
         "us_per_layer": 1e3 * ms / steps,
         "bytes_per_layer": step_bytes,
         "gbs": step_bytes / (1e6 * ms / steps),
+        "two_call_us_per_layer": 1e3 * ms_two / steps,
+        "two_call_gbs": step_bytes / (1e6 * ms_two / steps),
         "ffn_us": 1e3 * ms_ffn / steps,
         "ffn_bytes": ffn_bytes,
         "ffn_gbs": ffn_bytes / (1e6 * ms_ffn / steps),
@@ -177,8 +191,9 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
         "max_active_experts": max(s - 1 for s in n_slots),
     }
     res["frac_of_peak"] = res["gbs"] / PEAK_HBM_GBS
+    res["two_call_frac_of_peak"] = res["two_call_gbs"] / PEAK_HBM_GBS
     res["ffn_frac_of_peak"] = res["ffn_gbs"] / PEAK_HBM_GBS
-    del g_warm, g_main, g_ffn
+    del g_warm, g_main, g_two, g_ffn
     return res
 
 
@@ -335,7 +350,6 @@ def main(argv=None):
         cpu = cpu_baseline(synth, args.cpu_layers)
         log("cpu:", json.dumps(cpu))
 
-    ffn_achieved = r1["ffn_gbs"]
     line = {
         "metric": "µs/MoE layer + achieved HBM GB/s (% of peak) at M=1 and M=4; LM-head GEMV GB/s",
         "value": round(r1["gbs"], 1),
@@ -360,14 +374,14 @@ def main(argv=None):
         "frac_of_peak_m1": round(r1["frac_of_peak"], 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "moe_expert_ffn_mxfp4 (M=1)",
-            "achieved": round(ffn_achieved, 1),
+            "kernel": "moe_ffn_kernel (moe_layer_mxfp4: routing + routed/shared MXFP4 SwiGLU FFN, M=1)",
+            "achieved": round(r1["gbs"], 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(ffn_achieved / PEAK_HBM_GBS, 4),
+            "frac": round(r1["gbs"] / PEAK_HBM_GBS, 4),
             "traffic": None,
-            "bytes_per_launch": r1["ffn_bytes"],
-            "avg_launch_us": round(r1["ffn_us"], 3),
+            "bytes_per_launch": r1["bytes_per_layer"],
+            "avg_launch_us": round(r1["us_per_layer"], 3),
         },
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "extra": {"m1": r1, "m4": r4, "lmhead": lm,

@@ -197,6 +197,31 @@ def expert_ffn(weights, x, dispatch, k_max, workspace, y=None, y_f32=None, want_
     return y, y_f32
 
 
+def moe_layer(weights, x, logits, k, workspace, y=None, y_f32=None, want_f32=True,
+              ids=None, topk_w=None, dispatch=None):
+    """Routing and expert FFN in one launch.  x: [M][H] bfloat16, logits [M][E]
+    float32.  Returns (y bf16, y_f32 or None); ids / topk_w / dispatch are
+    filled when given (device tensors as route_topk returns them)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(logits, torch.float32, "logits", 2)
+    _need(workspace, torch.uint8, "workspace", 1)
+    m_tokens, hidden = x.shape
+    if logits.shape[0] != m_tokens or logits.shape[1] != weights.E:
+        raise ValueError(f"logits must be [{m_tokens}][{weights.E}], got {tuple(logits.shape)}")
+    for t, dt, n in ((ids, torch.int32, "ids"), (topk_w, torch.float32, "topk_w"),
+                     (dispatch, torch.uint8, "dispatch")):
+        if t is not None:
+            _need(t, dt, n)
+    if y is None:
+        y = torch.empty((m_tokens, hidden), dtype=torch.bfloat16, device=x.device)
+    if y_f32 is None and want_f32:
+        y_f32 = torch.empty((m_tokens, hidden), dtype=torch.float32, device=x.device)
+    _check(lib.moe_layer_mxfp4(ctypes.byref(weights.desc), _ptr(x), _ptr(logits), m_tokens, k,
+                               _ptr(ids), _ptr(topk_w), _ptr(dispatch), _ptr(y), _ptr(y_f32),
+                               _ptr(workspace), workspace.numel(), _stream(x)))
+    return y, y_f32
+
+
 # --------------------------------------------------------------------------
 # LM head
 

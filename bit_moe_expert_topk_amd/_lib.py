@@ -81,6 +81,8 @@ SIGNATURES = {
     "moe_ffn_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
     "moe_expert_ffn_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_int, c_void_p, c_int,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_layer_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "lmhead_quant_fp8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p,
                                  ctypes.POINTER(LMHeadFP8Desc), c_void_p]),
     "lmhead_gemv_fp8": (c_int, [ctypes.POINTER(LMHeadFP8Desc), c_void_p, c_int, c_void_p, c_void_p]),

@@ -26,34 +26,89 @@ __device__ __forceinline__ u32x4 load_stream16(const uint8_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+// Cross-lane exchange without LDS.  DPP row_ror:n rotates within each 16-lane
+// row; gfx950's permlane16/32 swaps exchange rows 0<->1, 2<->3 and the two
+// 32-lane halves.  Reductions below leave the result in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// {value of lane l, value of lane l ^ 16} in some order (same pair in both lanes)
+__device__ __forceinline__ u32x2 swap16(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return u32x2{r[0], r[1]};
+}
+__device__ __forceinline__ u32x2 swap32(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return u32x2{r[0], r[1]};
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += __uint_as_float(dpp_u32<kRowRor1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kRowRor2>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kRowRor4>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kRowRor8>(__float_as_uint(v)));
+    u32x2 p = swap16(__float_as_uint(v));
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    p = swap32(__float_as_uint(v));
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
+
+// Sum of the four lanes l, l^16, l^32, l^48 (one per 16-lane row), in every lane.
+__device__ __forceinline__ float row_sum_f32(float v) {
+    u32x2 p = swap16(__float_as_uint(v));
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    p = swap32(__float_as_uint(v));
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Kept for the LM-head kernels: plain wave sum in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return wave_sum_f32(v); }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+    uint32_t o;
+    o = dpp_u32<kRowRor1>(v); v = o > v ? o : v;
+    o = dpp_u32<kRowRor2>(v); v = o > v ? o : v;
+    o = dpp_u32<kRowRor4>(v); v = o > v ? o : v;
+    o = dpp_u32<kRowRor8>(v); v = o > v ? o : v;
+    u32x2 p = swap16(v); v = p[0] > p[1] ? p[0] : p[1];
+    p = swap32(v);
+    return p[0] > p[1] ? p[0] : p[1];
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    uint32_t o;
+    o = dpp_u32<kRowRor1>(v); v = o < v ? o : v;
+    o = dpp_u32<kRowRor2>(v); v = o < v ? o : v;
+    o = dpp_u32<kRowRor4>(v); v = o < v ? o : v;
+    o = dpp_u32<kRowRor8>(v); v = o < v ? o : v;
+    u32x2 p = swap16(v); v = p[0] < p[1] ? p[0] : p[1];
+    p = swap32(v);
+    return p[0] < p[1] ? p[0] : p[1];
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = dpp_u32<CTRL>((uint32_t)v), hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off, 64);
-        uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off, 64);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
+    v = max_u64(v, dpp_u64<kRowRor1>(v));
+    v = max_u64(v, dpp_u64<kRowRor2>(v));
+    v = max_u64(v, dpp_u64<kRowRor4>(v));
+    v = max_u64(v, dpp_u64<kRowRor8>(v));
+    {
+        const u32x2 lo = swap16((uint32_t)v), hi = swap16((uint32_t)(v >> 32));
+        v = max_u64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
+    }
+    {
+        const u32x2 lo = swap32((uint32_t)v), hi = swap32((uint32_t)(v >> 32));
+        v = max_u64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
     }
     return v;
 }

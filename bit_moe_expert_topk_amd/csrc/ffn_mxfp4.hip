@@ -1,339 +1,923 @@
-// Routed + shared SwiGLU expert FFN on packed MXFP4 weights, M = 1..4 tokens.
+// Routed + shared SwiGLU expert FFN on packed MXFP4 weights, M = 1..4 tokens,
+// in one kernel launch -- optionally with the top-k routing fused in front.
 //
 // The pages' premise: at batch 1 decode is bound by reading weights, the MoE
 // experts being the largest share, and their MXFP4 kernel is what lifted
 // throughput first (knowledge card at ai.cheesepanini.fun, background and
 // method point #1; news article yoususu.cn/post/959, "where the speed comes
 // from").  A verify window of 4 tokens touches up to 32 experts (card, method
-// point #3): the dispatch table lists each active expert once with its token
-// mask, so each expert's bytes are streamed once for all tokens using it.
+// point #3): each active expert's bytes are streamed once for all the tokens
+// that use it.
 //
-// Kernel 1 (gate/up): one block per (slot, group of 32 intermediate rows).
-//   Lane l of every wave owns one row -- gate row 32r+l for l < 32, up row
-//   32r+l-32 for l >= 32 -- and walks its MX blocks; the 4 waves split the
-//   blocks.  Weights arrive as one coalesced 1 KiB chunk per wave step; two
-//   E2M1 codes become a scaled bf16 pair in one gfx950 conversion, and
-//   v_dot2 accumulates pair products with the activation pair, which is the
-//   same for all lanes and so comes from scalar registers.  Products are
-//   exact (E2M1 x 2^k x bf16 fits in float32), accumulation is float32.  The
-//   gate and up sums meet across lanes l and l+32; h = silu(g) * u stays float32.
-// Kernel 2 (down + combine): one block per (slot, group of 64 output rows);
-//   lane owns an output row, waves split the blocks of I, h comes from scalar
-//   loads.  Each block writes its weighted partial row-group; the last block
-//   to finish a row-group (atomic ticket) sums the slots' partials in slot
-//   order -- deterministic -- writes y in float32 and rounds it once to bf16.
+// Grid.  A persistent grid of three blocks per CU, small enough that every
+// block is resident at once, walks the work units round-robin
+// (unit = blockIdx.x + i * gridDim.x).  Unit order is: gate/up units, then the
+// down units of slot groups 1.., then those of group 0.  Every block therefore
+// finishes all its gate/up units before it can wait for anything, and all its
+// other down units before it waits as a combiner, so no wait can close a cycle.
+//
+// Prologue (every block).  The block builds an LDS table of the layer's slots:
+// slot 0 is the shared expert (weight 1, every token), slots 1.. the distinct
+// routed experts in ascending id, each with its token mask and per-token
+// weights -- read from a moe_route_topk dispatch table, or computed right here
+// from the router logits (one wave per token).  (slot, token) pairs are
+// counted in slot order and cut into groups of at most pair_cap pairs so that
+// a group's h fits in LDS.
+//
+// Units.
+//   * gate/up (slot s, rg): h = silu(W_gate x) * (W_up x) for the 16
+//     intermediate rows 16rg..16rg+15 of the slot's expert, full K = H, every
+//     token the slot serves; each h value is published as one 64-bit word
+//     (launch generation, value).
+//   * down (group, g): for output rows 16g..16g+15, the sum over the group's
+//     slots of W_down[e] (w * h).  It issues its weight loads, then loads the
+//     group's tagged h words -- re-reading while any tag is stale -- stages
+//     w * h in LDS and finishes.  With one group it writes y; otherwise groups
+//     >= 1 publish tagged partial rows and the group-0 unit adds them in group
+//     order and writes y (deterministic).
+// Synchronisation uses no atomic read-modify-writes, no flags and no cache
+// flushes.  Data crossing CUs (h, partial rows) is written as 64-bit words
+// holding the value and the launch generation, with device-coherent stores
+// (single-copy atomic, through to the level all CUs share), and read with
+// device-coherent loads: a reader knows a word is from this launch when its
+// tag matches.  Each block keeps the generation in its own workspace word;
+// all blocks of every launch on a workspace see the same count, since the
+// grid size is fixed per device, so nothing needs resetting between calls.
+//
+// Lanes.  A 64-lane wave reads one 1 KiB chunk per load step: lane l holds the
+// 16 code bytes (32 E2M1 values, one MX block) of row 16u + (l & 15) and MX
+// block 4c + (l >> 4), so the four 16-lane rows of the wave cover four
+// consecutive MX blocks of the same 16 rows.  Gate/up chunks come in pairs
+// (gate rows, then the same up rows) sharing the activations.  Two codes
+// become a scaled bf16 (gate/up) or float32 (down) pair in one gfx950
+// conversion; bf16 x E2M1 x 2^k products are exact in float32 and every sum
+// is float32.  Activations are read from LDS, each 16-lane row broadcasting
+// its own MX block; LDS rows are padded so the four rows hit different banks.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
+#include "route_device.h"
 
 namespace moedec {
 
 namespace {
 
-struct GateUpArgs {
-    const uint8_t* codes;
-    const uint8_t* scales;
-    const uint8_t* sh_codes;
-    const uint8_t* sh_scales;
-    size_t codes_stride, scales_stride;   // bytes per routed expert
-    int E, H, I, KB, KB4, M;
-    const uint32_t* x;                    // [M][H/2] bf16 pairs
-    const moedec_dispatch* disp;
-    float* h;                             // [max_slots][M][I]
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kUnitRows = 16;
+constexpr int kXBlock = 80;          // LDS bytes per 32-value block of x (64 + 16 pad)
+constexpr int kHBlock = 144;         // LDS bytes per 32-value block of h (128 + 16 pad)
+constexpr int kDnBatch = 8;          // down chunks per load batch (two batches in flight)
+constexpr int kStageBatch = 8;       // float4 loads of h in flight per thread while staging
+constexpr int kMaxGroups = MOEDEC_MAX_M * MOEDEC_MAX_K + MOEDEC_MAX_M;
+constexpr int kMaxPairs = kMaxGroups + MOEDEC_MAX_M;
+constexpr int kMaxGrid = 4096;
+constexpr int kBlocksPerCU = 3;
+constexpr uint32_t kSpinLimit = 1u << 20;   // bounded waits; reached only if co-residency fails
+
+struct FfnArgs {
+    const uint8_t* gu_codes;
+    const uint8_t* gu_scales;
+    const uint8_t* dn_codes;
+    const uint8_t* dn_scales;
+    const uint8_t* sh_gu_codes;
+    const uint8_t* sh_gu_scales;
+    const uint8_t* sh_dn_codes;
+    const uint8_t* sh_dn_scales;
+    size_t gu_codes_stride, gu_scales_stride, dn_codes_stride, dn_scales_stride;
+    int E, H, I, k;
+    int kbh, kbh4, kbi, kbi4;        // MX blocks along H / I and groups of four
+    int gu_units;                    // I / 16
+    int dn_units;                    // H / 16
+    int max_slots, max_groups, pair_cap;
+    int n_gu, n_units;
+    int pair_bytes, red_off;         // LDS layout
+    const uint16_t* x;               // [M][H] bf16
+    const moedec_dispatch* disp;     // slots from moe_route_topk, or
+    const float* logits;             // [M][E]: route here
+    int32_t* ids_out;                // routing outputs of the fused path (block 0), nullable
+    float* w_out;
+    moedec_dispatch* disp_out;
+    uint32_t* gens;                  // [kMaxGrid] per-block launch counters
+    uint32_t* err;                   // set when a wait gave up
+    uint64_t* h;                     // [max_slots][M][I] tagged words (generation << 32 | float)
+    uint64_t* part;                  // [max_groups][M][H] tagged partial rows
+    int h_bytes;                     // size of h (device-coherent buffer loads)
+    uint16_t* y_bf16;                // [M][H]
+    float* y_f32;                    // [M][H] or null
 };
 
-struct DownArgs {
-    const uint8_t* codes;
-    const uint8_t* scales;
-    const uint8_t* sh_codes;
-    const uint8_t* sh_scales;
-    size_t codes_stride, scales_stride;
-    int E, H, I, KB, KB4, M, max_slots;
-    const float* h;                       // [max_slots][M][I]
-    const moedec_dispatch* disp;
-    float* part;                          // [H/64][max_slots][M][64]
-    uint32_t* tickets;                    // [H/64]
-    uint16_t* y_bf16;                     // [M][H]
-    float* y_f32;                         // [M][H] or null
+struct SlotTable {
+    int n_slots, n_groups;
+    int32_t expert[MOEDEC_MAX_SLOTS];            // E = shared expert, -1 = unusable entry
+    uint32_t mask[MOEDEC_MAX_SLOTS];
+    float weight[MOEDEC_MAX_SLOTS][MOEDEC_MAX_M];
+    int start[MOEDEC_MAX_SLOTS + 1];             // first (slot, token) pair of each slot
+    int gfirst[kMaxGroups + 1];                  // first slot of each group
+    int pair[kMaxPairs];                         // current down unit: pair -> slot << 8 | token
 };
 
-constexpr int kWavesPerBlock = 4;
-constexpr int kGroupsInFlight = 5;  // scale words (4 MX blocks each) preloaded per wave
+struct RouteScratch {                            // lives in the dynamic LDS during the prologue
+    int32_t id[MOEDEC_MAX_M][MOEDEC_MAX_K];
+    float w[MOEDEC_MAX_M][MOEDEC_MAX_K];
+    uint32_t bits[MOEDEC_MAX_E / 32];
+    int pre[MOEDEC_MAX_E / 32 + 1];
+    int32_t expert[MOEDEC_MAX_SLOTS];
+    uint32_t mask[MOEDEC_MAX_SLOTS];
+    float weight[MOEDEC_MAX_SLOTS][MOEDEC_MAX_M];
+};
+
+// Device-coherent ("sc1") stores and loads: they bypass the per-XCD L2 so that
+// data written by one CU is seen by every other without flushing caches.
+__device__ __forceinline__ void store_tagged(uint64_t* p, uint32_t gen, float v) {
+    __hip_atomic_store(p, ((uint64_t)gen << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_tagged(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kBufferRsrcWord3 = 0x00020000;    // raw 32-bit buffer, gfx9 family
+constexpr int kLoadCoherent = 16;               // cache-policy bit sc1
+
+
+__device__ __forceinline__ bf16x2 fp4x2_bf16(uint32_t word, float s, int sel) {
+    switch (sel) {
+        case 0: return MOEDEC_FP4X2_BF16(word, s, 0);
+        case 1: return MOEDEC_FP4X2_BF16(word, s, 1);
+        case 2: return MOEDEC_FP4X2_BF16(word, s, 2);
+        default: return MOEDEC_FP4X2_BF16(word, s, 3);
+    }
+}
+
+__device__ __forceinline__ f32x2 fp4x2_f32(uint32_t word, float s, int sel) {
+    switch (sel) {
+        case 0: return MOEDEC_FP4X2_F32(word, s, 0);
+        case 1: return MOEDEC_FP4X2_F32(word, s, 1);
+        case 2: return MOEDEC_FP4X2_F32(word, s, 2);
+        default: return MOEDEC_FP4X2_F32(word, s, 3);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prologue: the slot table
 
 template <int M_T>
-__global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
-    const int slot = blockIdx.y;
-    const moedec_dispatch* __restrict__ disp = a.disp;
-    if (slot >= disp->n_slots) return;
-    const int e = disp->expert[slot];
-    if (e < 0 || e > a.E) return;          // not a table from moe_route_topk
-    const uint32_t mask = disp->token_mask[slot];
-    const int r = blockIdx.x;
-    const uint8_t* cb = (e == a.E ? a.sh_codes : a.codes + (size_t)e * a.codes_stride) +
-                        (size_t)r * a.KB * 1024;
-    const uint8_t* sb = (e == a.E ? a.sh_scales : a.scales + (size_t)e * a.scales_stride) +
-                        (size_t)r * a.KB4 * 256;
-    const int w = wave_id_uniform();
+__device__ void table_from_dispatch(const FfnArgs& a, SlotTable& T) {
+    if (wave_id_uniform() != 0) return;
     const int lane = lane_id();
-    const uint32_t* __restrict__ x = a.x;
-    const int xrow = a.H / 2;
-
-    float acc[M_T];
+    const moedec_dispatch* __restrict__ d = a.disp;
+    const uint32_t full = (1u << M_T) - 1u;
+    const int n_tab = max(1, min(d->n_slots, a.max_slots));
+    for (int s = lane; s < n_tab; s += kWave) {
+        const int tab = (s == 0) ? n_tab - 1 : s - 1;   // the table lists the shared expert last
+        int e = d->expert[tab];
+        uint32_t msk = d->token_mask[tab] & full;
+        float wt[M_T];
 #pragma unroll
-    for (int m = 0; m < M_T; ++m) acc[m] = 0.f;
-
-    for (int p0 = w; p0 < a.KB4; p0 += kWavesPerBlock * kGroupsInFlight) {
-        u32x4 c[kGroupsInFlight][4];
-        uint32_t sc[kGroupsInFlight];
-#pragma unroll
-        for (int gi = 0; gi < kGroupsInFlight; ++gi) {
-            const int p = p0 + kWavesPerBlock * gi;
-            if (p < a.KB4) {
-                sc[gi] = *reinterpret_cast<const uint32_t*>(sb + (size_t)p * 256 + lane * 4);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int q = 4 * p + b;
-                    if (q < a.KB) c[gi][b] = load_stream16(cb + (size_t)q * 1024 + lane * 16);
-                }
-            }
+        for (int m = 0; m < M_T; ++m) wt[m] = d->weight[tab][m];
+        if (s == 0) {
+            e = a.E;
+            msk = full;
+        } else if (e < 0 || e >= a.E || msk == 0u) {
+            e = -1;
+            msk = 0u;
         }
+        T.expert[s] = e;
+        T.mask[s] = msk;
 #pragma unroll
-        for (int gi = 0; gi < kGroupsInFlight; ++gi) {
-            const int p = p0 + kWavesPerBlock * gi;
-            if (p >= a.KB4) break;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int q = 4 * p + b;
-                if (q >= a.KB) break;
-                const float s = e8m0_to_f32((sc[gi] >> (8 * b)) & 0xFFu);
-                bf16x2 wp[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const uint32_t word = c[gi][b][j >> 2];
-                    switch (j & 3) {
-                        case 0: wp[j] = MOEDEC_FP4X2_BF16(word, s, 0); break;
-                        case 1: wp[j] = MOEDEC_FP4X2_BF16(word, s, 1); break;
-                        case 2: wp[j] = MOEDEC_FP4X2_BF16(word, s, 2); break;
-                        default: wp[j] = MOEDEC_FP4X2_BF16(word, s, 3); break;
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < M_T; ++m) {
-                    if (!((mask >> m) & 1u)) continue;
-                    const uint32_t* xq = x + (size_t)m * xrow + q * 16;
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) acc[m] = dot2_bf16(wp[j], as_bf16x2(xq[j]), acc[m]);
-                }
-            }
-        }
+        for (int m = 0; m < M_T; ++m) T.weight[s][m] = wt[m];
     }
+    if (lane == 0) T.n_slots = n_tab;
+}
 
-    __shared__ float red[kWavesPerBlock][M_T][64];
+// One token (M = 1): wave 0 builds the whole table from its top-k -- slot
+// 1 + rank(id) for each chosen expert, one (slot, token) pair per slot, and
+// the group bounds -- and block 0 writes the routing outputs from registers.
+__device__ void table_from_logits_one(const FfnArgs& a, SlotTable& T, uint64_t* buf) {
+    if (wave_id_uniform() != 0) return;
+    const int lane = lane_id();
+    const int k = a.k;
+    float wv;
+    const uint64_t key = (a.E <= 512) ? wave_topk<8>(a.logits, a.E, k, wv, buf)
+                                      : wave_topk<16>(a.logits, a.E, k, wv, buf);
+    const int id = key_to_index(key);
+    const int rank = wave_rank_ids(lane < k ? id : 0x7FFFFFFF, k);
+    const int n = k + 1;
+    if (lane < k) {
+        T.expert[1 + rank] = id;
+        T.mask[1 + rank] = 1u;
+        T.weight[1 + rank][0] = wv;
+        T.start[1 + rank] = 1 + rank;
+    }
+    const int ng = min((n - 1) / a.pair_cap + 1, a.max_groups);
+    if (lane == 0) {
+        T.expert[0] = a.E;
+        T.mask[0] = 1u;
+        T.weight[0][0] = 1.f;
+        T.start[0] = 0;
+        T.start[n] = n;
+        T.n_slots = n;
+        T.n_groups = ng;
+    }
+    for (int g = lane; g <= ng; g += kWave) T.gfirst[g] = min(g * a.pair_cap, n);
+    if (blockIdx.x == 0) {                      // the routing outputs, as moe_route_topk writes them
+        if (lane < k) {
+            if (a.ids_out) a.ids_out[lane] = id;
+            if (a.w_out) a.w_out[lane] = wv;
+        }
+        if (a.disp_out) {
+            moedec_dispatch* __restrict__ o = a.disp_out;
+            if (lane < k) {
+                o->expert[rank] = id;
+                o->token_mask[rank] = 1u;
+                o->weight[rank][0] = wv;
 #pragma unroll
-    for (int m = 0; m < M_T; ++m) red[w][m][lane] = acc[m];
-    __syncthreads();
-    if (w == 0) {
+                for (int m = 1; m < MOEDEC_MAX_M; ++m) o->weight[rank][m] = 0.f;
+            }
+            for (int i = k + lane; i < MOEDEC_MAX_SLOTS; i += kWave) {
+                const bool shared = i == k;
+                o->expert[i] = shared ? a.E : 0;
+                o->token_mask[i] = shared ? 1u : 0u;
 #pragma unroll
-        for (int m = 0; m < M_T; ++m) {
-            float t = red[0][m][lane];
-#pragma unroll
-            for (int v = 1; v < kWavesPerBlock; ++v) t += red[v][m][lane];
-            const float other = __shfl_xor(t, 32, 64);   // up for gate lanes
-            if (lane < 32 && ((mask >> m) & 1u)) {
-                const float g = t, u = other;
-                const float hv = g / (1.f + expf(-g)) * u;
-                a.h[((size_t)slot * a.M + m) * a.I + 32 * r + lane] = hv;
+                for (int m = 0; m < MOEDEC_MAX_M; ++m) o->weight[i][m] = (shared && m == 0) ? 1.f : 0.f;
+            }
+            if (lane == 0) {
+                o->n_slots = n;
+                o->M = 1;
             }
         }
     }
 }
 
+// Several tokens: one wave per token selects its experts, the block groups
+// the choices by expert (the pair counts and groups follow in table_groups).
 template <int M_T>
-__global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
-    const int slot = blockIdx.y;
-    const moedec_dispatch* __restrict__ disp = a.disp;
-    // every slot below n_slots must arrive at the ticket exactly once
-    const int n_slots = min(disp->n_slots, a.max_slots);
-    if (slot >= n_slots) return;
-    const int e_raw = disp->expert[slot];
-    const bool valid = e_raw >= 0 && e_raw <= a.E;
-    const int e = valid ? e_raw : a.E;
-    const uint32_t mask = valid ? disp->token_mask[slot] : 0u;   // no work, still arrives
-    const int g = blockIdx.x;
-    const uint8_t* cb = (e == a.E ? a.sh_codes : a.codes + (size_t)e * a.codes_stride) +
-                        (size_t)g * a.KB * 1024;
-    const uint8_t* sb = (e == a.E ? a.sh_scales : a.scales + (size_t)e * a.scales_stride) +
-                        (size_t)g * a.KB4 * 256;
+__device__ void table_from_logits(const FfnArgs& a, SlotTable& T, uint64_t* buf) {
+    __shared__ RouteScratch R;
+    const int w = wave_id_uniform(), lane = lane_id(), tid = threadIdx.x;
+    const uint32_t full = (1u << M_T) - 1u;
+    if (w < M_T) {
+        float wv;
+        const float* row = a.logits + (size_t)w * a.E;
+        uint64_t* wbuf = buf + kWave * w;
+        const uint64_t key = (a.E <= 512) ? wave_topk<8>(row, a.E, a.k, wv, wbuf)
+                                          : wave_topk<16>(row, a.E, a.k, wv, wbuf);
+        if (lane < a.k) {
+            R.id[w][lane] = key_to_index(key);
+            R.w[w][lane] = wv;
+        }
+    }
+    __syncthreads();
+    const int n_routed = block_group_by_expert(R.id, R.w, M_T, a.k, R.bits, R.pre, R.expert, R.mask, R.weight);
+    for (int s = tid; s <= n_routed; s += kThreads) {
+        if (s == 0) {
+            T.expert[0] = a.E;
+            T.mask[0] = full;
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) T.weight[0][m] = 1.f;
+        } else {
+            T.expert[s] = R.expert[s - 1];
+            T.mask[s] = R.mask[s - 1];
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) T.weight[s][m] = R.weight[s - 1][m];
+        }
+    }
+    if (tid == 0) T.n_slots = n_routed + 1;
+    if (blockIdx.x == 0) {                      // the routing outputs, as moe_route_topk writes them
+        for (int t = tid; t < M_T * a.k; t += kThreads) {
+            const int m = t / a.k, r = t - m * a.k;
+            if (a.ids_out) a.ids_out[t] = R.id[m][r];
+            if (a.w_out) a.w_out[t] = R.w[m][r];
+        }
+        if (a.disp_out) {
+            moedec_dispatch* __restrict__ o = a.disp_out;
+            for (int i = tid; i < MOEDEC_MAX_SLOTS; i += kThreads) {
+                const bool routed = i < n_routed, shared = i == n_routed;
+                o->expert[i] = routed ? R.expert[i] : (shared ? a.E : 0);
+                o->token_mask[i] = routed ? R.mask[i] : (shared ? full : 0u);
+#pragma unroll
+                for (int m = 0; m < MOEDEC_MAX_M; ++m)
+                    o->weight[i][m] = (routed && m < M_T) ? R.weight[i][m] : ((shared && m < M_T) ? 1.f : 0.f);
+            }
+            if (tid == 0) {
+                o->n_slots = n_routed + 1;
+                o->M = M_T;
+            }
+        }
+    }
+}
+
+// Pair counts and slot groups (wave 0).
+__device__ void table_groups(const FfnArgs& a, SlotTable& T) {
+    if (wave_id_uniform() != 0) return;
+    const int lane = lane_id();
+    const int n = T.n_slots;
+    int carry = 0, last_start = 0;
+    for (int base = 0; base < n; base += kWave) {
+        const int s = base + lane;
+        const int cnt = (s < n) ? __popc(T.mask[s]) : 0;
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += o;
+        }
+        const int start = carry + incl - cnt;
+        if (s < n) T.start[s] = start;
+        int last = (cnt > 0) ? start : -1;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off, kWave));
+        if (last >= 0) last_start = last;
+        carry += __shfl(incl, kWave - 1, kWave);
+    }
+    // more groups than launched only with a table not made for this k_max: the rest is dropped
+    const int ng = min(last_start / a.pair_cap + 1, a.max_groups);
+    if (lane == 0) {
+        T.start[n] = carry;
+        T.n_groups = ng;
+        T.gfirst[0] = 0;
+        T.gfirst[ng] = n;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int base = 0; base < n; base += kWave) {
+        const int s = base + lane;
+        if (s > 0 && s < n) {
+            const int gs = min(T.start[s] / a.pair_cap, ng);
+            const int gp = min(T.start[s - 1] / a.pair_cap, ng);
+            for (int g = gp + 1; g <= gs; ++g) T.gfirst[g] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gate/up unit
+
+template <int M_T, int NB>
+__device__ void gateup_unit(const FfnArgs& a, const SlotTable& T, uint8_t* lds, int u, uint32_t gen) {
+    const int s = u / a.gu_units;
+    const int rg = u - s * a.gu_units;
+    if (s >= T.n_slots) return;
+    const int e = T.expert[s];
+    if (e < 0) return;
+    const uint32_t mask = T.mask[s];
     const int w = wave_id_uniform();
     const int lane = lane_id();
-    const float* __restrict__ h = a.h + (size_t)slot * a.M * a.I;
+    const uint8_t* cb = (e == a.E) ? a.sh_gu_codes : a.gu_codes + (size_t)e * a.gu_codes_stride;
+    const uint8_t* sb = (e == a.E) ? a.sh_gu_scales : a.gu_scales + (size_t)e * a.gu_scales_stride;
 
-    float acc[M_T];
+    // this wave's chunk pairs (each = 1 KiB gate + 1 KiB up, four MX blocks)
+    const int cpw = (a.kbh4 + kWaves - 1) / kWaves;
+    const int c_begin = w * cpw;
+    const int c_end = min(a.kbh4, c_begin + cpw);
+    const int n_c = c_end - c_begin;
+    const uint8_t* ub = cb + (size_t)rg * a.kbh4 * 2048 + lane * 16;
+    const uint8_t* usb = sb + (size_t)rg * a.kbh4 * 128 + lane * 2;
+    u32x4 cg[NB], cu[NB];
+    uint32_t sc[NB];
 #pragma unroll
-    for (int m = 0; m < M_T; ++m) acc[m] = 0.f;
+    for (int i = 0; i < NB; ++i) {
+        const int c = max(0, min(c_begin + i, c_end - 1));   // clamped; extra loads unused
+        cg[i] = load_stream16(ub + (size_t)c * 2048);
+        cu[i] = load_stream16(ub + (size_t)c * 2048 + 1024);
+        sc[i] = *reinterpret_cast<const uint16_t*>(usb + (size_t)c * 128);
+    }
 
-    for (int p0 = w; p0 < a.KB4; p0 += kWavesPerBlock * kGroupsInFlight) {
-        u32x4 c[kGroupsInFlight][4];
-        uint32_t sc[kGroupsInFlight];
+    const int xtok = a.kbh4 * 4 * kXBlock;      // x was staged in LDS by the prologue
+    const int quarter = lane >> 4;
+    float accg[M_T], accu[M_T];
 #pragma unroll
-        for (int gi = 0; gi < kGroupsInFlight; ++gi) {
-            const int p = p0 + kWavesPerBlock * gi;
-            if (p < a.KB4) {
-                sc[gi] = *reinterpret_cast<const uint32_t*>(sb + (size_t)p * 256 + lane * 4);
+    for (int m = 0; m < M_T; ++m) accg[m] = accu[m] = 0.f;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int q = 4 * p + b;
-                    if (q < a.KB) c[gi][b] = load_stream16(cb + (size_t)q * 1024 + lane * 16);
-                }
+    for (int i = 0; i < NB; ++i) {
+        if (i < n_c) {
+            const int c = c_begin + i;
+            const float sg = e8m0_to_f32(sc[i] & 0xFFu);
+            const float su = e8m0_to_f32(sc[i] >> 8);
+            bf16x2 wg[16], wu[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                wg[j] = fp4x2_bf16(cg[i][j >> 2], sg, j & 3);
+                wu[j] = fp4x2_bf16(cu[i][j >> 2], su, j & 3);
             }
-        }
+            const uint8_t* xq = lds + (4 * c + quarter) * kXBlock;
 #pragma unroll
-        for (int gi = 0; gi < kGroupsInFlight; ++gi) {
-            const int p = p0 + kWavesPerBlock * gi;
-            if (p >= a.KB4) break;
+            for (int m = 0; m < M_T; ++m) {
+                if (M_T > 1 && !((mask >> m) & 1u)) continue;   // the slot does not serve token m
+                const u32x4* xp = reinterpret_cast<const u32x4*>(xq + m * xtok);
+                u32x4 xr[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int q = 4 * p + b;
-                if (q >= a.KB) break;
-                const float s = e8m0_to_f32((sc[gi] >> (8 * b)) & 0xFFu);
-                f32x2 wv[16];
+                for (int v = 0; v < 4; ++v) xr[v] = xp[v];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const uint32_t word = c[gi][b][j >> 2];
-                    switch (j & 3) {
-                        case 0: wv[j] = MOEDEC_FP4X2_F32(word, s, 0); break;
-                        case 1: wv[j] = MOEDEC_FP4X2_F32(word, s, 1); break;
-                        case 2: wv[j] = MOEDEC_FP4X2_F32(word, s, 2); break;
-                        default: wv[j] = MOEDEC_FP4X2_F32(word, s, 3); break;
-                    }
+                    const bf16x2 xx = as_bf16x2(xr[j >> 2][j & 3]);
+                    accg[m] = dot2_bf16(wg[j], xx, accg[m]);
+                    accu[m] = dot2_bf16(wu[j], xx, accu[m]);
                 }
+            }
+        }
+        if (M_T > 2) __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // sum the four 16-lane rows (cross-lane), then the four waves (LDS)
+    float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][2][16]
 #pragma unroll
-                for (int m = 0; m < M_T; ++m) {
-                    if (!((mask >> m) & 1u)) continue;
-                    const float* hq = h + (size_t)m * a.I + q * 32;
+    for (int m = 0; m < M_T; ++m) {
+        const float g = row_sum_f32(accg[m]);
+        const float uu = row_sum_f32(accu[m]);
+        if (lane < kUnitRows) {
+            red[((w * M_T + m) * 2 + 0) * kUnitRows + lane] = g;
+            red[((w * M_T + m) * 2 + 1) * kUnitRows + lane] = uu;
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        if (lane < kUnitRows) {
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        acc[m] = fmaf(wv[j].x, hq[2 * j], acc[m]);
-                        acc[m] = fmaf(wv[j].y, hq[2 * j + 1], acc[m]);
-                    }
+            for (int m = 0; m < M_T; ++m) {
+                if (!((mask >> m) & 1u)) continue;
+                float g = 0.f, uu = 0.f;
+#pragma unroll
+                for (int v = 0; v < kWaves; ++v) {
+                    g += red[((v * M_T + m) * 2 + 0) * kUnitRows + lane];
+                    uu += red[((v * M_T + m) * 2 + 1) * kUnitRows + lane];
+                }
+                const float hv = g / (1.f + expf(-g)) * uu;
+                store_tagged(&a.h[((size_t)s * M_T + m) * a.I + kUnitRows * rg + lane], gen, hv);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down unit
+
+template <int M_T>
+__device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, uint32_t gen) {
+    const int n_nc = (a.max_groups - 1) * a.dn_units;    // units of groups 1.. come first
+    int grp, g;
+    if (d < n_nc) {
+        grp = 1 + d / a.dn_units;
+        g = d - (grp - 1) * a.dn_units;
+    } else {
+        grp = 0;
+        g = d - n_nc;
+    }
+    const int n_groups = T.n_groups;
+    if (grp >= n_groups) return;
+    const int w = wave_id_uniform();
+    const int lane = lane_id();
+    const int tid = threadIdx.x;
+    const int sb = T.gfirst[grp], se = T.gfirst[grp + 1];
+    const int pbase = T.start[sb];
+    const int n_pairs = T.start[se] - pbase;
+
+    // this wave's items: (slot, chunk), chunk fastest, over the group's slots
+    const int n_items = (se - sb) * a.kbi4;
+    const int i_begin = (w * n_items) / kWaves;
+    const int i_end = ((w + 1) * n_items) / kWaves;
+    const size_t rg_codes = (size_t)g * a.kbi4 * 1024;
+    const size_t rg_scales = (size_t)g * a.kbi4 * 64;
+    // Weights go in batches of kDnBatch chunks into two register sets (A, B):
+    // batch 0 before h is staged, each next batch while the previous computes.
+    u32x4 cwA[kDnBatch], cwB[kDnBatch];
+    uint32_t scA[kDnBatch], scB[kDnBatch];
+    auto load_batch = [&](int i0, u32x4 (&cw)[kDnBatch], uint32_t (&scw)[kDnBatch]) {
+        int ls = i0 / a.kbi4;
+        int ch = i0 - ls * a.kbi4;
+        const uint8_t* cp = nullptr;
+        const uint8_t* sp = nullptr;
+#pragma unroll
+        for (int k = 0; k < kDnBatch; ++k) {
+            if (k == 0 || i0 + k < i_end) {              // past the end: reload the last item (unused)
+                const int e = T.expert[sb + ls];
+                const uint8_t* cbase = (e == a.E) ? a.sh_dn_codes
+                                                  : a.dn_codes + (size_t)max(e, 0) * a.dn_codes_stride;
+                const uint8_t* sbase = (e == a.E) ? a.sh_dn_scales
+                                                  : a.dn_scales + (size_t)max(e, 0) * a.dn_scales_stride;
+                cp = cbase + rg_codes + (size_t)ch * 1024 + lane * 16;
+                sp = sbase + rg_scales + (size_t)ch * 64 + lane;
+                if (++ch == a.kbi4) {
+                    ch = 0;
+                    ++ls;
+                }
+            }
+            cw[k] = load_stream16(cp);
+            scw[k] = *sp;
+        }
+    };
+    if (i_begin < i_end) load_batch(i_begin, cwA, scA);
+
+    if (w == 0) {
+        // the group's (slot, token) pairs
+        for (int s = sb + lane; s < se; s += kWave) {
+            const uint32_t msk = T.mask[s];
+            int p = T.start[s] - pbase;
+#pragma unroll
+            for (int m = 0; m < M_T; ++m)
+                if ((msk >> m) & 1u) T.pair[p++] = (s << 8) | m;
+        }
+    }
+    __syncthreads();
+
+    // Stage w * h: pair p, MX block q at p * pair_bytes + q * 144; padding is
+    // zero.  Each 16-byte load brings two tagged h words.  The loads go out
+    // right behind the weight loads; a batch is read again (after a pause)
+    // while any of its tags is not this launch's, so detection and transfer
+    // take one round trip once h is there.
+    {
+        const __amdgpu_buffer_rsrc_t hrs =
+            __builtin_amdgcn_make_buffer_rsrc(a.h, 0, a.h_bytes, kBufferRsrcWord3);
+        const int per_pair = a.kbi4 * 4 * 16;              // 16-byte loads per pair, padding included
+        const int total = n_pairs * per_pair;
+        for (int i0 = 0; i0 < total; i0 += kThreads * kStageBatch) {
+            u32x4 raw[kStageBatch];
+            auto issue = [&]() {
+#pragma unroll
+                for (int q = 0; q < kStageBatch; ++q) {
+                    const int idx = min(i0 + tid + kThreads * q, total - 1);   // clamped: always in bounds
+                    const int p = idx / per_pair;
+                    const int k = min((idx - p * per_pair) * 2, a.I - 2);
+                    const int src = T.pair[p];
+                    const int off = (((src >> 8) * M_T + (src & 0xFF)) * a.I + k) * (int)sizeof(uint64_t);
+                    raw[q] = __builtin_amdgcn_raw_buffer_load_b128(hrs, off, 0, kLoadCoherent);
+                }
+            };
+            issue();
+            uint32_t spins = 0;
+            for (;;) {
+                bool ok = true;
+#pragma unroll
+                for (int q = 0; q < kStageBatch; ++q) {
+                    const int idx = i0 + tid + kThreads * q;
+                    const int f = idx - (idx / per_pair) * per_pair;
+                    const bool live = idx < total && 2 * f < a.I;
+                    ok &= !live || (raw[q][1] == gen && raw[q][3] == gen);
+                }
+                if (__syncthreads_and(ok)) break;
+                if (++spins > kSpinLimit) {                 // never expected: flag and go on
+                    if (tid == 0) atomicOr(a.err, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(16);                // not there yet: pause before re-reading
+                issue();
+            }
+#pragma unroll
+            for (int q = 0; q < kStageBatch; ++q) {
+                const int idx = i0 + tid + kThreads * q;
+                if (idx < total) {
+                    const int p = idx / per_pair;
+                    const int k = (idx - p * per_pair) * 2;
+                    const int src = T.pair[p];
+                    const float wt = T.weight[src >> 8][src & 0xFF];
+                    float2 o = make_float2(__uint_as_float(raw[q][0]) * wt, __uint_as_float(raw[q][2]) * wt);
+                    if (k >= a.I) o = make_float2(0.f, 0.f);         // MX blocks past I
+                    *reinterpret_cast<float2*>(lds + p * a.pair_bytes + (k >> 5) * kHBlock + (k & 31) * 4) = o;
                 }
             }
         }
     }
-
-    __shared__ float red[kWavesPerBlock][M_T][64];
-    __shared__ int s_last;
-#pragma unroll
-    for (int m = 0; m < M_T; ++m) red[w][m][lane] = acc[m];
     __syncthreads();
-    if (w == 0) {
+
+    const int quarter = lane >> 4;
+    float acc[M_T], acc2[M_T], acc3[M_T], acc4[M_T];   // four FMA chains per token
+#pragma unroll
+    for (int m = 0; m < M_T; ++m) acc[m] = acc2[m] = acc3[m] = acc4[m] = 0.f;
+    auto compute_batch = [&](int i0, const u32x4 (&cw)[kDnBatch], const uint32_t (&scw)[kDnBatch]) {
+        int ls = i0 / a.kbi4;
+        int ch = i0 - ls * a.kbi4;
+#pragma unroll
+        for (int k = 0; k < kDnBatch; ++k) {
+            if (i0 + k < i_end) {
+                const int s = sb + ls;
+                const uint32_t msk = T.mask[s];
+                const int p0 = T.start[s] - pbase;
+                const float sc = e8m0_to_f32(scw[k]);
+                const uint8_t* hq = lds + (4 * ch + quarter) * kHBlock;
+                int p = p0;
+#pragma unroll
+                for (int m = 0; m < M_T; ++m) {
+                    // with one token every slot of a group serves it; otherwise skip the
+                    // tokens the slot does not serve (its weight is zero anyway)
+                    if (M_T > 1 && !((msk >> m) & 1u)) continue;
+                    // the 8 LDS reads of this (slot, token) go out back to back
+                    const float4* hp = reinterpret_cast<const float4*>(hq + p * a.pair_bytes);
+                    float4 hv[8];
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) hv[v] = hp[v];
+                    ++p;
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) {
+                        // four weights: bytes 2v and 2v+1 of the lane's 16 code bytes
+                        const f32x2 w0 = fp4x2_f32(cw[k][v >> 1], sc, (2 * v) & 3);
+                        const f32x2 w1 = fp4x2_f32(cw[k][v >> 1], sc, (2 * v + 1) & 3);
+                        acc[m] = fmaf(w0.x, hv[v].x, acc[m]);
+                        acc2[m] = fmaf(w0.y, hv[v].y, acc2[m]);
+                        acc3[m] = fmaf(w1.x, hv[v].z, acc3[m]);
+                        acc4[m] = fmaf(w1.y, hv[v].w, acc4[m]);
+                    }
+                }
+            }
+            if (++ch == a.kbi4) {
+                ch = 0;
+                ++ls;
+            }
+            __builtin_amdgcn_sched_barrier(0);    // bound register pressure: one item at a time
+        }
+    };
+    for (int i0 = i_begin; i0 < i_end; i0 += 2 * kDnBatch) {
+        if (i0 + kDnBatch < i_end) load_batch(i0 + kDnBatch, cwB, scB);
+        compute_batch(i0, cwA, scA);
+        if (i0 + 2 * kDnBatch < i_end) load_batch(i0 + 2 * kDnBatch, cwA, scA);
+        if (i0 + kDnBatch < i_end) compute_batch(i0 + kDnBatch, cwB, scB);
+    }
+
+    float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][16]
+#pragma unroll
+    for (int m = 0; m < M_T; ++m) {
+        const float r = row_sum_f32((acc[m] + acc2[m]) + (acc3[m] + acc4[m]));
+        if (lane < kUnitRows) red[(w * M_T + m) * kUnitRows + lane] = r;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const int row = kUnitRows * g + lane;
+    float y[M_T];
+#pragma unroll
+    for (int m = 0; m < M_T; ++m) {
+        y[m] = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) y[m] += (lane < kUnitRows) ? red[(v * M_T + m) * kUnitRows + lane] : 0.f;
+    }
+    if (n_groups > 1) {
+        if (grp != 0) {
+            if (lane < kUnitRows) {
+#pragma unroll
+                for (int m = 0; m < M_T; ++m) store_tagged(&a.part[((size_t)grp * M_T + m) * a.H + row], gen, y[m]);
+            }
+            return;
+        }
+        // group 0 adds the other groups' partial rows, in group order, once
+        // their tags say they are from this launch
+        const int prow = kUnitRows * g + (lane & (kUnitRows - 1));    // in bounds for every lane
+        for (int gg = 1; gg < n_groups; ++gg) {
+            uint64_t pv[M_T];
+            uint32_t spins = 0;
+            for (;;) {
+                bool ok = true;
+#pragma unroll
+                for (int m = 0; m < M_T; ++m) {
+                    pv[m] = load_tagged(&a.part[((size_t)gg * M_T + m) * a.H + prow]);
+                    ok &= (uint32_t)(pv[m] >> 32) == gen;
+                }
+                if (__all(ok)) break;
+                if (++spins > kSpinLimit) {
+                    if (lane == 0) atomicOr(a.err, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) y[m] += __uint_as_float((uint32_t)pv[m]);
+        }
+    }
+    if (lane < kUnitRows) {
 #pragma unroll
         for (int m = 0; m < M_T; ++m) {
-            float t = red[0][m][lane];
+            const size_t o = (size_t)m * a.H + row;
+            if (a.y_f32) a.y_f32[o] = y[m];
+            a.y_bf16[o] = f32_to_bf16_rne(y[m]);
+        }
+    }
+}
+
+template <int M_T, int NB, bool ROUTE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBlocksPerCU)))
+void moe_ffn_kernel(FfnArgs a) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ SlotTable T;
+    __shared__ uint32_t s_gen;
+    const int tid = threadIdx.x;
+    const bool has_gu = (int)blockIdx.x < a.n_gu;          // the block runs a gate/up unit
+
+    // x does not depend on routing: its loads go out first (unconditional,
+    // clamped index), and are staged in LDS once the slot table is built.
+    constexpr int kXPieces = 2 * M_T;                     // covers M_T * 4096 / 8 pieces
+    const int per_tok = a.H / 8;
+    const int n_pieces = M_T * per_tok;
+    u32x4 xv[kXPieces];
+    if (has_gu) {
+        const u32x4* xg = reinterpret_cast<const u32x4*>(a.x);
 #pragma unroll
-            for (int v = 1; v < kWavesPerBlock; ++v) t += red[v][m][lane];
-            const float wt = ((mask >> m) & 1u) ? disp->weight[slot][m] : 0.f;
-            a.part[(((size_t)g * a.max_slots + slot) * a.M + m) * 64 + lane] = t * wt;
+        for (int i = 0; i < kXPieces; ++i) xv[i] = xg[min(tid + kThreads * i, n_pieces - 1)];
+    }
+    if (tid == kThreads - kWave) {                        // wave 3: keeps wave 0 free to route
+        const uint32_t g = a.gens[blockIdx.x] + 1u;       // this block's launch count on the workspace
+        a.gens[blockIdx.x] = g;
+        s_gen = g;
+    }
+    constexpr bool kDirectGroups = ROUTE && M_T == 1;     // the table arrives with its groups
+    // routing borrows the reduction area (M_T * 512 bytes: 64 words per routing
+    // wave), which the units use only after the prologue
+    uint64_t* route_buf = reinterpret_cast<uint64_t*>(lds + a.red_off);
+    if (kDirectGroups)
+        table_from_logits_one(a, T, route_buf);
+    else if (ROUTE)
+        table_from_logits<M_T>(a, T, route_buf);
+    else
+        table_from_dispatch<M_T>(a, T);
+    if (has_gu) {
+        const int xtok = a.kbh4 * 4 * kXBlock;            // token m, MX block q at m * xtok + q * 80
+#pragma unroll
+        for (int i = 0; i < kXPieces; ++i) {
+            const int p = tid + kThreads * i;
+            if (p < n_pieces) {
+                const int m = p / per_tok;
+                const int r = p - m * per_tok;
+                *reinterpret_cast<u32x4*>(lds + m * xtok + (r >> 2) * kXBlock + (r & 3) * 16) = xv[i];
+            }
         }
-        __threadfence();
+        const int pad_pieces = (a.kbh4 * 4 - a.kbh) * 4;  // MX blocks past H are zero
+        for (int p = tid; p < M_T * pad_pieces; p += kThreads) {
+            const int m = p / pad_pieces;
+            const int r = p - m * pad_pieces;
+            *reinterpret_cast<u32x4*>(lds + m * xtok + (a.kbh + (r >> 2)) * kXBlock + (r & 3) * 16) =
+                u32x4{0u, 0u, 0u, 0u};
+        }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t ticket = atomicAdd(&a.tickets[g], 1u);
-        s_last = (ticket == (uint32_t)(n_slots - 1));
+    if (!kDirectGroups) {
+        table_groups(a, T);
+        __syncthreads();
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (w == 0) {
-        for (int m = 0; m < a.M; ++m) {
-            float y = 0.f;
-            for (int s2 = 0; s2 < n_slots; ++s2)
-                y += __builtin_nontemporal_load(
-                    &a.part[(((size_t)g * a.max_slots + s2) * a.M + m) * 64 + lane]);
-            const size_t o = (size_t)m * a.H + 64 * g + lane;
-            if (a.y_f32) a.y_f32[o] = y;
-            a.y_bf16[o] = f32_to_bf16_rne(y);
-        }
-        if (lane == 0) atomicExch(&a.tickets[g], 0u);
+    const uint32_t gen = s_gen;
+    for (int u = blockIdx.x; u < a.n_units; u += gridDim.x) {
+        if (u < a.n_gu)
+            gateup_unit<M_T, NB>(a, T, lds, u, gen);
+        else
+            down_unit<M_T>(a, T, lds, u - a.n_gu, gen);
+        __syncthreads();
     }
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+constexpr size_t kLdsTarget = 40 * 1024;
+
+// Grid: kBlocksPerCU blocks per CU, the same for every launch on a device.
+struct DeviceInfo {
+    int grid = 0;
+    std::mutex mu;
+};
+DeviceInfo g_dev[64];
+
+int device_grid() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    DeviceInfo& d = g_dev[dev];
+    std::lock_guard<std::mutex> lock(d.mu);
+    if (d.grid == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        d.grid = std::min(kMaxGrid, kBlocksPerCU * cus);
+    }
+    return d.grid;
+}
+
+template <int M_T, int NB, bool ROUTE>
+hipError_t launch_variant(const FfnArgs& a, int grid, size_t lds, hipStream_t s) {
+    // every block must be resident at once: check the occupancy of this variant
+    static std::atomic<int> occ_ok[256];                      // per LDS size class of 256 B
+    const size_t cls = std::min<size_t>((lds + 255) / 256, 255);
+    int v = occ_ok[cls].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int blocks = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE>), kThreads, lds);
+        if (e != hipSuccess) return e;
+        v = (blocks >= kBlocksPerCU) ? 1 : 2;
+        occ_ok[cls].store(v, std::memory_order_relaxed);
+    }
+    if (v != 1) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE>), dim3(grid), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int M_T, bool ROUTE>
+hipError_t launch_m(const FfnArgs& a, int nb, int grid, size_t lds, hipStream_t s) {
+    switch (nb) {
+        case 1: return launch_variant<M_T, 1, ROUTE>(a, grid, lds, s);
+        case 2: return launch_variant<M_T, 2, ROUTE>(a, grid, lds, s);
+        case 4: return launch_variant<M_T, 4, ROUTE>(a, grid, lds, s);
+        case 5: return launch_variant<M_T, 5, ROUTE>(a, grid, lds, s);
+        default: return launch_variant<M_T, 8, ROUTE>(a, grid, lds, s);
+    }
+}
+
 }  // namespace
 
 FfnLayout ffn_layout(int M, int k_max, int H, int I) {
     FfnLayout L;
+    const int kbh4 = (H / 32 + 3) / 4, kbi4 = (I / 32 + 3) / 4;
     L.max_slots = M * k_max + 1;
-    L.h_off = 0;
-    L.part_off = align256((size_t)L.max_slots * M * I * sizeof(float));
-    L.ticket_off = L.part_off + align256((size_t)(H / 64) * L.max_slots * M * 64 * sizeof(float));
-    L.total = L.ticket_off + align256((size_t)(H / 64) * sizeof(uint32_t));
+    L.pair_bytes = kbi4 * 4 * kHBlock;
+    static_assert(kWaves * 2 * kUnitRows * sizeof(float) >= kWave * sizeof(uint64_t),
+                  "each routing wave borrows 64 words of the reduction area");
+    const size_t red_bytes = (size_t)kWaves * M * 2 * kUnitRows * sizeof(float);
+    const size_t x_bytes = (size_t)M * kbh4 * 4 * kXBlock;
+    const int fit = (int)((kLdsTarget - red_bytes) / L.pair_bytes) - (M - 1);
+    const int max_pairs = M * k_max + M;
+    L.pair_cap = std::max(1, std::min(fit, max_pairs));
+    L.max_groups = (max_pairs + L.pair_cap - 1) / L.pair_cap;
+    const size_t h_bytes = (size_t)(L.pair_cap + M - 1) * L.pair_bytes;
+    const size_t region = std::max(x_bytes, h_bytes);
+    L.red_off = (int)((region + 15) & ~(size_t)15);
+    L.lds_bytes = L.red_off + red_bytes;
+    // the fixed-size part first, so a workspace serves any M / k_max it is big enough for
+    L.ctl_off = 0;                                                      // gens + error word
+    L.yt_off = 0;
+    L.h_off = align256((size_t)(kMaxGrid + 64) * sizeof(uint32_t));
+    L.part_off = L.h_off + align256((size_t)L.max_slots * M * I * sizeof(uint64_t));
+    L.total = L.part_off + (L.max_groups > 1 ? align256((size_t)L.max_groups * M * H * sizeof(uint64_t)) : 0);
+    L.grid = 0;
     return L;
+}
+
+hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int k_max,
+                      const moedec_dispatch* disp, const float* logits, int32_t* ids_out,
+                      float* w_out, moedec_dispatch* disp_out, uint16_t* y_bf16, float* y_f32,
+                      void* ws, hipStream_t s) {
+    const FfnLayout L = ffn_layout(M, k_max, w.H, w.I);
+    const int grid = device_grid();
+    if (grid <= 0) return hipErrorInvalidDevice;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    moedec_mxfp4_sizes sz;
+    packed_sizes(w.H, w.I, &sz);
+
+    FfnArgs a;
+    a.gu_codes = w.gu_codes;
+    a.gu_scales = w.gu_scales;
+    a.dn_codes = w.dn_codes;
+    a.dn_scales = w.dn_scales;
+    a.sh_gu_codes = w.sh_gu_codes;
+    a.sh_gu_scales = w.sh_gu_scales;
+    a.sh_dn_codes = w.sh_dn_codes;
+    a.sh_dn_scales = w.sh_dn_scales;
+    a.gu_codes_stride = sz.gu_codes;
+    a.gu_scales_stride = sz.gu_scales;
+    a.dn_codes_stride = sz.dn_codes;
+    a.dn_scales_stride = sz.dn_scales;
+    a.E = w.E;
+    a.H = w.H;
+    a.I = w.I;
+    a.k = k_max;
+    a.kbh = w.H / 32;
+    a.kbh4 = (a.kbh + 3) / 4;
+    a.kbi = w.I / 32;
+    a.kbi4 = (a.kbi + 3) / 4;
+    a.gu_units = w.I / kUnitRows;
+    a.dn_units = w.H / kUnitRows;
+    a.max_slots = L.max_slots;
+    a.max_groups = L.max_groups;
+    a.pair_cap = L.pair_cap;
+    a.n_gu = L.max_slots * a.gu_units;
+    a.n_units = a.n_gu + L.max_groups * a.dn_units;
+    a.pair_bytes = L.pair_bytes;
+    a.red_off = L.red_off;
+    a.x = x;
+    a.disp = disp;
+    a.logits = logits;
+    a.ids_out = ids_out;
+    a.w_out = w_out;
+    a.disp_out = disp_out;
+    uint32_t* ctl = reinterpret_cast<uint32_t*>(base + L.ctl_off);
+    a.gens = ctl;
+    a.err = ctl + kMaxGrid;
+    a.h = reinterpret_cast<uint64_t*>(base + L.h_off);
+    a.part = reinterpret_cast<uint64_t*>(base + L.part_off);
+    a.h_bytes = (int)((size_t)L.max_slots * M * w.I * sizeof(uint64_t));
+    a.y_bf16 = y_bf16;
+    a.y_f32 = y_f32;
+
+    const int cpw = (a.kbh4 + kWaves - 1) / kWaves;   // chunk pairs per wave, <= 8 for H <= 4096
+    const int nb = cpw <= 1 ? 1 : cpw <= 2 ? 2 : cpw <= 4 ? 4 : cpw <= 5 ? 5 : 8;
+    const bool route = logits != nullptr;
+    switch (M) {
+        case 1: return route ? launch_m<1, true>(a, nb, grid, L.lds_bytes, s) : launch_m<1, false>(a, nb, grid, L.lds_bytes, s);
+        case 2: return route ? launch_m<2, true>(a, nb, grid, L.lds_bytes, s) : launch_m<2, false>(a, nb, grid, L.lds_bytes, s);
+        case 3: return route ? launch_m<3, true>(a, nb, grid, L.lds_bytes, s) : launch_m<3, false>(a, nb, grid, L.lds_bytes, s);
+        default: return route ? launch_m<4, true>(a, nb, grid, L.lds_bytes, s) : launch_m<4, false>(a, nb, grid, L.lds_bytes, s);
+    }
 }
 
 hipError_t launch_expert_ffn(const moedec_moe_weights& w, const uint16_t* x, int M,
                              const moedec_dispatch* disp, int k_max, uint16_t* y_bf16,
                              float* y_f32, void* ws, hipStream_t s) {
-    const FfnLayout L = ffn_layout(M, k_max, w.H, w.I);
-    uint8_t* base = static_cast<uint8_t*>(ws);
-    float* h = reinterpret_cast<float*>(base + L.h_off);
-    const int KBH = w.H / 32, KBI = w.I / 32;
-
-    GateUpArgs ga;
-    ga.codes = w.gu_codes;
-    ga.scales = w.gu_scales;
-    ga.sh_codes = w.sh_gu_codes;
-    ga.sh_scales = w.sh_gu_scales;
-    ga.codes_stride = (size_t)w.I * w.H;
-    ga.KB = KBH;
-    ga.KB4 = (KBH + 3) / 4;
-    ga.scales_stride = (size_t)(w.I / 32) * ga.KB4 * 256;
-    ga.E = w.E;
-    ga.H = w.H;
-    ga.I = w.I;
-    ga.M = M;
-    ga.x = reinterpret_cast<const uint32_t*>(x);
-    ga.disp = disp;
-    ga.h = h;
-    const dim3 g1(w.I / 32, L.max_slots), blk(256);
-    switch (M) {
-        case 1: hipLaunchKernelGGL(gateup_kernel<1>, g1, blk, 0, s, ga); break;
-        case 2: hipLaunchKernelGGL(gateup_kernel<2>, g1, blk, 0, s, ga); break;
-        case 3: hipLaunchKernelGGL(gateup_kernel<3>, g1, blk, 0, s, ga); break;
-        default: hipLaunchKernelGGL(gateup_kernel<4>, g1, blk, 0, s, ga); break;
-    }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-
-    DownArgs da;
-    da.codes = w.dn_codes;
-    da.scales = w.dn_scales;
-    da.sh_codes = w.sh_dn_codes;
-    da.sh_scales = w.sh_dn_scales;
-    da.codes_stride = (size_t)w.H * w.I / 2;
-    da.KB = KBI;
-    da.KB4 = (KBI + 3) / 4;
-    da.scales_stride = (size_t)(w.H / 64) * da.KB4 * 256;
-    da.E = w.E;
-    da.H = w.H;
-    da.I = w.I;
-    da.M = M;
-    da.max_slots = L.max_slots;
-    da.h = h;
-    da.disp = disp;
-    da.part = reinterpret_cast<float*>(base + L.part_off);
-    da.tickets = reinterpret_cast<uint32_t*>(base + L.ticket_off);
-    da.y_bf16 = y_bf16;
-    da.y_f32 = y_f32;
-    const dim3 g2(w.H / 64, L.max_slots);
-    switch (M) {
-        case 1: hipLaunchKernelGGL(down_kernel<1>, g2, blk, 0, s, da); break;
-        case 2: hipLaunchKernelGGL(down_kernel<2>, g2, blk, 0, s, da); break;
-        case 3: hipLaunchKernelGGL(down_kernel<3>, g2, blk, 0, s, da); break;
-        default: hipLaunchKernelGGL(down_kernel<4>, g2, blk, 0, s, da); break;
-    }
-    return hipGetLastError();
+    return launch_moe(w, x, M, k_max, disp, nullptr, nullptr, nullptr, nullptr, y_bf16, y_f32, ws, s);
 }
 
 }  // namespace moedec

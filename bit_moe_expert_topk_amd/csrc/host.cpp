@@ -52,10 +52,10 @@ int launched(hipError_t err, const char* what) {
 }
 
 int check_mxfp4_shape(int H, int I) {
-    if (H < 64 || H > 16384 || H % 64 != 0)
-        return fail(MOEDEC_ERR_SHAPE, "H=%d: need 64 <= H <= 16384 and H %% 64 == 0", H);
-    if (I < 32 || I > 16384 || I % 32 != 0)
-        return fail(MOEDEC_ERR_SHAPE, "I=%d: need 32 <= I <= 16384 and I %% 32 == 0", I);
+    if (H < 64 || H > 4096 || H % 64 != 0)
+        return fail(MOEDEC_ERR_SHAPE, "H=%d: need 64 <= H <= 4096 and H %% 64 == 0", H);
+    if (I < 32 || I > 2048 || I % 32 != 0)
+        return fail(MOEDEC_ERR_SHAPE, "I=%d: need 32 <= I <= 2048 and I %% 32 == 0", I);
     return MOEDEC_OK;
 }
 
@@ -102,11 +102,7 @@ int moe_route_topk(const float* logits, int M, int E, int k, int32_t* topk_ids, 
 int moedec_mxfp4_packed_sizes(int H, int I, moedec_mxfp4_sizes* out) {
     if (!out) return fail(MOEDEC_ERR_NULL, "out is NULL");
     if (int st = check_mxfp4_shape(H, I)) return st;
-    const size_t kbh4 = (size_t)(H / 32 + 3) / 4, kbi4 = (size_t)(I / 32 + 3) / 4;
-    out->gu_codes = (size_t)I * H;
-    out->gu_scales = (size_t)(I / 32) * kbh4 * 256;
-    out->dn_codes = (size_t)H * I / 2;
-    out->dn_scales = (size_t)(H / 64) * kbi4 * 256;
+    moedec::packed_sizes(H, I, out);
     g_last_error[0] = '\0';
     return MOEDEC_OK;
 }
@@ -121,7 +117,7 @@ int moe_pack_gateup_mxfp4(const uint8_t* gate_codes, const uint8_t* gate_scales,
     if (int st = check_mxfp4_shape(H, I)) return st;
     if (!aligned(gate_codes, 16) || !aligned(up_codes, 16) || !aligned(gu_codes, 16))
         return fail(MOEDEC_ERR_ALIGN, "code arrays must be 16-byte aligned");
-    if (!aligned(gu_scales, 4)) return fail(MOEDEC_ERR_ALIGN, "packed scales must be 4-byte aligned");
+    if (!aligned(gu_scales, 2)) return fail(MOEDEC_ERR_ALIGN, "packed scales must be 2-byte aligned");
     if (int st = check_device()) return st;
     return launched(moedec::launch_pack_gateup(gate_codes, gate_scales, up_codes, up_scales,
                                                n_experts, H, I, gu_codes, gu_scales,
@@ -139,7 +135,6 @@ int moe_pack_down_mxfp4(const uint8_t* down_codes, const uint8_t* down_scales, i
     if (int st = check_mxfp4_shape(H, I)) return st;
     if (!aligned(down_codes, 16) || !aligned(dn_codes, 16))
         return fail(MOEDEC_ERR_ALIGN, "code arrays must be 16-byte aligned");
-    if (!aligned(dn_scales, 4)) return fail(MOEDEC_ERR_ALIGN, "packed scales must be 4-byte aligned");
     if (int st = check_device()) return st;
     return launched(moedec::launch_pack_down(down_codes, down_scales, n_experts, H, I, dn_codes,
                                              dn_scales, static_cast<hipStream_t>(stream)),
@@ -147,15 +142,14 @@ int moe_pack_down_mxfp4(const uint8_t* down_codes, const uint8_t* down_scales, i
 }
 
 size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I) {
-    if (M < 1 || M > MOEDEC_MAX_M || k_max < 1 || k_max > MOEDEC_MAX_K || H < 64 || H % 64 ||
-        I < 32 || I % 32)
+    if (M < 1 || M > MOEDEC_MAX_M || k_max < 1 || k_max > MOEDEC_MAX_K || H < 64 || H > 4096 ||
+        H % 64 || I < 32 || I > 2048 || I % 32)
         return 0;
     return moedec::ffn_layout(M, k_max, H, I).total;
 }
 
-int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, int M,
-                         const moedec_dispatch* dispatch, int k_max, uint16_t* y_bf16, float* y_f32,
-                         void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+static int check_moe_args(const moedec_moe_weights* w, const uint16_t* x_bf16, int M, int k,
+                          uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes) {
     if (!w) return fail(MOEDEC_ERR_NULL, "weights descriptor is NULL");
     if (w->magic != MOEDEC_MOE_MAGIC)
         return fail(MOEDEC_ERR_FORMAT, "weights descriptor magic 0x%08x != 0x%08x", w->magic,
@@ -163,30 +157,51 @@ int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, in
     if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales || !w->sh_gu_codes ||
         !w->sh_gu_scales || !w->sh_dn_codes || !w->sh_dn_scales)
         return fail(MOEDEC_ERR_NULL, "a weight pointer is NULL");
-    if (!x_bf16 || !dispatch || !y_bf16 || !workspace)
-        return fail(MOEDEC_ERR_NULL, "x, dispatch, y_bf16 or workspace is NULL");
+    if (!x_bf16 || !y_bf16 || !workspace) return fail(MOEDEC_ERR_NULL, "x, y_bf16 or workspace is NULL");
     if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
-    if (k_max < 1 || k_max > MOEDEC_MAX_K || k_max > w->E)
-        return fail(MOEDEC_ERR_SHAPE, "k_max=%d not in 1..min(E, %d)", k_max, MOEDEC_MAX_K);
     if (w->E < 1 || w->E > MOEDEC_MAX_E) return fail(MOEDEC_ERR_SHAPE, "E=%d not in 1..%d", w->E, MOEDEC_MAX_E);
+    if (k < 1 || k > MOEDEC_MAX_K || k > w->E)
+        return fail(MOEDEC_ERR_SHAPE, "k=%d not in 1..min(E, %d)", k, MOEDEC_MAX_K);
     if (int st = check_mxfp4_shape(w->H, w->I)) return st;
     if (!aligned(w->gu_codes, 16) || !aligned(w->dn_codes, 16) || !aligned(w->sh_gu_codes, 16) ||
         !aligned(w->sh_dn_codes, 16))
         return fail(MOEDEC_ERR_ALIGN, "packed code arrays must be 16-byte aligned");
-    if (!aligned(w->gu_scales, 4) || !aligned(w->dn_scales, 4) || !aligned(w->sh_gu_scales, 4) ||
-        !aligned(w->sh_dn_scales, 4))
-        return fail(MOEDEC_ERR_ALIGN, "packed scale arrays must be 4-byte aligned");
-    if (!aligned(x_bf16, 4) || !aligned(y_bf16, 4) || !aligned(y_f32, 4))
-        return fail(MOEDEC_ERR_ALIGN, "x, y_bf16 and y_f32 must be 4-byte aligned");
-    if (!aligned(dispatch, 16) || !aligned(workspace, 16))
-        return fail(MOEDEC_ERR_ALIGN, "dispatch and workspace must be 16-byte aligned");
-    const size_t need = moedec::ffn_layout(M, k_max, w->H, w->I).total;
+    if (!aligned(w->gu_scales, 2) || !aligned(w->sh_gu_scales, 2))
+        return fail(MOEDEC_ERR_ALIGN, "packed gate/up scale arrays must be 2-byte aligned");
+    if (!aligned(x_bf16, 16) || !aligned(y_bf16, 4) || !aligned(y_f32, 4))
+        return fail(MOEDEC_ERR_ALIGN, "x must be 16-byte aligned, y_bf16 and y_f32 4-byte");
+    if (!aligned(workspace, 16)) return fail(MOEDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t need = moedec::ffn_layout(M, k, w->H, w->I).total;
     if (workspace_bytes < need)
         return fail(MOEDEC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    return MOEDEC_OK;
+}
+
+int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, int M,
+                         const moedec_dispatch* dispatch, int k_max, uint16_t* y_bf16, float* y_f32,
+                         void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+    if (int st = check_moe_args(w, x_bf16, M, k_max, y_bf16, y_f32, workspace, workspace_bytes)) return st;
+    if (!dispatch) return fail(MOEDEC_ERR_NULL, "dispatch is NULL");
+    if (!aligned(dispatch, 16)) return fail(MOEDEC_ERR_ALIGN, "dispatch must be 16-byte aligned");
     if (int st = check_device()) return st;
     return launched(moedec::launch_expert_ffn(*w, x_bf16, M, dispatch, k_max, y_bf16, y_f32,
                                               workspace, static_cast<hipStream_t>(stream)),
                     "moe_expert_ffn_mxfp4");
+}
+
+int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int M,
+                    int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
+                    uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
+                    moedec_stream_t stream) {
+    if (int st = check_moe_args(w, x_bf16, M, k, y_bf16, y_f32, workspace, workspace_bytes)) return st;
+    if (!logits) return fail(MOEDEC_ERR_NULL, "logits is NULL");
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+        return fail(MOEDEC_ERR_ALIGN, "logits/topk_ids/topk_w must be 4-byte aligned");
+    if (!aligned(dispatch, 16)) return fail(MOEDEC_ERR_ALIGN, "dispatch must be 16-byte aligned");
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_moe(*w, x_bf16, M, k, nullptr, logits, topk_ids, topk_w, dispatch,
+                                       y_bf16, y_f32, workspace, static_cast<hipStream_t>(stream)),
+                    "moe_layer_mxfp4");
 }
 
 int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H, uint8_t* codes, float* row_scale,

@@ -19,11 +19,27 @@ hipError_t launch_pack_gateup(const uint8_t* gc, const uint8_t* gs, const uint8_
 hipError_t launch_pack_down(const uint8_t* dc, const uint8_t* ds, int n_exp, int H, int I,
                             uint8_t* oc, uint8_t* os, hipStream_t s);
 
+// Per-expert packed MXFP4 sizes (bytes) for hidden H and intermediate I.
+void packed_sizes(int H, int I, moedec_mxfp4_sizes* out);
+
+// Workspace and launch layout of the fused FFN kernel.
 struct FfnLayout {
-    size_t h_off, part_off, ticket_off, total;
-    int max_slots;
+    int max_slots;      // M * k_max + 1 (routed slots + the shared expert)
+    int pair_cap;       // (slot, token) pairs per down slot group
+    int max_groups;     // slot groups at most
+    int pair_bytes;     // LDS bytes of one pair's h
+    int red_off;        // LDS offset of the reduction scratch
+    size_t lds_bytes;   // dynamic LDS per block
+    size_t ctl_off, yt_off, h_off, part_off, total;   // workspace layout
+    int grid;           // blocks per launch
 };
 FfnLayout ffn_layout(int M, int k_max, int H, int I);
+
+// Fused layer: routing from logits (when non-null) or the dispatch table, then the FFN.
+hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int k_max,
+                      const moedec_dispatch* disp, const float* logits, int32_t* ids_out,
+                      float* w_out, moedec_dispatch* disp_out, uint16_t* y_bf16, float* y_f32,
+                      void* ws, hipStream_t s);
 
 hipError_t launch_expert_ffn(const moedec_moe_weights& w, const uint16_t* x, int M,
                              const moedec_dispatch* disp, int k_max, uint16_t* y_bf16,

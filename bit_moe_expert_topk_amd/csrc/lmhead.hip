@@ -44,19 +44,18 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     const int waves = gridDim.x * (blockDim.x >> 6);
     for (int v = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); v < V; v += waves) {
         const uint8_t* row = reinterpret_cast<const uint8_t*>(w) + (size_t)v * H * 2;
+        // unconditional loads (clamped chunk index): all in flight at once
         u32x4 c[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) c[t] = load_stream16(row + (size_t)min(lane + 64 * t, n_ch - 1) * 16);
         uint32_t amax = 0;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int ch = lane + 64 * t;
-            if (ch < n_ch) {
-                c[t] = load_stream16(row + (size_t)ch * 16);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t lo = c[t][i] & 0x7FFFu, hi = (c[t][i] >> 16) & 0x7FFFu;
-                    amax = lo > amax ? lo : amax;
-                    amax = hi > amax ? hi : amax;
-                }
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = c[t][i] & 0x7FFFu, hi = (c[t][i] >> 16) & 0x7FFFu;
+                amax = lo > amax ? lo : amax;
+                amax = hi > amax ? hi : amax;
             }
         }
         amax = wave_max_u32(amax);
@@ -103,23 +102,23 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(const uint8_t* __restrict
         for (int t = 0; t < T; ++t) {
             const int ch = lane + 64 * t;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                xr[m][t][j] = (ch < n_ch) ? x[(size_t)m * (H / 2) + ch * 8 + j] : 0u;
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t xv = x[(size_t)m * (H / 2) + min(ch, n_ch - 1) * 8 + j];
+                xr[m][t][j] = (ch < n_ch) ? xv : 0u;     // chunks past H multiply by zero
+            }
         }
     const int v0 = gw * rows_per_wave;
     const int v1 = min(V, v0 + rows_per_wave);
     for (int v = v0; v < v1; v += kRows) {
+        // unconditional loads (clamped row and chunk): rows past v1 are computed
+        // but never stored, chunks past H meet zero activations
         u32x4 c[kRows][T];
 #pragma unroll
         for (int r = 0; r < kRows; ++r)
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int ch = lane + 64 * t;
-                if (v + r < v1 && ch < n_ch)
-                    c[r][t] = load_stream16(codes + (size_t)(v + r) * H + (size_t)ch * 16);
-                else
-                    c[r][t] = u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int t = 0; t < T; ++t)
+                c[r][t] = load_stream16(codes + (size_t)min(v + r, v1 - 1) * H +
+                                        (size_t)min(lane + 64 * t, n_ch - 1) * 16);
         float acc[kRows][M_T];
 #pragma unroll
         for (int r = 0; r < kRows; ++r)
@@ -163,8 +162,10 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
         for (int t = 0; t < T; ++t) {
             const int ch = lane + 64 * t;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                xr[m][t][j] = (ch < n_ch) ? x[(size_t)m * (H / 2) + ch * 4 + j] : 0u;
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t xv = x[(size_t)m * (H / 2) + min(ch, n_ch - 1) * 4 + j];
+                xr[m][t][j] = (ch < n_ch) ? xv : 0u;
+            }
         }
     const uint8_t* base = reinterpret_cast<const uint8_t*>(wt);
     const int v0 = gw * rows_per_wave;
@@ -174,13 +175,9 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
 #pragma unroll
         for (int r = 0; r < kRows; ++r)
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int ch = lane + 64 * t;
-                if (v + r < v1 && ch < n_ch)
-                    c[r][t] = load_stream16(base + ((size_t)(v + r) * H + (size_t)ch * 8) * 2);
-                else
-                    c[r][t] = u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int t = 0; t < T; ++t)
+                c[r][t] = load_stream16(base + ((size_t)min(v + r, v1 - 1) * H +
+                                                (size_t)min(lane + 64 * t, n_ch - 1) * 8) * 2);
         float acc[kRows][M_T];
 #pragma unroll
         for (int r = 0; r < kRows; ++r)

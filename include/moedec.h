@@ -100,29 +100,30 @@ int moe_route_topk(const float* logits, int M, int E, int k,
  * = even k; scales [N][K/32] bytes.  Experts are stacked along a leading axis.
  *
  * The FFN kernel reads a packed layout in which one 64-lane wave fetches one
- * contiguous 1 KiB chunk per step:
- *   gate/up, per expert, KB = H/32 blocks, KB4 = ceil(KB/4), I/32 row groups:
- *     codes  [I/32][KB][64][16]: lane l < 32 holds gate row 32r+l, lane l >= 32
- *            up row 32r+l-32, the 16 code bytes of block q
- *     scales [I/32][KB4][64][4]: byte b of lane l's word p = scale of block 4p+b
- *            (0 beyond KB)
- *   down, per expert, KB = I/32, KB4 = ceil(KB/4), H/64 row groups:
- *     codes  [H/64][KB][64][16]: lane l holds row 64g+l
- *     scales [H/64][KB4][64][4]
- * The packing is a byte permutation (plus zero padding of scales); it is done
- * once, by the two calls below.
+ * contiguous 1 KiB chunk per load step and lane l holds the 16 code bytes (one
+ * MX block) of row 16u + (l & 15), MX block 4c + (l >> 4).  Per expert, with
+ * KBH4 = ceil(H/32 / 4) and KBI4 = ceil(I/32 / 4):
+ *   gate/up, unit u = rows 16u..16u+15 of both W_gate and W_up:
+ *     codes  [I/16][KBH4][2][64][16]   half 0 = gate rows, half 1 = the same up rows
+ *     scales [I/16][KBH4][64] u16      low byte = gate scale, high byte = up scale
+ *   down, unit u = output rows 16u..16u+15:
+ *     codes  [H/16][KBI4][64][16]
+ *     scales [H/16][KBI4][64] u8
+ * MX blocks past the end of a row (block count not a multiple of four) are
+ * zero codes with scale 127.  The packing is a byte permutation plus that
+ * padding; it is done once, by the two calls below.
  * ---------------------------------------------------------------------- */
 typedef struct {
     size_t gu_codes, gu_scales, dn_codes, dn_scales;   /* bytes per expert */
 } moedec_mxfp4_sizes;
 
 /* Per-expert packed sizes; returns MOEDEC_ERR_SHAPE unless H % 64 == 0,
- * I % 32 == 0, 64 <= H <= 16384, 32 <= I <= 16384.  `out` is host memory. */
+ * I % 32 == 0, 64 <= H <= 4096, 32 <= I <= 2048.  `out` is host memory. */
 int moedec_mxfp4_packed_sizes(int H, int I, moedec_mxfp4_sizes* out);
 
 /* gate, up: canonical [n_experts][I][H/2] codes, [n_experts][I][H/32] scales.
- * Output: n_experts consecutive packed experts.  Codes pointers 16-byte
- * aligned, scale outputs 4-byte aligned. */
+ * Output: n_experts consecutive packed experts.  Code pointers 16-byte
+ * aligned, the gate/up scale output 2-byte aligned. */
 int moe_pack_gateup_mxfp4(const uint8_t* gate_codes, const uint8_t* gate_scales,
                           const uint8_t* up_codes, const uint8_t* up_scales,
                           int n_experts, int H, int I,
@@ -141,7 +142,7 @@ typedef struct {
     uint32_t magic;                    /* MOEDEC_MOE_MAGIC */
     int32_t  E, H, I;
     const uint8_t* gu_codes;           /* [E] packed gate/up codes (16-byte aligned) */
-    const uint8_t* gu_scales;          /* [E] packed gate/up scales (4-byte aligned) */
+    const uint8_t* gu_scales;          /* [E] packed gate/up scales (2-byte aligned) */
     const uint8_t* dn_codes;           /* [E] packed down codes */
     const uint8_t* dn_scales;          /* [E] packed down scales */
     const uint8_t* sh_gu_codes;        /* shared expert, same per-expert layout */
@@ -160,14 +161,18 @@ typedef struct {
  * accumulation, h kept in float32, y rounded once to bf16 (nearest even).
  *
  * w           host pointer to the layer's packed weights
- * x_bf16      [M][H] bf16, 4-byte aligned
+ * x_bf16      [M][H] bf16, 16-byte aligned
  * dispatch    from moe_route_topk for the same M (and k <= k_max)
  * k_max       the k used for routing (sizes the launch; 1..32)
  * y_bf16      [M][H] bf16 output, 4-byte aligned
  * y_f32       [M][H] float32 output or NULL
  * workspace   >= moe_ffn_workspace_bytes(M, k_max, H, I) bytes, 16-byte
  *             aligned, ZERO-FILLED ONCE before its first use; every call
- *             leaves it ready for the next.  Calls sharing it must not overlap.
+ *             leaves it ready for the next (its counters are reset by the
+ *             kernel).  Calls sharing it must not overlap.
+ * One kernel launch: gate/up, SiLU*mul, down, the weighted combine and the
+ * rounding are fused.  Shapes: 64 <= H <= 4096, H % 64 == 0; 32 <= I <= 2048,
+ * I % 32 == 0; 1 <= E <= 1024.
  * Values outside the formats' domain (E8M0 code 0 or 255, NaN) give
  * undefined results.
  */
@@ -178,6 +183,29 @@ int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, in
                          uint16_t* y_bf16, float* y_f32,
                          void* workspace, size_t workspace_bytes,
                          moedec_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Fused MoE layer: moe_route_topk followed by moe_expert_ffn_mxfp4 in ONE
+ * kernel launch (same results).  [card background and #1, #3; news where the
+ * speed comes from]  Each block of the launch selects the top-k experts of
+ * every token from the logits itself, so the FFN starts without waiting for
+ * a separate routing launch.
+ *
+ * logits      [M][E] float32 (E = w->E), 4-byte aligned
+ * k           experts per token, 1 <= k <= min(E, 32)
+ * topk_ids, topk_w, dispatch   optional outputs (NULL to skip), identical to
+ *             what moe_route_topk writes for the same logits
+ * workspace   >= moe_ffn_workspace_bytes(M, k, H, I), as for
+ *             moe_expert_ffn_mxfp4 (the two calls may share one workspace)
+ * Other arguments and limits as moe_expert_ffn_mxfp4.
+ * Both FFN calls run a persistent grid of 3 blocks per CU that must be
+ * resident together; they wait (boundedly) for each other's blocks, so do not
+ * run them concurrently with another kernel that holds most of the GPU.
+ */
+int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits,
+                    int M, int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
+                    uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
+                    moedec_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * LM head with online FP8 weights.  [news where the speed comes from; card

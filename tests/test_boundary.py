@@ -28,7 +28,7 @@ def m():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("moe_route_topk", "moe_expert_ffn_mxfp4", "lmhead_quant_fp8", "lmhead_gemv_fp8",
+    for want in ("moe_route_topk", "moe_expert_ffn_mxfp4", "moe_layer_mxfp4", "lmhead_quant_fp8", "lmhead_gemv_fp8",
                  "lmhead_gemv_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
                  "moedec_last_error", "moedec_abi_version"):
@@ -88,10 +88,11 @@ def test_packed_sizes(m):
     # Ling-shaped expert: packing adds no padding (80 and 24 blocks are multiples of 4)
     assert (s.gu_codes, s.gu_scales, s.dn_codes, s.dn_scales) == (1966080, 122880, 983040, 61440)
     assert s.gu_codes + s.gu_scales + s.dn_codes + s.dn_scales == 3133440
+    # tiny expert: 2 MX blocks along I are padded to 4 in the down stream
     t = m.packed_sizes(256, 64)
-    assert (t.gu_codes, t.gu_scales, t.dn_codes, t.dn_scales) == (16384, 1024, 8192, 1024)
+    assert (t.gu_codes, t.gu_scales, t.dn_codes, t.dn_scales) == (16384, 1024, 16384, 1024)
     out = m.MXFP4Sizes()
-    for H, I in ((2560, 48), (96, 64), (32, 64), (256, 0)):
+    for H, I in ((2560, 48), (96, 64), (32, 64), (256, 0), (4160, 64), (256, 2080)):
         assert m.lib.moedec_mxfp4_packed_sizes(H, I, ctypes.byref(out)) == -3
 
 
@@ -126,6 +127,23 @@ def test_ffn_argument_checks(m):
     assert call(_weights(m, E=4), k=8) == -3
     assert call(_weights(m, gu_codes=(1 << 20) + 4)) == -2
     assert call(_weights(m), x=ODD) == -2
+    assert call(_weights(m), x=ctypes.c_void_p((1 << 20) + 4)) == -2      # x needs 16 bytes
+    assert call(_weights(m, I=4096)) == -3
+    assert call(_weights(m, H=8192)) == -3
+    assert call(_weights(m), n=ws - 1) == -5
+
+
+def test_fused_layer_argument_checks(m):
+    L = m.lib
+    ws = m.ffn_workspace_bytes(1, 8, 2560, 768)
+    call = lambda w, lg=FAKE, M=1, k=8, n=ws, disp=None: L.moe_layer_mxfp4(
+        ctypes.byref(w), FAKE, lg, M, k, None, None, disp, FAKE, None, FAKE, n, None)
+    assert call(_weights(m), lg=None) == -1
+    assert call(_weights(m, magic=1)) == -4
+    assert call(_weights(m), k=33) == -3
+    assert call(_weights(m), M=5) == -3
+    assert call(_weights(m), lg=ODD) == -2
+    assert call(_weights(m), disp=ctypes.c_void_p((1 << 20) + 8)) == -2
     assert call(_weights(m), n=ws - 1) == -5
 
 

@@ -78,30 +78,44 @@ def test_route_shapes(m, M, E, k):
 
 # ---------------------------------------------------------------- packing
 
+PAD_SCALE = 127
+
+
+def _lanes(a, n_units, kb4):
+    """[n][rows][kb4*4][...] -> [n][rows/16][kb4][64][...] with lane l = row
+    16u + (l & 15), MX block 4c + (l >> 4)."""
+    n = a.shape[0]
+    tail = a.shape[3:]
+    a = a.reshape((n, n_units, 16, kb4, 4) + tail)
+    a = a.transpose((0, 1, 3, 4, 2) + tuple(range(5, 5 + len(tail))))
+    return np.ascontiguousarray(a).reshape((n, n_units, kb4, 64) + tail)
+
+
+def _pad_blocks(codes, scales, kb4):
+    n, rows, half_k = codes.shape
+    kb = 2 * half_k // 32
+    c = np.zeros((n, rows, kb4 * 4, 16), np.uint8)
+    c[:, :, :kb] = codes.reshape(n, rows, kb, 16)
+    s = np.full((n, rows, kb4 * 4), PAD_SCALE, np.uint8)
+    s[:, :, :kb] = scales
+    return c, s
+
+
 def np_pack_gateup(gc, gs, uc, us):
     n, I, hh = gc.shape
-    KB = 2 * hh // 32
-    KB4 = (KB + 3) // 4
-    codes = np.empty((n, I // 32, KB, 64, 16), np.uint8)
-    codes[:, :, :, :32] = gc.reshape(n, I // 32, 32, KB, 16).transpose(0, 1, 3, 2, 4)
-    codes[:, :, :, 32:] = uc.reshape(n, I // 32, 32, KB, 16).transpose(0, 1, 3, 2, 4)
-    scales = np.zeros((n, I // 32, KB4, 64, 4), np.uint8)
-    for half, src in ((0, gs), (1, us)):
-        pad = np.zeros((n, I, 4 * KB4), np.uint8)
-        pad[:, :, :KB] = src
-        scales[:, :, :, 32 * half:32 * half + 32] = pad.reshape(n, I // 32, 32, KB4, 4).transpose(0, 1, 3, 2, 4)
+    kb4 = (2 * hh // 32 + 3) // 4
+    gcp, gsp = _pad_blocks(gc, gs, kb4)
+    ucp, usp = _pad_blocks(uc, us, kb4)
+    codes = np.stack([_lanes(gcp, I // 16, kb4), _lanes(ucp, I // 16, kb4)], axis=3)
+    scales = np.stack([_lanes(gsp, I // 16, kb4), _lanes(usp, I // 16, kb4)], axis=-1)
     return codes.reshape(-1), scales.reshape(-1)
 
 
 def np_pack_down(dc, ds):
     n, H, hi = dc.shape
-    KB = 2 * hi // 32
-    KB4 = (KB + 3) // 4
-    codes = dc.reshape(n, H // 64, 64, KB, 16).transpose(0, 1, 3, 2, 4)
-    pad = np.zeros((n, H, 4 * KB4), np.uint8)
-    pad[:, :, :KB] = ds
-    scales = pad.reshape(n, H // 64, 64, KB4, 4).transpose(0, 1, 3, 2, 4)
-    return np.ascontiguousarray(codes).reshape(-1), np.ascontiguousarray(scales).reshape(-1)
+    kb4 = (2 * hi // 32 + 3) // 4
+    dcp, dsp = _pad_blocks(dc, ds, kb4)
+    return _lanes(dcp, H // 16, kb4).reshape(-1), _lanes(dsp, H // 16, kb4).reshape(-1)
 
 
 @pytest.mark.parametrize("H,I,E", [(256, 64, 4), (192, 96, 3), (2560, 768, 2)])
@@ -250,3 +264,96 @@ def test_ffn_ling_shared_tokens_overlap(m, ling_layer):
     lg = np.repeat(synth.logits_f32(9, 0, 1, synth.LING.E), 4, axis=0)
     lg[1:, :] += np.float32(0.0)
     _check_case(m, ling_layer, xb, lg, 8, _ling_expert, _ling_expert(synth.LING.E), "ling M=4 same experts")
+
+
+# ---------------------------------------------------------------- fused layer (routing in the FFN launch)
+
+def _run_fused(m, W, x_bits, logits, k, ws=None):
+    x = bf16_tensor(x_bits)
+    lg = torch.from_numpy(logits).cuda()
+    M = x.shape[0]
+    ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((M, k), dtype=torch.float32, device="cuda")
+    disp = torch.zeros(m.DISPATCH_BYTES, dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = m.make_ffn_workspace(M, k, W.H, W.I, "cuda")
+    y, y32 = m.moe_layer(W, x, lg, k, ws, ids=ids, topk_w=wts, dispatch=disp)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), wts.cpu().numpy(), disp, bits_of(y), y32.cpu().numpy()
+
+
+def _check_fused(m, W, x_bits, logits, k, expert_fn, shared, what):
+    say("fused", what)
+    ids, wts, disp, yb, y32 = _run_fused(m, W, x_bits, logits, k)
+    # routing outputs equal those of the separate routing call, bit for bit
+    r_ids, r_w, r_disp = m.route_topk(torch.from_numpy(logits).cuda(), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids, r_ids.cpu().numpy())
+    np.testing.assert_array_equal(wts.view(np.uint32), r_w.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(disp.cpu().numpy(), r_disp.cpu().numpy())
+    # the layer output equals the two-call path bit for bit, and the oracle within tolerance
+    _, yb2, y322, _ = _run_ffn(m, W, x_bits, logits, k)
+    np.testing.assert_array_equal(y32.view(np.uint32), y322.view(np.uint32))
+    np.testing.assert_array_equal(yb, yb2)
+    ref_ids, _, ref_y = oracle_layer(x_bits, logits, k, expert_fn, shared)
+    np.testing.assert_array_equal(ids, ref_ids)
+    check_acc(y32, ref_y, what)
+    check_bf16(yb, y32, ref_y, what)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_fused_tiny(m, M):
+    W, xb, lg, ef, sh, k = _host_layer_case(m, synth.TINY, M)
+    _check_fused(m, W, xb, lg, k, ef, sh, f"tiny M={M}")
+
+
+@pytest.mark.parametrize("H,I,E,k,M", [(192, 96, 8, 3, 2), (320, 160, 5, 2, 4), (64, 32, 3, 3, 1),
+                                       (4096, 64, 40, 32, 4)])
+def test_fused_ragged_and_extreme(m, H, I, E, k, M):
+    """Ragged block counts, and the largest hidden size with k = 32 at M = 4
+    (129 slots, many slot groups)."""
+    shape = synth.MoEShape(H=H, I=I, E=E, k=k, scale_lo=119, scale_hi=123)
+    W, xb, lg, ef, sh, k = _host_layer_case(m, shape, M, seed=4)
+    _check_fused(m, W, xb, lg, k, ef, sh, f"fused H={H} I={I} E={E} k={k} M={M}")
+
+
+def test_fused_tie_heavy_routing(m):
+    W, xb, _, ef, sh, k = _host_layer_case(m, synth.TINY, 4)
+    rng = np.random.default_rng(7)
+    lg = rng.choice(np.float32([-1.0, 0.0, -0.0, 1.0]), size=(4, synth.TINY.E))
+    _check_fused(m, W, xb, lg, k, ef, sh, "tiny M=4 tied logits")
+
+
+@pytest.mark.parametrize("name", ["ling_m1", "ling_m4"])
+def test_fused_ling(m, ling_layer, name):
+    wl = synth.WORKLOADS[name]
+    xb, lg = synth.moe_inputs(wl)
+    _check_fused(m, ling_layer, xb, lg, 8, _ling_expert, _ling_expert(synth.LING.E), f"fused {name}")
+
+
+def test_paths_share_one_workspace(m):
+    """The fused and two-call paths alternate on one workspace with different
+    M; every call still matches the oracle (launch generations stay in step)."""
+    W, xb, lg, ef, sh, k = _host_layer_case(m, synth.TINY, 4)
+    ws = m.make_ffn_workspace(4, k, W.H, W.I, "cuda")
+    for M, fused in ((4, True), (1, False), (2, True), (4, False), (3, True)):
+        say("shared workspace", M, fused)
+        xs, ls = xb[:M].copy(), lg[:M].copy()
+        if fused:
+            _, _, _, yb, y32 = _run_fused(m, W, xs, ls, k, ws)
+        else:
+            _, yb, y32, _ = _run_ffn(m, W, xs, ls, k, ws)
+        _, _, ref_y = oracle_layer(xs, ls, k, ef, sh)
+        check_acc(y32, ref_y, f"shared ws M={M} fused={fused}")
+
+
+def test_workspace_error_flag_stays_clear(m):
+    """No wait in any call so far gave up (the flag word follows the
+    per-block launch counters at the start of the workspace)."""
+    W, xb, lg, ef, sh, k = _host_layer_case(m, synth.TINY, 2)
+    ws = m.make_ffn_workspace(2, k, W.H, W.I, "cuda")
+    for _ in range(3):
+        _run_fused(m, W, xb, lg, k, ws)
+        _run_ffn(m, W, xb, lg, k, ws)
+    flag = ws[4096 * 4:4096 * 4 + 4].cpu().numpy().view(np.uint32)[0]
+    assert flag == 0
