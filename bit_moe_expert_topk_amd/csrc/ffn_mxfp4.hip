@@ -10,7 +10,8 @@
 // that use it.
 //
 // Grid.  A persistent grid of three blocks per CU, small enough that every
-// block is resident at once, walks the work units round-robin
+// block is resident at once (checked against the occupancy before each
+// launch), walks the work units round-robin
 // (unit = blockIdx.x + i * gridDim.x).  Unit order is: gate/up units, then the
 // down units of slot groups 1.., then those of group 0.  Every block therefore
 // finishes all its gate/up units before it can wait for anything, and all its
@@ -31,7 +32,7 @@
 //     (launch generation, value).
 //   * down (group, g): for output rows 16g..16g+15, the sum over the group's
 //     slots of W_down[e] (w * h).  It issues its weight loads, then loads the
-//     group's tagged h words -- re-reading while any tag is stale -- stages
+//     group's tagged h words -- re-reading those whose tag is stale -- stages
 //     w * h in LDS and finishes.  With one group it writes y; otherwise groups
 //     >= 1 publish tagged partial rows and the group-0 unit adds them in group
 //     order and writes y (deterministic).
@@ -40,9 +41,11 @@
 // holding the value and the launch generation, with device-coherent stores
 // (single-copy atomic, through to the level all CUs share), and read with
 // device-coherent loads: a reader knows a word is from this launch when its
-// tag matches.  Each block keeps the generation in its own workspace word;
-// all blocks of every launch on a workspace see the same count, since the
-// grid size is fixed per device, so nothing needs resetting between calls.
+// tag matches.  The generation is a launch count kept in kMaxGrid workspace
+// words that every launch advances together (block b writes words b, b +
+// grid, ...), so each block reads it from its own word and all blocks of a
+// launch agree, whatever grids earlier launches used; nothing needs resetting
+// between calls.
 //
 // Lanes.  A 64-lane wave reads one 1 KiB chunk per load step: lane l holds the
 // 16 code bytes (32 E2M1 values, one MX block) of row 16u + (l & 15) and MX
@@ -72,12 +75,23 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kUnitRows = 16;
 constexpr int kXBlock = 80;          // LDS bytes per 32-value block of x (64 + 16 pad)
 constexpr int kHBlock = 144;         // LDS bytes per 32-value block of h (128 + 16 pad)
-constexpr int kDnBatch = 8;          // down chunks per load batch (two batches in flight)
-constexpr int kStageBatch = 8;       // float4 loads of h in flight per thread while staging
+// Down chunks per load batch; two batches (A, B) are in flight before h is
+// staged, which covers the 13-14 chunks per wave of a 2560 x 768 layer at M = 1.
+constexpr int kDnBatch = 7;
+// 16-byte loads of tagged h in flight per thread while staging.  A slot
+// group holds at most as many pairs as one batch stages (see ffn_layout), so
+// a down unit sees h after a single round trip once it is there.
+template <int M_T>
+constexpr int stage_batch() { return 8; }
 constexpr int kMaxGroups = MOEDEC_MAX_M * MOEDEC_MAX_K + MOEDEC_MAX_M;
 constexpr int kMaxPairs = kMaxGroups + MOEDEC_MAX_M;
 constexpr int kMaxGrid = 4096;
-constexpr int kBlocksPerCU = 3;
+// Co-resident blocks per CU (168 VGPRs per lane).  Three blocks per CU give a
+// one-token 2560 x 768 layer a block for each of its 592 units, so every down
+// unit issues its weight loads right after routing; the generation words let
+// the count differ per token count.
+template <int M_T>
+constexpr int blocks_per_cu() { return 3; }
 constexpr uint32_t kSpinLimit = 1u << 20;   // bounded waits; reached only if co-residency fails
 
 struct FfnArgs {
@@ -167,6 +181,10 @@ __device__ __forceinline__ f32x2 fp4x2_f32(uint32_t word, float s, int sel) {
 // ---------------------------------------------------------------------------
 // prologue: the slot table
 
+// Table from a dispatch table (moe_route_topk's, or the caller's): slot 0 is
+// the shared expert (listed last in the table), then the valid routed entries
+// in table order.  Entries with an expert id outside [0, E) or an empty token
+// mask are dropped, so every slot serves at least one token.  Wave 0.
 template <int M_T>
 __device__ void table_from_dispatch(const FfnArgs& a, SlotTable& T) {
     if (wave_id_uniform() != 0) return;
@@ -174,26 +192,31 @@ __device__ void table_from_dispatch(const FfnArgs& a, SlotTable& T) {
     const moedec_dispatch* __restrict__ d = a.disp;
     const uint32_t full = (1u << M_T) - 1u;
     const int n_tab = max(1, min(d->n_slots, a.max_slots));
-    for (int s = lane; s < n_tab; s += kWave) {
-        const int tab = (s == 0) ? n_tab - 1 : s - 1;   // the table lists the shared expert last
-        int e = d->expert[tab];
-        uint32_t msk = d->token_mask[tab] & full;
-        float wt[M_T];
+    if (lane == 0) {
+        T.expert[0] = a.E;
+        T.mask[0] = full;
 #pragma unroll
-        for (int m = 0; m < M_T; ++m) wt[m] = d->weight[tab][m];
-        if (s == 0) {
-            e = a.E;
-            msk = full;
-        } else if (e < 0 || e >= a.E || msk == 0u) {
-            e = -1;
-            msk = 0u;
-        }
-        T.expert[s] = e;
-        T.mask[s] = msk;
-#pragma unroll
-        for (int m = 0; m < M_T; ++m) T.weight[s][m] = wt[m];
+        for (int m = 0; m < M_T; ++m) T.weight[0][m] = d->weight[n_tab - 1][m];
     }
-    if (lane == 0) T.n_slots = n_tab;
+    int n = 1;
+    for (int s0 = 1; s0 < n_tab; s0 += kWave) {
+        const int s = s0 + lane;
+        const int tab = min(s, n_tab - 1) - 1;            // clamped: always in bounds
+        const int e = d->expert[tab];
+        const uint32_t msk = d->token_mask[tab] & full;
+        const bool valid = s < n_tab && e >= 0 && e < a.E && msk != 0u;
+        const uint64_t bal = __ballot(valid);
+        const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (valid) {
+            T.expert[pos] = e;
+            T.mask[pos] = msk;
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) T.weight[pos][m] = d->weight[tab][m];
+        }
+        n += __popcll(bal);
+    }
+    if (lane == 0) T.n_slots = n;
 }
 
 // One token (M = 1): wave 0 builds the whole table from its top-k -- slot
@@ -484,34 +507,33 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     const size_t rg_codes = (size_t)g * a.kbi4 * 1024;
     const size_t rg_scales = (size_t)g * a.kbi4 * 64;
     // Weights go in batches of kDnBatch chunks into two register sets (A, B):
-    // batch 0 before h is staged, each next batch while the previous computes.
+    // batches 0 and 1 before h is staged, each next batch while the previous
+    // computes.
     u32x4 cwA[kDnBatch], cwB[kDnBatch];
     uint32_t scA[kDnBatch], scB[kDnBatch];
+    // items past i_end load the last item again (unused); the walk over
+    // (slot, chunk) is branch-free so that no per-item state is carried
     auto load_batch = [&](int i0, u32x4 (&cw)[kDnBatch], uint32_t (&scw)[kDnBatch]) {
         int ls = i0 / a.kbi4;
         int ch = i0 - ls * a.kbi4;
-        const uint8_t* cp = nullptr;
-        const uint8_t* sp = nullptr;
 #pragma unroll
         for (int k = 0; k < kDnBatch; ++k) {
-            if (k == 0 || i0 + k < i_end) {              // past the end: reload the last item (unused)
-                const int e = T.expert[sb + ls];
-                const uint8_t* cbase = (e == a.E) ? a.sh_dn_codes
-                                                  : a.dn_codes + (size_t)max(e, 0) * a.dn_codes_stride;
-                const uint8_t* sbase = (e == a.E) ? a.sh_dn_scales
-                                                  : a.dn_scales + (size_t)max(e, 0) * a.dn_scales_stride;
-                cp = cbase + rg_codes + (size_t)ch * 1024 + lane * 16;
-                sp = sbase + rg_scales + (size_t)ch * 64 + lane;
-                if (++ch == a.kbi4) {
-                    ch = 0;
-                    ++ls;
-                }
-            }
+            const int e = max(T.expert[sb + ls], 0);
+            const bool shared = e == a.E;
+            const size_t ce = shared ? 0 : (size_t)e * a.dn_codes_stride;
+            const size_t se = shared ? 0 : (size_t)e * a.dn_scales_stride;
+            const uint8_t* cp = (shared ? a.sh_dn_codes : a.dn_codes) + ce + rg_codes + ch * 1024 + lane * 16;
+            const uint8_t* sp = (shared ? a.sh_dn_scales : a.dn_scales) + se + rg_scales + ch * 64 + lane;
             cw[k] = load_stream16(cp);
             scw[k] = *sp;
+            const bool adv = i0 + k + 1 < i_end;
+            const bool wrap = ch + 1 == a.kbi4;
+            ls += (adv && wrap) ? 1 : 0;
+            ch = adv ? (wrap ? 0 : ch + 1) : ch;
         }
     };
     if (i_begin < i_end) load_batch(i_begin, cwA, scA);
+    if (i_begin + kDnBatch < i_end) load_batch(i_begin + kDnBatch, cwB, scB);
 
     if (w == 0) {
         // the group's (slot, token) pairs
@@ -527,58 +549,68 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
 
     // Stage w * h: pair p, MX block q at p * pair_bytes + q * 144; padding is
     // zero.  Each 16-byte load brings two tagged h words.  The loads go out
-    // right behind the weight loads; a batch is read again (after a pause)
-    // while any of its tags is not this launch's, so detection and transfer
-    // take one round trip once h is there.
+    // right behind the weight loads; after a pause, only the loads whose tags
+    // are not this launch's are issued again, until every tag of the batch
+    // is, so detection and transfer take one round trip once h is there.
     {
         const __amdgpu_buffer_rsrc_t hrs =
             __builtin_amdgcn_make_buffer_rsrc(a.h, 0, a.h_bytes, kBufferRsrcWord3);
         const int per_pair = a.kbi4 * 4 * 16;              // 16-byte loads per pair, padding included
         const int total = n_pairs * per_pair;
-        for (int i0 = 0; i0 < total; i0 += kThreads * kStageBatch) {
-            u32x4 raw[kStageBatch];
-            auto issue = [&]() {
+        constexpr int kStage = stage_batch<M_T>();
+        static_assert(kStage <= 32, "one done bit per load");
+        const uint32_t all = (1u << kStage) - 1u;
+        for (int i0 = 0; i0 < total; i0 += kThreads * kStage) {
+            // Load q of this thread covers pair pf[q] >> 16, h words k, k + 1
+            // with k = pf[q] & 0xFFFF.  Bit q of `done`: staged, or nothing to
+            // stage (past the pairs; MX padding past I, written as zeros here).
+            int pf[kStage];
+            uint32_t done = 0;
 #pragma unroll
-                for (int q = 0; q < kStageBatch; ++q) {
-                    const int idx = min(i0 + tid + kThreads * q, total - 1);   // clamped: always in bounds
-                    const int p = idx / per_pair;
-                    const int k = min((idx - p * per_pair) * 2, a.I - 2);
-                    const int src = T.pair[p];
-                    const int off = (((src >> 8) * M_T + (src & 0xFF)) * a.I + k) * (int)sizeof(uint64_t);
-                    raw[q] = __builtin_amdgcn_raw_buffer_load_b128(hrs, off, 0, kLoadCoherent);
+            for (int q = 0; q < kStage; ++q) {
+                const int idx = i0 + tid + kThreads * q;
+                const int ic = min(idx, total - 1);
+                const int p = ic / per_pair;
+                const int k = (ic - p * per_pair) * 2;
+                pf[q] = (p << 16) | k;
+                if (idx >= total) {
+                    done |= 1u << q;
+                } else if (k >= a.I) {
+                    *reinterpret_cast<float2*>(lds + p * a.pair_bytes + (k >> 5) * kHBlock + (k & 31) * 4) =
+                        make_float2(0.f, 0.f);
+                    done |= 1u << q;
                 }
-            };
-            issue();
+            }
             uint32_t spins = 0;
             for (;;) {
-                bool ok = true;
+                // every attempt consumes its own loads: nothing is carried over
+                u32x4 raw[kStage];
 #pragma unroll
-                for (int q = 0; q < kStageBatch; ++q) {
-                    const int idx = i0 + tid + kThreads * q;
-                    const int f = idx - (idx / per_pair) * per_pair;
-                    const bool live = idx < total && 2 * f < a.I;
-                    ok &= !live || (raw[q][1] == gen && raw[q][3] == gen);
+                for (int q = 0; q < kStage; ++q) {
+                    if (!((done >> q) & 1u)) {
+                        const int src = T.pair[pf[q] >> 16];
+                        const int off = (((src >> 8) * M_T + (src & 0xFF)) * a.I + (pf[q] & 0xFFFF)) *
+                                        (int)sizeof(uint64_t);
+                        raw[q] = __builtin_amdgcn_raw_buffer_load_b128(hrs, off, 0, kLoadCoherent);
+                    }
                 }
-                if (__syncthreads_and(ok)) break;
+#pragma unroll
+                for (int q = 0; q < kStage; ++q) {
+                    if (!((done >> q) & 1u) && raw[q][1] == gen && raw[q][3] == gen) {
+                        const int p = pf[q] >> 16, k = pf[q] & 0xFFFF;
+                        const int src = T.pair[p];
+                        const float wt = T.weight[src >> 8][src & 0xFF];
+                        *reinterpret_cast<float2*>(lds + p * a.pair_bytes + (k >> 5) * kHBlock + (k & 31) * 4) =
+                            make_float2(__uint_as_float(raw[q][0]) * wt, __uint_as_float(raw[q][2]) * wt);
+                        done |= 1u << q;
+                    }
+                }
+                if (__syncthreads_and(done == all)) break;
                 if (++spins > kSpinLimit) {                 // never expected: flag and go on
                     if (tid == 0) atomicOr(a.err, 1u);
                     break;
                 }
-                __builtin_amdgcn_s_sleep(16);                // not there yet: pause before re-reading
-                issue();
-            }
-#pragma unroll
-            for (int q = 0; q < kStageBatch; ++q) {
-                const int idx = i0 + tid + kThreads * q;
-                if (idx < total) {
-                    const int p = idx / per_pair;
-                    const int k = (idx - p * per_pair) * 2;
-                    const int src = T.pair[p];
-                    const float wt = T.weight[src >> 8][src & 0xFF];
-                    float2 o = make_float2(__uint_as_float(raw[q][0]) * wt, __uint_as_float(raw[q][2]) * wt);
-                    if (k >= a.I) o = make_float2(0.f, 0.f);         // MX blocks past I
-                    *reinterpret_cast<float2*>(lds + p * a.pair_bytes + (k >> 5) * kHBlock + (k & 31) * 4) = o;
-                }
+                __builtin_amdgcn_s_sleep(4);                 // not there yet: pause before re-reading
             }
         }
     }
@@ -595,8 +627,10 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
         for (int k = 0; k < kDnBatch; ++k) {
             if (i0 + k < i_end) {
                 const int s = sb + ls;
-                const uint32_t msk = T.mask[s];
-                const int p0 = T.start[s] - pbase;
+                // one token: every slot serves it, so slot sb + j holds pair j
+                // (no table lookups on the way to the LDS reads)
+                const uint32_t msk = (M_T == 1) ? 1u : T.mask[s];
+                const int p0 = (M_T == 1) ? ls : T.start[s] - pbase;
                 const float sc = e8m0_to_f32(scw[k]);
                 const uint8_t* hq = lds + (4 * ch + quarter) * kHBlock;
                 int p = p0;
@@ -627,14 +661,14 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
                 ch = 0;
                 ++ls;
             }
-            __builtin_amdgcn_sched_barrier(0);    // bound register pressure: one item at a time
+            if (M_T > 1) __builtin_amdgcn_sched_barrier(0);   // bound register pressure: one item at a time
         }
     };
     for (int i0 = i_begin; i0 < i_end; i0 += 2 * kDnBatch) {
-        if (i0 + kDnBatch < i_end) load_batch(i0 + kDnBatch, cwB, scB);
         compute_batch(i0, cwA, scA);
         if (i0 + 2 * kDnBatch < i_end) load_batch(i0 + 2 * kDnBatch, cwA, scA);
         if (i0 + kDnBatch < i_end) compute_batch(i0 + kDnBatch, cwB, scB);
+        if (i0 + 3 * kDnBatch < i_end) load_batch(i0 + 3 * kDnBatch, cwB, scB);
     }
 
     float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][16]
@@ -696,7 +730,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
 }
 
 template <int M_T, int NB, bool ROUTE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBlocksPerCU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(blocks_per_cu<M_T>())))
 void moe_ffn_kernel(FfnArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ SlotTable T;
@@ -716,8 +750,11 @@ void moe_ffn_kernel(FfnArgs a) {
         for (int i = 0; i < kXPieces; ++i) xv[i] = xg[min(tid + kThreads * i, n_pieces - 1)];
     }
     if (tid == kThreads - kWave) {                        // wave 3: keeps wave 0 free to route
-        const uint32_t g = a.gens[blockIdx.x] + 1u;       // this block's launch count on the workspace
-        a.gens[blockIdx.x] = g;
+        // the launch count on the workspace: every one of the kMaxGrid words
+        // advances once per launch (block b takes b, b + grid, ...), so all
+        // blocks agree whatever the grid of earlier launches
+        const uint32_t g = a.gens[blockIdx.x] + 1u;
+        for (int j = blockIdx.x; j < kMaxGrid; j += gridDim.x) a.gens[j] = g;
         s_gen = g;
     }
     constexpr bool kDirectGroups = ROUTE && M_T == 1;     // the table arrives with its groups
@@ -768,28 +805,30 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr size_t kLdsTarget = 40 * 1024;
 
-// Grid: kBlocksPerCU blocks per CU, the same for every launch on a device.
+// CU count of the current device (cached); the grid is blocks_per_cu * CUs.
 struct DeviceInfo {
-    int grid = 0;
+    int cus = 0;
     std::mutex mu;
 };
 DeviceInfo g_dev[64];
 
-int device_grid() {
+int device_cus() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     DeviceInfo& d = g_dev[dev];
     std::lock_guard<std::mutex> lock(d.mu);
-    if (d.grid == 0) {
+    if (d.cus == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        d.grid = std::min(kMaxGrid, kBlocksPerCU * cus);
+        d.cus = cus;
     }
-    return d.grid;
+    return d.cus;
 }
 
 template <int M_T, int NB, bool ROUTE>
-hipError_t launch_variant(const FfnArgs& a, int grid, size_t lds, hipStream_t s) {
+hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) {
+    constexpr int kBlocksPerCU = blocks_per_cu<M_T>();
+    const int grid = std::min(kMaxGrid, kBlocksPerCU * cus);
     // every block must be resident at once: check the occupancy of this variant
     static std::atomic<int> occ_ok[256];                      // per LDS size class of 256 B
     const size_t cls = std::min<size_t>((lds + 255) / 256, 255);
@@ -808,13 +847,13 @@ hipError_t launch_variant(const FfnArgs& a, int grid, size_t lds, hipStream_t s)
 }
 
 template <int M_T, bool ROUTE>
-hipError_t launch_m(const FfnArgs& a, int nb, int grid, size_t lds, hipStream_t s) {
+hipError_t launch_m(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     switch (nb) {
-        case 1: return launch_variant<M_T, 1, ROUTE>(a, grid, lds, s);
-        case 2: return launch_variant<M_T, 2, ROUTE>(a, grid, lds, s);
-        case 4: return launch_variant<M_T, 4, ROUTE>(a, grid, lds, s);
-        case 5: return launch_variant<M_T, 5, ROUTE>(a, grid, lds, s);
-        default: return launch_variant<M_T, 8, ROUTE>(a, grid, lds, s);
+        case 1: return launch_variant<M_T, 1, ROUTE>(a, cus, lds, s);
+        case 2: return launch_variant<M_T, 2, ROUTE>(a, cus, lds, s);
+        case 4: return launch_variant<M_T, 4, ROUTE>(a, cus, lds, s);
+        case 5: return launch_variant<M_T, 5, ROUTE>(a, cus, lds, s);
+        default: return launch_variant<M_T, 8, ROUTE>(a, cus, lds, s);
     }
 }
 
@@ -829,9 +868,15 @@ FfnLayout ffn_layout(int M, int k_max, int H, int I) {
                   "each routing wave borrows 64 words of the reduction area");
     const size_t red_bytes = (size_t)kWaves * M * 2 * kUnitRows * sizeof(float);
     const size_t x_bytes = (size_t)M * kbh4 * 4 * kXBlock;
-    const int fit = (int)((kLdsTarget - red_bytes) / L.pair_bytes) - (M - 1);
+    // a group (at most pair_cap + M - 1 pairs: it ends on a slot boundary)
+    // must fit the LDS target; with one token it must also fit one staging
+    // batch of the down unit (more tokens have more units than blocks, and
+    // fewer, larger groups there save partial-row exchanges)
+    const int fit_lds = (int)((kLdsTarget - red_bytes) / L.pair_bytes) - (M - 1);
+    const int loads_per_pair = kbi4 * 4 * 16;                       // 16-byte loads (two h words each)
+    const int fit_stage = (M == 1) ? stage_batch<1>() * kThreads / loads_per_pair : fit_lds;
     const int max_pairs = M * k_max + M;
-    L.pair_cap = std::max(1, std::min(fit, max_pairs));
+    L.pair_cap = std::max(1, std::min(std::min(fit_lds, fit_stage), max_pairs));
     L.max_groups = (max_pairs + L.pair_cap - 1) / L.pair_cap;
     const size_t h_bytes = (size_t)(L.pair_cap + M - 1) * L.pair_bytes;
     const size_t region = std::max(x_bytes, h_bytes);
@@ -852,8 +897,8 @@ hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int
                       float* w_out, moedec_dispatch* disp_out, uint16_t* y_bf16, float* y_f32,
                       void* ws, hipStream_t s) {
     const FfnLayout L = ffn_layout(M, k_max, w.H, w.I);
-    const int grid = device_grid();
-    if (grid <= 0) return hipErrorInvalidDevice;
+    const int cus = device_cus();
+    if (cus <= 0) return hipErrorInvalidDevice;
     uint8_t* base = static_cast<uint8_t*>(ws);
     moedec_mxfp4_sizes sz;
     packed_sizes(w.H, w.I, &sz);
@@ -907,10 +952,10 @@ hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int
     const int nb = cpw <= 1 ? 1 : cpw <= 2 ? 2 : cpw <= 4 ? 4 : cpw <= 5 ? 5 : 8;
     const bool route = logits != nullptr;
     switch (M) {
-        case 1: return route ? launch_m<1, true>(a, nb, grid, L.lds_bytes, s) : launch_m<1, false>(a, nb, grid, L.lds_bytes, s);
-        case 2: return route ? launch_m<2, true>(a, nb, grid, L.lds_bytes, s) : launch_m<2, false>(a, nb, grid, L.lds_bytes, s);
-        case 3: return route ? launch_m<3, true>(a, nb, grid, L.lds_bytes, s) : launch_m<3, false>(a, nb, grid, L.lds_bytes, s);
-        default: return route ? launch_m<4, true>(a, nb, grid, L.lds_bytes, s) : launch_m<4, false>(a, nb, grid, L.lds_bytes, s);
+        case 1: return route ? launch_m<1, true>(a, nb, cus, L.lds_bytes, s) : launch_m<1, false>(a, nb, cus, L.lds_bytes, s);
+        case 2: return route ? launch_m<2, true>(a, nb, cus, L.lds_bytes, s) : launch_m<2, false>(a, nb, cus, L.lds_bytes, s);
+        case 3: return route ? launch_m<3, true>(a, nb, cus, L.lds_bytes, s) : launch_m<3, false>(a, nb, cus, L.lds_bytes, s);
+        default: return route ? launch_m<4, true>(a, nb, cus, L.lds_bytes, s) : launch_m<4, false>(a, nb, cus, L.lds_bytes, s);
     }
 }
 

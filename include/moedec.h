@@ -199,8 +199,10 @@ int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, in
  *             moe_expert_ffn_mxfp4 (the two calls may share one workspace)
  * Other arguments and limits as moe_expert_ffn_mxfp4.
  * Both FFN calls run a persistent grid of 3 blocks per CU that must be
- * resident together; they wait (boundedly) for each other's blocks, so do not
- * run them concurrently with another kernel that holds most of the GPU.
+ * resident together; they wait (boundedly) for each other's
+ * blocks, so do not run them concurrently with another kernel that holds most
+ * of the GPU.  The launch is refused (MOEDEC_ERR_LAUNCH) if the device cannot
+ * hold that many blocks per CU.
  */
 int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits,
                     int M, int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,

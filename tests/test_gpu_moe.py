@@ -206,6 +206,53 @@ def test_ffn_ragged_block_counts(m, H, I, E, k, M):
     _check_case(m, W, xb, lg, k, ef, sh, f"ragged H={H} I={I} E={E} k={k} M={M}")
 
 
+def test_ffn_dispatch_with_invalid_entries(m):
+    """Table entries with an expert id outside [0, E) or an empty token mask
+    contribute nothing: the result equals the oracle over the valid entries,
+    and is bit-identical to the same table with those entries left out."""
+    say("dispatch with invalid entries")
+    M = 3
+    W, xb, lg, ef, sh, k = _host_layer_case(m, synth.TINY, M, seed=3, k=4)
+    x = bf16_tensor(xb)
+    _, _, disp = m.route_topk(torch.from_numpy(lg).cuda(), k)
+    d = m.decode_dispatch(disp)
+    n = d["n_slots"]
+    routed = [(int(d["expert"][i]), int(d["token_mask"][i]), d["weight"][i].copy()) for i in range(n - 1)]
+    shared_entry = (int(d["expert"][n - 1]), int(d["token_mask"][n - 1]), d["weight"][n - 1].copy())
+    assert len(routed) >= 4
+    bad = {0: (-1, routed[0][1]), 2: (synth.TINY.E + 7, routed[2][1]), 3: (routed[3][0], 0)}
+    with_bad = [(bad[i][0], bad[i][1], wt) if i in bad else (e, mk, wt) for i, (e, mk, wt) in enumerate(routed)]
+    valid = [ent for i, ent in enumerate(routed) if i not in bad]
+
+    def table(entries):
+        t = m.Dispatch()
+        rows = entries + [shared_entry]
+        t.n_slots = len(rows)
+        t.M = M
+        for i, (e, mk, wt) in enumerate(rows):
+            t.expert[i] = e
+            t.token_mask[i] = mk
+            for j in range(m.MAX_M):
+                t.weight[i][j] = float(wt[j]) if j < len(wt) else 0.0
+        return torch.frombuffer(bytearray(bytes(t)), dtype=torch.uint8).cuda()
+
+    ws = m.make_ffn_workspace(M, k, W.H, W.I, "cuda")
+    y_bad, y32_bad = m.expert_ffn(W, x, table(with_bad), k, ws)
+    y_ok, y32_ok = m.expert_ffn(W, x, table(valid), k, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits_of(y_bad), bits_of(y_ok))
+    np.testing.assert_array_equal(y32_bad.cpu().numpy(), y32_ok.cpu().numpy())
+    # oracle over the valid entries: per token, the experts whose mask has its bit
+    ids = np.zeros((M, len(valid)), np.int64)
+    w = np.zeros((M, len(valid)), np.float64)
+    for j, (e, mk, wt) in enumerate(valid):
+        for t in range(M):
+            ids[t, j] = e
+            w[t, j] = float(wt[t]) if (mk >> t) & 1 else 0.0
+    ref = oracle.moe_layer(synth.bf16_values(xb).astype(np.float64), ids, w, ef, sh)
+    check_acc(y32_ok.cpu().numpy(), ref, "valid entries only")
+
+
 def test_ffn_zero_input_is_exact_zero(m):
     W, _, lg, _, _, k = _host_layer_case(m, synth.TINY, 2)
     xb = np.zeros((2, synth.TINY.H), np.uint16)
