@@ -13,6 +13,9 @@ Reported next to the headline (M = 1) figure, each measured the same way:
   * the same layers in the 4-token verify window (M = 4);
   * the two-call path (moe_route_topk, then moe_expert_ffn_mxfp4), and the
     FFN call alone on precomputed dispatch tables;
+  * the cold stack: passes over the layers in order on a residual stream
+    (moe_layer_rmsnorm_mxfp4), each layer's input formed from the previous
+    layer's output, as a HIP graph and eagerly;
   * the LM head 157,184 x 2,560: one-off FP8 quantisation, FP8 GEMV at M = 1
     and 4, and the bf16 GEMV comparator;
   * the CPU oracle on a bounded sample of the same layers (cpu_baseline).
@@ -35,6 +38,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = "moe_ffn_kernel_ling_m1_hbm_traffic.md"
+COPY_PROBE_ELEMS = 1 << 28                 # float32: 1 GiB read and 1 GiB written
+PMC_KERNEL = "moe_ffn_kernel"
 EXPERT_BYTES_LING = 3 * (768 * 2560 // 2 + 768 * 2560 // 32)     # 3,133,440 B
 
 
@@ -51,9 +57,18 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head measurements")
     ap.add_argument("--no-m4", action="store_true", help="skip the M = 4 measurement")
+    ap.add_argument("--no-stack", action="store_true", help="skip the residual-stack measurement")
+    ap.add_argument("--stack-passes", type=int, default=100, help="graph passes over the layers (stack)")
     ap.add_argument("--cpu-layers", type=int, default=3, help="layers in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="short eager run for rocprofv3 --pmc: a calibration copy of known size, "
+                         "then fused M=1 layers")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of --pmc-run (FETCH_SIZE, then WRITE_SIZE) "
+                         "into the markdown file given by --traffic-out")
+    ap.add_argument("--traffic-out", default=os.path.join(ROOT, "profiles", TRAFFIC_FILE))
     return ap.parse_args(argv)
 
 
@@ -198,6 +213,54 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
 
 
 # ----------------------------------------------------------------------------
+# Cold stack: the layers in sequence on a residual stream
+
+def stack_bench(m, torch, synth, layers, passes, eager_passes, dev):
+    """Passes over all layers in order at M = 1, each layer on the residual
+    stream (moe_layer_rmsnorm_mxfp4: x = bf16(RMSNorm(r)), r += MoE layer(x)),
+    so every layer's input depends on the previous layer's output.  Timed as a
+    HIP graph of `passes` passes and eagerly (one launch per layer from Python)."""
+    n_layers = len(layers)
+    shape = synth.LING
+    k = shape.k
+    _, lgs = layer_inputs(synth, n_layers, 1, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    r0 = torch.randn((1, shape.H), generator=gen, device=dev, dtype=torch.float32)
+    bufs = [r0.clone(), torch.empty_like(r0)]
+    ws = m.make_ffn_workspace(1, k, shape.H, shape.I, dev)
+
+    def one_pass():
+        for L in range(n_layers):
+            m.moe_layer_rmsnorm(layers[L], bufs[L % 2], lgs[L], k, ws, r_out=bufs[(L + 1) % 2])
+        if n_layers % 2:
+            bufs.reverse()
+
+    one_pass()
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    g = capture(torch, lambda: [one_pass() for _ in range(passes)])
+    g.replay()
+    ms_graph = t.run(g.replay)
+    del g
+    one_pass()
+    ms_eager = t.run(lambda: [one_pass() for _ in range(eager_passes)])
+    finite = bool(torch.isfinite(bufs[0]).all().item())
+    steps_g, steps_e = passes * n_layers, eager_passes * n_layers
+    layer_bytes = (shape.k + 1) * EXPERT_BYTES_LING + shape.E * 4 + 2 * shape.H * 4   # + r in, r out
+    return {
+        "layers": n_layers, "passes_graph": passes, "passes_eager": eager_passes,
+        "us_per_layer_graph": 1e3 * ms_graph / steps_g,
+        "us_per_layer_eager": 1e3 * ms_eager / steps_e,
+        "us_per_pass_graph": 1e3 * ms_graph / passes,
+        "bytes_per_layer": layer_bytes,
+        "gbs_graph": layer_bytes * steps_g / (1e6 * ms_graph),
+        "frac_of_peak_graph": layer_bytes * steps_g / (1e6 * ms_graph) / PEAK_HBM_GBS,
+        "residual_finite": finite,
+    }
+
+
+# ----------------------------------------------------------------------------
 # LM head measurements
 
 def lmhead_bench(m, torch, synth, dev, reps=50):
@@ -313,8 +376,128 @@ def copy_probe(torch, dev):
     print(json.dumps({"copy_probe_bytes_each_way": n, "ms": ms, "gbs": 2 * n / (1e6 * ms)}), flush=True)
 
 
+# ----------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters
+
+def kernel_source_hash():
+    """Hash of the HIP sources and ABI header that define the measured kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_moe_expert_topk_amd", "csrc")
+    paths = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    paths.append(os.path.join(ROOT, "include", "moedec.h"))
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_run(m, torch, synth, dev, n_layers=8, passes=2):
+    """Dispatches for the counter runs: three float32 copies of COPY_PROBE_ELEMS
+    elements (an elementwise kernel with known bytes), then `passes` eager
+    passes of the fused M=1 layer over n_layers layers."""
+    a = torch.ones(COPY_PROBE_ELEMS, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    layers = make_layers(m, synth, n_layers, dev)
+    k = synth.LING.k
+    xs, lgs = layer_inputs(synth, n_layers, 1, dev)
+    ws = m.make_ffn_workspace(1, k, synth.LING.H, synth.LING.I, dev)
+    y = torch.empty((1, synth.LING.H), dtype=torch.bfloat16, device=dev)
+    for _ in range(passes):
+        for L in range(n_layers):
+            m.moe_layer(layers[L], xs[L], lgs[L], k, ws, y=y, want_f32=False)
+    torch.cuda.synchronize()
+    log(f"pmc run: {passes} x {n_layers} fused M=1 layers")
+
+
+def _counter_rows(run_dir, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 csv counter file."""
+    import csv
+    rows = []
+    for dirpath, _, files in os.walk(run_dir):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(dirpath, fn)) as f:
+                    for r in csv.DictReader(f):
+                        if r.get("Counter_Name") == counter:
+                            rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_summary(fetch_dir, write_dir, out_path):
+    """Per-dispatch HBM bytes of the fused M=1 kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by bytes / counter of the calibration copy."""
+    import statistics
+    copy_bytes = COPY_PROBE_ELEMS * 4
+    res = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(run_dir, counter)
+        cal = [v for name, v in rows if "elementwise" in name.lower() and v * 1024 > copy_bytes / 2]
+        ker = [v for name, v in rows if PMC_KERNEL in name]
+        if not cal or not ker:
+            raise SystemExit(f"{counter}: no calibration ({len(cal)}) or kernel ({len(ker)}) dispatches in {run_dir}")
+        factor = copy_bytes / (1024 * statistics.median(cal))
+        res[counter] = {"kib_per_dispatch": statistics.mean(ker), "dispatches": len(ker),
+                        "calibration_kib": statistics.median(cal), "factor": factor,
+                        "bytes_per_dispatch": 1024 * statistics.mean(ker) * factor}
+    total = res["FETCH_SIZE"]["bytes_per_dispatch"] + res["WRITE_SIZE"]["bytes_per_dispatch"]
+    summary = {"kernel": PMC_KERNEL + " (fused M=1 Ling layer)", "source_hash": kernel_source_hash(),
+               "fetch_bytes": round(res["FETCH_SIZE"]["bytes_per_dispatch"]),
+               "write_bytes": round(res["WRITE_SIZE"]["bytes_per_dispatch"]),
+               "traffic_bytes": round(total)}
+    lines = [
+        "# HBM traffic of the fused MoE layer kernel, Ling-shaped layer, M = 1",
+        "",
+        "Commands (from the repository root on the GPU host):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --pmc-run",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --pmc-run",
+        "python3 bench.py --traffic-from gpurun_out/pmc_fetch gpurun_out/pmc_write --traffic-out <this file>",
+        "```",
+        "",
+        "Calibration: an elementwise float32 copy of 2^28 elements (1 GiB read, 1 GiB written);",
+        "factor = known bytes / counter bytes.",
+        "",
+        "| counter | KiB per dispatch (mean) | dispatches | calibration KiB | factor | bytes per dispatch |",
+        "|---|---|---|---|---|---|",
+    ]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = res[c]
+        lines.append(f"| {c} | {r['kib_per_dispatch']:.1f} | {r['dispatches']} | {r['calibration_kib']:.0f} | "
+                     f"{r['factor']:.4f} | {r['bytes_per_dispatch']:.0f} |")
+    lines += ["", f"Algorithmic bytes per launch: 9 experts x {EXPERT_BYTES_LING} B + activations.", "",
+              "```json", json.dumps(summary), "```", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(summary), flush=True)
+
+
+def stored_traffic():
+    """Traffic bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
+    try:
+        with open(path) as f:
+            text = f.read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        summary = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    if summary.get("source_hash") != kernel_source_hash():
+        return None
+    return summary
+
+
 def main(argv=None):
     args = parse_args(argv)
+    if args.traffic_from:
+        traffic_summary(args.traffic_from[0], args.traffic_from[1], args.traffic_out)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this path has no multi-GPU mode)", file=sys.stderr)
@@ -330,6 +513,9 @@ def main(argv=None):
         return 0
     import bit_moe_expert_topk_amd as m
     import synth
+    if args.pmc_run:
+        pmc_run(m, torch, synth, dev)
+        return 0
 
     log(f"device: {torch.cuda.get_device_name(0)}; layers {args.layers}, steps {args.steps}, warmup {args.warmup}")
     layers = make_layers(m, synth, args.layers, dev)
@@ -339,6 +525,10 @@ def main(argv=None):
     if not args.no_m4:
         r4 = moe_bench(m, torch, synth, layers, 4, args.steps, args.warmup, dev)
         log("M=4:", json.dumps(r4))
+    stack = None
+    if not args.no_stack:
+        stack = stack_bench(m, torch, synth, layers, args.stack_passes, max(1, args.stack_passes // 10), dev)
+        log("stack:", json.dumps(stack))
     del layers
     torch.cuda.empty_cache()
     lm = None
@@ -350,6 +540,7 @@ def main(argv=None):
         cpu = cpu_baseline(synth, args.cpu_layers)
         log("cpu:", json.dumps(cpu))
 
+    traffic = stored_traffic()
     line = {
         "metric": "µs/MoE layer + achieved HBM GB/s (% of peak) at M=1 and M=4; LM-head GEMV GB/s",
         "value": round(r1["gbs"], 1),
@@ -379,18 +570,22 @@ def main(argv=None):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(r1["gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else traffic["traffic_bytes"],
+            "traffic_fetch_write": None if traffic is None else [traffic["fetch_bytes"], traffic["write_bytes"]],
             "bytes_per_launch": r1["bytes_per_layer"],
             "avg_launch_us": round(r1["us_per_layer"], 3),
         },
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
-        "extra": {"m1": r1, "m4": r4, "lmhead": lm,
+        "extra": {"m1": r1, "m4": r4, "stack": stack, "lmhead": lm,
                   "cpu": cpu},
     }
     if r4 is not None:
         line["us_per_layer_m4"] = round(r4["us_per_layer"], 3)
         line["gbs_m4"] = round(r4["gbs"], 1)
         line["frac_of_peak_m4"] = round(r4["frac_of_peak"], 4)
+    if stack is not None:
+        line["stack_us_per_layer_graph"] = round(stack["us_per_layer_graph"], 3)
+        line["stack_us_per_layer_eager"] = round(stack["us_per_layer_eager"], 3)
     if lm is not None:
         line["lmhead_fp8_gbs_m1"] = round(lm["fp8_m1_gbs"], 1)
         line["lmhead_fp8_gbs_m4"] = round(lm["fp8_m4_gbs"], 1)

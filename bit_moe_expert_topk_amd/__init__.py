@@ -222,6 +222,31 @@ def moe_layer(weights, x, logits, k, workspace, y=None, y_f32=None, want_f32=Tru
     return y, y_f32
 
 
+def moe_layer_rmsnorm(weights, r_in, logits, k, workspace, r_out=None, eps=1e-6, x_out=None,
+                      y_f32=None):
+    """One layer on the residual stream, in one launch: x = bf16(RMSNorm(r_in)),
+    y = MoE layer(x), r_out = r_in + y.  r_in: [M][H] float32 (not modified),
+    logits [M][E] float32.  Returns r_out; x_out (bf16) and y_f32 are filled
+    when given."""
+    _need(r_in, torch.float32, "r_in", 2)
+    _need(logits, torch.float32, "logits", 2)
+    _need(workspace, torch.uint8, "workspace", 1)
+    m_tokens, hidden = r_in.shape
+    if logits.shape[0] != m_tokens or logits.shape[1] != weights.E:
+        raise ValueError(f"logits must be [{m_tokens}][{weights.E}], got {tuple(logits.shape)}")
+    if r_out is None:
+        r_out = torch.empty_like(r_in)
+    _need(r_out, torch.float32, "r_out", 2)
+    if x_out is not None:
+        _need(x_out, torch.bfloat16, "x_out", 2)
+    if y_f32 is not None:
+        _need(y_f32, torch.float32, "y_f32", 2)
+    _check(lib.moe_layer_rmsnorm_mxfp4(ctypes.byref(weights.desc), _ptr(r_in), _ptr(logits), m_tokens, k,
+                                       float(eps), _ptr(r_out), _ptr(x_out), _ptr(y_f32),
+                                       _ptr(workspace), workspace.numel(), _stream(r_in)))
+    return r_out
+
+
 # --------------------------------------------------------------------------
 # LM head
 

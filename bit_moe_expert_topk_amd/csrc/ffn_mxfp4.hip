@@ -111,7 +111,11 @@ struct FfnArgs {
     int max_slots, max_groups, pair_cap;
     int n_gu, n_units;
     int pair_bytes, red_off;         // LDS layout
-    const uint16_t* x;               // [M][H] bf16
+    const uint16_t* x;               // [M][H] bf16 (null when r_in is given)
+    const float* r_in;               // [M][H] residual: x = bf16(RMSNorm(r_in)), or null
+    float* r_out;                    // [M][H] r_in + y, or null
+    uint16_t* x_out;                 // [M][H] the normalised x (block 0 writes it), or null
+    float eps;                       // RMSNorm epsilon
     const moedec_dispatch* disp;     // slots from moe_route_topk, or
     const float* logits;             // [M][E]: route here
     int32_t* ids_out;                // routing outputs of the fused path (block 0), nullable
@@ -122,7 +126,7 @@ struct FfnArgs {
     uint64_t* h;                     // [max_slots][M][I] tagged words (generation << 32 | float)
     uint64_t* part;                  // [max_groups][M][H] tagged partial rows
     int h_bytes;                     // size of h (device-coherent buffer loads)
-    uint16_t* y_bf16;                // [M][H]
+    uint16_t* y_bf16;                // [M][H] or null
     float* y_f32;                    // [M][H] or null
 };
 
@@ -724,12 +728,13 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
         for (int m = 0; m < M_T; ++m) {
             const size_t o = (size_t)m * a.H + row;
             if (a.y_f32) a.y_f32[o] = y[m];
-            a.y_bf16[o] = f32_to_bf16_rne(y[m]);
+            if (a.y_bf16) a.y_bf16[o] = f32_to_bf16_rne(y[m]);
+            if (a.r_out) a.r_out[o] = a.r_in[o] + y[m];
         }
     }
 }
 
-template <int M_T, int NB, bool ROUTE>
+template <int M_T, int NB, bool ROUTE, bool NORM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(blocks_per_cu<M_T>())))
 void moe_ffn_kernel(FfnArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -740,14 +745,17 @@ void moe_ffn_kernel(FfnArgs a) {
 
     // x does not depend on routing: its loads go out first (unconditional,
     // clamped index), and are staged in LDS once the slot table is built.
-    constexpr int kXPieces = 2 * M_T;                     // covers M_T * 4096 / 8 pieces
-    const int per_tok = a.H / 8;
+    // With a residual input the loads bring r (float32, twice the bytes) and
+    // x = bf16(RMSNorm(r)) is formed after routing.
+    constexpr bool norm = NORM;
+    constexpr int kPieces = (norm ? 4 : 2) * M_T;         // 16-byte pieces of M_T * 4096 values
+    const int per_tok = norm ? a.H / 4 : a.H / 8;
     const int n_pieces = M_T * per_tok;
-    u32x4 xv[kXPieces];
+    u32x4 xv[kPieces];
     if (has_gu) {
-        const u32x4* xg = reinterpret_cast<const u32x4*>(a.x);
+        const u32x4* src = norm ? reinterpret_cast<const u32x4*>(a.r_in) : reinterpret_cast<const u32x4*>(a.x);
 #pragma unroll
-        for (int i = 0; i < kXPieces; ++i) xv[i] = xg[min(tid + kThreads * i, n_pieces - 1)];
+        for (int i = 0; i < kPieces; ++i) xv[i] = src[min(tid + kThreads * i, n_pieces - 1)];
     }
     if (tid == kThreads - kWave) {                        // wave 3: keeps wave 0 free to route
         // the launch count on the workspace: every one of the kMaxGrid words
@@ -767,10 +775,60 @@ void moe_ffn_kernel(FfnArgs a) {
         table_from_logits<M_T>(a, T, route_buf);
     else
         table_from_dispatch<M_T>(a, T);
-    if (has_gu) {
+    if (has_gu && norm) {
+        // RMSNorm with unit gain: x = r / sqrt(mean(r^2) + eps), float32, then
+        // rounded to bf16 (nearest even); piece p holds elements 4r..4r+3
+        __shared__ float s_ss[kWaves][MOEDEC_MAX_M];
+        float ss[M_T];
+#pragma unroll
+        for (int m = 0; m < M_T; ++m) ss[m] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kPieces; ++i) {
+            const int p = tid + kThreads * i;
+            if (p < n_pieces) {
+                const int pm = p / per_tok;
+                const float v0 = __uint_as_float(xv[i][0]), v1 = __uint_as_float(xv[i][1]);
+                const float v2 = __uint_as_float(xv[i][2]), v3 = __uint_as_float(xv[i][3]);
+                const float sq = (v0 * v0 + v1 * v1) + (v2 * v2 + v3 * v3);
+#pragma unroll
+                for (int m = 0; m < M_T; ++m) ss[m] += (m == pm) ? sq : 0.f;
+            }
+        }
+        const int w = tid / kWave;
+#pragma unroll
+        for (int m = 0; m < M_T; ++m) {
+            const float t = wave_sum_f32(ss[m]);
+            if ((tid & (kWave - 1)) == 0) s_ss[w][m] = t;
+        }
+        __syncthreads();
+        float inv[M_T];
+#pragma unroll
+        for (int m = 0; m < M_T; ++m)
+            inv[m] = 1.0f / sqrtf(((s_ss[0][m] + s_ss[1][m]) + (s_ss[2][m] + s_ss[3][m])) / (float)a.H + a.eps);
         const int xtok = a.kbh4 * 4 * kXBlock;            // token m, MX block q at m * xtok + q * 80
 #pragma unroll
-        for (int i = 0; i < kXPieces; ++i) {
+        for (int i = 0; i < kPieces; ++i) {
+            const int p = tid + kThreads * i;
+            if (p < n_pieces) {
+                const int pm = p / per_tok;
+                const int e0 = 4 * (p - pm * per_tok);
+                float sc = inv[0];
+#pragma unroll
+                for (int m = 1; m < M_T; ++m) sc = (m == pm) ? inv[m] : sc;
+                const uint32_t b0 = f32_to_bf16_rne(__uint_as_float(xv[i][0]) * sc);
+                const uint32_t b1 = f32_to_bf16_rne(__uint_as_float(xv[i][1]) * sc);
+                const uint32_t b2 = f32_to_bf16_rne(__uint_as_float(xv[i][2]) * sc);
+                const uint32_t b3 = f32_to_bf16_rne(__uint_as_float(xv[i][3]) * sc);
+                const uint2 packed = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                *reinterpret_cast<uint2*>(lds + pm * xtok + (e0 >> 5) * kXBlock + (e0 & 31) * 2) = packed;
+                if (blockIdx.x == 0 && a.x_out)
+                    *reinterpret_cast<uint2*>(a.x_out + (size_t)pm * a.H + e0) = packed;
+            }
+        }
+    } else if (has_gu) {
+        const int xtok = a.kbh4 * 4 * kXBlock;            // token m, MX block q at m * xtok + q * 80
+#pragma unroll
+        for (int i = 0; i < kPieces; ++i) {
             const int p = tid + kThreads * i;
             if (p < n_pieces) {
                 const int m = p / per_tok;
@@ -778,6 +836,9 @@ void moe_ffn_kernel(FfnArgs a) {
                 *reinterpret_cast<u32x4*>(lds + m * xtok + (r >> 2) * kXBlock + (r & 3) * 16) = xv[i];
             }
         }
+    }
+    if (has_gu) {
+        const int xtok = a.kbh4 * 4 * kXBlock;
         const int pad_pieces = (a.kbh4 * 4 - a.kbh) * 4;  // MX blocks past H are zero
         for (int p = tid; p < M_T * pad_pieces; p += kThreads) {
             const int m = p / pad_pieces;
@@ -804,6 +865,7 @@ void moe_ffn_kernel(FfnArgs a) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr size_t kLdsTarget = 40 * 1024;
+constexpr int kMultiTokenPairs = 4;
 
 // CU count of the current device (cached); the grid is blocks_per_cu * CUs.
 struct DeviceInfo {
@@ -825,7 +887,7 @@ int device_cus() {
     return d.cus;
 }
 
-template <int M_T, int NB, bool ROUTE>
+template <int M_T, int NB, bool ROUTE, bool NORM>
 hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) {
     constexpr int kBlocksPerCU = blocks_per_cu<M_T>();
     const int grid = std::min(kMaxGrid, kBlocksPerCU * cus);
@@ -836,25 +898,33 @@ hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) 
     if (v == 0) {
         int blocks = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE>), kThreads, lds);
+            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE, NORM>), kThreads, lds);
         if (e != hipSuccess) return e;
         v = (blocks >= kBlocksPerCU) ? 1 : 2;
         occ_ok[cls].store(v, std::memory_order_relaxed);
     }
     if (v != 1) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE, NORM>), dim3(grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
-template <int M_T, bool ROUTE>
-hipError_t launch_m(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
+template <int M_T, bool ROUTE, bool NORM>
+hipError_t launch_nb(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     switch (nb) {
-        case 1: return launch_variant<M_T, 1, ROUTE>(a, cus, lds, s);
-        case 2: return launch_variant<M_T, 2, ROUTE>(a, cus, lds, s);
-        case 4: return launch_variant<M_T, 4, ROUTE>(a, cus, lds, s);
-        case 5: return launch_variant<M_T, 5, ROUTE>(a, cus, lds, s);
-        default: return launch_variant<M_T, 8, ROUTE>(a, cus, lds, s);
+        case 1: return launch_variant<M_T, 1, ROUTE, NORM>(a, cus, lds, s);
+        case 2: return launch_variant<M_T, 2, ROUTE, NORM>(a, cus, lds, s);
+        case 4: return launch_variant<M_T, 4, ROUTE, NORM>(a, cus, lds, s);
+        case 5: return launch_variant<M_T, 5, ROUTE, NORM>(a, cus, lds, s);
+        default: return launch_variant<M_T, 8, ROUTE, NORM>(a, cus, lds, s);
     }
+}
+
+// routing from logits with or without the residual stream, or from a table
+template <int M_T>
+hipError_t launch_m(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
+    if (a.r_in) return launch_nb<M_T, true, true>(a, nb, cus, lds, s);
+    if (a.logits) return launch_nb<M_T, true, false>(a, nb, cus, lds, s);
+    return launch_nb<M_T, false, false>(a, nb, cus, lds, s);
 }
 
 }  // namespace
@@ -869,12 +939,14 @@ FfnLayout ffn_layout(int M, int k_max, int H, int I) {
     const size_t red_bytes = (size_t)kWaves * M * 2 * kUnitRows * sizeof(float);
     const size_t x_bytes = (size_t)M * kbh4 * 4 * kXBlock;
     // a group (at most pair_cap + M - 1 pairs: it ends on a slot boundary)
-    // must fit the LDS target; with one token it must also fit one staging
-    // batch of the down unit (more tokens have more units than blocks, and
-    // fewer, larger groups there save partial-row exchanges)
+    // must fit the LDS target.  With one token it must also fit one staging
+    // batch of the down unit, so h arrives in one round trip; with more
+    // tokens (more units than blocks) groups of kMultiTokenPairs pairs
+    // balanced staging against partial-row exchanges best on a 2560 x 768
+    // layer at M = 4 (42 us against 46 us for the LDS limit of 8).
     const int fit_lds = (int)((kLdsTarget - red_bytes) / L.pair_bytes) - (M - 1);
     const int loads_per_pair = kbi4 * 4 * 16;                       // 16-byte loads (two h words each)
-    const int fit_stage = (M == 1) ? stage_batch<1>() * kThreads / loads_per_pair : fit_lds;
+    const int fit_stage = (M == 1) ? stage_batch<1>() * kThreads / loads_per_pair : kMultiTokenPairs;
     const int max_pairs = M * k_max + M;
     L.pair_cap = std::max(1, std::min(std::min(fit_lds, fit_stage), max_pairs));
     L.max_groups = (max_pairs + L.pair_cap - 1) / L.pair_cap;
@@ -895,7 +967,7 @@ FfnLayout ffn_layout(int M, int k_max, int H, int I) {
 hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int k_max,
                       const moedec_dispatch* disp, const float* logits, int32_t* ids_out,
                       float* w_out, moedec_dispatch* disp_out, uint16_t* y_bf16, float* y_f32,
-                      void* ws, hipStream_t s) {
+                      void* ws, hipStream_t s, const ResidualArgs* res) {
     const FfnLayout L = ffn_layout(M, k_max, w.H, w.I);
     const int cus = device_cus();
     if (cus <= 0) return hipErrorInvalidDevice;
@@ -947,15 +1019,19 @@ hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int
     a.h_bytes = (int)((size_t)L.max_slots * M * w.I * sizeof(uint64_t));
     a.y_bf16 = y_bf16;
     a.y_f32 = y_f32;
+    a.r_in = res ? res->r_in : nullptr;
+    a.r_out = res ? res->r_out : nullptr;
+    a.x_out = res ? res->x_out : nullptr;
+    a.eps = res ? res->eps : 0.f;
 
     const int cpw = (a.kbh4 + kWaves - 1) / kWaves;   // chunk pairs per wave, <= 8 for H <= 4096
     const int nb = cpw <= 1 ? 1 : cpw <= 2 ? 2 : cpw <= 4 ? 4 : cpw <= 5 ? 5 : 8;
-    const bool route = logits != nullptr;
+    if (a.r_in && !a.logits) return hipErrorInvalidValue;     // the residual form routes from logits
     switch (M) {
-        case 1: return route ? launch_m<1, true>(a, nb, cus, L.lds_bytes, s) : launch_m<1, false>(a, nb, cus, L.lds_bytes, s);
-        case 2: return route ? launch_m<2, true>(a, nb, cus, L.lds_bytes, s) : launch_m<2, false>(a, nb, cus, L.lds_bytes, s);
-        case 3: return route ? launch_m<3, true>(a, nb, cus, L.lds_bytes, s) : launch_m<3, false>(a, nb, cus, L.lds_bytes, s);
-        default: return route ? launch_m<4, true>(a, nb, cus, L.lds_bytes, s) : launch_m<4, false>(a, nb, cus, L.lds_bytes, s);
+        case 1: return launch_m<1>(a, nb, cus, L.lds_bytes, s);
+        case 2: return launch_m<2>(a, nb, cus, L.lds_bytes, s);
+        case 3: return launch_m<3>(a, nb, cus, L.lds_bytes, s);
+        default: return launch_m<4>(a, nb, cus, L.lds_bytes, s);
     }
 }
 

@@ -149,7 +149,8 @@ size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I) {
 }
 
 static int check_moe_args(const moedec_moe_weights* w, const uint16_t* x_bf16, int M, int k,
-                          uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes) {
+                          uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
+                          bool residual = false) {
     if (!w) return fail(MOEDEC_ERR_NULL, "weights descriptor is NULL");
     if (w->magic != MOEDEC_MOE_MAGIC)
         return fail(MOEDEC_ERR_FORMAT, "weights descriptor magic 0x%08x != 0x%08x", w->magic,
@@ -157,7 +158,8 @@ static int check_moe_args(const moedec_moe_weights* w, const uint16_t* x_bf16, i
     if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales || !w->sh_gu_codes ||
         !w->sh_gu_scales || !w->sh_dn_codes || !w->sh_dn_scales)
         return fail(MOEDEC_ERR_NULL, "a weight pointer is NULL");
-    if (!x_bf16 || !y_bf16 || !workspace) return fail(MOEDEC_ERR_NULL, "x, y_bf16 or workspace is NULL");
+    if (!residual && (!x_bf16 || !y_bf16)) return fail(MOEDEC_ERR_NULL, "x or y_bf16 is NULL");
+    if (!workspace) return fail(MOEDEC_ERR_NULL, "workspace is NULL");
     if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
     if (w->E < 1 || w->E > MOEDEC_MAX_E) return fail(MOEDEC_ERR_SHAPE, "E=%d not in 1..%d", w->E, MOEDEC_MAX_E);
     if (k < 1 || k > MOEDEC_MAX_K || k > w->E)
@@ -202,6 +204,26 @@ int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const f
     return launched(moedec::launch_moe(*w, x_bf16, M, k, nullptr, logits, topk_ids, topk_w, dispatch,
                                        y_bf16, y_f32, workspace, static_cast<hipStream_t>(stream)),
                     "moe_layer_mxfp4");
+}
+
+int moe_layer_rmsnorm_mxfp4(const moedec_moe_weights* w, const float* r_in, const float* logits, int M,
+                            int k, float eps, float* r_out, uint16_t* x_bf16, float* y_f32,
+                            void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+    if (int st = check_moe_args(w, x_bf16, M, k, nullptr, y_f32, workspace, workspace_bytes, true))
+        return st;
+    if (!r_in || !r_out || !logits) return fail(MOEDEC_ERR_NULL, "r_in, r_out or logits is NULL");
+    if (!(eps >= 0.f) || eps > 1.f) return fail(MOEDEC_ERR_SHAPE, "eps=%g not in [0, 1]", (double)eps);
+    if (!aligned(r_in, 16) || !aligned(r_out, 16) || !aligned(logits, 4))
+        return fail(MOEDEC_ERR_ALIGN, "r_in and r_out must be 16-byte aligned, logits 4-byte");
+    const size_t bytes = (size_t)M * w->H * sizeof(float);
+    const auto lo_in = reinterpret_cast<uintptr_t>(r_in), lo_out = reinterpret_cast<uintptr_t>(r_out);
+    if (lo_in < lo_out + bytes && lo_out < lo_in + bytes)
+        return fail(MOEDEC_ERR_SHAPE, "r_out overlaps r_in (use two buffers)");
+    if (int st = check_device()) return st;
+    moedec::ResidualArgs res{r_in, r_out, x_bf16, eps};
+    return launched(moedec::launch_moe(*w, nullptr, M, k, nullptr, logits, nullptr, nullptr, nullptr,
+                                       nullptr, y_f32, workspace, static_cast<hipStream_t>(stream), &res),
+                    "moe_layer_rmsnorm_mxfp4");
 }
 
 int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H, uint8_t* codes, float* row_scale,

@@ -35,11 +35,20 @@ struct FfnLayout {
 };
 FfnLayout ffn_layout(int M, int k_max, int H, int I);
 
+// Residual stream of a decode stack: x = bf16(RMSNorm(r_in)) replaces the x
+// input, and r_out = r_in + y is written next to y.
+struct ResidualArgs {
+    const float* r_in;
+    float* r_out;
+    uint16_t* x_out;    // the normalised x, or null
+    float eps;
+};
+
 // Fused layer: routing from logits (when non-null) or the dispatch table, then the FFN.
 hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int k_max,
                       const moedec_dispatch* disp, const float* logits, int32_t* ids_out,
                       float* w_out, moedec_dispatch* disp_out, uint16_t* y_bf16, float* y_f32,
-                      void* ws, hipStream_t s);
+                      void* ws, hipStream_t s, const ResidualArgs* res = nullptr);
 
 hipError_t launch_expert_ffn(const moedec_moe_weights& w, const uint16_t* x, int M,
                              const moedec_dispatch* disp, int k_max, uint16_t* y_bf16,

@@ -210,6 +210,31 @@ int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const f
                     moedec_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * One MoE layer of a decode stack, on the residual stream.  The model the
+ * pages measure stacks 42 such layers [card background]; between layers a
+ * residual stream carries the sum of the layer outputs.  This call forms the
+ * layer input from that stream and adds the layer output back, in the same
+ * single launch as moe_layer_mxfp4:
+ *     x     = bf16(RMSNorm(r_in)),  RMSNorm(r) = r / sqrt(mean(r^2) + eps)
+ *             per token, unit gain, float32, rounded to nearest even
+ *     y     = the MoE layer of moe_layer_mxfp4 applied to x
+ *     r_out = r_in + y                                  (float32)
+ * (The norm's form and its unit gain are a reading: the pages give no
+ * formula for it, and its trained gains are weights this path does not have.)
+ *
+ * r_in        [M][H] float32, 16-byte aligned
+ * r_out       [M][H] float32, 16-byte aligned; must not overlap r_in
+ * eps         0 <= eps <= 1
+ * x_bf16      [M][H] bf16 output (the normalised layer input) or NULL,
+ *             16-byte aligned
+ * y_f32       [M][H] float32 layer output or NULL
+ * Other arguments, limits and the workspace as moe_layer_mxfp4.
+ */
+int moe_layer_rmsnorm_mxfp4(const moedec_moe_weights* w, const float* r_in, const float* logits,
+                            int M, int k, float eps, float* r_out, uint16_t* x_bf16, float* y_f32,
+                            void* workspace, size_t workspace_bytes, moedec_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * LM head with online FP8 weights.  [news where the speed comes from; card
  * #2: the 157,184 x 2,560 vocabulary projection is read whole for every
  * token; a dynamic FP8 config applied when the head is built halves that

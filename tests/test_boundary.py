@@ -28,7 +28,8 @@ def m():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("moe_route_topk", "moe_expert_ffn_mxfp4", "moe_layer_mxfp4", "lmhead_quant_fp8", "lmhead_gemv_fp8",
+    for want in ("moe_route_topk", "moe_expert_ffn_mxfp4", "moe_layer_mxfp4", "moe_layer_rmsnorm_mxfp4",
+                 "lmhead_quant_fp8", "lmhead_gemv_fp8",
                  "lmhead_gemv_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
                  "moedec_last_error", "moedec_abi_version"):
@@ -144,6 +145,27 @@ def test_fused_layer_argument_checks(m):
     assert call(_weights(m), M=5) == -3
     assert call(_weights(m), lg=ODD) == -2
     assert call(_weights(m), disp=ctypes.c_void_p((1 << 20) + 8)) == -2
+    assert call(_weights(m), n=ws - 1) == -5
+
+
+def test_residual_layer_argument_checks(m):
+    L = m.lib
+    ws = m.ffn_workspace_bytes(1, 8, 2560, 768)
+    far = ctypes.c_void_p(1 << 24)
+
+    def call(w, r_in=FAKE, r_out=far, lg=FAKE, eps=1e-6, x=None, M=1, k=8, n=ws):
+        return L.moe_layer_rmsnorm_mxfp4(ctypes.byref(w), r_in, lg, M, k, eps, r_out, x, None, FAKE, n, None)
+
+    assert call(_weights(m), r_in=None) == -1
+    assert call(_weights(m), r_out=None) == -1
+    assert call(_weights(m), lg=None) == -1
+    assert call(_weights(m, magic=1)) == -4
+    assert call(_weights(m), eps=-1.0) == -3
+    assert call(_weights(m), eps=float("nan")) == -3
+    assert call(_weights(m), r_out=ctypes.c_void_p((1 << 20) + 4096)) == -3     # overlaps r_in
+    assert call(_weights(m), r_out=ctypes.c_void_p((1 << 24) + 4)) == -2
+    assert call(_weights(m), x=ctypes.c_void_p((1 << 22) + 8)) == -2
+    assert call(_weights(m), M=5) == -3
     assert call(_weights(m), n=ws - 1) == -5
 
 

@@ -378,6 +378,74 @@ def test_fused_ling(m, ling_layer, name):
     _check_fused(m, ling_layer, xb, lg, 8, _ling_expert, _ling_expert(synth.LING.E), f"fused {name}")
 
 
+# ------------------------------------------------------- residual stack
+
+def _check_rmsnorm_x(x_bits, r, eps, what):
+    """x = bf16(RMSNorm(r)): equal to the float64 value rounded to nearest even,
+    except where that value lies within 1e-5 (relative) of the midpoint between
+    two bf16 neighbours, where either rounding is accepted."""
+    xr = oracle.rmsnorm(np.asarray(r, np.float64), eps=eps)
+    want = oracle.bf16_bits(oracle.bf16_round(xr))
+    got = np.asarray(x_bits, np.uint16)
+    bad = got != want
+    if bad.any():
+        gv = synth.bf16_values(got[bad]).astype(np.float64)
+        wv = synth.bf16_values(want[bad]).astype(np.float64)
+        mid = (gv + wv) / 2
+        ok = np.abs(xr[bad] - mid) <= 1e-5 * np.abs(xr[bad])
+        assert ok.all(), f"{what}: {int((~ok).sum())} x values differ from bf16(RMSNorm(r))"
+
+
+def _residual_stack(m, layers, r0, logits_per_layer, k, expert_fns, shareds, what, eps=1e-6):
+    M, H = r0.shape
+    W0 = layers[0]
+    ws = m.make_ffn_workspace(M, k, W0.H, W0.I, "cuda")
+    r = torch.from_numpy(r0).cuda()
+    for L, W in enumerate(layers):
+        say(f"{what} layer {L}")
+        lg = torch.from_numpy(logits_per_layer[L]).cuda()
+        x_out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        y32 = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        r_out = m.moe_layer_rmsnorm(W, r, lg, k, ws, eps=eps, x_out=x_out, y_f32=y32)
+        torch.cuda.synchronize()
+        r_in_h, r_out_h, y_h = r.cpu().numpy(), r_out.cpu().numpy(), y32.cpu().numpy()
+        xb = bits_of(x_out)
+        _check_rmsnorm_x(xb, r_in_h, eps, f"{what} layer {L}")
+        # the same kernel on the same x without the residual: bit-identical y
+        _, y32_plain = m.moe_layer(W, x_out, lg, k, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y_h, y32_plain.cpu().numpy())
+        _, _, ref_y = oracle_layer(xb, logits_per_layer[L], k, expert_fns[L], shareds[L])
+        check_acc(y_h, ref_y, f"{what} layer {L}")
+        np.testing.assert_array_equal(r_out_h, r_in_h + y_h)        # float32 sum, exact
+        r = r_out
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_residual_stack_tiny(m, M):
+    """Three layers with their own weights and logits: every layer's x is
+    bf16(RMSNorm(r)), its y matches the oracle on that x, and r advances by y."""
+    shape = synth.TINY
+    layers, efs, shs, lgs = [], [], [], []
+    for L in range(3):
+        W, _, _, ef, sh, k = _host_layer_case(m, shape, M, seed=5, layer=L,
+                                              logits=synth.logits_f32(5, L, M, shape.E))
+        layers.append(W)
+        efs.append(ef)
+        shs.append(sh)
+        lgs.append(synth.logits_f32(5, L, M, shape.E))
+    r0 = np.random.default_rng(7).standard_normal((M, shape.H)).astype(np.float32) * 3.0
+    _residual_stack(m, layers, r0, lgs, k, efs, shs, f"residual tiny M={M}")
+
+
+def test_residual_layer_ling_m1(m, ling_layer):
+    wl = synth.WORKLOADS["ling_m1"]
+    _, lg = synth.moe_inputs(wl)
+    r0 = np.random.default_rng(8).standard_normal((1, synth.LING.H)).astype(np.float32)
+    _residual_stack(m, [ling_layer], r0, [lg], 8, [_ling_expert], [_ling_expert(synth.LING.E)],
+                    "residual ling M=1")
+
+
 def test_paths_share_one_workspace(m):
     """The fused and two-call paths alternate on one workspace with different
     M; every call still matches the oracle (launch generations stay in step)."""
