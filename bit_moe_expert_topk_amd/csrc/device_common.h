@@ -67,6 +67,60 @@ __device__ __forceinline__ float row_sum_f32(float v) {
 // Kept for the LM-head kernels: plain wave sum in every lane.
 __device__ __forceinline__ float wave_sum(float v) { return wave_sum_f32(v); }
 
+// Wave sums of N values at once (N a power of two, <= 64).  Each cross-lane
+// step pairs two values and keeps one of them per half of the exchanging
+// lanes, so the set halves while the partial sums double: N values cost
+// N - 1 pair steps plus (6 - log2 N) single steps instead of 6 N.  On return
+// lane l holds the sum of v[l >> (6 - log2 N)] over all 64 lanes.
+constexpr int kRowMirror = 0x140, kRowHalfMirror = 0x141, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
+
+template <int D>
+__device__ __forceinline__ float pair_sum(float a, float b) {
+    // lanes with bit D clear return a + a(partner), lanes with it set b + b(partner)
+    if constexpr (D == 32 || D == 16) {
+        const auto r = (D == 32)
+            ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+            : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        constexpr int kCtrl = D == 8 ? kRowMirror : D == 4 ? kRowHalfMirror : D == 2 ? kQuadSwap2 : kQuadSwap1;
+        const float sa = a + __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(a)));
+        const float sb = b + __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(b)));
+        return (lane_id() & D) ? sb : sa;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ float partner_sum(float a) {
+    if constexpr (D == 32 || D == 16) {
+        const u32x2 p = (D == 32) ? swap32(__float_as_uint(a)) : swap16(__float_as_uint(a));
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    } else {
+        constexpr int kCtrl = D == 8 ? kRowMirror : D == 4 ? kRowHalfMirror : D == 2 ? kQuadSwap2 : kQuadSwap1;
+        return a + __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(a)));
+    }
+}
+
+template <int N, int D = 32>
+__device__ __forceinline__ float multi_sum(float (&v)[N]) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+    if constexpr (N == 1) {
+        float r = v[0];
+        if constexpr (D >= 32) r = partner_sum<32>(r);
+        if constexpr (D >= 16) r = partner_sum<16>(r);
+        if constexpr (D >= 8) r = partner_sum<8>(r);
+        if constexpr (D >= 4) r = partner_sum<4>(r);
+        if constexpr (D >= 2) r = partner_sum<2>(r);
+        if constexpr (D >= 1) r = partner_sum<1>(r);
+        return r;
+    } else {
+        float h[N / 2];
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) h[i] = pair_sum<D>(v[i], v[i + N / 2]);
+        return multi_sum<N / 2, D / 2>(h);
+    }
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     uint32_t o;
     o = dpp_u32<kRowRor1>(v); v = o > v ? o : v;
