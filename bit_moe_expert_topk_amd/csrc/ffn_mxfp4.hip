@@ -865,6 +865,7 @@ void moe_ffn_kernel(FfnArgs a) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr size_t kLdsTarget = 40 * 1024;
+constexpr int kOneTokenPairs = 3;
 constexpr int kMultiTokenPairs = 4;
 
 // CU count of the current device (cached); the grid is blocks_per_cu * CUs.
@@ -939,16 +940,25 @@ FfnLayout ffn_layout(int M, int k_max, int H, int I) {
     const size_t red_bytes = (size_t)kWaves * M * 2 * kUnitRows * sizeof(float);
     const size_t x_bytes = (size_t)M * kbh4 * 4 * kXBlock;
     // a group (at most pair_cap + M - 1 pairs: it ends on a slot boundary)
-    // must fit the LDS target.  With one token it must also fit one staging
-    // batch of the down unit, so h arrives in one round trip; with more
-    // tokens (more units than blocks) groups of kMultiTokenPairs pairs
-    // balanced staging against partial-row exchanges best on a 2560 x 768
-    // layer at M = 4 (42 us against 46 us for the LDS limit of 8).
+    // must fit the LDS target.  Smaller groups shorten each down unit and cost
+    // partial-row exchanges; on a 2560 x 768 layer the best balance was groups
+    // of 3 pairs at M = 1 (14.8 us against 15.3 for 4 and 15.9 for 5), made
+    // equal in size and within one staging batch so h arrives in one round
+    // trip, and of kMultiTokenPairs at M = 4, staged in several batches
+    // (42 us against 46 us for the LDS limit of 8 and 58 us for groups of 2).
     const int fit_lds = (int)((kLdsTarget - red_bytes) / L.pair_bytes) - (M - 1);
-    const int loads_per_pair = kbi4 * 4 * 16;                       // 16-byte loads (two h words each)
-    const int fit_stage = (M == 1) ? stage_batch<1>() * kThreads / loads_per_pair : kMultiTokenPairs;
     const int max_pairs = M * k_max + M;
-    L.pair_cap = std::max(1, std::min(std::min(fit_lds, fit_stage), max_pairs));
+    int cap;
+    if (M == 1) {
+        const int loads_per_pair = kbi4 * 4 * 16;                   // 16-byte loads (two h words each)
+        const int fit_stage = stage_batch<1>() * kThreads / loads_per_pair;
+        cap = std::max(1, std::min(std::min(fit_lds, fit_stage), std::min(kOneTokenPairs, max_pairs)));
+        const int n_groups = (max_pairs + cap - 1) / cap;
+        cap = (max_pairs + n_groups - 1) / n_groups;                // equal groups
+    } else {
+        cap = std::max(1, std::min(fit_lds, std::min(kMultiTokenPairs, max_pairs)));
+    }
+    L.pair_cap = cap;
     L.max_groups = (max_pairs + L.pair_cap - 1) / L.pair_cap;
     const size_t h_bytes = (size_t)(L.pair_cap + M - 1) * L.pair_bytes;
     const size_t region = std::max(x_bytes, h_bytes);
