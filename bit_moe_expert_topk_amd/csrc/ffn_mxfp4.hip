@@ -385,8 +385,46 @@ __device__ void table_groups(const FfnArgs& a, SlotTable& T) {
 // ---------------------------------------------------------------------------
 // gate/up unit
 
+// The weights of one gate/up unit in flight: NB chunk pairs per wave.
+template <int NB>
+struct GuLoads {
+    u32x4 cg[NB], cu[NB];
+    uint32_t sc[NB];
+};
+
+// Issue a gate/up unit's weight loads (nothing when the slot is unused).
 template <int M_T, int NB>
-__device__ void gateup_unit(const FfnArgs& a, const SlotTable& T, uint8_t* lds, int u, uint32_t gen) {
+__device__ __forceinline__ void gateup_issue(const FfnArgs& a, const SlotTable& T, int u, GuLoads<NB>& L) {
+    const int s = u / a.gu_units;
+    const int rg = u - s * a.gu_units;
+    if (s >= T.n_slots) return;
+    const int e = T.expert[s];
+    if (e < 0) return;
+    const int w = wave_id_uniform();
+    const int lane = lane_id();
+    const uint8_t* cb = (e == a.E) ? a.sh_gu_codes : a.gu_codes + (size_t)e * a.gu_codes_stride;
+    const uint8_t* sb = (e == a.E) ? a.sh_gu_scales : a.gu_scales + (size_t)e * a.gu_scales_stride;
+    // this wave's chunk pairs (each = 1 KiB gate + 1 KiB up, four MX blocks)
+    const int cpw = (a.kbh4 + kWaves - 1) / kWaves;
+    const int c_begin = w * cpw;
+    const int c_end = min(a.kbh4, c_begin + cpw);
+    const uint8_t* ub = cb + (size_t)rg * a.kbh4 * 2048 + lane * 16;
+    const uint8_t* usb = sb + (size_t)rg * a.kbh4 * 128 + lane * 2;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int c = max(0, min(c_begin + i, c_end - 1));   // clamped; extra loads unused
+        L.cg[i] = load_stream16(ub + (size_t)c * 2048);
+        L.cu[i] = load_stream16(ub + (size_t)c * 2048 + 1024);
+        L.sc[i] = *reinterpret_cast<const uint16_t*>(usb + (size_t)c * 128);
+    }
+}
+
+// Finish a gate/up unit whose loads gateup_issue put in L: the dot products
+// with x (LDS), the reduction over lanes and waves, h = silu(g) * u and its
+// publication.
+template <int M_T, int NB>
+__device__ void gateup_compute(const FfnArgs& a, const SlotTable& T, uint8_t* lds, int u, uint32_t gen,
+                               const GuLoads<NB>& L) {
     const int s = u / a.gu_units;
     const int rg = u - s * a.gu_units;
     if (s >= T.n_slots) return;
@@ -395,25 +433,10 @@ __device__ void gateup_unit(const FfnArgs& a, const SlotTable& T, uint8_t* lds, 
     const uint32_t mask = T.mask[s];
     const int w = wave_id_uniform();
     const int lane = lane_id();
-    const uint8_t* cb = (e == a.E) ? a.sh_gu_codes : a.gu_codes + (size_t)e * a.gu_codes_stride;
-    const uint8_t* sb = (e == a.E) ? a.sh_gu_scales : a.gu_scales + (size_t)e * a.gu_scales_stride;
-
-    // this wave's chunk pairs (each = 1 KiB gate + 1 KiB up, four MX blocks)
     const int cpw = (a.kbh4 + kWaves - 1) / kWaves;
     const int c_begin = w * cpw;
     const int c_end = min(a.kbh4, c_begin + cpw);
     const int n_c = c_end - c_begin;
-    const uint8_t* ub = cb + (size_t)rg * a.kbh4 * 2048 + lane * 16;
-    const uint8_t* usb = sb + (size_t)rg * a.kbh4 * 128 + lane * 2;
-    u32x4 cg[NB], cu[NB];
-    uint32_t sc[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int c = max(0, min(c_begin + i, c_end - 1));   // clamped; extra loads unused
-        cg[i] = load_stream16(ub + (size_t)c * 2048);
-        cu[i] = load_stream16(ub + (size_t)c * 2048 + 1024);
-        sc[i] = *reinterpret_cast<const uint16_t*>(usb + (size_t)c * 128);
-    }
 
     const int xtok = a.kbh4 * 4 * kXBlock;      // x was staged in LDS by the prologue
     const int quarter = lane >> 4;
@@ -424,13 +447,13 @@ __device__ void gateup_unit(const FfnArgs& a, const SlotTable& T, uint8_t* lds, 
     for (int i = 0; i < NB; ++i) {
         if (i < n_c) {
             const int c = c_begin + i;
-            const float sg = e8m0_to_f32(sc[i] & 0xFFu);
-            const float su = e8m0_to_f32(sc[i] >> 8);
+            const float sg = e8m0_to_f32(L.sc[i] & 0xFFu);
+            const float su = e8m0_to_f32(L.sc[i] >> 8);
             bf16x2 wg[16], wu[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                wg[j] = fp4x2_bf16(cg[i][j >> 2], sg, j & 3);
-                wu[j] = fp4x2_bf16(cu[i][j >> 2], su, j & 3);
+                wg[j] = fp4x2_bf16(L.cg[i][j >> 2], sg, j & 3);
+                wu[j] = fp4x2_bf16(L.cu[i][j >> 2], su, j & 3);
             }
             const uint8_t* xq = lds + (4 * c + quarter) * kXBlock;
 #pragma unroll
@@ -853,11 +876,22 @@ void moe_ffn_kernel(FfnArgs a) {
         __syncthreads();
     }
     const uint32_t gen = s_gen;
-    for (int u = blockIdx.x; u < a.n_units; u += gridDim.x) {
-        if (u < a.n_gu)
-            gateup_unit<M_T, NB>(a, T, lds, u, gen);
-        else
-            down_unit<M_T>(a, T, lds, u - a.n_gu, gen);
+    // Gate/up units come first: a block's next one has its weight loads in
+    // flight while the current one computes.  Then its down units.
+    int u = blockIdx.x;
+    if (u < a.n_gu) {
+        GuLoads<NB> cur, nxt;
+        gateup_issue<M_T, NB>(a, T, u, cur);
+        for (; u < a.n_gu; u += gridDim.x) {
+            const int un = u + gridDim.x;
+            if (un < a.n_gu) gateup_issue<M_T, NB>(a, T, un, nxt);
+            gateup_compute<M_T, NB>(a, T, lds, u, gen, cur);
+            cur = nxt;
+            __syncthreads();
+        }
+    }
+    for (; u < a.n_units; u += gridDim.x) {
+        down_unit<M_T>(a, T, lds, u - a.n_gu, gen);
         __syncthreads();
     }
 }
