@@ -30,8 +30,9 @@
 //     intermediate rows 16rg..16rg+15 of the slot's expert, full K = H, every
 //     token the slot serves; each h value is published as one 64-bit word
 //     (launch generation, value).
-//   * down (group, g): for output rows 16g..16g+15, the sum over the group's
-//     slots of W_down[e] (w * h).  It issues its weight loads, then loads the
+//   * down (group, g): for output rows 16 SUB g .. 16 SUB (g + 1) - 1 (SUB = 1
+//     for one token, 2 for more), the sum over the group's slots of
+//     W_down[e] (w * h).  It issues its weight loads, then loads the
 //     group's tagged h words -- re-reading those whose tag is stale -- stages
 //     w * h in LDS and finishes.  With one group it writes y; otherwise groups
 //     >= 1 publish tagged partial rows and the group-0 unit adds them in group
@@ -75,9 +76,18 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kUnitRows = 16;
 constexpr int kXBlock = 80;          // LDS bytes per 32-value block of x (64 + 16 pad)
 constexpr int kHBlock = 144;         // LDS bytes per 32-value block of h (128 + 16 pad)
-// Down chunks per load batch; two batches (A, B) are in flight before h is
-// staged, which covers the 13-14 chunks per wave of a 2560 x 768 layer at M = 1.
-constexpr int kDnBatch = 7;
+// A down unit covers SUB consecutive 16-row blocks: lane l takes the rows
+// 16 (SUB g + j) + (l & 15), j < SUB, of the same MX block, so every h value it
+// reads feeds SUB rows and SUB times fewer units stage h.  Several tokens:
+// 32 rows (their h staging traffic is what bounds the down phase); one token:
+// 16 rows (its down units are bound by each wave's serial arithmetic, which
+// fewer, larger units would lengthen: 16.8 against 14.9 us).
+template <int M_T>
+constexpr int dn_sub() { return M_T == 1 ? 1 : 2; }
+// Down chunks (per 16-row block) per load batch; two batches (A, B) are in
+// flight before h is staged.
+template <int M_T>
+constexpr int dn_batch() { return dn_sub<M_T>() == 2 ? 2 : 7; }
 // 16-byte loads of tagged h in flight per thread while staging.  A slot
 // group holds at most as many pairs as one batch stages (see ffn_layout), so
 // a down unit sees h after a single round trip once it is there.
@@ -107,7 +117,7 @@ struct FfnArgs {
     int E, H, I, k;
     int kbh, kbh4, kbi, kbi4;        // MX blocks along H / I and groups of four
     int gu_units;                    // I / 16
-    int dn_units;                    // H / 16
+    int dn_units;                    // H / (16 * dn_sub)
     int max_slots, max_groups, pair_cap;
     int n_gu, n_units;
     int pair_bytes, red_off;         // LDS layout
@@ -531,16 +541,19 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     const int n_items = (se - sb) * a.kbi4;
     const int i_begin = (w * n_items) / kWaves;
     const int i_end = ((w + 1) * n_items) / kWaves;
-    const size_t rg_codes = (size_t)g * a.kbi4 * 1024;
-    const size_t rg_scales = (size_t)g * a.kbi4 * 64;
+    constexpr int SUB = dn_sub<M_T>();
+    constexpr int kDnBatch = dn_batch<M_T>();
+    const size_t rg_codes = (size_t)(SUB * g) * a.kbi4 * 1024;
+    const size_t rg_scales = (size_t)(SUB * g) * a.kbi4 * 64;
+    const int sub_codes = a.kbi4 * 1024, sub_scales = a.kbi4 * 64;   // next 16-row block
     // Weights go in batches of kDnBatch chunks into two register sets (A, B):
     // batches 0 and 1 before h is staged, each next batch while the previous
     // computes.
-    u32x4 cwA[kDnBatch], cwB[kDnBatch];
-    uint32_t scA[kDnBatch], scB[kDnBatch];
+    u32x4 cwA[kDnBatch][SUB], cwB[kDnBatch][SUB];
+    uint32_t scA[kDnBatch][SUB], scB[kDnBatch][SUB];
     // items past i_end load the last item again (unused); the walk over
     // (slot, chunk) is branch-free so that no per-item state is carried
-    auto load_batch = [&](int i0, u32x4 (&cw)[kDnBatch], uint32_t (&scw)[kDnBatch]) {
+    auto load_batch = [&](int i0, u32x4 (&cw)[kDnBatch][SUB], uint32_t (&scw)[kDnBatch][SUB]) {
         int ls = i0 / a.kbi4;
         int ch = i0 - ls * a.kbi4;
 #pragma unroll
@@ -551,8 +564,11 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
             const size_t se = shared ? 0 : (size_t)e * a.dn_scales_stride;
             const uint8_t* cp = (shared ? a.sh_dn_codes : a.dn_codes) + ce + rg_codes + ch * 1024 + lane * 16;
             const uint8_t* sp = (shared ? a.sh_dn_scales : a.dn_scales) + se + rg_scales + ch * 64 + lane;
-            cw[k] = load_stream16(cp);
-            scw[k] = *sp;
+#pragma unroll
+            for (int j = 0; j < SUB; ++j) {
+                cw[k][j] = load_stream16(cp + j * sub_codes);
+                scw[k][j] = sp[j * sub_scales];
+            }
             const bool adv = i0 + k + 1 < i_end;
             const bool wrap = ch + 1 == a.kbi4;
             ls += (adv && wrap) ? 1 : 0;
@@ -644,10 +660,15 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     __syncthreads();
 
     const int quarter = lane >> 4;
-    float acc[M_T], acc2[M_T], acc3[M_T], acc4[M_T];   // four FMA chains per token
+    constexpr int kCh = SUB == 2 ? 2 : 4;                     // FMA chains per (row, token)
+    float acc[kCh][SUB][M_T];
 #pragma unroll
-    for (int m = 0; m < M_T; ++m) acc[m] = acc2[m] = acc3[m] = acc4[m] = 0.f;
-    auto compute_batch = [&](int i0, const u32x4 (&cw)[kDnBatch], const uint32_t (&scw)[kDnBatch]) {
+    for (int c = 0; c < kCh; ++c)
+#pragma unroll
+        for (int j = 0; j < SUB; ++j)
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) acc[c][j][m] = 0.f;
+    auto compute_batch = [&](int i0, const u32x4 (&cw)[kDnBatch][SUB], const uint32_t (&scw)[kDnBatch][SUB]) {
         int ls = i0 / a.kbi4;
         int ch = i0 - ls * a.kbi4;
 #pragma unroll
@@ -658,7 +679,9 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
                 // (no table lookups on the way to the LDS reads)
                 const uint32_t msk = (M_T == 1) ? 1u : T.mask[s];
                 const int p0 = (M_T == 1) ? ls : T.start[s] - pbase;
-                const float sc = e8m0_to_f32(scw[k]);
+                float sc[SUB];
+#pragma unroll
+                for (int j = 0; j < SUB; ++j) sc[j] = e8m0_to_f32(scw[k][j]);
                 const uint8_t* hq = lds + (4 * ch + quarter) * kHBlock;
                 int p = p0;
 #pragma unroll
@@ -673,14 +696,17 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
                     for (int v = 0; v < 8; ++v) hv[v] = hp[v];
                     ++p;
 #pragma unroll
-                    for (int v = 0; v < 8; ++v) {
-                        // four weights: bytes 2v and 2v+1 of the lane's 16 code bytes
-                        const f32x2 w0 = fp4x2_f32(cw[k][v >> 1], sc, (2 * v) & 3);
-                        const f32x2 w1 = fp4x2_f32(cw[k][v >> 1], sc, (2 * v + 1) & 3);
-                        acc[m] = fmaf(w0.x, hv[v].x, acc[m]);
-                        acc2[m] = fmaf(w0.y, hv[v].y, acc2[m]);
-                        acc3[m] = fmaf(w1.x, hv[v].z, acc3[m]);
-                        acc4[m] = fmaf(w1.y, hv[v].w, acc4[m]);
+                    for (int j = 0; j < SUB; ++j) {
+#pragma unroll
+                        for (int v = 0; v < 8; ++v) {
+                            // four weights: bytes 2v and 2v+1 of the lane's 16 code bytes
+                            const f32x2 w0 = fp4x2_f32(cw[k][j][v >> 1], sc[j], (2 * v) & 3);
+                            const f32x2 w1 = fp4x2_f32(cw[k][j][v >> 1], sc[j], (2 * v + 1) & 3);
+                            acc[0][j][m] = fmaf(w0.x, hv[v].x, acc[0][j][m]);
+                            acc[1 % kCh][j][m] = fmaf(w0.y, hv[v].y, acc[1 % kCh][j][m]);
+                            acc[2 % kCh][j][m] = fmaf(w1.x, hv[v].z, acc[2 % kCh][j][m]);
+                            acc[3 % kCh][j][m] = fmaf(w1.y, hv[v].w, acc[3 % kCh][j][m]);
+                        }
                     }
                 }
             }
@@ -698,25 +724,31 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
         if (i0 + 3 * kDnBatch < i_end) load_batch(i0 + 3 * kDnBatch, cwB, scB);
     }
 
-    float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][16]
+    float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][SUB][16]
 #pragma unroll
-    for (int m = 0; m < M_T; ++m) {
-        const float r = row_sum_f32((acc[m] + acc2[m]) + (acc3[m] + acc4[m]));
-        if (lane < kUnitRows) red[(w * M_T + m) * kUnitRows + lane] = r;
-    }
+    for (int m = 0; m < M_T; ++m)
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+            float t = acc[0][j][m] + acc[1][j][m];
+            if constexpr (kCh == 4) t += acc[2 % kCh][j][m] + acc[3 % kCh][j][m];
+            const float r = row_sum_f32(t);
+            if (lane < kUnitRows) red[((w * M_T + m) * SUB + j) * kUnitRows + lane] = r;
+        }
     __syncthreads();
     if (w != 0) return;
-    const int row = kUnitRows * g + lane;
+    constexpr int kRows = SUB * kUnitRows;                      // output rows of this unit
+    const int lr = lane & (kRows - 1);                          // lanes >= kRows mirror lanes < kRows
+    const int row = kRows * g + lr;
     float y[M_T];
 #pragma unroll
     for (int m = 0; m < M_T; ++m) {
         y[m] = 0.f;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) y[m] += (lane < kUnitRows) ? red[(v * M_T + m) * kUnitRows + lane] : 0.f;
+        for (int v = 0; v < kWaves; ++v) y[m] += red[((v * M_T + m) * SUB + (lr >> 4)) * kUnitRows + (lr & 15)];
     }
     if (n_groups > 1) {
         if (grp != 0) {
-            if (lane < kUnitRows) {
+            if (lane < kRows) {
 #pragma unroll
                 for (int m = 0; m < M_T; ++m) store_tagged(&a.part[((size_t)grp * M_T + m) * a.H + row], gen, y[m]);
             }
@@ -724,7 +756,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
         }
         // group 0 adds the other groups' partial rows, in group order, once
         // their tags say they are from this launch
-        const int prow = kUnitRows * g + (lane & (kUnitRows - 1));    // in bounds for every lane
+        const int prow = row;                                   // in bounds for every lane
         for (int gg = 1; gg < n_groups; ++gg) {
             uint64_t pv[M_T];
             uint32_t spins = 0;
@@ -746,7 +778,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
             for (int m = 0; m < M_T; ++m) y[m] += __uint_as_float((uint32_t)pv[m]);
         }
     }
-    if (lane < kUnitRows) {
+    if (lane < kRows) {
 #pragma unroll
         for (int m = 0; m < M_T; ++m) {
             const size_t o = (size_t)m * a.H + row;
@@ -1041,7 +1073,7 @@ hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int
     a.kbi = w.I / 32;
     a.kbi4 = (a.kbi + 3) / 4;
     a.gu_units = w.I / kUnitRows;
-    a.dn_units = w.H / kUnitRows;
+    a.dn_units = w.H / (kUnitRows * (M == 1 ? dn_sub<1>() : dn_sub<2>()));
     a.max_slots = L.max_slots;
     a.max_groups = L.max_groups;
     a.pair_cap = L.pair_cap;
