@@ -358,20 +358,22 @@ __device__ void table_groups(const FfnArgs& a, SlotTable& T) {
     int carry = 0, last_start = 0;
     for (int base = 0; base < n; base += kWave) {
         const int s = base + lane;
-        const int cnt = (s < n) ? __popc(T.mask[s]) : 0;
-        int incl = cnt;
+        static_assert(MOEDEC_MAX_M < 8, "pair counts take three bits");
+        const int cnt = (s < n) ? __popc(T.mask[s]) : 0;          // 0..MOEDEC_MAX_M
+        // exclusive prefix of the counts, bit by bit: one ballot per bit
+        int excl = 0, total = 0;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int o = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += o;
+        for (int b = 0; b < 3; ++b) {
+            const uint64_t bal = __ballot((cnt >> b) & 1);
+            excl += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << b;
+            total += __popcll(bal) << b;
         }
-        const int start = carry + incl - cnt;
+        const int start = carry + excl;
         if (s < n) T.start[s] = start;
-        int last = (cnt > 0) ? start : -1;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off, kWave));
-        if (last >= 0) last_start = last;
-        carry += __shfl(incl, kWave - 1, kWave);
+        const uint64_t nz = __ballot(cnt > 0);                      // the last slot with a pair
+        if (nz) last_start = __builtin_amdgcn_readlane(start, 63 - __clzll((long long)nz));
+        carry += total;
     }
     // more groups than launched only with a table not made for this k_max: the rest is dropped
     const int ng = min(last_start / a.pair_cap + 1, a.max_groups);

@@ -182,16 +182,19 @@ __device__ __forceinline__ int block_group_by_expert(
     }
     __syncthreads();
     if (tid < kWave) {
-        // exclusive prefix of popcounts over the 32 bitmap words
+        // exclusive prefix of popcounts (0..32) over the 32 bitmap words, bit
+        // by bit: one ballot per bit of the count
         const int c = (tid < MOEDEC_MAX_E / 32) ? __popc(bits[tid]) : 0;
-        int incl = c;
+        int excl = 0, total = 0;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int o = __shfl_up(incl, off, kWave);
-            if (tid >= off) incl += o;
+        for (int b = 0; b < 6; ++b) {
+            const uint64_t bal = __ballot((c >> b) & 1);
+            excl += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << b;
+            total += __popcll(bal) << b;
         }
-        if (tid < MOEDEC_MAX_E / 32) pre[tid] = incl - c;
-        if (tid == MOEDEC_MAX_E / 32 - 1) pre[MOEDEC_MAX_E / 32] = incl;
+        if (tid < MOEDEC_MAX_E / 32) pre[tid] = excl;
+        if (tid == 0) pre[MOEDEC_MAX_E / 32] = total;
     }
     __syncthreads();
     for (int t = tid; t < n_entries; t += n) {
