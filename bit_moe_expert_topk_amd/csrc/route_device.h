@@ -49,9 +49,9 @@ __device__ __forceinline__ float order_to_float(uint32_t ord) {
 // every one of the top k.  T is found from the 64 per-lane maxima by a radix
 // search over the top 16 bits of their integer image: the largest 16-bit
 // prefix that at least k lane maxima reach (each such lane holds a value >= T).
-// The values >= T ("survivors", typically a dozen) are compacted into LDS, one
-// per lane, and each is ranked against all of them by (logit desc, index asc);
-// rank r < k is the r-th choice.  If ties leave more than 64 survivors, the
+// The values >= T ("survivors", typically a dozen) are compacted into LDS and
+// each is ranked against all of them by (logit desc, index asc); rank r < k is
+// the r-th choice.  If ties leave more than 64 survivors, the
 // choices are taken one at a time instead: the largest remaining value (32-bit
 // wave maximum), then the smallest index holding it (32-bit wave minimum).
 template <int KPL>
@@ -95,7 +95,28 @@ __device__ __forceinline__ uint64_t wave_topk(const float* __restrict__ row, int
     __builtin_amdgcn_wave_barrier();
 
     uint64_t mine = 0ull;
-    if (base <= kWave) {
+    if (base <= 16) {
+        // the common case: survivor i = lane & 15 is compared with survivors
+        // 4q..4q+3, q = lane >> 4 (one batch of LDS reads), and the four
+        // partial counts of survivor i (lanes i, i + 16, i + 32, i + 48) are
+        // summed by two lane swaps
+        const int i = lane & 15, q4 = 4 * (lane >> 4);
+        const uint64_t my = buf[min(i, base - 1)];
+        uint64_t other[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) other[j] = buf[min(q4 + j, base - 1)];
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r += (q4 + j < base && other[j] > my) ? 1 : 0;
+        u32x2 p = swap16((uint32_t)r);
+        r = (int)(p[0] + p[1]);
+        p = swap32((uint32_t)r);
+        r = (int)(p[0] + p[1]);
+        __builtin_amdgcn_wave_barrier();
+        if (lane < 16 && i < base && r < k) buf[r] = my;
+        __builtin_amdgcn_wave_barrier();
+        mine = (lane < k) ? buf[min(lane, k - 1)] : 0ull;
+    } else if (base <= kWave) {
         // rank each survivor against all of them (broadcast one per step); rank
         // r < k is choice r
         const uint64_t my = buf[min(lane, base - 1)];
