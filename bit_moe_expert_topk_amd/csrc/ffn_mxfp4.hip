@@ -302,7 +302,7 @@ __device__ void table_from_logits(const FfnArgs& a, SlotTable& T, uint64_t* buf)
     if (w < M_T) {
         float wv;
         const float* row = a.logits + (size_t)w * a.E;
-        uint64_t* wbuf = buf + kWave * w;
+        uint64_t* wbuf = buf + kTopkBufWords * w;
         const uint64_t key = (a.E <= 512) ? wave_topk<8>(row, a.E, a.k, wv, wbuf)
                                           : wave_topk<16>(row, a.E, a.k, wv, wbuf);
         if (lane < a.k) {
@@ -823,7 +823,7 @@ void moe_ffn_kernel(FfnArgs a) {
         s_gen = g;
     }
     constexpr bool kDirectGroups = ROUTE && M_T == 1;     // the table arrives with its groups
-    // routing borrows the reduction area (M_T * 512 bytes: 64 words per routing
+    // routing borrows the reduction area (kTopkBufWords words per routing
     // wave), which the units use only after the prologue
     uint64_t* route_buf = reinterpret_cast<uint64_t*>(lds + a.red_off);
     if (kDirectGroups)
@@ -1003,9 +1003,9 @@ FfnLayout ffn_layout(int M, int k_max, int H, int I) {
     const int kbh4 = (H / 32 + 3) / 4, kbi4 = (I / 32 + 3) / 4;
     L.max_slots = M * k_max + 1;
     L.pair_bytes = kbi4 * 4 * kHBlock;
-    static_assert(kWaves * 2 * kUnitRows * sizeof(float) >= kWave * sizeof(uint64_t),
-                  "each routing wave borrows 64 words of the reduction area");
-    const size_t red_bytes = (size_t)kWaves * M * 2 * kUnitRows * sizeof(float);
+    // the reduction area, also lent to the routing waves (kTopkBufWords each)
+    const size_t red_bytes = std::max((size_t)kWaves * M * 2 * kUnitRows * sizeof(float),
+                                      (size_t)M * kTopkBufWords * sizeof(uint64_t));
     const size_t x_bytes = (size_t)M * kbh4 * 4 * kXBlock;
     // a group (at most pair_cap + M - 1 pairs: it ends on a slot boundary)
     // must fit the LDS target.  Smaller groups shorten each down unit and cost

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     __shared__ int32_t s_exp[MOEDEC_MAX_SLOTS];
     __shared__ uint32_t s_mask[MOEDEC_MAX_SLOTS];
     __shared__ float s_wt[MOEDEC_MAX_SLOTS][MOEDEC_MAX_M];
-    __shared__ uint64_t s_buf[MOEDEC_MAX_M][kWave];
+    __shared__ uint64_t s_buf[MOEDEC_MAX_M][kTopkBufWords];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();

@@ -20,6 +20,9 @@ namespace moedec {
 
 __device__ __forceinline__ int key_to_index(uint64_t key) { return (int)(~(uint32_t)key); }
 
+// LDS words (64-bit) wave_topk needs per wave: 64 survivors + one scratch word.
+constexpr int kTopkBufWords = 72;
+
 // Order-preserving integer image of a float32: 2^31 + |f| for f >= 0 and
 // 2^31 - |f| for f < 0, with |f| the magnitude bits.  a > b as floats <=>
 // ord(a) > ord(b); +0.0 and -0.0 map to the same image and every float maps
@@ -42,8 +45,8 @@ __device__ __forceinline__ float order_to_float(uint32_t ord) {
 // weight exp(l_r - l_0) / sum_j exp(l_j - l_0) (the softmax over all E
 // renormalised over the k chosen equals the softmax over the k chosen
 // logits).  Lanes >= k return key 0, weight 0.  KPL = keys per lane,
-// E <= 64 * KPL, 1 <= k <= min(E, 32).  `buf` is 64 words of LDS owned by
-// the calling wave (its contents are overwritten).
+// E <= 64 * KPL, 1 <= k <= min(E, 32).  `buf` is kTopkBufWords words of LDS
+// owned by the calling wave (its contents are overwritten).
 //
 // Method (exact).  Any threshold T that at least k of the values reach admits
 // every one of the top k.  T is found from the 64 per-lane maxima by a radix
@@ -80,17 +83,27 @@ __device__ __forceinline__ uint64_t wave_topk(const float* __restrict__ row, int
         if (__popcll(__ballot(lmax >= c)) >= k) T = c;
     }
 
-    // compact the survivors (value >= T) into LDS: order t-major, then lane
-    int base = 0;
+    // compact the survivors (value >= T) into LDS, lane by lane: per-lane
+    // counts, lane offsets by a ballot prefix sum (one ballot per count bit),
+    // then every lane writes all its values -- survivors to their place,
+    // the rest (and survivors past 64) to the scratch word buf[64]
+    static_assert(KPL < 32, "per-lane survivor counts take five bits");
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) cnt += (o[t] >= T) ? 1 : 0;
+    int pos = 0, base = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+        const uint64_t bal = __ballot((cnt >> b) & 1);
+        pos += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << b;
+        base += __popcll(bal) << b;
+    }
 #pragma unroll
     for (int t = 0; t < KPL; ++t) {
         const bool keep = o[t] >= T;
-        const uint64_t bal = __ballot(keep);
-        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        if (keep && pos < kWave)
-            buf[pos] = ((uint64_t)o[t] << 32) | (uint64_t)(~(uint32_t)(lane + kWave * t));
-        base += __popcll(bal);
+        buf[(keep && pos < kWave) ? pos : kWave] = ((uint64_t)o[t] << 32) | (uint64_t)(~(uint32_t)(lane + kWave * t));
+        pos += keep ? 1 : 0;
     }
     __builtin_amdgcn_wave_barrier();
 
