@@ -236,13 +236,13 @@ __device__ void table_from_dispatch(const FfnArgs& a, SlotTable& T) {
 // One token (M = 1): wave 0 builds the whole table from its top-k -- slot
 // 1 + rank(id) for each chosen expert, one (slot, token) pair per slot, and
 // the group bounds -- and block 0 writes the routing outputs from registers.
-__device__ void table_from_logits_one(const FfnArgs& a, SlotTable& T, uint64_t* buf) {
+__device__ void table_from_logits_one(const FfnArgs& a, SlotTable& T, uint64_t* buf, const float (&lv)[16]) {
     if (wave_id_uniform() != 0) return;
     const int lane = lane_id();
     const int k = a.k;
     float wv;
-    const uint64_t key = (a.E <= 512) ? wave_topk<8>(a.logits, a.E, k, wv, buf)
-                                      : wave_topk<16>(a.logits, a.E, k, wv, buf);
+    const uint64_t key = (a.E <= 512) ? wave_topk_of<8>(*reinterpret_cast<const float(*)[8]>(lv), a.E, k, wv, buf)
+                                      : wave_topk_of<16>(lv, a.E, k, wv, buf);
     const int id = key_to_index(key);
     const int rank = wave_rank_ids(lane < k ? id : 0x7FFFFFFF, k);
     const int n = k + 1;
@@ -295,16 +295,16 @@ __device__ void table_from_logits_one(const FfnArgs& a, SlotTable& T, uint64_t* 
 // Several tokens: one wave per token selects its experts, the block groups
 // the choices by expert (the pair counts and groups follow in table_groups).
 template <int M_T>
-__device__ void table_from_logits(const FfnArgs& a, SlotTable& T, uint64_t* buf) {
+__device__ void table_from_logits(const FfnArgs& a, SlotTable& T, uint64_t* buf, const float (&lv)[16]) {
     __shared__ RouteScratch R;
     const int w = wave_id_uniform(), lane = lane_id(), tid = threadIdx.x;
     const uint32_t full = (1u << M_T) - 1u;
     if (w < M_T) {
         float wv;
-        const float* row = a.logits + (size_t)w * a.E;
         uint64_t* wbuf = buf + kTopkBufWords * w;
-        const uint64_t key = (a.E <= 512) ? wave_topk<8>(row, a.E, a.k, wv, wbuf)
-                                          : wave_topk<16>(row, a.E, a.k, wv, wbuf);
+        const uint64_t key = (a.E <= 512)
+            ? wave_topk_of<8>(*reinterpret_cast<const float(*)[8]>(lv), a.E, a.k, wv, wbuf)
+            : wave_topk_of<16>(lv, a.E, a.k, wv, wbuf);
         if (lane < a.k) {
             R.id[w][lane] = key_to_index(key);
             R.w[w][lane] = wv;
@@ -800,7 +800,17 @@ void moe_ffn_kernel(FfnArgs a) {
     const int tid = threadIdx.x;
     const bool has_gu = (int)blockIdx.x < a.n_gu;          // the block runs a gate/up unit
 
-    // x does not depend on routing: its loads go out first (unconditional,
+    // The routing waves' logits go out first (loads return in order and the
+    // top-k needs them before anything else; lane l holds entries l + 64 t).
+    float lv[16];
+    if (ROUTE && wave_id_uniform() < M_T) {
+        const float* row = a.logits + (size_t)wave_id_uniform() * a.E;
+        if (a.E <= 512)
+            topk_load<8>(row, a.E, *reinterpret_cast<float(*)[8]>(lv));
+        else
+            topk_load<16>(row, a.E, lv);
+    }
+    // x does not depend on routing: its loads go out next (unconditional,
     // clamped index), and are staged in LDS once the slot table is built.
     // With a residual input the loads bring r (float32, twice the bytes) and
     // x = bf16(RMSNorm(r)) is formed after routing.
@@ -827,9 +837,9 @@ void moe_ffn_kernel(FfnArgs a) {
     // wave), which the units use only after the prologue
     uint64_t* route_buf = reinterpret_cast<uint64_t*>(lds + a.red_off);
     if (kDirectGroups)
-        table_from_logits_one(a, T, route_buf);
+        table_from_logits_one(a, T, route_buf, lv);
     else if (ROUTE)
-        table_from_logits<M_T>(a, T, route_buf);
+        table_from_logits<M_T>(a, T, route_buf, lv);
     else
         table_from_dispatch<M_T>(a, T);
     if (has_gu && norm) {

@@ -57,18 +57,36 @@ __device__ __forceinline__ float order_to_float(uint32_t ord) {
 // the r-th choice.  If ties leave more than 64 survivors, the
 // choices are taken one at a time instead: the largest remaining value (32-bit
 // wave maximum), then the smallest index holding it (32-bit wave minimum).
+// The logits of one token as the top-k reads them: lane l holds entries
+// l + 64 t.  The loads are unconditional (clamped index) so that they are all
+// in flight at once; lanes past E are masked by wave_topk_of.
+template <int KPL>
+__device__ __forceinline__ void topk_load(const float* __restrict__ row, int E, float (&v)[KPL]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) v[t] = row[min(lane + kWave * t, E - 1)];
+}
+
+template <int KPL>
+__device__ __forceinline__ uint64_t wave_topk_of(const float (&v)[KPL], int E, int k, float& weight,
+                                                 uint64_t* buf);
+
 template <int KPL>
 __device__ __forceinline__ uint64_t wave_topk(const float* __restrict__ row, int E, int k, float& weight,
                                               uint64_t* buf) {
+    float v[KPL];
+    topk_load<KPL>(row, E, v);
+    return wave_topk_of<KPL>(v, E, k, weight, buf);
+}
+
+// wave_topk on logits already loaded by topk_load.
+template <int KPL>
+__device__ __forceinline__ uint64_t wave_topk_of(const float (&v)[KPL], int E, int k, float& weight,
+                                                 uint64_t* buf) {
     // buf holds the survivors, then the k choices; one wave's LDS operations
     // complete in issue order, so the reads of one phase are done before the
     // writes of the next land
     const int lane = lane_id();
-    // loads are unconditional (clamped index) so that they are all in flight at
-    // once; lanes past E are masked afterwards
-    float v[KPL];
-#pragma unroll
-    for (int t = 0; t < KPL; ++t) v[t] = row[min(lane + kWave * t, E - 1)];
     uint32_t o[KPL];
 #pragma unroll
     for (int t = 0; t < KPL; ++t) o[t] = (lane + kWave * t < E) ? float_order(v[t]) : 0u;
