@@ -11,6 +11,9 @@
 // every row each lane loads the same 16-byte column chunks (chunk lane + 64t),
 // so its slice of x is loaded into registers once and reused for every row
 // the wave visits.  Rows are summed across the wave at the end.
+#include <algorithm>
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -18,19 +21,57 @@ namespace moedec {
 
 namespace {
 
-// E4M3 code of a float32, nearest-even, saturating to +-448, sign kept.
-__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    if (a >= 0x43E00000u) return sign | 0x7Eu;                // |v| >= 448
-    if (a >= 0x3C800000u) {                                    // |v| >= 2^-6: normal
-        const uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);   // keep 3 mantissa bits
-        return sign | ((rounded - (120u << 23)) >> 20);        // rebias 127 -> 7
+// E4M3 magnitude code (0x00..0x7E) of a non-negative float32 q: nearest
+// value, ties to the even code, saturating at 448.  At and above 2^-6 the code
+// keeps 3 of the 23 mantissa bits (round to nearest even on the 20 dropped
+// bits) and rebiases the exponent from 127 to 7; below 2^-6 it is q / 2^-9
+// rounded to the nearest even integer, read from the low bits of q + 2^14
+// (whose float32 spacing is 2^-9).  Values above 448 and NaN give codes above
+// 0x7E and are clamped to it; CLAMP = false leaves that out for quotients
+// known to stay below 464, the midpoint above 448.
+template <bool CLAMP = true>
+__device__ __forceinline__ uint32_t e4m3_mag_code(float q) {
+    const uint32_t b = __float_as_uint(q);
+    const uint32_t nrm = (b + (0x7FFFFu - (120u << 23)) + ((b >> 20) & 1u)) >> 20;
+    const uint32_t sub = __float_as_uint(q + 16384.0f) - 0x46800000u;
+    const uint32_t c = b >= 0x3C800000u ? nrm : sub;
+    if constexpr (CLAMP) return c < 0x7Eu ? c : 0x7Eu;
+    return c;
+}
+
+// Quotient |w| / s of a bf16 magnitude (its 15 low bits, placed in the top of
+// a float) by the row scale.  FAST replaces the division by the product with
+// the rounded reciprocal y = 1/s and one correction with the exact remainder
+// (Markstein's method: q0 = w*y, r = w - q0*s by fused multiply-add, q = q0 +
+// r*y).  For every bf16 w and every s >= 2^-90 of a bf16 absmax this equals
+// the IEEE quotient wherever the quotient is at least 2^-14; below that both
+// round to E4M3 code 0.  Rows with a smaller scale divide.
+template <bool FAST>
+__device__ __forceinline__ float row_quotient(uint32_t mag_bits, float s, float y) {
+    const float w = __uint_as_float(mag_bits);
+    if constexpr (FAST) {
+        const float q0 = w * y;
+        const float r = __builtin_fmaf(-q0, s, w);
+        return __builtin_fmaf(r, y, q0);
+    } else {
+        return w / s;
     }
-    // subnormal: multiple of 2^-9, 0..8 (8 is the least normal, code 0x08)
-    const float scaled = __uint_as_float(a) * 512.0f;
-    return sign | (uint32_t)__builtin_rintf(scaled);
+}
+
+// Four E4M3 codes of the four bf16 values in (d0, d1), low half first; the
+// sign bit of each code is the bf16 sign bit (the scale is positive).  With a
+// normal scale s = fl32(a / 448) >= a / 448 * (1 - 2^-24) and |w| <= a, every
+// quotient is at most one float32 step above 448, which rounds to 448: FAST
+// needs no clamp.  Subnormal scales lose precision, so the dividing path clamps.
+template <bool FAST>
+__device__ __forceinline__ uint32_t quant4(uint32_t d0, uint32_t d1, float s, float y) {
+    const uint32_t c0 = e4m3_mag_code<!FAST>(row_quotient<FAST>((d0 & 0x7FFFu) << 16, s, y));
+    const uint32_t c1 = e4m3_mag_code<!FAST>(row_quotient<FAST>(d0 & 0x7FFF0000u, s, y));
+    const uint32_t c2 = e4m3_mag_code<!FAST>(row_quotient<FAST>((d1 & 0x7FFFu) << 16, s, y));
+    const uint32_t c3 = e4m3_mag_code<!FAST>(row_quotient<FAST>(d1 & 0x7FFF0000u, s, y));
+    const uint32_t sign = ((d0 >> 8) & 0x80u) | ((d0 >> 16) & 0x8000u) | ((d1 << 8) & 0x800000u) |
+                          (d1 & 0x80000000u);
+    return (c0 | (c1 << 8) | (c2 << 16) | (c3 << 24)) | sign;
 }
 
 constexpr int kRows = 4;   // rows per wave step
@@ -57,49 +98,47 @@ __device__ __forceinline__ void store_row_sums(const float (&acc)[R][M_T], int v
     }
 }
 
+// Quantisation.  T = 16-byte chunks (8 bf16) per lane per row, exactly
+// ceil(H / 8 / 64); each wave quantises one row per step, all of its loads in
+// flight at once, and many waves per SIMD keep the rows overlapping.
 template <int T>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ w, int V,
                                                         int H, uint8_t* __restrict__ codes,
                                                         float* __restrict__ rs) {
     const int lane = lane_id();
-    const int n_ch = H / 8;                                   // 8 bf16 per chunk
+    const int n_ch = H / 8;
     const int waves = gridDim.x * (blockDim.x >> 6);
     for (int v = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); v < V; v += waves) {
-        const uint8_t* row = reinterpret_cast<const uint8_t*>(w) + (size_t)v * H * 2;
         // unconditional loads (clamped chunk index): all in flight at once
+        const uint8_t* row = reinterpret_cast<const uint8_t*>(w) + (size_t)v * H * 2;
         u32x4 c[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) c[t] = load_stream16(row + (size_t)min(lane + 64 * t, n_ch - 1) * 16);
-        uint32_t amax = 0;
+        uint32_t am = 0;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = c[t][i] & 0x7FFFu, hi = (c[t][i] >> 16) & 0x7FFFu;
-                amax = lo > amax ? lo : amax;
-                amax = hi > amax ? hi : amax;
-            }
+            for (int i = 0; i < 4; ++i) am = max(am, max(c[t][i] & 0x7FFFu, (c[t][i] >> 16) & 0x7FFFu));
         }
-        amax = wave_max_u32(amax);
-        const float a = bf16_to_f32(amax);
+        const float a = bf16_to_f32(wave_max_u32(am));
         const float s = (a == 0.f) ? 1.0f : a / 448.0f;
+        const float y = 1.0f / s;
+        const bool fast = s >= 0x1p-90f && s <= 0x1.fffffep127f;   // wave-uniform
+        uint8_t* out_row = codes + (size_t)v * H;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             const int ch = lane + 64 * t;
-            if (ch < n_ch) {
-                u32x2 out;
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const uint32_t d = c[t][2 * i + (b >> 1)];
-                        const uint32_t bits = (b & 1) ? (d >> 16) : (d & 0xFFFFu);
-                        word |= f32_to_e4m3_sat(bf16_to_f32(bits) / s) << (8 * b);
-                    }
-                    out[i] = word;
+            if (64 * (t + 1) <= n_ch || ch < n_ch) {
+                const u32x4 d = c[t];
+                u32x2 o;
+                if (fast) {
+                    o[0] = quant4<true>(d[0], d[1], s, y);
+                    o[1] = quant4<true>(d[2], d[3], s, y);
+                } else {
+                    o[0] = quant4<false>(d[0], d[1], s, y);
+                    o[1] = quant4<false>(d[2], d[3], s, y);
                 }
-                *reinterpret_cast<u32x2*>(codes + (size_t)v * H + (size_t)ch * 8) = out;
+                *reinterpret_cast<u32x2*>(out_row + (size_t)ch * 8) = o;
             }
         }
         if (lane == 0) rs[v] = s;
@@ -268,20 +307,46 @@ hipError_t gemv_bf16_m(const uint16_t* w, int V, int H, const uint32_t* x, float
     return hipGetLastError();
 }
 
+// Rows are handed out grid-stride, so the grid is sized to what is resident
+// at once (occupancy of the instantiation times the CU count), not beyond.
+template <int T>
+hipError_t quant_t(const uint16_t* w, int V, int H, uint8_t* codes, float* rs, hipStream_t s) {
+    static std::atomic<int> resident{0};            // blocks resident on the whole device
+    int blocks = resident.load(std::memory_order_relaxed);
+    if (blocks == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(&quant_fp8_kernel<T>), 256, 0);
+        if (e != hipSuccess) return e;
+        blocks = std::max(1, cus * per_cu);
+        resident.store(blocks, std::memory_order_relaxed);
+    }
+    const int need = (V + 3) / 4;                   // one row per wave step, 4 waves per block
+    const dim3 grid(need < blocks ? need : blocks), blk(256);
+    hipLaunchKernelGGL((quant_fp8_kernel<T>), grid, blk, 0, s, w, V, H, codes, rs);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_lmhead_quant(const uint16_t* w, int V, int H, uint8_t* codes, float* rs,
                                hipStream_t s) {
-    const int T = (H / 8 + 63) / 64;      // H <= 8192 -> T <= 16
-    const int waves = V < 8192 ? V : 8192;
-    const dim3 grid((waves + 3) / 4), blk(256);
-    switch ((T + 3) / 4) {
-        case 1: hipLaunchKernelGGL(quant_fp8_kernel<4>, grid, blk, 0, s, w, V, H, codes, rs); break;
-        case 2: hipLaunchKernelGGL(quant_fp8_kernel<8>, grid, blk, 0, s, w, V, H, codes, rs); break;
-        case 3: hipLaunchKernelGGL(quant_fp8_kernel<12>, grid, blk, 0, s, w, V, H, codes, rs); break;
-        default: hipLaunchKernelGGL(quant_fp8_kernel<16>, grid, blk, 0, s, w, V, H, codes, rs); break;
+    switch ((H / 8 + 63) / 64) {          // 16 <= H <= 8192, H % 16 == 0 -> T in 1..16
+        case 1: return quant_t<1>(w, V, H, codes, rs, s);
+        case 2: return quant_t<2>(w, V, H, codes, rs, s);
+        case 3: return quant_t<3>(w, V, H, codes, rs, s);
+        case 4: return quant_t<4>(w, V, H, codes, rs, s);
+        case 5: return quant_t<5>(w, V, H, codes, rs, s);
+        case 6: return quant_t<6>(w, V, H, codes, rs, s);
+        case 7: return quant_t<7>(w, V, H, codes, rs, s);
+        case 8: return quant_t<8>(w, V, H, codes, rs, s);
+        case 9: case 10: return quant_t<10>(w, V, H, codes, rs, s);
+        case 11: case 12: return quant_t<12>(w, V, H, codes, rs, s);
+        default: return quant_t<16>(w, V, H, codes, rs, s);
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_gemv_fp8(const uint8_t* codes, const float* rs, int V, int H,

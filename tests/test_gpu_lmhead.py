@@ -44,6 +44,11 @@ def test_quant_small(m, V, H):
     wb[0] = 0                                   # all-zero row -> scale 1, codes 0
     wb[1, :] = synth.bf16_bits_from_f32(np.float32([-(2.0 ** -20)] * H))   # tiny negative row
     wb[2, 3] = synth.bf16_bits_from_f32(np.float32([-3.0]))[0]            # negative absmax
+    # scale below 2^-90: the kernel divides element by element for this row
+    rng = np.random.default_rng(V)
+    wb[3] = synth.bf16_bits_from_f32((rng.standard_normal(H) * 2.0 ** -100).astype(np.float32))
+    # bf16 subnormals (and -0.0) beside normal values: quotients far below code 0x01
+    wb[4, :4] = [0x0001, 0x8003, 0x007F, 0x8000]
     _check_quant(m, wb)
 
 
