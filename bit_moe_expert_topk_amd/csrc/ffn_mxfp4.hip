@@ -85,9 +85,11 @@ constexpr int kHBlock = 144;         // LDS bytes per 32-value block of h (128 +
 template <int M_T>
 constexpr int dn_sub() { return M_T == 1 ? 1 : 2; }
 // Down chunks (per 16-row block) per load batch; two batches (A, B) are in
-// flight before h is staged.
-template <int M_T>
-constexpr int dn_batch() { return dn_sub<M_T>() == 2 ? 2 : 7; }
+// flight before h is staged.  With one unit per block (ONE) a single batch of
+// 5 covers a one-token unit of three 768-wide pairs (4.5 chunks per wave) and
+// frees the registers of the second set.
+template <int M_T, bool ONE>
+constexpr int dn_batch() { return ONE ? 5 : (dn_sub<M_T>() == 2 ? 2 : 7); }
 // 16-byte loads of tagged h in flight per thread while staging.  A slot
 // group holds at most as many pairs as one batch stages (see ffn_layout), so
 // a down unit sees h after a single round trip once it is there.
@@ -96,12 +98,15 @@ constexpr int stage_batch() { return 8; }
 constexpr int kMaxGroups = MOEDEC_MAX_M * MOEDEC_MAX_K + MOEDEC_MAX_M;
 constexpr int kMaxPairs = kMaxGroups + MOEDEC_MAX_M;
 constexpr int kMaxGrid = 4096;
-// Co-resident blocks per CU (168 VGPRs per lane).  Three blocks per CU give a
-// one-token 2560 x 768 layer a block for each of its 592 units, so every down
-// unit issues its weight loads right after routing; the generation words let
-// the count differ per token count.
-template <int M_T>
-constexpr int blocks_per_cu() { return 3; }
+// Co-resident blocks per CU.  The general form keeps a block's next gate/up
+// unit and a second down batch in flight (168 VGPRs per lane: three blocks).
+// When the grid has a block for every unit (ONE, one token), neither is
+// needed and 128 VGPRs give four blocks per CU: a one-token 2560 x 768 layer's
+// 912 units then all start at once, so every down unit issues its weight
+// loads right after routing.  The generation words let the grid differ
+// between launches.
+template <bool ONE>
+constexpr int blocks_per_cu() { return ONE ? 4 : 3; }
 constexpr uint32_t kSpinLimit = 1u << 20;   // bounded waits; reached only if co-residency fails
 
 struct FfnArgs {
@@ -519,7 +524,7 @@ __device__ void gateup_compute(const FfnArgs& a, const SlotTable& T, uint8_t* ld
 // ---------------------------------------------------------------------------
 // down unit
 
-template <int M_T>
+template <int M_T, bool ONE>
 __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, uint32_t gen) {
     const int n_nc = (a.max_groups - 1) * a.dn_units;    // units of groups 1.. come first
     int grp, g;
@@ -544,15 +549,17 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     const int i_begin = (w * n_items) / kWaves;
     const int i_end = ((w + 1) * n_items) / kWaves;
     constexpr int SUB = dn_sub<M_T>();
-    constexpr int kDnBatch = dn_batch<M_T>();
+    constexpr int kDnBatch = dn_batch<M_T, ONE>();
     const size_t rg_codes = (size_t)(SUB * g) * a.kbi4 * 1024;
     const size_t rg_scales = (size_t)(SUB * g) * a.kbi4 * 64;
     const int sub_codes = a.kbi4 * 1024, sub_scales = a.kbi4 * 64;   // next 16-row block
     // Weights go in batches of kDnBatch chunks into two register sets (A, B):
     // batches 0 and 1 before h is staged, each next batch while the previous
     // computes.
-    u32x4 cwA[kDnBatch][SUB], cwB[kDnBatch][SUB];
-    uint32_t scA[kDnBatch][SUB], scB[kDnBatch][SUB];
+    // (ONE: one register set; later batches load after the previous computes)
+    constexpr int kSetB = ONE ? 1 : kDnBatch;
+    u32x4 cwA[kDnBatch][SUB], cwB[kSetB][SUB];
+    uint32_t scA[kDnBatch][SUB], scB[kSetB][SUB];
     // items past i_end load the last item again (unused); the walk over
     // (slot, chunk) is branch-free so that no per-item state is carried
     auto load_batch = [&](int i0, u32x4 (&cw)[kDnBatch][SUB], uint32_t (&scw)[kDnBatch][SUB]) {
@@ -578,7 +585,9 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
         }
     };
     if (i_begin < i_end) load_batch(i_begin, cwA, scA);
-    if (i_begin + kDnBatch < i_end) load_batch(i_begin + kDnBatch, cwB, scB);
+    if constexpr (!ONE) {
+        if (i_begin + kDnBatch < i_end) load_batch(i_begin + kDnBatch, cwB, scB);
+    }
 
     if (w == 0) {
         // the group's (slot, token) pairs
@@ -719,11 +728,18 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
             if (M_T > 1) __builtin_amdgcn_sched_barrier(0);   // bound register pressure: one item at a time
         }
     };
-    for (int i0 = i_begin; i0 < i_end; i0 += 2 * kDnBatch) {
-        compute_batch(i0, cwA, scA);
-        if (i0 + 2 * kDnBatch < i_end) load_batch(i0 + 2 * kDnBatch, cwA, scA);
-        if (i0 + kDnBatch < i_end) compute_batch(i0 + kDnBatch, cwB, scB);
-        if (i0 + 3 * kDnBatch < i_end) load_batch(i0 + 3 * kDnBatch, cwB, scB);
+    if constexpr (ONE) {
+        for (int i0 = i_begin; i0 < i_end; i0 += kDnBatch) {
+            if (i0 != i_begin) load_batch(i0, cwA, scA);
+            compute_batch(i0, cwA, scA);
+        }
+    } else {
+        for (int i0 = i_begin; i0 < i_end; i0 += 2 * kDnBatch) {
+            compute_batch(i0, cwA, scA);
+            if (i0 + 2 * kDnBatch < i_end) load_batch(i0 + 2 * kDnBatch, cwA, scA);
+            if (i0 + kDnBatch < i_end) compute_batch(i0 + kDnBatch, cwB, scB);
+            if (i0 + 3 * kDnBatch < i_end) load_batch(i0 + 3 * kDnBatch, cwB, scB);
+        }
     }
 
     float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][SUB][16]
@@ -791,8 +807,8 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     }
 }
 
-template <int M_T, int NB, bool ROUTE, bool NORM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(blocks_per_cu<M_T>())))
+template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(blocks_per_cu<ONE>())))
 void moe_ffn_kernel(FfnArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ SlotTable T;
@@ -923,7 +939,14 @@ void moe_ffn_kernel(FfnArgs a) {
     // Gate/up units come first: a block's next one has its weight loads in
     // flight while the current one computes.  Then its down units.
     int u = blockIdx.x;
-    if (u < a.n_gu) {
+    if (ONE) {
+        for (; u < a.n_gu; u += gridDim.x) {
+            GuLoads<NB> cur;
+            gateup_issue<M_T, NB>(a, T, u, cur);
+            gateup_compute<M_T, NB>(a, T, lds, u, gen, cur);
+            __syncthreads();
+        }
+    } else if (u < a.n_gu) {
         GuLoads<NB> cur, nxt;
         gateup_issue<M_T, NB>(a, T, u, cur);
         for (; u < a.n_gu; u += gridDim.x) {
@@ -935,7 +958,7 @@ void moe_ffn_kernel(FfnArgs a) {
         }
     }
     for (; u < a.n_units; u += gridDim.x) {
-        down_unit<M_T>(a, T, lds, u - a.n_gu, gen);
+        down_unit<M_T, ONE>(a, T, lds, u - a.n_gu, gen);
         __syncthreads();
     }
 }
@@ -966,10 +989,11 @@ int device_cus() {
     return d.cus;
 }
 
-template <int M_T, int NB, bool ROUTE, bool NORM>
+template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE>
 hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) {
-    constexpr int kBlocksPerCU = blocks_per_cu<M_T>();
-    const int grid = std::min(kMaxGrid, kBlocksPerCU * cus);
+    constexpr int kBlocksPerCU = blocks_per_cu<ONE>();
+    // ONE: a block per unit (the host picks ONE only when they all fit)
+    const int grid = ONE ? std::min(a.n_units, kMaxGrid) : std::min(kMaxGrid, kBlocksPerCU * cus);
     // every block must be resident at once: check the occupancy of this variant
     static std::atomic<int> occ_ok[256];                      // per LDS size class of 256 B
     const size_t cls = std::min<size_t>((lds + 255) / 256, 255);
@@ -977,33 +1001,46 @@ hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) 
     if (v == 0) {
         int blocks = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE, NORM>), kThreads, lds);
+            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE>), kThreads, lds);
         if (e != hipSuccess) return e;
         v = (blocks >= kBlocksPerCU) ? 1 : 2;
         occ_ok[cls].store(v, std::memory_order_relaxed);
     }
     if (v != 1) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE, NORM>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE>), dim3(grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
-template <int M_T, bool ROUTE, bool NORM>
+template <int M_T, bool ROUTE, bool NORM, bool ONE>
 hipError_t launch_nb(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     switch (nb) {
-        case 1: return launch_variant<M_T, 1, ROUTE, NORM>(a, cus, lds, s);
-        case 2: return launch_variant<M_T, 2, ROUTE, NORM>(a, cus, lds, s);
-        case 4: return launch_variant<M_T, 4, ROUTE, NORM>(a, cus, lds, s);
-        case 5: return launch_variant<M_T, 5, ROUTE, NORM>(a, cus, lds, s);
-        default: return launch_variant<M_T, 8, ROUTE, NORM>(a, cus, lds, s);
+        case 1: return launch_variant<M_T, 1, ROUTE, NORM, ONE>(a, cus, lds, s);
+        case 2: return launch_variant<M_T, 2, ROUTE, NORM, ONE>(a, cus, lds, s);
+        case 4: return launch_variant<M_T, 4, ROUTE, NORM, ONE>(a, cus, lds, s);
+        case 5: return launch_variant<M_T, 5, ROUTE, NORM, ONE>(a, cus, lds, s);
+        default: return launch_variant<M_T, 8, ROUTE, NORM, ONE>(a, cus, lds, s);
     }
+}
+
+// One token: a block per unit when the units fit four blocks per CU (and the
+// variant's occupancy allows it), else the general three-block grid.
+template <int M_T, bool ROUTE, bool NORM>
+hipError_t launch_one(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
+    if constexpr (M_T == 1) {
+        if (a.n_units <= std::min(kMaxGrid, blocks_per_cu<true>() * cus)) {
+            const hipError_t e = launch_nb<M_T, ROUTE, NORM, true>(a, nb, cus, lds, s);
+            if (e != hipErrorInvalidConfiguration) return e;
+        }
+    }
+    return launch_nb<M_T, ROUTE, NORM, false>(a, nb, cus, lds, s);
 }
 
 // routing from logits with or without the residual stream, or from a table
 template <int M_T>
 hipError_t launch_m(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
-    if (a.r_in) return launch_nb<M_T, true, true>(a, nb, cus, lds, s);
-    if (a.logits) return launch_nb<M_T, true, false>(a, nb, cus, lds, s);
-    return launch_nb<M_T, false, false>(a, nb, cus, lds, s);
+    if (a.r_in) return launch_one<M_T, true, true>(a, nb, cus, lds, s);
+    if (a.logits) return launch_one<M_T, true, false>(a, nb, cus, lds, s);
+    return launch_one<M_T, false, false>(a, nb, cus, lds, s);
 }
 
 }  // namespace
