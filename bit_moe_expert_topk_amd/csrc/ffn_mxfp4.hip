@@ -82,19 +82,19 @@ constexpr int kHBlock = 144;         // LDS bytes per 32-value block of h (128 +
 // 32 rows (their h staging traffic is what bounds the down phase); one token:
 // 16 rows (its down units are bound by each wave's serial arithmetic, which
 // fewer, larger units would lengthen: 16.8 against 14.9 us).
-template <int M_T>
-constexpr int dn_sub() { return M_T == 1 ? 1 : 2; }
+template <int M_T, bool ONE>
+constexpr int dn_sub() { return (M_T == 1 && !ONE) ? 1 : 2; }
 // Down chunks (per 16-row block) per load batch; two batches (A, B) are in
 // flight before h is staged.  With one unit per block (ONE) a single batch of
 // 5 covers a one-token unit of three 768-wide pairs (4.5 chunks per wave) and
 // frees the registers of the second set.
 template <int M_T, bool ONE>
-constexpr int dn_batch() { return ONE ? 5 : (dn_sub<M_T>() == 2 ? 2 : 7); }
+constexpr int dn_batch() { return ONE ? 5 : (dn_sub<M_T, ONE>() == 2 ? 2 : 7); }
 // 16-byte loads of tagged h in flight per thread while staging.  A slot
 // group holds at most as many pairs as one batch stages (see ffn_layout), so
 // a down unit sees h after a single round trip once it is there.
-template <int M_T>
-constexpr int stage_batch() { return 8; }
+template <int M_T, bool ONE>
+constexpr int stage_batch() { return ONE ? 5 : 8; }
 constexpr int kMaxGroups = MOEDEC_MAX_M * MOEDEC_MAX_K + MOEDEC_MAX_M;
 constexpr int kMaxPairs = kMaxGroups + MOEDEC_MAX_M;
 constexpr int kMaxGrid = 4096;
@@ -548,7 +548,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     const int n_items = (se - sb) * a.kbi4;
     const int i_begin = (w * n_items) / kWaves;
     const int i_end = ((w + 1) * n_items) / kWaves;
-    constexpr int SUB = dn_sub<M_T>();
+    constexpr int SUB = dn_sub<M_T, ONE>();
     constexpr int kDnBatch = dn_batch<M_T, ONE>();
     const size_t rg_codes = (size_t)(SUB * g) * a.kbi4 * 1024;
     const size_t rg_scales = (size_t)(SUB * g) * a.kbi4 * 64;
@@ -611,7 +611,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
             __builtin_amdgcn_make_buffer_rsrc(a.h, 0, a.h_bytes, kBufferRsrcWord3);
         const int per_pair = a.kbi4 * 4 * 16;              // 16-byte loads per pair, padding included
         const int total = n_pairs * per_pair;
-        constexpr int kStage = stage_batch<M_T>();
+        constexpr int kStage = stage_batch<M_T, ONE>();
         static_assert(kStage <= 32, "one done bit per load");
         const uint32_t all = (1u << kStage) - 1u;
         for (int i0 = 0; i0 < total; i0 += kThreads * kStage) {
@@ -700,24 +700,30 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
                     // with one token every slot of a group serves it; otherwise skip the
                     // tokens the slot does not serve (its weight is zero anyway)
                     if (M_T > 1 && !((msk >> m) & 1u)) continue;
-                    // the 8 LDS reads of this (slot, token) go out back to back
+                    // the LDS reads of this (slot, token) go out back to back, in
+                    // halves when the unit has two row blocks (register pressure)
                     const float4* hp = reinterpret_cast<const float4*>(hq + p * a.pair_bytes);
-                    float4 hv[8];
-#pragma unroll
-                    for (int v = 0; v < 8; ++v) hv[v] = hp[v];
+                    constexpr int kHv = SUB == 2 ? 4 : 8;
                     ++p;
+#pragma unroll
+                    for (int v0 = 0; v0 < 8; v0 += kHv) {
+                    float4 hv[kHv];
+#pragma unroll
+                    for (int v = 0; v < kHv; ++v) hv[v] = hp[v0 + v];
 #pragma unroll
                     for (int j = 0; j < SUB; ++j) {
 #pragma unroll
-                        for (int v = 0; v < 8; ++v) {
+                        for (int vv = 0; vv < kHv; ++vv) {
+                            const int v = v0 + vv;
                             // four weights: bytes 2v and 2v+1 of the lane's 16 code bytes
                             const f32x2 w0 = fp4x2_f32(cw[k][j][v >> 1], sc[j], (2 * v) & 3);
                             const f32x2 w1 = fp4x2_f32(cw[k][j][v >> 1], sc[j], (2 * v + 1) & 3);
-                            acc[0][j][m] = fmaf(w0.x, hv[v].x, acc[0][j][m]);
-                            acc[1 % kCh][j][m] = fmaf(w0.y, hv[v].y, acc[1 % kCh][j][m]);
-                            acc[2 % kCh][j][m] = fmaf(w1.x, hv[v].z, acc[2 % kCh][j][m]);
-                            acc[3 % kCh][j][m] = fmaf(w1.y, hv[v].w, acc[3 % kCh][j][m]);
+                            acc[0][j][m] = fmaf(w0.x, hv[vv].x, acc[0][j][m]);
+                            acc[1 % kCh][j][m] = fmaf(w0.y, hv[vv].y, acc[1 % kCh][j][m]);
+                            acc[2 % kCh][j][m] = fmaf(w1.x, hv[vv].z, acc[2 % kCh][j][m]);
+                            acc[3 % kCh][j][m] = fmaf(w1.y, hv[vv].w, acc[3 % kCh][j][m]);
                         }
+                    }
                     }
                 }
             }
@@ -1027,8 +1033,11 @@ hipError_t launch_nb(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t 
 template <int M_T, bool ROUTE, bool NORM>
 hipError_t launch_one(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     if constexpr (M_T == 1) {
-        if (a.n_units <= std::min(kMaxGrid, blocks_per_cu<true>() * cus)) {
-            const hipError_t e = launch_nb<M_T, ROUTE, NORM, true>(a, nb, cus, lds, s);
+        FfnArgs b = a;                                  // the down units of the ONE form
+        b.dn_units = a.H / (kUnitRows * dn_sub<1, true>());
+        b.n_units = b.n_gu + b.max_groups * b.dn_units;
+        if (b.n_units <= std::min(kMaxGrid, blocks_per_cu<true>() * cus)) {
+            const hipError_t e = launch_nb<M_T, ROUTE, NORM, true>(b, nb, cus, lds, s);
             if (e != hipErrorInvalidConfiguration) return e;
         }
     }
@@ -1066,7 +1075,7 @@ FfnLayout ffn_layout(int M, int k_max, int H, int I) {
     int cap;
     if (M == 1) {
         const int loads_per_pair = kbi4 * 4 * 16;                   // 16-byte loads (two h words each)
-        const int fit_stage = stage_batch<1>() * kThreads / loads_per_pair;
+        const int fit_stage = stage_batch<1, false>() * kThreads / loads_per_pair;
         cap = std::max(1, std::min(std::min(fit_lds, fit_stage), std::min(kOneTokenPairs, max_pairs)));
         const int n_groups = (max_pairs + cap - 1) / cap;
         cap = (max_pairs + n_groups - 1) / n_groups;                // equal groups
@@ -1122,7 +1131,7 @@ hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int
     a.kbi = w.I / 32;
     a.kbi4 = (a.kbi + 3) / 4;
     a.gu_units = w.I / kUnitRows;
-    a.dn_units = w.H / (kUnitRows * (M == 1 ? dn_sub<1>() : dn_sub<2>()));
+    a.dn_units = w.H / (kUnitRows * (M == 1 ? dn_sub<1, false>() : dn_sub<2, false>()));
     a.max_slots = L.max_slots;
     a.max_groups = L.max_groups;
     a.pair_cap = L.pair_cap;
