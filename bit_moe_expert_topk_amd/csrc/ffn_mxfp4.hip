@@ -16,6 +16,10 @@
 // down units of slot groups 1.., then those of group 0.  Every block therefore
 // finishes all its gate/up units before it can wait for anything, and all its
 // other down units before it waits as a combiner, so no wait can close a cycle.
+// When four blocks per CU give every unit a block of its own (ONE: one token),
+// the grid is one block per unit, all resident, and no block waits on itself;
+// the shared expert's gate/up blocks then skip routing and load their weights
+// first thing.
 //
 // Prologue (every block).  The block builds an LDS table of the layer's slots:
 // slot 0 is the shared expert (weight 1, every token), slots 1.. the distinct
@@ -125,11 +129,12 @@ struct FfnArgs {
     int dn_units;                    // H / (16 * dn_sub)
     int max_slots, max_groups, pair_cap;
     int n_gu, n_units;
+    int writer;                      // the block that writes routing outputs and x_out (runs a gate/up unit)
     int pair_bytes, red_off;         // LDS layout
     const uint16_t* x;               // [M][H] bf16 (null when r_in is given)
     const float* r_in;               // [M][H] residual: x = bf16(RMSNorm(r_in)), or null
     float* r_out;                    // [M][H] r_in + y, or null
-    uint16_t* x_out;                 // [M][H] the normalised x (block 0 writes it), or null
+    uint16_t* x_out;                 // [M][H] the normalised x (the writer block writes it), or null
     float eps;                       // RMSNorm epsilon
     const moedec_dispatch* disp;     // slots from moe_route_topk, or
     const float* logits;             // [M][E]: route here
@@ -268,7 +273,7 @@ __device__ void table_from_logits_one(const FfnArgs& a, SlotTable& T, uint64_t* 
         T.n_groups = ng;
     }
     for (int g = lane; g <= ng; g += kWave) T.gfirst[g] = min(g * a.pair_cap, n);
-    if (blockIdx.x == 0) {                      // the routing outputs, as moe_route_topk writes them
+    if ((int)blockIdx.x == a.writer) {          // the routing outputs, as moe_route_topk writes them
         if (lane < k) {
             if (a.ids_out) a.ids_out[lane] = id;
             if (a.w_out) a.w_out[lane] = wv;
@@ -331,7 +336,7 @@ __device__ void table_from_logits(const FfnArgs& a, SlotTable& T, uint64_t* buf,
         }
     }
     if (tid == 0) T.n_slots = n_routed + 1;
-    if (blockIdx.x == 0) {                      // the routing outputs, as moe_route_topk writes them
+    if ((int)blockIdx.x == a.writer) {          // the routing outputs, as moe_route_topk writes them
         for (int t = tid; t < M_T * a.k; t += kThreads) {
             const int m = t / a.k, r = t - m * a.k;
             if (a.ids_out) a.ids_out[t] = R.id[m][r];
@@ -411,12 +416,7 @@ struct GuLoads {
 
 // Issue a gate/up unit's weight loads (nothing when the slot is unused).
 template <int M_T, int NB>
-__device__ __forceinline__ void gateup_issue(const FfnArgs& a, const SlotTable& T, int u, GuLoads<NB>& L) {
-    const int s = u / a.gu_units;
-    const int rg = u - s * a.gu_units;
-    if (s >= T.n_slots) return;
-    const int e = T.expert[s];
-    if (e < 0) return;
+__device__ __forceinline__ void gateup_issue_e(const FfnArgs& a, int e, int rg, GuLoads<NB>& L) {
     const int w = wave_id_uniform();
     const int lane = lane_id();
     const uint8_t* cb = (e == a.E) ? a.sh_gu_codes : a.gu_codes + (size_t)e * a.gu_codes_stride;
@@ -434,6 +434,16 @@ __device__ __forceinline__ void gateup_issue(const FfnArgs& a, const SlotTable& 
         L.cu[i] = load_stream16(ub + (size_t)c * 2048 + 1024);
         L.sc[i] = *reinterpret_cast<const uint16_t*>(usb + (size_t)c * 128);
     }
+}
+
+template <int M_T, int NB>
+__device__ __forceinline__ void gateup_issue(const FfnArgs& a, const SlotTable& T, int u, GuLoads<NB>& L) {
+    const int s = u / a.gu_units;
+    const int rg = u - s * a.gu_units;
+    if (s >= T.n_slots) return;
+    const int e = T.expert[s];
+    if (e < 0) return;
+    gateup_issue_e<M_T, NB>(a, e, rg, L);
 }
 
 // Finish a gate/up unit whose loads gateup_issue put in L: the dot products
@@ -813,60 +823,37 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     }
 }
 
-template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(blocks_per_cu<ONE>())))
-void moe_ffn_kernel(FfnArgs a) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ SlotTable T;
-    __shared__ uint32_t s_gen;
-    const int tid = threadIdx.x;
-    const bool has_gu = (int)blockIdx.x < a.n_gu;          // the block runs a gate/up unit
+// ---------------------------------------------------------------------------
+// prologue pieces
 
-    // The routing waves' logits go out first (loads return in order and the
-    // top-k needs them before anything else; lane l holds entries l + 64 t).
-    float lv[16];
-    if (ROUTE && wave_id_uniform() < M_T) {
-        const float* row = a.logits + (size_t)wave_id_uniform() * a.E;
-        if (a.E <= 512)
-            topk_load<8>(row, a.E, *reinterpret_cast<float(*)[8]>(lv));
-        else
-            topk_load<16>(row, a.E, lv);
-    }
-    // x does not depend on routing: its loads go out next (unconditional,
-    // clamped index), and are staged in LDS once the slot table is built.
-    // With a residual input the loads bring r (float32, twice the bytes) and
-    // x = bf16(RMSNorm(r)) is formed after routing.
-    constexpr bool norm = NORM;
-    constexpr int kPieces = (norm ? 4 : 2) * M_T;         // 16-byte pieces of M_T * 4096 values
-    const int per_tok = norm ? a.H / 4 : a.H / 8;
+// 16-byte pieces of the layer input per thread: M_T * H bf16 values, or the
+// float32 residual stream (twice the bytes) when x is formed by RMSNorm.
+template <int M_T, bool NORM>
+constexpr int x_pieces() { return (NORM ? 4 : 2) * M_T; }
+
+// x (or r) loads: unconditional, clamped index; H <= 4096 fits the pieces.
+template <int M_T, bool NORM>
+__device__ __forceinline__ void x_issue(const FfnArgs& a, u32x4 (&xv)[x_pieces<M_T, NORM>()]) {
+    const int per_tok = NORM ? a.H / 4 : a.H / 8;
     const int n_pieces = M_T * per_tok;
-    u32x4 xv[kPieces];
-    if (has_gu) {
-        const u32x4* src = norm ? reinterpret_cast<const u32x4*>(a.r_in) : reinterpret_cast<const u32x4*>(a.x);
+    const u32x4* src = NORM ? reinterpret_cast<const u32x4*>(a.r_in) : reinterpret_cast<const u32x4*>(a.x);
 #pragma unroll
-        for (int i = 0; i < kPieces; ++i) xv[i] = src[min(tid + kThreads * i, n_pieces - 1)];
-    }
-    if (tid == kThreads - kWave) {                        // wave 3: keeps wave 0 free to route
-        // the launch count on the workspace: every one of the kMaxGrid words
-        // advances once per launch (block b takes b, b + grid, ...), so all
-        // blocks agree whatever the grid of earlier launches
-        const uint32_t g = a.gens[blockIdx.x] + 1u;
-        for (int j = blockIdx.x; j < kMaxGrid; j += gridDim.x) a.gens[j] = g;
-        s_gen = g;
-    }
-    constexpr bool kDirectGroups = ROUTE && M_T == 1;     // the table arrives with its groups
-    // routing borrows the reduction area (kTopkBufWords words per routing
-    // wave), which the units use only after the prologue
-    uint64_t* route_buf = reinterpret_cast<uint64_t*>(lds + a.red_off);
-    if (kDirectGroups)
-        table_from_logits_one(a, T, route_buf, lv);
-    else if (ROUTE)
-        table_from_logits<M_T>(a, T, route_buf, lv);
-    else
-        table_from_dispatch<M_T>(a, T);
-    if (has_gu && norm) {
-        // RMSNorm with unit gain: x = r / sqrt(mean(r^2) + eps), float32, then
-        // rounded to bf16 (nearest even); piece p holds elements 4r..4r+3
+    for (int i = 0; i < x_pieces<M_T, NORM>(); ++i) xv[i] = src[min((int)threadIdx.x + kThreads * i, n_pieces - 1)];
+}
+
+// x into the LDS x area (token m, MX block q at m * xtok + q * 80), zero past
+// H.  With NORM, x = bf16(RMSNorm(r)) with unit gain: r / sqrt(mean(r^2) + eps)
+// in float32, rounded to bf16 (nearest even); the writer block also exports x.
+// Contains a block barrier (NORM); the caller's barrier publishes the stores.
+template <int M_T, bool NORM>
+__device__ void x_stage(const FfnArgs& a, const u32x4 (&xv)[x_pieces<M_T, NORM>()], uint8_t* lds) {
+    constexpr int kPieces = x_pieces<M_T, NORM>();
+    const int tid = threadIdx.x;
+    const int per_tok = NORM ? a.H / 4 : a.H / 8;
+    const int n_pieces = M_T * per_tok;
+    const int xtok = a.kbh4 * 4 * kXBlock;
+    if constexpr (NORM) {
+        // piece p holds elements 4r..4r+3
         __shared__ float s_ss[kWaves][MOEDEC_MAX_M];
         float ss[M_T];
 #pragma unroll
@@ -894,7 +881,7 @@ void moe_ffn_kernel(FfnArgs a) {
 #pragma unroll
         for (int m = 0; m < M_T; ++m)
             inv[m] = 1.0f / sqrtf(((s_ss[0][m] + s_ss[1][m]) + (s_ss[2][m] + s_ss[3][m])) / (float)a.H + a.eps);
-        const int xtok = a.kbh4 * 4 * kXBlock;            // token m, MX block q at m * xtok + q * 80
+        const bool export_x = (int)blockIdx.x == a.writer && a.x_out != nullptr;
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) {
             const int p = tid + kThreads * i;
@@ -910,12 +897,10 @@ void moe_ffn_kernel(FfnArgs a) {
                 const uint32_t b3 = f32_to_bf16_rne(__uint_as_float(xv[i][3]) * sc);
                 const uint2 packed = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
                 *reinterpret_cast<uint2*>(lds + pm * xtok + (e0 >> 5) * kXBlock + (e0 & 31) * 2) = packed;
-                if (blockIdx.x == 0 && a.x_out)
-                    *reinterpret_cast<uint2*>(a.x_out + (size_t)pm * a.H + e0) = packed;
+                if (export_x) *reinterpret_cast<uint2*>(a.x_out + (size_t)pm * a.H + e0) = packed;
             }
         }
-    } else if (has_gu) {
-        const int xtok = a.kbh4 * 4 * kXBlock;            // token m, MX block q at m * xtok + q * 80
+    } else {
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) {
             const int p = tid + kThreads * i;
@@ -926,16 +911,85 @@ void moe_ffn_kernel(FfnArgs a) {
             }
         }
     }
-    if (has_gu) {
-        const int xtok = a.kbh4 * 4 * kXBlock;
-        const int pad_pieces = (a.kbh4 * 4 - a.kbh) * 4;  // MX blocks past H are zero
-        for (int p = tid; p < M_T * pad_pieces; p += kThreads) {
-            const int m = p / pad_pieces;
-            const int r = p - m * pad_pieces;
-            *reinterpret_cast<u32x4*>(lds + m * xtok + (a.kbh + (r >> 2)) * kXBlock + (r & 3) * 16) =
-                u32x4{0u, 0u, 0u, 0u};
+    const int pad_pieces = (a.kbh4 * 4 - a.kbh) * 4;      // MX blocks past H are zero
+    for (int p = tid; p < M_T * pad_pieces; p += kThreads) {
+        const int m = p / pad_pieces;
+        const int r = p - m * pad_pieces;
+        *reinterpret_cast<u32x4*>(lds + m * xtok + (a.kbh + (r >> 2)) * kXBlock + (r & 3) * 16) =
+            u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// The launch count on the workspace: every one of the kMaxGrid words advances
+// once per launch (block b takes b, b + grid, ...), so all blocks agree
+// whatever the grid of earlier launches.  One thread per block.
+__device__ __forceinline__ uint32_t gens_advance(const FfnArgs& a) {
+    const uint32_t g = a.gens[blockIdx.x] + 1u;
+    for (int j = blockIdx.x; j < kMaxGrid; j += gridDim.x) a.gens[j] = g;
+    return g;
+}
+
+template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(blocks_per_cu<ONE>())))
+void moe_ffn_kernel(FfnArgs a) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ SlotTable T;
+    __shared__ uint32_t s_gen;
+    const int tid = threadIdx.x;
+    const int unit0 = (int)blockIdx.x;                     // first unit (ONE: the only one)
+    const bool has_gu = unit0 < a.n_gu;                    // the block runs a gate/up unit
+    constexpr int kPieces = x_pieces<M_T, NORM>();
+
+    if constexpr (ONE) {
+        // The shared expert (slot 0) does not depend on routing: with a block
+        // per unit, its gate/up blocks issue their weight loads first thing and
+        // never route (the writer block is another), so these bytes stream
+        // while the other blocks select their experts.
+        if (unit0 < a.gu_units) {
+            GuLoads<NB> cur;
+            gateup_issue_e<M_T, NB>(a, a.E, unit0, cur);
+            u32x4 xv[kPieces];
+            x_issue<M_T, NORM>(a, xv);
+            if (tid == kThreads - kWave) s_gen = gens_advance(a);
+            if (tid == 0) {
+                T.n_slots = 1;
+                T.expert[0] = a.E;
+                T.mask[0] = (1u << M_T) - 1u;
+            }
+            x_stage<M_T, NORM>(a, xv, lds);
+            __syncthreads();
+            gateup_compute<M_T, NB>(a, T, lds, unit0, s_gen, cur);
+            return;
         }
     }
+
+    // The routing waves' logits go out first (loads return in order and the
+    // top-k needs them before anything else; lane l holds entries l + 64 t).
+    float lv[16];
+    if (ROUTE && wave_id_uniform() < M_T) {
+        const float* row = a.logits + (size_t)wave_id_uniform() * a.E;
+        if (a.E <= 512)
+            topk_load<8>(row, a.E, *reinterpret_cast<float(*)[8]>(lv));
+        else
+            topk_load<16>(row, a.E, lv);
+    }
+    // x does not depend on routing: its loads go out next, and are staged in
+    // LDS once the slot table is built.  With a residual input the loads bring
+    // r and x = bf16(RMSNorm(r)) is formed after routing.
+    u32x4 xv[kPieces];
+    if (has_gu) x_issue<M_T, NORM>(a, xv);
+    if (tid == kThreads - kWave) s_gen = gens_advance(a);   // wave 3: keeps wave 0 free to route
+    constexpr bool kDirectGroups = ROUTE && M_T == 1;     // the table arrives with its groups
+    // routing borrows the reduction area (kTopkBufWords words per routing
+    // wave), which the units use only after the prologue
+    uint64_t* route_buf = reinterpret_cast<uint64_t*>(lds + a.red_off);
+    if (kDirectGroups)
+        table_from_logits_one(a, T, route_buf, lv);
+    else if (ROUTE)
+        table_from_logits<M_T>(a, T, route_buf, lv);
+    else
+        table_from_dispatch<M_T>(a, T);
+    if (has_gu) x_stage<M_T, NORM>(a, xv, lds);
     __syncthreads();
     if (!kDirectGroups) {
         table_groups(a, T);
@@ -944,7 +998,7 @@ void moe_ffn_kernel(FfnArgs a) {
     const uint32_t gen = s_gen;
     // Gate/up units come first: a block's next one has its weight loads in
     // flight while the current one computes.  Then its down units.
-    int u = blockIdx.x;
+    int u = unit0;
     if (ONE) {
         for (; u < a.n_gu; u += gridDim.x) {
             GuLoads<NB> cur;
@@ -953,6 +1007,9 @@ void moe_ffn_kernel(FfnArgs a) {
             __syncthreads();
         }
     } else if (u < a.n_gu) {
+        // (Issuing the first down unit's weights during the last gate/up unit
+        // instead was slower at 4 tokens, 34.3 against 32.4 us: they compete
+        // with the gate/up stream that every down unit waits for.)
         GuLoads<NB> cur, nxt;
         gateup_issue<M_T, NB>(a, T, u, cur);
         for (; u < a.n_gu; u += gridDim.x) {
@@ -1036,6 +1093,7 @@ hipError_t launch_one(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t
         FfnArgs b = a;                                  // the down units of the ONE form
         b.dn_units = a.H / (kUnitRows * dn_sub<1, true>());
         b.n_units = b.n_gu + b.max_groups * b.dn_units;
+        b.writer = b.gu_units;                          // slot 1's first gate/up block routes; slot 0's do not
         if (b.n_units <= std::min(kMaxGrid, blocks_per_cu<true>() * cus)) {
             const hipError_t e = launch_nb<M_T, ROUTE, NORM, true>(b, nb, cus, lds, s);
             if (e != hipErrorInvalidConfiguration) return e;
@@ -1139,6 +1197,7 @@ hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int
     a.n_units = a.n_gu + L.max_groups * a.dn_units;
     a.pair_bytes = L.pair_bytes;
     a.red_off = L.red_off;
+    a.writer = 0;
     a.x = x;
     a.disp = disp;
     a.logits = logits;
