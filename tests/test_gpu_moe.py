@@ -364,6 +364,18 @@ def test_fused_ragged_and_extreme(m, H, I, E, k, M):
     _check_fused(m, W, xb, lg, k, ef, sh, f"fused H={H} I={I} E={E} k={k} M={M}")
 
 
+@pytest.mark.parametrize("H,I,E,k", [(256, 768, 40, 32), (1536, 768, 20, 16), (1024, 768, 20, 16)])
+def test_fused_one_token_grid_forms(m, H, I, E, k):
+    """One token: the kernel gives every work unit a block of its own when the
+    units fit four blocks per CU, and otherwise walks them with the persistent
+    three-block grid.  On a 256-CU MI355X the first two shapes (1,584 + 240 and
+    816 + 288 units) take the persistent form and the last (816 + 192 = 1,008)
+    the block-per-unit form at its limit; both forms must match the oracle."""
+    shape = synth.MoEShape(H=H, I=I, E=E, k=k, scale_lo=119, scale_hi=123)
+    W, xb, lg, ef, sh, k = _host_layer_case(m, shape, 1, seed=5)
+    _check_fused(m, W, xb, lg, k, ef, sh, f"fused one token H={H} I={I} E={E} k={k}")
+
+
 def test_fused_tie_heavy_routing(m):
     W, xb, _, ef, sh, k = _host_layer_case(m, synth.TINY, 4)
     rng = np.random.default_rng(7)
