@@ -58,6 +58,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head measurements")
     ap.add_argument("--no-m4", action="store_true", help="skip the M = 4 measurement")
     ap.add_argument("--no-stack", action="store_true", help="skip the residual-stack measurement")
+    ap.add_argument("--no-router", action="store_true", help="skip the router-logits measurement")
     ap.add_argument("--stack-passes", type=int, default=100, help="graph passes over the layers (stack)")
     ap.add_argument("--cpu-layers", type=int, default=3, help="layers in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -258,6 +259,52 @@ def stack_bench(m, torch, synth, layers, passes, eager_passes, dev):
         "frac_of_peak_graph": layer_bytes * steps_g / (1e6 * ms_graph) / PEAK_HBM_GBS,
         "residual_finite": finite,
     }
+
+
+def router_bench(m, torch, synth, layers, steps, dev, n_router=128):
+    """The step before routing: router logits from x (moe_router_logits_bf16,
+    bf16 W_router [512][2560], seeded N(0, 1/H)), alone over n_router distinct
+    matrices (335 MB, beyond the Infinity Cache) at M = 1 and 4, and in front
+    of the fused layer at M = 1 (router logits, then moe_layer_mxfp4 on them)."""
+    shape = synth.LING
+    E, H, k = shape.E, shape.H, shape.k
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    wrs = [(torch.randn((E, H), generator=gen, device=dev) * (1.0 / H ** 0.5)).to(torch.bfloat16)
+           for _ in range(n_router)]
+    t = Timer(torch)
+    out = {"E": E, "H": H, "matrices": n_router, "bytes_per_call_m1": E * H * 2 + H * 2 + E * 4}
+    for M in (1, 4):
+        xs, _ = layer_inputs(synth, 4, M, dev)
+        lg = torch.empty((M, E), dtype=torch.float32, device=dev)
+        reps = 2 * n_router
+        m.router_logits(wrs[0], xs[0], out=lg)
+        g = capture(torch, lambda: [m.router_logits(wrs[i % n_router], xs[i % 4], out=lg) for i in range(reps)])
+        g.replay()
+        ms = t.run(g.replay)
+        out[f"us_m{M}"] = 1e3 * ms / reps
+        out[f"gbs_m{M}"] = (E * H * 2 + M * H * 2 + M * E * 4) / (1e3 * out[f"us_m{M}"])
+        del g
+    # router + fused layer, M = 1, cycling over the resident layers
+    n_layers = len(layers)
+    xs, _ = layer_inputs(synth, n_layers, 1, dev)
+    lg = torch.empty((1, E), dtype=torch.float32, device=dev)
+    ws = m.make_ffn_workspace(1, k, H, shape.I, dev)
+    y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        L = i % n_layers
+        m.router_logits(wrs[L % n_router], xs[L], out=lg)
+        m.moe_layer(layers[L], xs[L], lg, k, ws, y=y, want_f32=False)
+
+    step(0)
+    g = capture(torch, lambda: [step(i) for i in range(steps)])
+    g.replay()
+    ms = t.run(g.replay)
+    out["router_plus_layer_us_m1"] = 1e3 * ms / steps
+    del g, wrs
+    torch.cuda.empty_cache()
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -529,6 +576,10 @@ def main(argv=None):
     if not args.no_stack:
         stack = stack_bench(m, torch, synth, layers, args.stack_passes, max(1, args.stack_passes // 10), dev)
         log("stack:", json.dumps(stack))
+    router = None
+    if not args.no_router:
+        router = router_bench(m, torch, synth, layers, min(args.steps, 2100), dev)
+        log("router:", json.dumps(router))
     del layers
     torch.cuda.empty_cache()
     lm = None
@@ -576,9 +627,12 @@ def main(argv=None):
             "avg_launch_us": round(r1["us_per_layer"], 3),
         },
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
-        "extra": {"m1": r1, "m4": r4, "stack": stack, "lmhead": lm,
+        "extra": {"m1": r1, "m4": r4, "stack": stack, "router": router, "lmhead": lm,
                   "cpu": cpu},
     }
+    if router is not None:
+        line["router_us_m1"] = round(router["us_m1"], 3)
+        line["router_plus_layer_us_m1"] = round(router["router_plus_layer_us_m1"], 3)
     if r4 is not None:
         line["us_per_layer_m4"] = round(r4["us_per_layer"], 3)
         line["gbs_m4"] = round(r4["gbs"], 1)

@@ -279,6 +279,18 @@ def lmhead_gemv_fp8(head, x, out=None):
     return out
 
 
+def router_logits(w_router, x, out=None):
+    """logits [M][E] float32 = x W_router^T (moe_router_logits_bf16)."""
+    _need(w_router, torch.bfloat16, "w_router", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    E, H = w_router.shape
+    m_tokens = x.shape[0]
+    if out is None:
+        out = torch.empty((m_tokens, E), dtype=torch.float32, device=x.device)
+    _check(lib.moe_router_logits_bf16(_ptr(w_router), E, H, _ptr(x), m_tokens, _ptr(out), _stream(x)))
+    return out
+
+
 def lmhead_gemv_bf16(w_bf16, x, out=None):
     _need(w_bf16, torch.bfloat16, "w_bf16", 2)
     _need(x, torch.bfloat16, "x", 2)

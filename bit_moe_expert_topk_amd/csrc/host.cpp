@@ -288,4 +288,19 @@ int lmhead_gemv_bf16(const uint16_t* w_bf16, int V, int H, const uint16_t* x_bf1
                     "lmhead_gemv_bf16");
 }
 
+int moe_router_logits_bf16(const uint16_t* w_router, int E, int H, const uint16_t* x_bf16, int M,
+                           float* logits, moedec_stream_t stream) {
+    if (!w_router || !x_bf16 || !logits) return fail(MOEDEC_ERR_NULL, "w_router, x or logits is NULL");
+    if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
+    if (E < 1 || E > MOEDEC_MAX_E) return fail(MOEDEC_ERR_SHAPE, "E=%d not in 1..%d", E, MOEDEC_MAX_E);
+    if (H < 8 || H > 4096 || H % 8)
+        return fail(MOEDEC_ERR_SHAPE, "H=%d: need 8 <= H <= 4096 and H %% 8 == 0", H);
+    if (!aligned(w_router, 16) || !aligned(x_bf16, 4) || !aligned(logits, 4))
+        return fail(MOEDEC_ERR_ALIGN, "w_router 16-byte, x/logits 4-byte alignment needed");
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_gemv_bf16(w_router, E, H, x_bf16, M, logits,
+                                             static_cast<hipStream_t>(stream)),
+                    "moe_router_logits_bf16");
+}
+
 }  // extern "C"

@@ -259,7 +259,11 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
     }
 }
 
-constexpr int kRowsPerWave = 16;   // bf16 GEMV
+// bf16 GEMV: 16 rows per wave for a vocabulary-sized matrix; a short one (a
+// router's 512 rows) takes 4 so that it still spreads over 128 waves.
+constexpr int kRowsPerWave = 16;
+constexpr int kRowsPerWaveShort = 4;
+constexpr int kShortRows = 16384;
 
 // 8 rows per wave step and 32 rows per wave: 59.5 us (M = 1) and 73 us (M = 4)
 // on the 157,184 x 2,560 head, against 66 and 124 us for 4 rows, 16 rows per
@@ -292,17 +296,18 @@ template <int M_T>
 hipError_t gemv_bf16_m(const uint16_t* w, int V, int H, const uint32_t* x, float* logits,
                        hipStream_t s) {
     const int T = (H / 8 + 63) / 64;
-    const int waves = (V + kRowsPerWave - 1) / kRowsPerWave;
+    const int rpw = V <= kShortRows ? kRowsPerWaveShort : kRowsPerWave;
+    const int waves = (V + rpw - 1) / rpw;
     const dim3 grid((waves + 3) / 4), blk(256);
     switch (T) {
-        case 1: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 1>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave); break;
-        case 2: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 2>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave); break;
-        case 3: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 3>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave); break;
-        case 4: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 4>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave); break;
-        case 5: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 5>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave); break;
-        case 6: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 6>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave); break;
-        case 7: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 7>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave); break;
-        default: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 8>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave); break;
+        case 1: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 1>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
+        case 2: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 2>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
+        case 3: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 3>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
+        case 4: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 4>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
+        case 5: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 5>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
+        case 6: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 6>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
+        case 7: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 7>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
+        default: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 8>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
     }
     return hipGetLastError();
 }

@@ -92,6 +92,19 @@ int moe_route_topk(const float* logits, int M, int E, int k,
                    int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
                    moedec_stream_t stream);
 
+/*
+ * Router logits, the step before routing [card background: the router picks
+ * 8 of the 512 routed experts of each layer from the token's hidden state]:
+ * logits[m][e] = sum_k x[m][k] * W_router[e][k], bf16 inputs, float32
+ * accumulation and output (no bias).  The same GEMV as lmhead_gemv_bf16 with
+ * the expert count in place of the vocabulary, launched for a short matrix.
+ * w_router [E][H] bf16, 16-byte aligned; x_bf16 [M][H], 4-byte aligned;
+ * logits [M][E] float32, 4-byte aligned (moe_route_topk's input).
+ * 1 <= M <= 4, 1 <= E <= 1024, 8 <= H <= 4096, H % 8 == 0.
+ */
+int moe_router_logits_bf16(const uint16_t* w_router, int E, int H, const uint16_t* x_bf16, int M,
+                           float* logits, moedec_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * MXFP4 expert weights.  [ic three scalpels: routed experts are MXFP4;
  * MX §5: 32 E2M1 codes share one E8M0 scale]

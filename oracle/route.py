@@ -20,10 +20,25 @@ Parity status: pinned (tests/test_oracle_route.py) by the invariant that the
 selection equals the first k entries of a stable full sort done by a library
 routine (numpy lexsort) on random and tie-heavy logits, by k = E, by the
 softmax-over-selected closed form (scipy), by sum(w) = 1 and k = 1 -> w = 1, and
-by a hand-worked tie fixture under tests/golden/.
+by a hand-worked tie fixture under tests/golden/.  The router logits are pinned
+by a hand-worked 3 x 2 example, one-hot activations selecting one column of the
+router matrix per expert (orientation), x = 0, and linearity in x.
 """
 
 import numpy as np
+
+
+def router_logits(w_router, x):
+    """Router logits, the step before the selection [card §background: the
+    router picks 8 of 512 experts from the token's hidden state]: logits[m, e]
+    = sum_k x[m, k] W_router[e, k] in float64 (products of bf16 values are
+    exact there), no bias.
+
+    w_router [E][H] and x [M][H] bf16-exact values; returns float64 [M][E].
+    """
+    w = np.asarray(w_router, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    return x @ w.T
 
 
 def route_topk(logits, k):

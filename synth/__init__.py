@@ -134,6 +134,7 @@ def _rng(seed, stream):
 
 # Stream numbers for Gaussian tensors.
 GAUSS_X, GAUSS_LOGITS, GAUSS_ROUTER, GAUSS_LMHEAD_W, GAUSS_LMHEAD_X = 1, 2, 3, 4, 5
+GAUSS_ROUTER_W = 6
 
 
 def bf16_bits_from_f32(v):
@@ -169,6 +170,13 @@ def router_logits_f32(seed, x_bits, n_experts):
     hidden = x.shape[1]
     wr = _rng(seed, GAUSS_ROUTER).standard_normal((hidden, n_experts)) / np.sqrt(hidden)
     return (x @ wr).astype(np.float32)
+
+
+def router_weight_bf16(seed, layer, n_experts, hidden):
+    """bf16 router matrix W_router [E][H] ~ N(0, 1/H) (uint16 patterns), so
+    that with N(0,1) activations the logits are about N(0,1)."""
+    g = _rng(seed, GAUSS_ROUTER_W * 1000 + layer).standard_normal((n_experts, hidden), dtype=np.float32)
+    return bf16_bits_from_f32(g * np.float32(1.0 / np.sqrt(hidden)))
 
 
 def lmhead_weight_bf16(seed, vocab, hidden, std=0.02, row_start=0, n_rows=None):

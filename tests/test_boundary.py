@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("moe_route_topk", "moe_expert_ffn_mxfp4", "moe_layer_mxfp4", "moe_layer_rmsnorm_mxfp4",
                  "lmhead_quant_fp8", "lmhead_gemv_fp8",
-                 "lmhead_gemv_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
+                 "lmhead_gemv_bf16", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
                  "moedec_last_error", "moedec_abi_version"):
         assert want in names
@@ -74,6 +74,18 @@ def test_route_argument_checks(m):
     assert L.moe_route_topk(ODD, 1, 512, 8, FAKE, FAKE, FAKE, None) == -2
     assert L.moe_route_topk(FAKE, 1, 512, 8, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 4), None) == -2
     assert b"k=33" in L.moedec_last_error() or True
+
+
+def test_router_argument_checks(m):
+    L = m.lib
+    assert L.moe_router_logits_bf16(None, 512, 2560, FAKE, 1, FAKE, None) == -1
+    assert L.moe_router_logits_bf16(FAKE, 512, 2560, FAKE, 0, FAKE, None) == -3
+    assert L.moe_router_logits_bf16(FAKE, 512, 2560, FAKE, 5, FAKE, None) == -3
+    assert L.moe_router_logits_bf16(FAKE, 0, 2560, FAKE, 1, FAKE, None) == -3
+    assert L.moe_router_logits_bf16(FAKE, 1025, 2560, FAKE, 1, FAKE, None) == -3
+    assert L.moe_router_logits_bf16(FAKE, 512, 2564, FAKE, 1, FAKE, None) == -3
+    assert L.moe_router_logits_bf16(FAKE, 512, 8192, FAKE, 1, FAKE, None) == -3
+    assert L.moe_router_logits_bf16(ODD, 512, 2560, FAKE, 1, FAKE, None) == -2
 
 
 def test_valid_arguments_without_gpu_report_device(m):

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import (W_ATOL, bf16_tensor, bits_of, check_acc, check_bf16, dense_expert,
+from gpu_helpers import (ACC_RTOL, W_ATOL, bf16_tensor, bits_of, check_acc, check_bf16, dense_expert,
                          oracle_layer, say)
 
 pytestmark = pytest.mark.gpu
@@ -146,6 +146,52 @@ def test_device_generator_matches_host_twin(m):
         for name in ("gate", "up", "down"):
             np.testing.assert_array_equal(lay[name][0][e].cpu().numpy(), host[name][0])
             np.testing.assert_array_equal(lay[name][1][e].cpu().numpy(), host[name][1])
+
+
+# ---------------------------------------------------------------- router logits
+
+def _check_route_from_router(ids, w, ref_logits, k, what):
+    """Selection from the kernel's float32 logits against the float64 oracle
+    logits.  The two differ by float32 rounding, so where two logits that
+    decide the selection or its order lie within 2 * tol of each other either
+    outcome is correct; there only validity is required.  Elsewhere the ids
+    must equal the oracle's, and the weights its softmax over the chosen."""
+    E = ref_logits.shape[1]
+    for m in range(ref_logits.shape[0]):
+        L = ref_logits[m]
+        tol = ACC_RTOL * np.max(np.abs(L))
+        g = ids[m].astype(np.int64)
+        assert len(set(g.tolist())) == k, f"{what} token {m}: repeated ids"
+        chosen = np.zeros(E, dtype=bool)
+        chosen[g] = True
+        if k < E:
+            assert L[g].min() >= L[~chosen].max() - 2 * tol, f"{what} token {m}: not a top-{k}"
+        assert np.all(L[g][:-1] >= L[g][1:] - 2 * tol), f"{what} token {m}: order"
+        order = np.lexsort((np.arange(E), -L))
+        top = L[order[:min(k + 1, E)]]
+        if np.all(np.abs(np.diff(top)) > 2 * tol):
+            np.testing.assert_array_equal(g, order[:k], err_msg=f"{what} token {m}")
+        p = np.exp(L[g] - L[g].max())
+        np.testing.assert_allclose(w[m], p / p.sum(), rtol=0, atol=1e-5, err_msg=f"{what} token {m}")
+
+
+@pytest.mark.parametrize("E,H,k,M", [(512, 2560, 8, 1), (512, 2560, 8, 4), (16, 256, 2, 3), (1000, 72, 32, 2)])
+def test_router_logits_and_route_from_x(m, E, H, k, M):
+    """Router GEMV (bf16 W_router [E][H] ~ N(0, 1/H), x ~ N(0, 1)) within the
+    float32-accumulator tolerance of the oracle, and the experts chosen from
+    those logits under the near-tie rule."""
+    say(f"router E={E} H={H} k={k} M={M}")
+    wr_bits = synth.router_weight_bf16(0, 0, E, H)
+    x_bits = synth.activations_bf16(0, 0, M, H)
+    lg = m.router_logits(bf16_tensor(wr_bits), bf16_tensor(x_bits))
+    ids, w, _ = m.route_topk(lg, k)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(synth.bf16_values(wr_bits), synth.bf16_values(x_bits))
+    check_acc(lg.cpu().numpy(), ref, f"router logits E={E} H={H} M={M}")
+    # routing on the kernel's own float32 logits is bit-exact against the oracle's
+    ref_ids, ref_w = oracle.route_topk(lg.cpu().numpy(), k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    _check_route_from_router(ids.cpu().numpy(), w.cpu().numpy(), ref, k, f"route from x E={E} M={M}")
 
 
 # ---------------------------------------------------------------- FFN

@@ -80,3 +80,30 @@ def test_dispatch_bound_verify_window():
         # every (token, choice) appears exactly once
         assert sum(bin(int(mk)).count("1") for mk in masks[:-1]) == 32
         np.testing.assert_allclose(weights[:-1].sum(axis=0), 1.0, rtol=1e-14)
+
+
+def test_router_logits_hand_worked():
+    # W_router [E=3][H=2], x [M=1][H=2], worked by hand:
+    # e0: 1*2 + 2*(-1) = 0;  e1: -1*2 + 0.5*(-1) = -2.5;  e2: 0*2 + 3*(-1) = -3
+    w = np.array([[1.0, 2.0], [-1.0, 0.5], [0.0, 3.0]])
+    x = np.array([[2.0, -1.0]])
+    np.testing.assert_array_equal(oracle.router_logits(w, x), [[0.0, -2.5, -3.0]])
+
+
+def test_router_logits_one_hot_selects_a_column_and_zero_input():
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((5, 7))           # E = 5 experts, H = 7
+    for j in range(7):
+        x = np.zeros((1, 7))
+        x[0, j] = 1.0
+        np.testing.assert_array_equal(oracle.router_logits(w, x)[0], w[:, j])
+    np.testing.assert_array_equal(oracle.router_logits(w, np.zeros((2, 7))), np.zeros((2, 5)))
+
+
+def test_router_logits_linear_in_x():
+    rng = np.random.default_rng(12)
+    w = rng.integers(-8, 8, size=(6, 16)).astype(np.float64)     # integer values: sums exact
+    x1 = rng.integers(-8, 8, size=(3, 16)).astype(np.float64)
+    x2 = rng.integers(-8, 8, size=(3, 16)).astype(np.float64)
+    np.testing.assert_array_equal(oracle.router_logits(w, x1 + x2),
+                                  oracle.router_logits(w, x1) + oracle.router_logits(w, x2))
