@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(const uint8_t* __restrict
     }
 }
 
-template <int M_T, int T>
+template <int M_T, int T, int R>
 __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restrict__ wt, int V,
                                                         int H, const uint32_t* __restrict__ x,
                                                         float* __restrict__ logits,
@@ -227,21 +227,21 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
     const uint8_t* base = reinterpret_cast<const uint8_t*>(wt);
     const int v0 = gw * rows_per_wave;
     const int v1 = min(V, v0 + rows_per_wave);
-    for (int v = v0; v < v1; v += kRows) {
-        u32x4 c[kRows][T];
+    for (int v = v0; v < v1; v += R) {
+        u32x4 c[R][T];
 #pragma unroll
-        for (int r = 0; r < kRows; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 c[r][t] = load_stream16(base + ((size_t)min(v + r, v1 - 1) * H +
                                                 (size_t)min(lane + 64 * t, n_ch - 1) * 8) * 2);
-        float acc[kRows][M_T];
+        float acc[R][M_T];
 #pragma unroll
-        for (int r = 0; r < kRows; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int m = 0; m < M_T; ++m) acc[r][m] = 0.f;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
                     for (int m = 0; m < M_T; ++m)
                         acc[r][m] = dot2_bf16(as_bf16x2(c[r][t][j]), as_bf16x2(xr[m][t][j]), acc[r][m]);
 #pragma unroll
-        for (int r = 0; r < kRows; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int m = 0; m < M_T; ++m) {
                 const float tot = wave_sum(acc[r][m]);
@@ -259,11 +259,23 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
     }
 }
 
-// bf16 GEMV: 16 rows per wave for a vocabulary-sized matrix; a short one (a
-// router's 512 rows) takes 4 so that it still spreads over 128 waves.
+// bf16 GEMV: 16 rows per wave, 4 per step, for a vocabulary-sized matrix; a
+// short one (a router's 512 rows) takes one row per wave so that its few
+// megabytes spread over as many waves as it has rows (latency-bound).
 constexpr int kRowsPerWave = 16;
-constexpr int kRowsPerWaveShort = 4;
 constexpr int kShortRows = 16384;
+
+template <int M_T, int T>
+void launch_bf16_t(const uint16_t* w, int V, int H, const uint32_t* x, float* logits, hipStream_t s) {
+    if (V <= kShortRows) {
+        const dim3 grid((V + 3) / 4), blk(256);
+        hipLaunchKernelGGL((gemv_bf16_kernel<M_T, T, 1>), grid, blk, 0, s, w, V, H, x, logits, 1);
+    } else {
+        const int waves = (V + kRowsPerWave - 1) / kRowsPerWave;
+        const dim3 grid((waves + 3) / 4), blk(256);
+        hipLaunchKernelGGL((gemv_bf16_kernel<M_T, T, kRows>), grid, blk, 0, s, w, V, H, x, logits, kRowsPerWave);
+    }
+}
 
 // 8 rows per wave step and 32 rows per wave: 59.5 us (M = 1) and 73 us (M = 4)
 // on the 157,184 x 2,560 head, against 66 and 124 us for 4 rows, 16 rows per
@@ -295,19 +307,15 @@ hipError_t gemv_fp8_m(const uint8_t* codes, const float* rs, int V, int H, const
 template <int M_T>
 hipError_t gemv_bf16_m(const uint16_t* w, int V, int H, const uint32_t* x, float* logits,
                        hipStream_t s) {
-    const int T = (H / 8 + 63) / 64;
-    const int rpw = V <= kShortRows ? kRowsPerWaveShort : kRowsPerWave;
-    const int waves = (V + rpw - 1) / rpw;
-    const dim3 grid((waves + 3) / 4), blk(256);
-    switch (T) {
-        case 1: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 1>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
-        case 2: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 2>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
-        case 3: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 3>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
-        case 4: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 4>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
-        case 5: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 5>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
-        case 6: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 6>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
-        case 7: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 7>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
-        default: hipLaunchKernelGGL((gemv_bf16_kernel<M_T, 8>), grid, blk, 0, s, w, V, H, x, logits, rpw); break;
+    switch ((H / 8 + 63) / 64) {
+        case 1: launch_bf16_t<M_T, 1>(w, V, H, x, logits, s); break;
+        case 2: launch_bf16_t<M_T, 2>(w, V, H, x, logits, s); break;
+        case 3: launch_bf16_t<M_T, 3>(w, V, H, x, logits, s); break;
+        case 4: launch_bf16_t<M_T, 4>(w, V, H, x, logits, s); break;
+        case 5: launch_bf16_t<M_T, 5>(w, V, H, x, logits, s); break;
+        case 6: launch_bf16_t<M_T, 6>(w, V, H, x, logits, s); break;
+        case 7: launch_bf16_t<M_T, 7>(w, V, H, x, logits, s); break;
+        default: launch_bf16_t<M_T, 8>(w, V, H, x, logits, s); break;
     }
     return hipGetLastError();
 }
