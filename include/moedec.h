@@ -211,8 +211,9 @@ int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, in
  * workspace   >= moe_ffn_workspace_bytes(M, k, H, I), as for
  *             moe_expert_ffn_mxfp4 (the two calls may share one workspace)
  * Other arguments and limits as moe_expert_ffn_mxfp4.
- * Both FFN calls run a persistent grid of 3 blocks per CU that must be
- * resident together; they wait (boundedly) for each other's
+ * Both FFN calls run a grid whose blocks must be resident together (one
+ * block per work unit at four blocks per CU for one token when the units fit,
+ * otherwise three blocks per CU); they wait (boundedly) for each other's
  * blocks, so do not run them concurrently with another kernel that holds most
  * of the GPU.  The launch is refused (MOEDEC_ERR_LAUNCH) if the device cannot
  * hold that many blocks per CU.
