@@ -34,8 +34,8 @@
 //     intermediate rows 16rg..16rg+15 of the slot's expert, full K = H, every
 //     token the slot serves; each h value is published as one 64-bit word
 //     (launch generation, value).
-//   * down (group, g): for output rows 16 SUB g .. 16 SUB (g + 1) - 1 (SUB = 1
-//     for one token, 2 for more), the sum over the group's slots of
+//   * down (group, g): for output rows 16 SUB g .. 16 SUB (g + 1) - 1 (SUB = 2,
+//     or 1 for one token in the persistent grid), the sum over the group's slots of
 //     W_down[e] (w * h).  It issues its weight loads, then loads the
 //     group's tagged h words -- re-reading those whose tag is stale -- stages
 //     w * h in LDS and finishes.  With one group it writes y; otherwise groups
@@ -105,9 +105,9 @@ constexpr int kMaxGrid = 4096;
 // Co-resident blocks per CU.  The general form keeps a block's next gate/up
 // unit and a second down batch in flight (168 VGPRs per lane: three blocks).
 // When the grid has a block for every unit (ONE, one token), neither is
-// needed and 128 VGPRs give four blocks per CU: a one-token 2560 x 768 layer's
-// 912 units then all start at once, so every down unit issues its weight
-// loads right after routing.  The generation words let the grid differ
+// needed and at most 128 VGPRs give four blocks per CU: a one-token 2560 x 768
+// layer's 672 units then all start at once, so every down unit issues its
+// weight loads right after routing.  The generation words let the grid differ
 // between launches.
 template <bool ONE>
 constexpr int blocks_per_cu() { return ONE ? 4 : 3; }
@@ -138,7 +138,7 @@ struct FfnArgs {
     float eps;                       // RMSNorm epsilon
     const moedec_dispatch* disp;     // slots from moe_route_topk, or
     const float* logits;             // [M][E]: route here
-    int32_t* ids_out;                // routing outputs of the fused path (block 0), nullable
+    int32_t* ids_out;                // routing outputs of the fused path (the writer block), nullable
     float* w_out;
     moedec_dispatch* disp_out;
     uint32_t* gens;                  // [kMaxGrid] per-block launch counters
@@ -245,7 +245,7 @@ __device__ void table_from_dispatch(const FfnArgs& a, SlotTable& T) {
 
 // One token (M = 1): wave 0 builds the whole table from its top-k -- slot
 // 1 + rank(id) for each chosen expert, one (slot, token) pair per slot, and
-// the group bounds -- and block 0 writes the routing outputs from registers.
+// the group bounds -- and the writer block writes the routing outputs from registers.
 __device__ void table_from_logits_one(const FfnArgs& a, SlotTable& T, uint64_t* buf, const float (&lv)[16]) {
     if (wave_id_uniform() != 0) return;
     const int lane = lane_id();
