@@ -336,10 +336,19 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
         m.lmhead_gemv_bf16(w, x, out=lo)
         g8 = capture(torch, lambda: [m.lmhead_gemv_fp8(head, x, out=lo) for _ in range(reps)])
         gb = capture(torch, lambda: [m.lmhead_gemv_bf16(w, x, out=lo) for _ in range(reps)])
+        # greedy decode: FP8 GEMV with the argmax epilogue, logits not written
+        aws = torch.empty(max(8, m.lib.lmhead_argmax_workspace_bytes(V, M)), dtype=torch.uint8, device=dev)
+        ids = torch.empty(M, dtype=torch.int32, device=dev)
+        m.lmhead_argmax_fp8(head, x, workspace=aws, ids=ids)
+        ga = capture(torch, lambda: [m.lmhead_argmax_fp8(head, x, workspace=aws, ids=ids) for _ in range(reps)])
         g8.replay()
         gb.replay()
+        ga.replay()
         ms8 = t.run(g8.replay) / reps
         msb = t.run(gb.replay) / reps
+        msa = t.run(ga.replay) / reps
+        out[f"fp8_argmax_m{M}_us"] = 1e3 * msa
+        out[f"fp8_argmax_m{M}_gbs"] = (V * H + V * 4 + M * H * 2) / (1e6 * msa)
         b8 = V * H + V * 4 + M * H * 2 + M * V * 4
         bb = V * H * 2 + M * H * 2 + M * V * 4
         out[f"fp8_m{M}_us"] = 1e3 * ms8
@@ -349,7 +358,7 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
         out[f"bf16_m{M}_us"] = 1e3 * msb
         out[f"bf16_m{M}_gbs"] = bb / (1e6 * msb)
         out[f"bf16_m{M}_frac_of_peak"] = bb / (1e6 * msb) / PEAK_HBM_GBS
-        del g8, gb
+        del g8, gb, ga
     del head, w
     torch.cuda.empty_cache()
     return out

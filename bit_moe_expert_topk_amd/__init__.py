@@ -279,6 +279,24 @@ def lmhead_gemv_fp8(head, x, out=None):
     return out
 
 
+def lmhead_argmax_fp8(head, x, workspace=None, ids=None, logits=None):
+    """Greedy token ids [M] int32 from the FP8 head (lmhead_gemv_fp8_argmax);
+    logits [M][V] float32 are written too when a tensor is given."""
+    _need(x, torch.bfloat16, "x", 2)
+    m_tokens = x.shape[0]
+    need = lib.lmhead_argmax_workspace_bytes(head.V, m_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    if ids is None:
+        ids = torch.empty(m_tokens, dtype=torch.int32, device=x.device)
+    if logits is not None:
+        _need(logits, torch.float32, "logits", 2)
+    _check(lib.lmhead_gemv_fp8_argmax(ctypes.byref(head.desc), _ptr(x), m_tokens, _ptr(logits), _ptr(ids),
+                                      _ptr(workspace), workspace.numel(), _stream(x)))
+    return ids
+
+
 def router_logits(w_router, x, out=None):
     """logits [M][E] float32 = x W_router^T (moe_router_logits_bf16)."""
     _need(w_router, torch.bfloat16, "w_router", 2)

@@ -74,6 +74,9 @@ SIGNATURES = {
     "moedec_status_string": (ctypes.c_char_p, [c_int]),
     "moedec_last_error": (ctypes.c_char_p, []),
     "moe_route_topk": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "lmhead_argmax_workspace_bytes": (c_size_t, [c_int, c_int]),
+    "lmhead_gemv_fp8_argmax": (c_int, [ctypes.POINTER(LMHeadFP8Desc), c_void_p, c_int, c_void_p, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
     "moe_router_logits_bf16": (c_int, [c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p]),
     "moedec_mxfp4_packed_sizes": (c_int, [c_int, c_int, ctypes.POINTER(MXFP4Sizes)]),
     "moe_pack_gateup_mxfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,

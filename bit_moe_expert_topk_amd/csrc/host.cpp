@@ -288,6 +288,41 @@ int lmhead_gemv_bf16(const uint16_t* w_bf16, int V, int H, const uint16_t* x_bf1
                     "lmhead_gemv_bf16");
 }
 
+size_t lmhead_argmax_workspace_bytes(int V, int M) {
+    if (V < 1 || M < 1 || M > MOEDEC_MAX_M) return 0;
+    return moedec::lmhead_argmax_keys_bytes(V, M);
+}
+
+int lmhead_gemv_fp8_argmax(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M, float* logits,
+                           int32_t* token_ids, void* workspace, size_t workspace_bytes,
+                           moedec_stream_t stream) {
+    if (!head) return fail(MOEDEC_ERR_NULL, "head descriptor is NULL");
+    if (head->magic != MOEDEC_LMHEAD_MAGIC)
+        return fail(MOEDEC_ERR_FORMAT, "head magic 0x%08x is not an FP8 LM-head descriptor",
+                    head->magic);
+    if (head->format != MOEDEC_FMT_E4M3FN_ROWSCALE_F32)
+        return fail(MOEDEC_ERR_FORMAT, "head format %u is not E4M3 with per-row float32 scales",
+                    head->format);
+    if (!head->codes || !head->row_scale || !x_bf16 || !token_ids || !workspace)
+        return fail(MOEDEC_ERR_NULL, "codes, row_scale, x, token_ids or workspace is NULL");
+    if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
+    if (head->V < 1) return fail(MOEDEC_ERR_SHAPE, "V=%d < 1", head->V);
+    if (head->H < 16 || head->H > 4096 || head->H % 16)
+        return fail(MOEDEC_ERR_SHAPE, "H=%d: need 16 <= H <= 4096 and H %% 16 == 0", head->H);
+    if (!aligned(head->codes, 16) || !aligned(head->row_scale, 4) || !aligned(x_bf16, 4) ||
+        !aligned(logits, 4) || !aligned(token_ids, 4) || !aligned(workspace, 8))
+        return fail(MOEDEC_ERR_ALIGN,
+                    "codes 16-byte, row_scale/x/logits/token_ids 4-byte, workspace 8-byte alignment needed");
+    const size_t need = moedec::lmhead_argmax_keys_bytes(head->V, M);
+    if (workspace_bytes < need)
+        return fail(MOEDEC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_gemv_fp8(head->codes, head->row_scale, head->V, head->H, x_bf16, M,
+                                            logits, static_cast<hipStream_t>(stream),
+                                            static_cast<uint64_t*>(workspace), token_ids),
+                    "lmhead_gemv_fp8_argmax");
+}
+
 int moe_router_logits_bf16(const uint16_t* w_router, int E, int H, const uint16_t* x_bf16, int M,
                            float* logits, moedec_stream_t stream) {
     if (!w_router || !x_bf16 || !logits) return fail(MOEDEC_ERR_NULL, "w_router, x or logits is NULL");

@@ -56,8 +56,12 @@ hipError_t launch_expert_ffn(const moedec_moe_weights& w, const uint16_t* x, int
 
 hipError_t launch_lmhead_quant(const uint16_t* w, int V, int H, uint8_t* codes, float* rs,
                                hipStream_t s);
+// keys / ids non-null: the greedy epilogue (per-wave argmax keys, then one
+// reducing block writes ids[M]); logits may then be null.
 hipError_t launch_gemv_fp8(const uint8_t* codes, const float* rs, int V, int H,
-                           const uint16_t* x, int M, float* logits, hipStream_t s);
+                           const uint16_t* x, int M, float* logits, hipStream_t s,
+                           uint64_t* keys = nullptr, int32_t* ids = nullptr);
+size_t lmhead_argmax_keys_bytes(int V, int M);
 hipError_t launch_gemv_bf16(const uint16_t* w, int V, int H, const uint16_t* x, int M,
                             float* logits, hipStream_t s);
 

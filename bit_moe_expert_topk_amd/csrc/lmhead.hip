@@ -16,6 +16,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "route_device.h"
 
 namespace moedec {
 
@@ -79,11 +80,30 @@ constexpr int kRows = 4;   // rows per wave step
 constexpr int pow2_ceil(int n) { return n <= 1 ? 1 : 2 * pow2_ceil((n + 1) / 2); }
 constexpr int log2_exact(int n) { return n <= 1 ? 0 : 1 + log2_exact(n / 2); }
 
+// Argmax key of logit `val` at row `row`: larger logit first, then the lower
+// row (float_order puts -0.0 and +0.0 together, so the row decides there too).
+__device__ __forceinline__ uint64_t argmax_key(float val, int row) {
+    return ((uint64_t)float_order(val) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)k, off);
+        const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        k = o > k ? o : k;
+    }
+    return k;
+}
+
 // Writes the R x M_T row sums of a wave step: acc[r][m] summed over the wave
 // (multi_sum: lane l ends with value l >> kShift) and scaled by scale(r).
-template <int R, int M_T, typename Scale>
+// Logits are stored when `logits` is non-null; `best` keeps this lane's
+// running argmax key (its token is (lane >> kShift) % M_T in every step).
+template <int R, int M_T, bool KEYS, typename Scale>
 __device__ __forceinline__ void store_row_sums(const float (&acc)[R][M_T], int v, int v1, int V,
-                                               float* __restrict__ logits, Scale scale) {
+                                               float* __restrict__ logits, Scale scale, uint64_t& best) {
     constexpr int kN = pow2_ceil(R * M_T);
     constexpr int kShift = 6 - log2_exact(kN);
     float vals[kN];
@@ -94,7 +114,14 @@ __device__ __forceinline__ void store_row_sums(const float (&acc)[R][M_T], int v
     const int idx = lane >> kShift;
     if ((lane & ((1 << kShift) - 1)) == 0 && idx < R * M_T) {
         const int r = idx / M_T, m = idx - (idx / M_T) * M_T;
-        if (v + r < v1) logits[(size_t)m * V + v + r] = tot * scale(v + r);
+        if (v + r < v1) {
+            const float val = tot * scale(v + r);
+            if (!KEYS || logits) logits[(size_t)m * V + v + r] = val;
+            if constexpr (KEYS) {
+                const uint64_t key = argmax_key(val, v + r);
+                best = key > best ? key : best;
+            }
+        }
     }
 }
 
@@ -149,12 +176,14 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
 // per wave step.  Each lane keeps its slice of x (every token) in registers
 // and reuses it for every row the wave visits; the R x M_T row sums of a
 // step are reduced together (store_row_sums).
-template <int M_T, int T, int R>
+// KEYS (the greedy epilogue): this wave's argmax key per token at
+// keys[wave * M_T + m] (0 when the wave has no rows); logits may be null.
+template <int M_T, int T, int R, bool KEYS>
 __global__ __launch_bounds__(256) void gemv_fp8_kernel(const uint8_t* __restrict__ codes,
                                                        const float* __restrict__ rs, int V, int H,
                                                        const uint32_t* __restrict__ x,
                                                        float* __restrict__ logits,
-                                                       int rows_per_wave) {
+                                                       int rows_per_wave, uint64_t* __restrict__ keys) {
     const int lane = lane_id();
     const int n_ch = H / 16;
     const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -173,6 +202,7 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(const uint8_t* __restrict
         }
     const int v0 = gw * rows_per_wave;
     const int v1 = min(V, v0 + rows_per_wave);
+    uint64_t best = 0;
     for (int v = v0; v < v1; v += R) {
         // unconditional loads (clamped row and chunk): rows past v1 are computed
         // but never stored, chunks past H meet zero activations
@@ -200,7 +230,56 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(const uint8_t* __restrict
                     for (int m = 0; m < M_T; ++m)
                         acc[r][m] = dot2_bf16(wp, as_bf16x2(xr[m][t][j]), acc[r][m]);
                 }
-        store_row_sums<R, M_T>(acc, v, v1, V, logits, [&](int row) { return rs[row]; });
+        store_row_sums<R, M_T, KEYS>(acc, v, v1, V, logits, [&](int row) { return rs[row]; }, best);
+    }
+    if constexpr (KEYS) {
+        constexpr int kShift = 6 - log2_exact(pow2_ceil(R * M_T));
+        const int lane_m = (lane >> kShift) % M_T;
+#pragma unroll
+        for (int m = 0; m < M_T; ++m) {
+            const uint64_t k = wave_max_u64(lane_m == m ? best : 0ull);
+            if (lane == 0) keys[(size_t)gw * M_T + m] = k;
+        }
+    }
+}
+
+// Greedy token per row of x: the maximum over the waves' keys, one block of
+// 1,024 threads whose loads go out in batches of kArgBatch (a 157,184-row
+// head has 4,912 waves: one batch).
+constexpr int kArgThreads = 1024;
+constexpr int kArgBatch = 8;
+
+template <int M_T>
+__global__ __launch_bounds__(kArgThreads) void argmax_reduce_kernel(const uint64_t* __restrict__ keys,
+                                                                    int n_waves, int32_t* __restrict__ ids) {
+    __shared__ uint64_t s_best[kArgThreads / 64][M_T];
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    uint64_t b[M_T];
+#pragma unroll
+    for (int m = 0; m < M_T; ++m) b[m] = 0;
+    for (int i0 = threadIdx.x; i0 < n_waves; i0 += kArgThreads * kArgBatch) {
+        uint64_t k[kArgBatch][M_T];
+#pragma unroll
+        for (int j = 0; j < kArgBatch; ++j) {
+            const int i = i0 + kArgThreads * j;
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) k[j][m] = (i < n_waves) ? keys[(size_t)i * M_T + m] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < kArgBatch; ++j)
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) b[m] = k[j][m] > b[m] ? k[j][m] : b[m];
+    }
+#pragma unroll
+    for (int m = 0; m < M_T; ++m) {
+        const uint64_t t = wave_max_u64(b[m]);
+        if (lane == 0) s_best[w][m] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < M_T) {
+        uint64_t t = 0;
+        for (int i = 0; i < kArgThreads / 64; ++i) t = s_best[i][threadIdx.x] > t ? s_best[i][threadIdx.x] : t;
+        ids[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)t);
     }
 }
 
@@ -283,24 +362,37 @@ void launch_bf16_t(const uint16_t* w, int V, int H, const uint32_t* x, float* lo
 constexpr int kFp8Rows = 8;
 constexpr int kFp8RowsPerWave = 32;
 
+int fp8_waves(int V) {                              // waves launched (4 per block)
+    const int waves = (V + kFp8RowsPerWave - 1) / kFp8RowsPerWave;
+    return 4 * ((waves + 3) / 4);
+}
+
 template <int M_T, int T>
 hipError_t gemv_fp8_t(const uint8_t* codes, const float* rs, int V, int H, const uint32_t* x,
-                      float* logits, hipStream_t s) {
-    const int waves = (V + kFp8RowsPerWave - 1) / kFp8RowsPerWave;
-    const dim3 grid((waves + 3) / 4), blk(256);
-    hipLaunchKernelGGL((gemv_fp8_kernel<M_T, T, kFp8Rows>), grid, blk, 0, s, codes, rs, V, H, x, logits,
-                       kFp8RowsPerWave);
+                      float* logits, uint64_t* keys, int32_t* ids, hipStream_t s) {
+    const int n_waves = fp8_waves(V);
+    const dim3 grid(n_waves / 4), blk(256);
+    if (!keys) {
+        hipLaunchKernelGGL((gemv_fp8_kernel<M_T, T, kFp8Rows, false>), grid, blk, 0, s, codes, rs, V, H, x,
+                           logits, kFp8RowsPerWave, nullptr);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((gemv_fp8_kernel<M_T, T, kFp8Rows, true>), grid, blk, 0, s, codes, rs, V, H, x, logits,
+                       kFp8RowsPerWave, keys);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((argmax_reduce_kernel<M_T>), dim3(1), dim3(kArgThreads), 0, s, keys, n_waves, ids);
     return hipGetLastError();
 }
 
 template <int M_T>
 hipError_t gemv_fp8_m(const uint8_t* codes, const float* rs, int V, int H, const uint32_t* x,
-                      float* logits, hipStream_t s) {
+                      float* logits, uint64_t* keys, int32_t* ids, hipStream_t s) {
     switch ((H / 16 + 63) / 64) {
-        case 1: return gemv_fp8_t<M_T, 1>(codes, rs, V, H, x, logits, s);
-        case 2: return gemv_fp8_t<M_T, 2>(codes, rs, V, H, x, logits, s);
-        case 3: return gemv_fp8_t<M_T, 3>(codes, rs, V, H, x, logits, s);
-        default: return gemv_fp8_t<M_T, 4>(codes, rs, V, H, x, logits, s);
+        case 1: return gemv_fp8_t<M_T, 1>(codes, rs, V, H, x, logits, keys, ids, s);
+        case 2: return gemv_fp8_t<M_T, 2>(codes, rs, V, H, x, logits, keys, ids, s);
+        case 3: return gemv_fp8_t<M_T, 3>(codes, rs, V, H, x, logits, keys, ids, s);
+        default: return gemv_fp8_t<M_T, 4>(codes, rs, V, H, x, logits, keys, ids, s);
     }
 }
 
@@ -363,15 +455,18 @@ hipError_t launch_lmhead_quant(const uint16_t* w, int V, int H, uint8_t* codes, 
 }
 
 hipError_t launch_gemv_fp8(const uint8_t* codes, const float* rs, int V, int H,
-                           const uint16_t* x, int M, float* logits, hipStream_t s) {
+                           const uint16_t* x, int M, float* logits, hipStream_t s,
+                           uint64_t* keys, int32_t* ids) {
     const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
     switch (M) {
-        case 1: return gemv_fp8_m<1>(codes, rs, V, H, x32, logits, s);
-        case 2: return gemv_fp8_m<2>(codes, rs, V, H, x32, logits, s);
-        case 3: return gemv_fp8_m<3>(codes, rs, V, H, x32, logits, s);
-        default: return gemv_fp8_m<4>(codes, rs, V, H, x32, logits, s);
+        case 1: return gemv_fp8_m<1>(codes, rs, V, H, x32, logits, keys, ids, s);
+        case 2: return gemv_fp8_m<2>(codes, rs, V, H, x32, logits, keys, ids, s);
+        case 3: return gemv_fp8_m<3>(codes, rs, V, H, x32, logits, keys, ids, s);
+        default: return gemv_fp8_m<4>(codes, rs, V, H, x32, logits, keys, ids, s);
     }
 }
+
+size_t lmhead_argmax_keys_bytes(int V, int M) { return (size_t)fp8_waves(V) * M * sizeof(uint64_t); }
 
 hipError_t launch_gemv_bf16(const uint16_t* w, int V, int H, const uint16_t* x, int M,
                             float* logits, hipStream_t s) {

@@ -286,6 +286,25 @@ int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H,
 int lmhead_gemv_fp8(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M,
                     float* logits, moedec_stream_t stream);
 
+/*
+ * Greedy decode on the FP8 head [news two easily missed details and card
+ * results: the decode step samples the next token from these logits; greedy
+ * choice is the temperature-0 case]: the GEMV of lmhead_gemv_fp8 followed by
+ * token_ids[m] = the row v of the largest logits[m][v], the lowest such row
+ * on ties (+0.0 and -0.0 are equal), without a pass over the logits: each
+ * wave keeps the best (logit, row) of its rows and one reducing block picks
+ * among the waves.  Two launches on `stream`.
+ * logits      [M][V] float32, optional (NULL: not written)
+ * token_ids   [M] int32, 4-byte aligned
+ * workspace   >= lmhead_argmax_workspace_bytes(V, M) bytes, 8-byte aligned
+ *             (per-wave keys; no initial contents needed)
+ * Other arguments and limits as lmhead_gemv_fp8.
+ */
+size_t lmhead_argmax_workspace_bytes(int V, int M);   /* 0 for sizes out of range */
+int lmhead_gemv_fp8_argmax(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M, float* logits,
+                           int32_t* token_ids, void* workspace, size_t workspace_bytes,
+                           moedec_stream_t stream);
+
 /* Comparator: logits = W x with bf16 W [V][H] (16-byte aligned), float32
  * accumulation.  1 <= M <= 4, H % 8 == 0, H <= 4096. */
 int lmhead_gemv_bf16(const uint16_t* w_bf16, int V, int H, const uint16_t* x_bf16, int M,

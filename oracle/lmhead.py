@@ -20,7 +20,8 @@ Parity status: quantisation pinned (tests/test_oracle_lmhead.py) by rows whose
 absmax is 448 (scale exactly 1, codes equal to the direct E4M3 encoding), an
 all-zero row, the per-element error bound of E4M3, and torch's float8_e4m3fn
 cast for in-range values; the GEMVs by one-hot activations selecting a single
-column times its row scale (orientation and scale) and x = 0.
+column times its row scale (orientation and scale) and x = 0; the greedy
+argmax by hand-worked rows with ties and signed zeros and by a library sort.
 """
 
 import numpy as np
@@ -50,6 +51,15 @@ def lmhead_gemv_fp8(codes, row_scale, x):
     x = np.asarray(x, dtype=np.float64)                       # [M][H]
     s = np.asarray(row_scale, dtype=np.float64)               # [V]
     return (x @ wq.T) * s[None, :]
+
+
+def lmhead_argmax(logits):
+    """Greedy token of each row of logits [M][V]: the index of the largest
+    logit, the lowest such index on ties (+0.0 equals -0.0); int64 [M].
+    Greedy choice is the temperature-0 case of the sampling the pages' decode
+    step runs on these logits [card results]."""
+    logits = np.asarray(logits, dtype=np.float64)
+    return np.argmax(logits, axis=1).astype(np.int64)     # first index of the maximum
 
 
 def lmhead_gemv_bf16(w, x):

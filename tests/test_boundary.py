@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("moe_route_topk", "moe_expert_ffn_mxfp4", "moe_layer_mxfp4", "moe_layer_rmsnorm_mxfp4",
                  "lmhead_quant_fp8", "lmhead_gemv_fp8",
-                 "lmhead_gemv_bf16", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
+                 "lmhead_gemv_bf16", "lmhead_gemv_fp8_argmax", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
                  "moedec_last_error", "moedec_abi_version"):
         assert want in names
@@ -74,6 +74,22 @@ def test_route_argument_checks(m):
     assert L.moe_route_topk(ODD, 1, 512, 8, FAKE, FAKE, FAKE, None) == -2
     assert L.moe_route_topk(FAKE, 1, 512, 8, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 4), None) == -2
     assert b"k=33" in L.moedec_last_error() or True
+
+
+def test_argmax_workspace_and_argument_checks(m):
+    L = m.lib
+    assert L.lmhead_argmax_workspace_bytes(157184, 1) == 4 * ((4912 + 3) // 4) * 1 * 8
+    assert L.lmhead_argmax_workspace_bytes(157184, 4) == 4 * ((4912 + 3) // 4) * 4 * 8
+    assert L.lmhead_argmax_workspace_bytes(0, 1) == 0 and L.lmhead_argmax_workspace_bytes(10, 5) == 0
+    desc = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32, 157184, 2560, FAKE, FAKE)
+    ws = L.lmhead_argmax_workspace_bytes(157184, 1)
+    assert L.lmhead_gemv_fp8_argmax(None, FAKE, 1, None, FAKE, FAKE, ws, None) == -1
+    assert L.lmhead_gemv_fp8_argmax(ctypes.byref(desc), FAKE, 1, None, None, FAKE, ws, None) == -1
+    assert L.lmhead_gemv_fp8_argmax(ctypes.byref(desc), FAKE, 5, None, FAKE, FAKE, ws, None) == -3
+    assert L.lmhead_gemv_fp8_argmax(ctypes.byref(desc), FAKE, 1, None, FAKE, FAKE, ws - 8, None) == -5
+    assert L.lmhead_gemv_fp8_argmax(ctypes.byref(desc), FAKE, 1, None, ODD, FAKE, ws, None) == -2
+    bad = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, 7, 157184, 2560, FAKE, FAKE)
+    assert L.lmhead_gemv_fp8_argmax(ctypes.byref(bad), FAKE, 1, None, FAKE, FAKE, ws, None) == -4
 
 
 def test_router_argument_checks(m):

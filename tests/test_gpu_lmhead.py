@@ -105,3 +105,68 @@ def test_full_size_quant_and_gemv(m, full_head):
         check_acc(got, oracle.lmhead_gemv_fp8(codes, scale, x), f"full fp8 M={M}")
         gotb = _check_gemv(m, w_dev, xb, None, f"full bf16 gemv M={M}", fp8=False)[:, rows]
         check_acc(gotb, oracle.lmhead_gemv_bf16(synth.bf16_values(full_head[rows]), x), f"full bf16 M={M}")
+
+
+def _check_argmax(m, head, xb, what, ref_logits=None):
+    """Greedy ids: equal to the argmax (lowest index on ties) of the kernel's
+    own float32 logits, which the epilogue leaves unchanged; with float64
+    oracle logits, equal to their argmax unless the top two lie within the
+    float32-accumulator tolerance of each other (then either is correct)."""
+    say("argmax", what)
+    x = bf16_tensor(xb)
+    M = x.shape[0]
+    lg_plain = m.lmhead_gemv_fp8(head, x)
+    lg = torch.empty_like(lg_plain)
+    ids = m.lmhead_argmax_fp8(head, x, logits=lg)
+    ids_only = m.lmhead_argmax_fp8(head, x)                  # logits not written
+    torch.cuda.synchronize()
+    lg_np = lg.cpu().numpy()
+    np.testing.assert_array_equal(lg_np.view(np.uint32), lg_plain.cpu().numpy().view(np.uint32))
+    got = ids.cpu().numpy()
+    np.testing.assert_array_equal(got, ids_only.cpu().numpy())
+    np.testing.assert_array_equal(got, oracle.lmhead_argmax(lg_np), err_msg=what)
+    if ref_logits is not None:
+        for mm in range(M):
+            r = ref_logits[mm]
+            tol = 1e-5 * np.max(np.abs(r))
+            top2 = np.sort(r)[-2:]
+            if top2[1] - top2[0] > 2 * tol:
+                assert got[mm] == int(np.argmax(r)), f"{what} token {mm}"
+            else:
+                assert r[got[mm]] >= top2[1] - 2 * tol, f"{what} token {mm}: not a near-maximum"
+
+
+@pytest.mark.parametrize("V,H", [(300, 2560), (77, 256), (129, 4096), (5, 16), (4097, 64)])
+@pytest.mark.parametrize("M", [1, 4])
+def test_argmax_small(m, V, H, M):
+    wb = _weights(V, H, seed=V + 2)
+    head = _check_quant(m, wb)
+    xb = synth.lmhead_x_bf16(M + 7, M, H)
+    ref = oracle.lmhead_gemv_fp8(head.codes.cpu().numpy(), head.row_scale.cpu().numpy(),
+                                 synth.bf16_values(xb).astype(np.float64))
+    _check_argmax(m, head, xb, f"V={V} H={H} M={M}", ref)
+
+
+def test_argmax_exact_tie_takes_the_lower_row(m):
+    """Two identical rows hold the largest logit (identical codes and scales give
+    bit-identical sums): the lower row wins, across waves as within one."""
+    V, H = 700, 256
+    wb = _weights(V, H, seed=3)
+    xb = synth.lmhead_x_bf16(9, 2, H)
+    sign = np.sign(synth.bf16_values(xb[0])).astype(np.float32)
+    big = synth.bf16_bits_from_f32(0.05 * sign)
+    for row in (650, 37, 41):                    # rows in different waves (32 rows per wave)
+        wb[row] = big
+    head = _check_quant(m, wb)
+    ids = m.lmhead_argmax_fp8(head, bf16_tensor(xb))
+    torch.cuda.synchronize()
+    assert int(ids.cpu().numpy()[0]) == 37
+    _check_argmax(m, head, xb, "tie rows 37/41/650")
+
+
+def test_argmax_full_size(m, full_head):
+    """157,184 x 2,560 at M = 1 and 4: the epilogue's ids against the argmax of
+    the kernel's own logits."""
+    head = m.lmhead_quant_fp8(bf16_tensor(full_head))
+    for M in (1, 4):
+        _check_argmax(m, head, synth.lmhead_x_bf16(5, M, synth.LMHEAD_H), f"full M={M}")

@@ -71,3 +71,18 @@ def test_gemv_bf16_one_hot_orientation():
     got = oracle.lmhead_gemv_bf16(w, x)
     np.testing.assert_array_equal(got[0], w[:, 3])
     np.testing.assert_array_equal(got[1], -2.0 * w[:, 63])
+
+
+def test_argmax_hand_worked_ties_and_signed_zeros():
+    lg = np.array([[0.5, 2.0, -1.0, 2.0],        # tie at the top: the lower index, 1
+                   [-0.0, 0.0, -3.0, -2.0],      # +0 and -0 are equal: index 0
+                   [-5.0, -4.0, -4.5, -7.0],     # all negative: index 1
+                   [1.0, 1.0, 1.0, 1.0]])        # all equal: index 0
+    np.testing.assert_array_equal(oracle.lmhead_argmax(lg), [1, 0, 1, 0])
+
+
+def test_argmax_matches_a_stable_sort():
+    rng = np.random.default_rng(21)
+    lg = rng.integers(-3, 4, size=(6, 50)).astype(np.float64)      # many ties
+    order = [np.lexsort((np.arange(50), -row))[0] for row in lg]   # largest, then lowest index
+    np.testing.assert_array_equal(oracle.lmhead_argmax(lg), order)
