@@ -287,9 +287,9 @@ int lmhead_gemv_fp8(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M
                     float* logits, moedec_stream_t stream);
 
 /*
- * Greedy decode on the FP8 head [news two easily missed details and card
- * results: the decode step samples the next token from these logits; greedy
- * choice is the temperature-0 case]: the GEMV of lmhead_gemv_fp8 followed by
+ * Greedy decode on the FP8 head [card results: the measured decode samples
+ * the next token from these logits with temperature 0.6, top-p 0.95, top-k 29;
+ * greedy choice is the temperature-0 case]: the GEMV of lmhead_gemv_fp8 followed by
  * token_ids[m] = the row v of the largest logits[m][v], the lowest such row
  * on ties (+0.0 and -0.0 are equal), without a pass over the logits: each
  * wave keeps the best (logit, row) of its rows and one reducing block picks
