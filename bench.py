@@ -651,6 +651,7 @@ def main(argv=None):
         line["stack_us_per_layer_eager"] = round(stack["us_per_layer_eager"], 3)
     if lm is not None:
         line["lmhead_fp8_gbs_m1"] = round(lm["fp8_m1_gbs"], 1)
+        line["lmhead_fp8_argmax_us_m1"] = round(lm["fp8_argmax_m1_us"], 2)
         line["lmhead_fp8_gbs_m4"] = round(lm["fp8_m4_gbs"], 1)
         line["lmhead_bf16_gbs_m1"] = round(lm["bf16_m1_gbs"], 1)
     print(json.dumps(line), flush=True)
