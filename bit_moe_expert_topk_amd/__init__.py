@@ -297,6 +297,16 @@ def lmhead_argmax_fp8(head, x, workspace=None, ids=None, logits=None):
     return ids
 
 
+def selftest(device="cuda"):
+    """moedec_selftest on the current stream of `device`: closed-form cases
+    through routing, the fused MXFP4 layer and the FP8 head; raises on a
+    mismatch."""
+    scratch = torch.empty(lib.moedec_selftest_bytes() + 256, dtype=torch.uint8, device=device)
+    off = (-scratch.data_ptr()) % 256
+    buf = scratch[off:off + lib.moedec_selftest_bytes()]
+    _check(lib.moedec_selftest(_ptr(buf), buf.numel(), _stream(buf)))
+
+
 def router_logits(w_router, x, out=None):
     """logits [M][E] float32 = x W_router^T (moe_router_logits_bf16)."""
     _need(w_router, torch.bfloat16, "w_router", 2)

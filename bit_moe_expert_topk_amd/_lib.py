@@ -19,6 +19,7 @@ MOEDEC_ERR_FORMAT = -4
 MOEDEC_ERR_WORKSPACE = -5
 MOEDEC_ERR_LAUNCH = -6
 MOEDEC_ERR_DEVICE = -7
+MOEDEC_ERR_SELFTEST = -8
 
 MAX_M = 4
 MAX_K = 32
@@ -74,6 +75,8 @@ SIGNATURES = {
     "moedec_status_string": (ctypes.c_char_p, [c_int]),
     "moedec_last_error": (ctypes.c_char_p, []),
     "moe_route_topk": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moedec_selftest_bytes": (c_size_t, []),
+    "moedec_selftest": (c_int, [c_void_p, c_size_t, c_void_p]),
     "lmhead_argmax_workspace_bytes": (c_size_t, [c_int, c_int]),
     "lmhead_gemv_fp8_argmax": (c_int, [ctypes.POINTER(LMHeadFP8Desc), c_void_p, c_int, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),

@@ -5,7 +5,9 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "launch.h"
 #include "moedec.h"
@@ -75,6 +77,7 @@ const char* moedec_status_string(int status) {
         case MOEDEC_ERR_WORKSPACE: return "workspace too small";
         case MOEDEC_ERR_LAUNCH: return "kernel launch failed";
         case MOEDEC_ERR_DEVICE: return "device is not gfx950";
+        case MOEDEC_ERR_SELFTEST: return "self-test mismatch";
         default: return "unknown status";
     }
 }
@@ -336,6 +339,154 @@ int moe_router_logits_bf16(const uint16_t* w_router, int E, int H, const uint16_
     return launched(moedec::launch_gemv_bf16(w_router, E, H, x_bf16, M, logits,
                                              static_cast<hipStream_t>(stream)),
                     "moe_router_logits_bf16");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Start-up self-check: closed-form cases (no stored expected values).
+
+namespace {
+
+constexpr int kStE = 4, kStH = 64, kStI = 32, kStK = 2;        // MoE case
+constexpr int kStV = 2, kStHv = 16;                            // LM-head case
+
+struct StLayout {
+    size_t gate_c, gate_s, up_c, up_s, down_c, down_s;           // canonical routed experts
+    size_t sgate_c, sgate_s, sup_c, sup_s, sdown_c, sdown_s;     // canonical shared expert
+    size_t gu_c, gu_s, dn_c, dn_s, sgu_c, sgu_s, sdn_c, sdn_s;   // packed
+    size_t x, logits, ids, w, disp, y, y32, ws;
+    size_t lw, lcodes, lscale, lx, llogits, lid, lws;
+    size_t total;
+    moedec_mxfp4_sizes sz;
+};
+
+StLayout st_layout() {
+    StLayout L{};
+    moedec::packed_sizes(kStH, kStI, &L.sz);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { off = (off + 255) & ~(size_t)255; const size_t at = off; off += bytes; return at; };
+    const size_t gc = (size_t)kStI * kStH / 2, gs = (size_t)kStI * kStH / 32;
+    const size_t dc = (size_t)kStH * kStI / 2, ds = (size_t)kStH * kStI / 32;
+    L.gate_c = take(kStE * gc); L.gate_s = take(kStE * gs); L.up_c = take(kStE * gc); L.up_s = take(kStE * gs);
+    L.down_c = take(kStE * dc); L.down_s = take(kStE * ds);
+    L.sgate_c = take(gc); L.sgate_s = take(gs); L.sup_c = take(gc); L.sup_s = take(gs);
+    L.sdown_c = take(dc); L.sdown_s = take(ds);
+    L.gu_c = take(kStE * L.sz.gu_codes); L.gu_s = take(kStE * L.sz.gu_scales);
+    L.dn_c = take(kStE * L.sz.dn_codes); L.dn_s = take(kStE * L.sz.dn_scales);
+    L.sgu_c = take(L.sz.gu_codes); L.sgu_s = take(L.sz.gu_scales);
+    L.sdn_c = take(L.sz.dn_codes); L.sdn_s = take(L.sz.dn_scales);
+    L.x = take(kStH * 2); L.logits = take(kStE * 4); L.ids = take(kStK * 4); L.w = take(kStK * 4);
+    L.disp = take(sizeof(moedec_dispatch)); L.y = take(kStH * 2); L.y32 = take(kStH * 4);
+    L.ws = take(moedec::ffn_layout(1, kStK, kStH, kStI).total);
+    L.lw = take(kStV * kStHv * 2); L.lcodes = take(kStV * kStHv); L.lscale = take(kStV * 4);
+    L.lx = take(kStHv * 2); L.llogits = take(kStV * 4); L.lid = take(4);
+    L.lws = take(moedec::lmhead_argmax_keys_bytes(kStV, 1));
+    L.total = (off + 255) & ~(size_t)255;
+    return L;
+}
+
+float st_bf16_to_f32(uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moedec_selftest_bytes(void) { return st_layout().total; }
+
+int moedec_selftest(void* scratch, size_t scratch_bytes, moedec_stream_t stream) {
+    const StLayout L = st_layout();
+    if (!scratch) return fail(MOEDEC_ERR_NULL, "scratch is NULL");
+    if (!aligned(scratch, 256)) return fail(MOEDEC_ERR_ALIGN, "scratch must be 256-byte aligned");
+    if (scratch_bytes < L.total)
+        return fail(MOEDEC_ERR_WORKSPACE, "scratch %zu bytes < %zu needed", scratch_bytes, L.total);
+    if (int st = check_device()) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* d = static_cast<uint8_t*>(scratch);
+    // host inputs: every E2M1 nibble is code 2 (+1.0); gate/up scales 2^0, down scales 2^-5
+    std::vector<uint8_t> ones(kStE * (size_t)kStI * kStH / 2, 0x22);
+    std::vector<uint8_t> sc0(kStE * (size_t)kStI * kStH / 32, 127), scd(kStE * (size_t)kStH * kStI / 32, 122);
+    std::vector<uint16_t> x(kStH, 0x3C80);                              // bf16 2^-6
+    const float logits[kStE] = {1.5f, 0.5f, 1.5f, -1.0f};
+    // LM head: row 0 = {448, -2, 1, 0.5, 0...}, row 1 = 0.25 everywhere; x = one-hot at 1
+    std::vector<uint16_t> lw(kStV * kStHv, 0), lx(kStHv, 0);
+    lw[0] = 0x43E0; lw[1] = 0xC000; lw[2] = 0x3F80; lw[3] = 0x3F00;
+    for (int j = 0; j < kStHv; ++j) lw[kStHv + j] = 0x3E80;
+    lx[1] = 0x3F80;
+    const size_t gc = (size_t)kStI * kStH / 2, gs = (size_t)kStI * kStH / 32, ds = (size_t)kStH * kStI / 32;
+    struct Copy { size_t at; const void* p; size_t n; } copies[] = {
+        {L.gate_c, ones.data(), kStE * gc}, {L.up_c, ones.data(), kStE * gc}, {L.down_c, ones.data(), kStE * gc},
+        {L.gate_s, sc0.data(), kStE * gs}, {L.up_s, sc0.data(), kStE * gs}, {L.down_s, scd.data(), kStE * ds},
+        {L.sgate_c, ones.data(), gc}, {L.sup_c, ones.data(), gc}, {L.sdown_c, ones.data(), gc},
+        {L.sgate_s, sc0.data(), gs}, {L.sup_s, sc0.data(), gs}, {L.sdown_s, scd.data(), ds},
+        {L.x, x.data(), kStH * 2}, {L.logits, logits, sizeof(logits)},
+        {L.lw, lw.data(), lw.size() * 2}, {L.lx, lx.data(), lx.size() * 2}};
+    for (const Copy& c : copies)
+        if (hipMemcpyAsync(d + c.at, c.p, c.n, hipMemcpyHostToDevice, s) != hipSuccess)
+            return fail(MOEDEC_ERR_LAUNCH, "self-test: copy to scratch failed");
+    if (hipMemsetAsync(d + L.ws, 0, moedec::ffn_layout(1, kStK, kStH, kStI).total, s) != hipSuccess)
+        return fail(MOEDEC_ERR_LAUNCH, "self-test: workspace clear failed");
+    int st;
+    if ((st = moe_pack_gateup_mxfp4(d + L.gate_c, d + L.gate_s, d + L.up_c, d + L.up_s, kStE, kStH, kStI,
+                                    d + L.gu_c, d + L.gu_s, stream)) ||
+        (st = moe_pack_gateup_mxfp4(d + L.sgate_c, d + L.sgate_s, d + L.sup_c, d + L.sup_s, 1, kStH, kStI,
+                                    d + L.sgu_c, d + L.sgu_s, stream)) ||
+        (st = moe_pack_down_mxfp4(d + L.down_c, d + L.down_s, kStE, kStH, kStI, d + L.dn_c, d + L.dn_s, stream)) ||
+        (st = moe_pack_down_mxfp4(d + L.sdown_c, d + L.sdown_s, 1, kStH, kStI, d + L.sdn_c, d + L.sdn_s, stream)))
+        return st;
+    moedec_moe_weights w{MOEDEC_MOE_MAGIC, kStE, kStH, kStI, d + L.gu_c, d + L.gu_s, d + L.dn_c, d + L.dn_s,
+                         d + L.sgu_c, d + L.sgu_s, d + L.sdn_c, d + L.sdn_s};
+    if ((st = moe_layer_mxfp4(&w, reinterpret_cast<uint16_t*>(d + L.x), reinterpret_cast<float*>(d + L.logits), 1,
+                              kStK, reinterpret_cast<int32_t*>(d + L.ids), reinterpret_cast<float*>(d + L.w),
+                              reinterpret_cast<moedec_dispatch*>(d + L.disp), reinterpret_cast<uint16_t*>(d + L.y),
+                              reinterpret_cast<float*>(d + L.y32), d + L.ws,
+                              moedec::ffn_layout(1, kStK, kStH, kStI).total, stream)))
+        return st;
+    moedec_lmhead_fp8 head{};
+    if ((st = lmhead_quant_fp8(reinterpret_cast<uint16_t*>(d + L.lw), kStV, kStHv, d + L.lcodes,
+                               reinterpret_cast<float*>(d + L.lscale), &head, stream)) ||
+        (st = lmhead_gemv_fp8_argmax(&head, reinterpret_cast<uint16_t*>(d + L.lx), 1,
+                                     reinterpret_cast<float*>(d + L.llogits), reinterpret_cast<int32_t*>(d + L.lid),
+                                     d + L.lws, moedec::lmhead_argmax_keys_bytes(kStV, 1), stream)))
+        return st;
+    int32_t ids[kStK], lid = -1;
+    float wts[kStK], y32[kStH], lsc[kStV], llg[kStV];
+    uint16_t yb[kStH];
+    uint8_t codes[kStV * kStHv];
+    struct Back { void* p; size_t at; size_t n; } backs[] = {
+        {ids, L.ids, sizeof(ids)}, {wts, L.w, sizeof(wts)}, {y32, L.y32, sizeof(y32)}, {yb, L.y, sizeof(yb)},
+        {codes, L.lcodes, sizeof(codes)}, {lsc, L.lscale, sizeof(lsc)}, {llg, L.llogits, sizeof(llg)},
+        {&lid, L.lid, sizeof(lid)}};
+    for (const Back& b : backs)
+        if (hipMemcpyAsync(b.p, d + b.at, b.n, hipMemcpyDeviceToHost, s) != hipSuccess)
+            return fail(MOEDEC_ERR_LAUNCH, "self-test: copy back failed");
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(MOEDEC_ERR_LAUNCH, "self-test: stream failed");
+    if (ids[0] != 0 || ids[1] != 2 || wts[0] != 0.5f || wts[1] != 0.5f)
+        return fail(MOEDEC_ERR_SELFTEST, "self-test routing: ids {%d, %d} weights {%g, %g}, want {0, 2} {0.5, 0.5}",
+                    ids[0], ids[1], (double)wts[0], (double)wts[1]);
+    const double want = 2.0 / (1.0 + std::exp(-1.0));
+    for (int r = 0; r < kStH; ++r) {
+        if (!(std::fabs(y32[r] - want) <= 1e-5 * want))
+            return fail(MOEDEC_ERR_SELFTEST, "self-test MoE layer: y[%d] = %.9g, want %.9g", r, (double)y32[r], want);
+        if (!(std::fabs((double)st_bf16_to_f32(yb[r]) - y32[r]) <= std::ldexp(1.0, -8) * want))
+            return fail(MOEDEC_ERR_SELFTEST, "self-test MoE layer: bf16 y[%d] does not round y_f32", r);
+    }
+    const uint8_t want_c0[5] = {0x7E, 0xC0, 0x38, 0x30, 0x00};
+    for (int j = 0; j < kStHv; ++j) {
+        if (codes[j] != want_c0[j < 4 ? j : 4] || codes[kStHv + j] != 0x7E)
+            return fail(MOEDEC_ERR_SELFTEST, "self-test FP8 codes: column %d {0x%02x, 0x%02x}", j, codes[j],
+                        codes[kStHv + j]);
+    }
+    if (lsc[0] != 1.0f || llg[0] != -2.0f || !(std::fabs(llg[1] - 0.25) <= 1e-6) || lid != 1)
+        return fail(MOEDEC_ERR_SELFTEST, "self-test FP8 head: scale %g, logits {%g, %g}, token %d",
+                    (double)lsc[0], (double)llg[0], (double)llg[1], lid);
+    g_last_error[0] = '\0';
+    return MOEDEC_OK;
 }
 
 }  // extern "C"

@@ -51,6 +51,7 @@ typedef void* moedec_stream_t;
 #define MOEDEC_ERR_WORKSPACE -5   /* workspace smaller than required */
 #define MOEDEC_ERR_LAUNCH    -6   /* the HIP runtime rejected a launch */
 #define MOEDEC_ERR_DEVICE    -7   /* the current device is not a gfx950 GPU */
+#define MOEDEC_ERR_SELFTEST  -8   /* moedec_selftest: a result differs from its closed form */
 
 /* Limits. */
 #define MOEDEC_MAX_M      4       /* tokens per call: 1, or the 4-token verify window [card #3] */
@@ -309,6 +310,28 @@ int lmhead_gemv_fp8_argmax(const moedec_lmhead_fp8* head, const uint16_t* x_bf16
  * accumulation.  1 <= M <= 4, H % 8 == 0, H <= 4096. */
 int lmhead_gemv_bf16(const uint16_t* w_bf16, int V, int H, const uint16_t* x_bf16, int M,
                      float* logits, moedec_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Start-up self-check.  [news two easily missed details; card limits: a
+ * draft model that received the FP8 head's weight tensor instead of the
+ * whole head module ran silently wrong and slower; the advice is to verify
+ * the wiring at start-up]  Runs small cases whose results have closed forms
+ * through the calls of this library on `stream` and compares them on the host:
+ *   - routing: logits {1.5, 0.5, 1.5, -1}, k = 2 -> ids {0, 2} (tie to the
+ *     lower index), weights {0.5, 0.5} exactly;
+ *   - the fused MXFP4 layer (H = 64, I = 32, 4 routed experts + shared, every
+ *     gate/up weight 1, every down weight 2^-5, x = 2^-6): g = u = 1, every
+ *     output 0.5 h + 0.5 h + h = 2 / (1 + e^-1) (float32 rounding only);
+ *   - the FP8 head: codes of {448, -2, 1, 0.5, 0} and a row of 0.25 under
+ *     per-row scales, the GEMV of a one-hot x, and its greedy token.
+ * scratch: device memory of >= moedec_selftest_bytes() bytes, 256-byte
+ * aligned, contents ignored.  Unlike every other call this one WAITS for the
+ * stream.  Returns MOEDEC_OK, or MOEDEC_ERR_SELFTEST with
+ * moedec_last_error() naming the first case that differs (or the status of
+ * a call that failed).
+ */
+size_t moedec_selftest_bytes(void);
+int moedec_selftest(void* scratch, size_t scratch_bytes, moedec_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -92,6 +92,16 @@ def test_argmax_workspace_and_argument_checks(m):
     assert L.lmhead_gemv_fp8_argmax(ctypes.byref(bad), FAKE, 1, None, FAKE, FAKE, ws, None) == -4
 
 
+def test_selftest_argument_checks(m):
+    L = m.lib
+    n = L.moedec_selftest_bytes()
+    assert n > 0 and n % 256 == 0
+    assert L.moedec_selftest(None, n, None) == -1
+    assert L.moedec_selftest(ctypes.c_void_p((1 << 20) + 16), n, None) == -2
+    assert L.moedec_selftest(FAKE, n - 256, None) == -5
+    assert L.moedec_status_string(-8) == b"self-test mismatch"
+
+
 def test_router_argument_checks(m):
     L = m.lib
     assert L.moe_router_logits_bf16(None, 512, 2560, FAKE, 1, FAKE, None) == -1

@@ -530,3 +530,11 @@ def test_workspace_error_flag_stays_clear(m):
         _run_ffn(m, W, xb, lg, k, ws)
     flag = ws[4096 * 4:4096 * 4 + 4].cpu().numpy().view(np.uint32)[0]
     assert flag == 0
+
+
+def test_selftest_passes(m):
+    """The library's start-up check (closed-form routing, MXFP4 layer and FP8
+    head cases) passes on the device, twice on the same scratch."""
+    say("selftest")
+    m.selftest()
+    m.selftest()
