@@ -594,6 +594,15 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
             ch = adv ? (wrap ? 0 : ch + 1) : ch;
         }
     };
+    // The group-0 unit finishes the rows: with a residual stream it adds r_in,
+    // loaded now (ahead of the weights) rather than after the combine.
+    constexpr int kRowsU = SUB * kUnitRows;                     // output rows of this unit
+    float rin[M_T];
+    if (grp == 0 && a.r_out != nullptr && w == 0) {
+        const int row = kRowsU * g + (lane & (kRowsU - 1));
+#pragma unroll
+        for (int m = 0; m < M_T; ++m) rin[m] = a.r_in[(size_t)m * a.H + row];
+    }
     if (i_begin < i_end) load_batch(i_begin, cwA, scA);
     if constexpr (!ONE) {
         if (i_begin + kDnBatch < i_end) load_batch(i_begin + kDnBatch, cwB, scB);
@@ -818,7 +827,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
             const size_t o = (size_t)m * a.H + row;
             if (a.y_f32) a.y_f32[o] = y[m];
             if (a.y_bf16) a.y_bf16[o] = f32_to_bf16_rne(y[m]);
-            if (a.r_out) a.r_out[o] = a.r_in[o] + y[m];
+            if (a.r_out) a.r_out[o] = rin[m] + y[m];
         }
     }
 }
