@@ -170,3 +170,23 @@ def test_argmax_full_size(m, full_head):
     head = m.lmhead_quant_fp8(bf16_tensor(full_head))
     for M in (1, 4):
         _check_argmax(m, head, synth.lmhead_x_bf16(5, M, synth.LMHEAD_H), f"full M={M}")
+
+
+def test_argmax_graph_replays(m):
+    """The greedy epilogue captured in a HIP graph: every replay (with eager
+    calls between) gives the eager ids."""
+    wb = _weights(3000, 256, seed=8)
+    head = m.lmhead_quant_fp8(bf16_tensor(wb))
+    x = bf16_tensor(synth.lmhead_x_bf16(3, 4, 256))
+    ref = m.lmhead_argmax_fp8(head, x).cpu().numpy()
+    ws = torch.empty(m.lib.lmhead_argmax_workspace_bytes(3000, 4), dtype=torch.uint8, device="cuda")
+    ids = torch.empty(4, dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.lmhead_argmax_fp8(head, x, workspace=ws, ids=ids)
+    for _ in range(3):
+        ids.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids.cpu().numpy(), ref)
+        np.testing.assert_array_equal(m.lmhead_argmax_fp8(head, x).cpu().numpy(), ref)

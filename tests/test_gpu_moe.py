@@ -538,3 +538,34 @@ def test_selftest_passes(m):
     say("selftest")
     m.selftest()
     m.selftest()
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_graph_replays_match_eager(m, M):
+    """The fused layer captured in a HIP graph (as the benchmark runs it):
+    every replay, with eager calls and synchronisations between replays,
+    gives the eager result bit for bit (workspace generations advance per
+    launch, so replays must not see stale tags)."""
+    say(f"graph replays M={M}")
+    W, xb, lg, _, _, k = _host_layer_case(m, synth.TINY, M)
+    x = bf16_tensor(xb)
+    lgt = torch.from_numpy(lg).cuda()
+    ws = m.make_ffn_workspace(M, k, W.H, W.I, "cuda")
+    y_e, y32_e = m.moe_layer(W, x, lgt, k, ws)
+    torch.cuda.synchronize()
+    ref_b, ref_f = bits_of(y_e), y32_e.cpu().numpy().view(np.uint32)
+    y = torch.empty_like(y_e)
+    y32 = torch.empty_like(y32_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):                      # several launches in one graph
+            m.moe_layer(W, x, lgt, k, ws, y=y, y_f32=y32)
+    for _ in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_of(y), ref_b)
+        np.testing.assert_array_equal(y32.cpu().numpy().view(np.uint32), ref_f)
+        yb2, _ = m.moe_layer(W, x, lgt, k, ws)  # eager work between replays
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_of(yb2), ref_b)
+    assert ws[4096 * 4:4096 * 4 + 4].cpu().numpy().view(np.uint32)[0] == 0
