@@ -111,3 +111,30 @@ def test_rmsnorm_hand_worked():
     np.testing.assert_allclose(oracle.rmsnorm(r, eps=0.0), [[1.2, -1.6, 0.0, 0.0]], rtol=1e-15)
     r2 = np.random.default_rng(1).standard_normal((2, 64))
     np.testing.assert_allclose(oracle.rmsnorm(r2 * 7.0, eps=0.0), oracle.rmsnorm(r2, eps=0.0), rtol=1e-13)
+
+
+def test_library_selftest_cases_agree_with_the_oracle():
+    """The start-up self-test inside the library (moedec_selftest) expects
+    closed forms written from the mathematics; the oracle, computing the same
+    cases from their definitions, must agree: routing of {1.5, 0.5, 1.5, -1}
+    with k = 2 is ids {0, 2} with weights {0.5, 0.5}; an MXFP4 layer whose
+    every gate/up weight is code 2 (1.0) at scale 2^0 and every down weight is
+    code 2 at scale 2^-5, with x = 2^-6 over H = 64 and I = 32, gives
+    2 / (1 + e^-1) on every output; the FP8 codes of {448, -2, 1, 0.5, 0} and
+    of a row of 0.25 are {0x7E, 0xC0, 0x38, 0x30, 0x00} and 0x7E."""
+    ids, w = oracle.route_topk(np.float32([[1.5, 0.5, 1.5, -1.0]]), 2)
+    np.testing.assert_array_equal(ids, [[0, 2]])
+    np.testing.assert_array_equal(w, [[0.5, 0.5]])
+    H, I = 64, 32
+    gate = oracle.mxfp4_dequant(np.full((I, H // 2), 0x22, np.uint8), np.full((I, H // 32), 127, np.uint8))
+    down = oracle.mxfp4_dequant(np.full((H, I // 2), 0x22, np.uint8), np.full((H, I // 32), 122, np.uint8))
+    x = np.full((1, H), 2.0 ** -6)
+    y = oracle.moe_layer(x, ids, w, lambda e: (gate, gate, down), (gate, gate, down))
+    np.testing.assert_allclose(y, 2.0 / (1.0 + math.exp(-1.0)), rtol=1e-15)
+    row0 = np.array([448.0, -2.0, 1.0, 0.5] + [0.0] * 12)
+    codes, scale = oracle.lmhead_quant_fp8(np.stack([row0, np.full(16, 0.25)]))
+    np.testing.assert_array_equal(codes[0, :5], [0x7E, 0xC0, 0x38, 0x30, 0x00])
+    assert (codes[0, 4:] == 0).all() and (codes[1] == 0x7E).all() and scale[0] == 1.0
+    logits = oracle.lmhead_gemv_fp8(codes, scale, np.eye(16)[1:2])
+    np.testing.assert_allclose(logits, [[-2.0, 0.25]], rtol=1e-6)
+    assert oracle.lmhead_argmax(logits)[0] == 1
