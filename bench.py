@@ -511,9 +511,9 @@ def traffic_summary(fetch_dir, write_dir, out_path):
         "Commands (from the repository root on the GPU host):",
         "",
         "```",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --pmc-run",
-        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --pmc-run",
-        "python3 bench.py --traffic-from gpurun_out/pmc_fetch gpurun_out/pmc_write --traffic-out <this file>",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py --pmc-run",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py --pmc-run",
+        f"python3 bench.py --traffic-from {fetch_dir} {write_dir} --traffic-out <this file>",
         "```",
         "",
         "Calibration: an elementwise float32 copy of 2^28 elements (1 GiB read, 1 GiB written);",

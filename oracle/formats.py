@@ -9,7 +9,7 @@ public OCP definitions:
   subnormal (0 or 0.5); no Inf/NaN.  Magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
 * E8M0 [MX §5.4.1]: unsigned 8-bit power of two 2^(b-127); 0xFF is NaN.
 * MXFP4 block [MX §5.2]: 32 E2M1 elements share one E8M0 scale.  Memory
-  packing (not fixed by MX, a reading of this build): codes [N][K/2] bytes with
+  packing (not fixed by MX; the reading adopted here): codes [N][K/2] bytes with
   the LOW nibble holding the even k, scales [N][K/32] row-major.
 * E4M3 [OFP8 §4]: 1 sign, 4 exponent (bias 7), 3 mantissa; exponent 0 is
   subnormal (m * 2^-9); S.1111.111 is NaN; no Inf; largest finite 448.
