@@ -410,6 +410,15 @@ def test_fused_ragged_and_extreme(m, H, I, E, k, M):
     _check_fused(m, W, xb, lg, k, ef, sh, f"fused H={H} I={I} E={E} k={k} M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_fused_largest_intermediate(m, M):
+    """I = 2048, the largest supported intermediate size (64 MX blocks per down
+    row, the widest h staging and the smallest slot groups the LDS allows)."""
+    shape = synth.MoEShape(H=64, I=2048, E=6, k=2, scale_lo=119, scale_hi=123)
+    W, xb, lg, ef, sh, k = _host_layer_case(m, shape, M, seed=9)
+    _check_fused(m, W, xb, lg, k, ef, sh, f"fused H=64 I=2048 M={M}")
+
+
 @pytest.mark.parametrize("H,I,E,k", [(256, 768, 40, 32), (1536, 768, 20, 16), (1024, 768, 20, 16)])
 def test_fused_one_token_grid_forms(m, H, I, E, k):
     """One token: the kernel gives every work unit a block of its own when the
