@@ -1000,7 +1000,13 @@ void moe_ffn_kernel(FfnArgs a) {
         table_from_dispatch<M_T>(a, T);
     if (has_gu) x_stage<M_T, NORM>(a, xv, lds);
     __syncthreads();
-    if (!kDirectGroups) {
+    // The slot groups (pair starts, group bounds) matter only to down units.
+    // A persistent block with gate/up units builds them while its first
+    // unit's weight loads are in flight (that unit's barriers publish them):
+    // on a busy CU wave 0 needs up to ~2.6 us for it, which must not hold up
+    // the loads.  Other blocks build them here.
+    const bool groups_late = !kDirectGroups && !ONE && has_gu;
+    if (!kDirectGroups && !groups_late) {
         table_groups(a, T);
         __syncthreads();
     }
@@ -1021,9 +1027,14 @@ void moe_ffn_kernel(FfnArgs a) {
         // with the gate/up stream that every down unit waits for.)
         GuLoads<NB> cur, nxt;
         gateup_issue<M_T, NB>(a, T, u, cur);
+        bool groups_pending = groups_late;
         for (; u < a.n_gu; u += gridDim.x) {
             const int un = u + gridDim.x;
             if (un < a.n_gu) gateup_issue<M_T, NB>(a, T, un, nxt);
+            if (groups_pending) {                          // wave 0; published by the unit's barrier
+                table_groups(a, T);
+                groups_pending = false;
+            }
             gateup_compute<M_T, NB>(a, T, lds, u, gen, cur);
             cur = nxt;
             __syncthreads();
