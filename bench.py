@@ -188,6 +188,7 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
     wall1 = time.perf_counter()
     ms_two = t.run(g_two.replay)
     ms_ffn = t.run(g_ffn.replay)
+    m.check_ffn_workspace(ws)              # raises if a cross-block wait gave up
     ffn_bytes = step_bytes - M * shape.E * 4                   # no logits read
     res = {
         "M": M,
@@ -246,6 +247,7 @@ def stack_bench(m, torch, synth, layers, passes, eager_passes, dev):
     del g
     one_pass()
     ms_eager = t.run(lambda: [one_pass() for _ in range(eager_passes)])
+    m.check_ffn_workspace(ws)
     finite = bool(torch.isfinite(bufs[0]).all().item())
     steps_g, steps_e = passes * n_layers, eager_passes * n_layers
     layer_bytes = (shape.k + 1) * EXPERT_BYTES_LING + shape.E * 4 + 2 * shape.H * 4   # + r in, r out
@@ -302,6 +304,7 @@ def router_bench(m, torch, synth, layers, steps, dev, n_router=128):
     g.replay()
     ms = t.run(g.replay)
     out["router_plus_layer_us_m1"] = 1e3 * ms / steps
+    m.check_ffn_workspace(ws)
     del g, wrs
     torch.cuda.empty_cache()
     return out
@@ -365,46 +368,119 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
 
 
 # ----------------------------------------------------------------------------
-# CPU oracle baseline (bounded sample of the same workload)
+# CPU oracle baseline (bounded samples of the same workloads)
+#
+# The oracle functions run unchanged.  Each measurement runs jobs in worker
+# processes (spawned, so they never inherit this process's GPU state), one
+# BLAS thread each: the 1-thread setting runs its jobs one after another in a
+# single worker; the all-cores setting runs one job per host core at once
+# (whole layers, or row chunks of the LM head) and takes the wall time from
+# the common start (a barrier after each worker has prepared its inputs) to
+# the last finish.  Input preparation (drawing the synthetic weights, and
+# quantising the LM-head sample) is never timed.
 
-def cpu_baseline(synth, n_layers):
-    import numpy as np
-    import oracle
+_CPU_BARRIER = None
+
+
+def _cpu_worker_init(barrier):
+    global _CPU_BARRIER
+    _CPU_BARRIER = barrier
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+        threadpool_limits(limits=1)
     except Exception:                     # pragma: no cover - threadpoolctl is installed
-        limiter = None
-    shape = synth.LING
-    total_s = 0.0
-    total_bytes = 0
-    for layer in range(n_layers):
-        xb = synth.activations_bf16(0, layer, 1, shape.H)
-        lg = synth.logits_f32(0, layer, 1, shape.E)
-        # input preparation, untimed: regenerate only the experts this layer routes to
+        pass
+
+
+def _cpu_job(args):
+    """One oracle job: ("moe", layer, M) = route + MXFP4 dequantisation of the
+    layer's active experts + the float64 SwiGLU layer; ("lmhead", chunk, rows)
+    = the FP8 LM-head GEMV on `rows` rows.  Returns (t0, t1, algorithmic bytes)."""
+    import numpy as np
+    import oracle
+    import synth
+    kind, idx, n = args
+    if kind == "moe":
+        shape = synth.LING
+        M = n
+        xb = synth.activations_bf16(0, idx, M, shape.H)
+        lg = synth.logits_f32(0, idx, M, shape.E)
         pre_ids, _ = oracle.route_topk(lg, shape.k)
-        canon = {int(e): synth.mxfp4_expert(0, layer, int(e), shape) for e in list(pre_ids[0]) + [shape.E]}
+        active = sorted(set(int(e) for e in pre_ids.flatten()))
+        canon = {e: synth.mxfp4_expert(0, idx, e, shape) for e in active + [shape.E]}
         x = synth.bf16_values(xb).astype(np.float64)
+        nbytes = (len(active) + 1) * EXPERT_BYTES_LING + M * shape.E * 4 + 2 * M * shape.H * 2
+        _CPU_BARRIER.wait()
         t0 = time.perf_counter()
         ids, w = oracle.route_topk(lg, shape.k)
-        dense = {e: tuple(oracle.mxfp4_dequant(*canon[int(e)][n]) for n in ("gate", "up", "down"))
-                 for e in list(ids[0]) + [shape.E]}
-        oracle.moe_layer(x, ids, w, lambda e: dense[e], dense[shape.E])
-        total_s += time.perf_counter() - t0
-        total_bytes += (shape.k + 1) * EXPERT_BYTES_LING + shape.E * 4 + 2 * shape.H * 2
-        log(f"oracle layer {layer}: {total_s:.2f} s so far")
-    if limiter is not None:
-        limiter.restore_original_limits()
+        dense = {e: tuple(oracle.mxfp4_dequant(*canon[e][nm]) for nm in ("gate", "up", "down")) for e in canon}
+        oracle.moe_layer(x, ids, w, lambda e: dense[int(e)], dense[shape.E])
+        t1 = time.perf_counter()
+    else:
+        rows, H = n, synth.LMHEAD_H
+        wb = synth.lmhead_weight_bf16(1000 + idx, rows, H)
+        codes, scale = oracle.lmhead_quant_fp8(synth.bf16_values(wb))
+        x = synth.bf16_values(synth.lmhead_x_bf16(0, 1, H)).astype(np.float64)
+        nbytes = rows * H + rows * 4 + rows * 4 + H * 2 * rows / synth.LMHEAD_V
+        _CPU_BARRIER.wait()
+        t0 = time.perf_counter()
+        oracle.lmhead_gemv_fp8(codes, scale, x)
+        t1 = time.perf_counter()
+    return t0, t1, nbytes
+
+
+def _cpu_run(jobs, workers):
+    """Run jobs in `workers` spawned processes; with one worker they run one
+    after another.  Returns (algorithmic bytes / s, seconds timed, bytes)."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(workers)
+    with ctx.Pool(workers, initializer=_cpu_worker_init, initargs=(barrier,)) as pool:
+        res = pool.map(_cpu_job, jobs, chunksize=1)
+    nbytes = sum(r[2] for r in res)
+    if workers == 1:
+        secs = sum(r[1] - r[0] for r in res)
+    else:
+        secs = max(r[1] for r in res) - min(r[0] for r in res)
+    return nbytes / secs, secs, nbytes
+
+
+def cpu_baseline(synth, n_layers):
+    """The oracle on the host: Ling-shaped M = 1 layers (the headline workload),
+    M = 4 layers and an FP8 LM-head row sample, each at 1 thread and at all
+    host cores.  The headline figure is M = 1 at all cores."""
+    cores = len(os.sched_getaffinity(0))
+    lm_rows = 8192
+    settings = {}
+    plans = {
+        "m1": ([("moe", L, 1) for L in range(n_layers)], [("moe", L, 1) for L in range(cores)]),
+        "m4": ([("moe", 0, 4)], [("moe", L, 4) for L in range(cores)]),
+        "lmhead_fp8_m1": ([("lmhead", 0, lm_rows)], [("lmhead", c, lm_rows) for c in range(cores)]),
+    }
+    for name, (one, many) in plans.items():
+        for label, jobs, workers in (("1_thread", one, 1), ("all_cores", many, cores)):
+            t0 = time.perf_counter()
+            gbs, secs, nbytes = _cpu_run(jobs, workers)
+            entry = {"gbs": gbs / 1e9, "seconds_timed": secs, "bytes": nbytes, "jobs": len(jobs),
+                     "threads": workers, "wall_incl_setup_s": time.perf_counter() - t0}
+            if name != "lmhead_fp8_m1":
+                entry["us_per_layer"] = 1e6 * secs / (len(jobs) if workers == 1 else len(jobs) / workers)
+            else:
+                entry["us_per_token_full_head"] = 1e6 * (synth.LMHEAD_V * (synth.LMHEAD_H + 8)) / gbs
+            settings[f"{name}_{label}"] = entry
+            log(f"oracle {name} {label}: {entry}")
+    head = settings["m1_all_cores"]
     return {
-        "value": total_bytes / (1e9 * total_s),
+        "value": head["gbs"],
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{n_layers} Ling-shaped MoE layers at M=1 (route + MXFP4 dequant of the 9 active "
-                  f"experts + SwiGLU FFN in float64, numpy, BLAS limited to 1 thread): "
-                  f"{1e6 * total_s / n_layers:.0f} us/layer",
-        "us_per_layer": 1e6 * total_s / n_layers,
-        "host_cores_available": len(os.sched_getaffinity(0)),
+        "sample": f"{cores} Ling-shaped MoE layers at M=1 run at once, one per host core (route + MXFP4 "
+                  f"dequant of the 9 active experts + SwiGLU FFN in float64, numpy, 1 BLAS thread each); "
+                  f"{head['seconds_timed']:.2f} s wall; 1 thread: "
+                  f"{settings['m1_1_thread']['gbs']:.4f} GB/s ({settings['m1_1_thread']['us_per_layer']:.0f} us/layer)",
+        "settings": settings,
+        "host_cores_available": cores,
         "host_cpu": _cpu_model(),
     }
 

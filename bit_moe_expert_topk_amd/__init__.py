@@ -222,6 +222,18 @@ def moe_layer(weights, x, logits, k, workspace, y=None, y_f32=None, want_f32=Tru
     return y, y_f32
 
 
+def check_ffn_workspace(workspace):
+    """Wait for the stream and raise MoedecError (MOEDEC_ERR_TIMEOUT) when a
+    cross-block wait of any FFN call on `workspace` gave up since the last
+    check (those results are invalid; the library has cleared the workspace).
+    Returns the raw status word (0)."""
+    flags = ctypes.c_uint32(0)
+    _need(workspace, torch.uint8, "workspace", 1)
+    _check(lib.moe_ffn_workspace_status(_ptr(workspace), workspace.numel(), ctypes.byref(flags),
+                                        _stream(workspace)))
+    return int(flags.value)
+
+
 def moe_layer_rmsnorm(weights, r_in, logits, k, workspace, r_out=None, eps=1e-6, x_out=None,
                       y_f32=None):
     """One layer on the residual stream, in one launch: x = bf16(RMSNorm(r_in)),

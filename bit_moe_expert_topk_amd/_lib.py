@@ -20,6 +20,7 @@ MOEDEC_ERR_WORKSPACE = -5
 MOEDEC_ERR_LAUNCH = -6
 MOEDEC_ERR_DEVICE = -7
 MOEDEC_ERR_SELFTEST = -8
+MOEDEC_ERR_TIMEOUT = -9
 
 MAX_M = 4
 MAX_K = 32
@@ -93,6 +94,7 @@ SIGNATURES = {
     "moe_layer_rmsnorm_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int,
                                         ctypes.c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]),
+    "moe_ffn_workspace_status": (c_int, [c_void_p, c_size_t, ctypes.POINTER(c_uint32), c_void_p]),
     "lmhead_quant_fp8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p,
                                  ctypes.POINTER(LMHeadFP8Desc), c_void_p]),
     "lmhead_gemv_fp8": (c_int, [ctypes.POINTER(LMHeadFP8Desc), c_void_p, c_int, c_void_p, c_void_p]),

@@ -112,6 +112,7 @@ constexpr int kMaxGrid = 4096;
 template <bool ONE>
 constexpr int blocks_per_cu() { return ONE ? 4 : 3; }
 constexpr uint32_t kSpinLimit = 1u << 20;   // bounded waits; reached only if co-residency fails
+static_assert(kMaxGrid * sizeof(uint32_t) == kWsStatusOffset, "the error word follows the launch counters");
 
 struct FfnArgs {
     const uint8_t* gu_codes;

@@ -78,6 +78,7 @@ const char* moedec_status_string(int status) {
         case MOEDEC_ERR_LAUNCH: return "kernel launch failed";
         case MOEDEC_ERR_DEVICE: return "device is not gfx950";
         case MOEDEC_ERR_SELFTEST: return "self-test mismatch";
+        case MOEDEC_ERR_TIMEOUT: return "a cross-block wait gave up (results invalid)";
         default: return "unknown status";
     }
 }
@@ -151,9 +152,9 @@ size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I) {
     return moedec::ffn_layout(M, k_max, H, I).total;
 }
 
-static int check_moe_args(const moedec_moe_weights* w, const uint16_t* x_bf16, int M, int k,
-                          uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
-                          bool residual = false) {
+// Checks of a MoE call's weights, activations and sizes (not its workspace).
+static int check_moe_core(const moedec_moe_weights* w, const uint16_t* x_bf16, int M, int k,
+                          uint16_t* y_bf16, float* y_f32, bool residual) {
     if (!w) return fail(MOEDEC_ERR_NULL, "weights descriptor is NULL");
     if (w->magic != MOEDEC_MOE_MAGIC)
         return fail(MOEDEC_ERR_FORMAT, "weights descriptor magic 0x%08x != 0x%08x", w->magic,
@@ -162,7 +163,6 @@ static int check_moe_args(const moedec_moe_weights* w, const uint16_t* x_bf16, i
         !w->sh_gu_scales || !w->sh_dn_codes || !w->sh_dn_scales)
         return fail(MOEDEC_ERR_NULL, "a weight pointer is NULL");
     if (!residual && (!x_bf16 || !y_bf16)) return fail(MOEDEC_ERR_NULL, "x or y_bf16 is NULL");
-    if (!workspace) return fail(MOEDEC_ERR_NULL, "workspace is NULL");
     if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
     if (w->E < 1 || w->E > MOEDEC_MAX_E) return fail(MOEDEC_ERR_SHAPE, "E=%d not in 1..%d", w->E, MOEDEC_MAX_E);
     if (k < 1 || k > MOEDEC_MAX_K || k > w->E)
@@ -175,6 +175,14 @@ static int check_moe_args(const moedec_moe_weights* w, const uint16_t* x_bf16, i
         return fail(MOEDEC_ERR_ALIGN, "packed gate/up scale arrays must be 2-byte aligned");
     if (!aligned(x_bf16, 16) || !aligned(y_bf16, 4) || !aligned(y_f32, 4))
         return fail(MOEDEC_ERR_ALIGN, "x must be 16-byte aligned, y_bf16 and y_f32 4-byte");
+    return MOEDEC_OK;
+}
+
+static int check_moe_args(const moedec_moe_weights* w, const uint16_t* x_bf16, int M, int k,
+                          uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
+                          bool residual = false) {
+    if (int st = check_moe_core(w, x_bf16, M, k, y_bf16, y_f32, residual)) return st;
+    if (!workspace) return fail(MOEDEC_ERR_NULL, "workspace is NULL");
     if (!aligned(workspace, 16)) return fail(MOEDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
     const size_t need = moedec::ffn_layout(M, k, w->H, w->I).total;
     if (workspace_bytes < need)
@@ -207,6 +215,36 @@ int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const f
     return launched(moedec::launch_moe(*w, x_bf16, M, k, nullptr, logits, topk_ids, topk_w, dispatch,
                                        y_bf16, y_f32, workspace, static_cast<hipStream_t>(stream)),
                     "moe_layer_mxfp4");
+}
+
+int moe_ffn_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* flags_out,
+                             moedec_stream_t stream) {
+    if (flags_out) *flags_out = 0;
+    if (!workspace) return fail(MOEDEC_ERR_NULL, "workspace is NULL");
+    if (workspace_bytes < moedec::kWsStatusOffset + sizeof(uint32_t))
+        return fail(MOEDEC_ERR_WORKSPACE, "workspace %zu bytes holds no status word (need > %zu)",
+                    workspace_bytes, moedec::kWsStatusOffset);
+    if (!aligned(workspace, 16)) return fail(MOEDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (int st = check_device()) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const size_t bytes = workspace_bytes;
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, ws + moedec::kWsStatusOffset, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return fail(MOEDEC_ERR_LAUNCH, "reading the workspace status word failed");
+    if (flags_out) *flags_out = word;
+    if (word != 0) {
+        // the calls since the last check are invalid and may have left tagged
+        // words behind: clear the whole workspace so it can be used again
+        if (hipMemsetAsync(ws, 0, bytes, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+            return fail(MOEDEC_ERR_LAUNCH, "clearing the workspace failed");
+        return fail(MOEDEC_ERR_TIMEOUT,
+                    "a cross-block wait gave up in a call on this workspace (status 0x%x): results since the "
+                    "last check are invalid; the workspace was cleared", word);
+    }
+    g_last_error[0] = '\0';
+    return MOEDEC_OK;
 }
 
 int moe_layer_rmsnorm_mxfp4(const moedec_moe_weights* w, const float* r_in, const float* logits, int M,

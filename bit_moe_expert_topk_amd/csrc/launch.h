@@ -35,6 +35,12 @@ struct FfnLayout {
 };
 FfnLayout ffn_layout(int M, int k_max, int H, int I);
 
+// Byte offset of the wait-timeout word in an FFN workspace: it follows the
+// 4,096 per-block launch counters.  A kernel whose bounded cross-block wait
+// gave up sets it (and its results are invalid); moe_ffn_workspace_status
+// reads and clears it.
+constexpr size_t kWsStatusOffset = 4096 * sizeof(uint32_t);
+
 // Residual stream of a decode stack: x = bf16(RMSNorm(r_in)) replaces the x
 // input, and r_out = r_in + y is written next to y.
 struct ResidualArgs {

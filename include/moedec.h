@@ -16,9 +16,10 @@
  *
  * Conventions for every call
  *   - All pointers are DEVICE pointers unless marked "host".  The caller owns
- *     every buffer; the library never allocates, frees or synchronises.
+ *     every buffer; the library never allocates or frees device memory.
  *   - Work is enqueued on `stream` (a hipStream_t, NULL = null stream) and the
- *     call returns without waiting.  The return value reports host-side
+ *     call returns without waiting (moedec_selftest and
+ *     moe_ffn_workspace_status are the two calls that wait for the stream).  The return value reports host-side
  *     argument checks and launch errors only; a fault inside a kernel shows
  *     up at the caller's next synchronisation.
  *   - On a non-zero return nothing was enqueued, and moedec_last_error()
@@ -52,6 +53,7 @@ typedef void* moedec_stream_t;
 #define MOEDEC_ERR_LAUNCH    -6   /* the HIP runtime rejected a launch */
 #define MOEDEC_ERR_DEVICE    -7   /* the current device is not a gfx950 GPU */
 #define MOEDEC_ERR_SELFTEST  -8   /* moedec_selftest: a result differs from its closed form */
+#define MOEDEC_ERR_TIMEOUT   -9   /* moe_ffn_workspace_status: a cross-block wait gave up */
 
 /* Limits. */
 #define MOEDEC_MAX_M      4       /* tokens per call: 1, or the 4-token verify window [card #3] */
@@ -223,6 +225,28 @@ int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const f
                     int M, int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
                     uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
                     moedec_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Health of an FFN workspace.  The FFN calls above (and the residual-stream
+ * call below) run blocks that wait for one another across CUs; every such
+ * wait is bounded, and one that gives up -- possible only when the blocks of
+ * a launch are not all resident together, e.g. beside another kernel that
+ * holds most of the GPU -- records it in a status word of the workspace and
+ * lets the kernel finish, so the launch returns with WRONG results and its
+ * call had returned MOEDEC_OK.  This call waits for `stream`, reads that word
+ * and reports it:
+ *   MOEDEC_OK           no wait gave up in any call on this workspace since
+ *                       the last check;
+ *   MOEDEC_ERR_TIMEOUT  at least one did: the results of those calls are
+ *                       invalid.  The workspace is zero-filled again before
+ *                       the call returns, so it can be used right away.
+ * workspace        the workspace
+ * workspace_bytes  its size in bytes
+ * flags_out        host, may be NULL: the raw status word (0 when clear)
+ * Like moedec_selftest, this call waits for the stream.
+ * ---------------------------------------------------------------------- */
+int moe_ffn_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* flags_out,
+                             moedec_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * One MoE layer of a decode stack, on the residual stream.  The model the

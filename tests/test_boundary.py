@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
                  "lmhead_quant_fp8", "lmhead_gemv_fp8",
                  "lmhead_gemv_bf16", "lmhead_gemv_fp8_argmax", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
-                 "moedec_last_error", "moedec_abi_version"):
+                 "moedec_last_error", "moedec_abi_version", "moe_ffn_workspace_status"):
         assert want in names
 
 
@@ -73,7 +73,9 @@ def test_route_argument_checks(m):
     assert L.moe_route_topk(FAKE, 1, 512, 33, FAKE, FAKE, FAKE, None) == -3
     assert L.moe_route_topk(ODD, 1, 512, 8, FAKE, FAKE, FAKE, None) == -2
     assert L.moe_route_topk(FAKE, 1, 512, 8, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 4), None) == -2
-    assert b"k=33" in L.moedec_last_error() or True
+    # the message belongs to the call just made
+    assert L.moe_route_topk(FAKE, 1, 512, 33, FAKE, FAKE, FAKE, None) == -3
+    assert b"k=33" in L.moedec_last_error()
 
 
 def test_argmax_workspace_and_argument_checks(m):
@@ -224,3 +226,17 @@ def test_lmhead_descriptor_guards_format(m):
     assert L.lmhead_quant_fp8(ODD, 10, 2560, FAKE, FAKE, None, None) == -2
     assert L.lmhead_gemv_bf16(FAKE, 10, 2560, FAKE, 0, FAKE, None) == -3
     assert L.lmhead_gemv_bf16(FAKE, 10, 2560, None, 1, FAKE, None) == -1
+
+
+def test_workspace_status_argument_checks(m):
+    """The status call rejects a NULL workspace, one too small to hold the
+    status word and a misaligned one on the host, before any device work."""
+    L = m.lib
+    FAKE = ctypes.c_void_p(1 << 20)
+    flags = ctypes.c_uint32(7)
+    assert L.moe_ffn_workspace_status(FAKE, 64, ctypes.byref(flags), None) == m._lib.MOEDEC_ERR_WORKSPACE
+    assert flags.value == 0
+    assert b"status word" in L.moedec_last_error()
+    assert L.moe_ffn_workspace_status(None, 1 << 20, None, None) == -1
+    assert L.moe_ffn_workspace_status(ctypes.c_void_p((1 << 20) + 8), 1 << 20, None, None) == -2
+    assert m.lib.moedec_status_string(-9) != b"unknown status"

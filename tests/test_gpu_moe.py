@@ -216,6 +216,7 @@ def _run_ffn(m, W, x_bits, logits, k, ws=None):
         ws = m.make_ffn_workspace(x.shape[0], k, W.H, W.I, "cuda")
     y, y32 = m.expert_ffn(W, x, disp, k, ws)
     torch.cuda.synchronize()
+    assert m.check_ffn_workspace(ws) == 0          # no cross-block wait gave up
     return ids.cpu().numpy(), bits_of(y), y32.cpu().numpy(), disp
 
 
@@ -372,6 +373,7 @@ def _run_fused(m, W, x_bits, logits, k, ws=None):
         ws = m.make_ffn_workspace(M, k, W.H, W.I, "cuda")
     y, y32 = m.moe_layer(W, x, lg, k, ws, ids=ids, topk_w=wts, dispatch=disp)
     torch.cuda.synchronize()
+    assert m.check_ffn_workspace(ws) == 0          # no cross-block wait gave up
     return ids.cpu().numpy(), wts.cpu().numpy(), disp, bits_of(y), y32.cpu().numpy()
 
 
@@ -445,6 +447,16 @@ def test_fused_ling(m, ling_layer, name):
     _check_fused(m, ling_layer, xb, lg, 8, _ling_expert, _ling_expert(synth.LING.E), f"fused {name}")
 
 
+@pytest.mark.parametrize("M,seed", [(1, 1), (1, 2), (2, 0), (3, 0), (2, 3), (3, 4)])
+def test_fused_ling_more_tokens_and_seeds(m, ling_layer, M, seed):
+    """The Ling-shaped layer at every window size the verify path takes (M = 2
+    and 3 besides the headline 1 and 4) and on further seeds."""
+    xb = synth.activations_bf16(seed, 0, M, synth.LING.H)
+    lg = synth.logits_f32(seed, 0, M, synth.LING.E)
+    _check_fused(m, ling_layer, xb, lg, 8, _ling_expert, _ling_expert(synth.LING.E),
+                 f"fused ling M={M} seed {seed}")
+
+
 # ------------------------------------------------------- residual stack
 
 def _check_rmsnorm_x(x_bits, r, eps, what):
@@ -475,6 +487,7 @@ def _residual_stack(m, layers, r0, logits_per_layer, k, expert_fns, shareds, wha
         y32 = torch.empty((M, H), dtype=torch.float32, device="cuda")
         r_out = m.moe_layer_rmsnorm(W, r, lg, k, ws, eps=eps, x_out=x_out, y_f32=y32)
         torch.cuda.synchronize()
+        assert m.check_ffn_workspace(ws) == 0
         r_in_h, r_out_h, y_h = r.cpu().numpy(), r_out.cpu().numpy(), y32.cpu().numpy()
         xb = bits_of(x_out)
         _check_rmsnorm_x(xb, r_in_h, eps, f"{what} layer {L}")
@@ -488,10 +501,13 @@ def _residual_stack(m, layers, r0, logits_per_layer, k, expert_fns, shareds, wha
         r = r_out
 
 
-@pytest.mark.parametrize("M", [1, 3])
-def test_residual_stack_tiny(m, M):
+@pytest.mark.parametrize("M,scale,eps", [(1, 3.0, 1e-6), (3, 3.0, 1e-6), (1, 1e-3, 1e-6), (3, 1e-3, 2e-6),
+                                         (2, 1.0, 0.5)])
+def test_residual_stack_tiny(m, M, scale, eps):
     """Three layers with their own weights and logits: every layer's x is
-    bf16(RMSNorm(r)), its y matches the oracle on that x, and r advances by y."""
+    bf16(RMSNorm(r)), its y matches the oracle on that x, and r advances by y.
+    With r of about 1e-3 (mean square about 1e-6) or eps = 0.5 the epsilon
+    moves x far beyond the tolerance, so its place in the norm is checked."""
     shape = synth.TINY
     layers, efs, shs, lgs = [], [], [], []
     for L in range(3):
@@ -501,8 +517,8 @@ def test_residual_stack_tiny(m, M):
         efs.append(ef)
         shs.append(sh)
         lgs.append(synth.logits_f32(5, L, M, shape.E))
-    r0 = np.random.default_rng(7).standard_normal((M, shape.H)).astype(np.float32) * 3.0
-    _residual_stack(m, layers, r0, lgs, k, efs, shs, f"residual tiny M={M}")
+    r0 = (np.random.default_rng(7).standard_normal((M, shape.H)) * scale).astype(np.float32)
+    _residual_stack(m, layers, r0, lgs, k, efs, shs, f"residual tiny M={M} scale={scale} eps={eps}", eps=eps)
 
 
 def test_residual_layer_ling_m1(m, ling_layer):
@@ -529,16 +545,18 @@ def test_paths_share_one_workspace(m):
         check_acc(y32, ref_y, f"shared ws M={M} fused={fused}")
 
 
-def test_workspace_error_flag_stays_clear(m):
-    """No wait in any call so far gave up (the flag word follows the
-    per-block launch counters at the start of the workspace)."""
+def test_workspace_status_stays_clear(m):
+    """No wait in any call gave up: moe_ffn_workspace_status reports a clear
+    workspace after fused and two-call runs back to back."""
     W, xb, lg, ef, sh, k = _host_layer_case(m, synth.TINY, 2)
     ws = m.make_ffn_workspace(2, k, W.H, W.I, "cuda")
     for _ in range(3):
         _run_fused(m, W, xb, lg, k, ws)
         _run_ffn(m, W, xb, lg, k, ws)
-    flag = ws[4096 * 4:4096 * 4 + 4].cpu().numpy().view(np.uint32)[0]
-    assert flag == 0
+    flags = np.zeros(1, np.uint32)
+    assert m.lib.moe_ffn_workspace_status(m._ptr(ws), ws.numel(), flags.ctypes.data_as(
+        __import__("ctypes").POINTER(__import__("ctypes").c_uint32)), m._stream(ws)) == 0
+    assert flags[0] == 0
 
 
 def test_selftest_passes(m):
@@ -577,4 +595,4 @@ def test_graph_replays_match_eager(m, M):
         yb2, _ = m.moe_layer(W, x, lgt, k, ws)  # eager work between replays
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits_of(yb2), ref_b)
-    assert ws[4096 * 4:4096 * 4 + 4].cpu().numpy().view(np.uint32)[0] == 0
+    assert m.check_ffn_workspace(ws) == 0

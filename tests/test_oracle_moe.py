@@ -109,6 +109,12 @@ def test_moe_closed_form_constant_layer():
 def test_rmsnorm_hand_worked():
     r = np.array([[3.0, -4.0, 0.0, 0.0]])     # mean square 25/4, rms 2.5
     np.testing.assert_allclose(oracle.rmsnorm(r, eps=0.0), [[1.2, -1.6, 0.0, 0.0]], rtol=1e-15)
+    # eps inside the square root: 25/4 + 3/4 = 7, so the result is r / sqrt(7)
+    # (eps outside the root, 3/sqrt(6.25) + 0.75, or dropped, 3/2.5, both differ)
+    s7 = np.sqrt(7.0)
+    np.testing.assert_allclose(oracle.rmsnorm(r, eps=0.75), [[3.0 / s7, -4.0 / s7, 0.0, 0.0]], rtol=1e-15)
+    # eps dominating a tiny vector: r = 1e-3 * [1, 1], eps = 3e-6 -> r / sqrt(1e-6 + 3e-6) = r / 2e-3
+    np.testing.assert_allclose(oracle.rmsnorm(np.array([[1e-3, -1e-3]]), eps=3e-6), [[0.5, -0.5]], rtol=1e-13)
     r2 = np.random.default_rng(1).standard_normal((2, 64))
     np.testing.assert_allclose(oracle.rmsnorm(r2 * 7.0, eps=0.0), oracle.rmsnorm(r2, eps=0.0), rtol=1e-13)
 
