@@ -222,16 +222,44 @@ def moe_layer(weights, x, logits, k, workspace, y=None, y_f32=None, want_f32=Tru
     return y, y_f32
 
 
-def check_ffn_workspace(workspace):
+def check_ffn_workspace(workspace=None, device=None):
     """Wait for the stream and raise MoedecError (MOEDEC_ERR_TIMEOUT) when a
     cross-block wait of any FFN call on `workspace` gave up since the last
     check (those results are invalid; the library has cleared the workspace).
-    Returns the raw status word (0)."""
+    workspace=None checks the no-alloc scratch of `device` (default: current)."""
     flags = ctypes.c_uint32(0)
-    _need(workspace, torch.uint8, "workspace", 1)
-    _check(lib.moe_ffn_workspace_status(_ptr(workspace), workspace.numel(), ctypes.byref(flags),
-                                        _stream(workspace)))
+    if workspace is None:
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        _check(lib.moe_ffn_workspace_status(None, 0, ctypes.byref(flags), stream))
+    else:
+        _need(workspace, torch.uint8, "workspace", 1)
+        _check(lib.moe_ffn_workspace_status(_ptr(workspace), workspace.numel(), ctypes.byref(flags),
+                                            _stream(workspace)))
     return int(flags.value)
+
+
+def moe_layer_noalloc(weights, x, logits, k, y=None, y_f32=None, want_f32=True, ids=None, topk_w=None,
+                      dispatch=None):
+    """moe_layer without a workspace argument (moe_layer_mxfp4_noalloc): the
+    library's per-device scratch array serves as the workspace."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(logits, torch.float32, "logits", 2)
+    m_tokens, hidden = x.shape
+    if logits.shape[0] != m_tokens or logits.shape[1] != weights.E:
+        raise ValueError(f"logits must be [{m_tokens}][{weights.E}], got {tuple(logits.shape)}")
+    for t, dt, n in ((ids, torch.int32, "ids"), (topk_w, torch.float32, "topk_w"),
+                     (dispatch, torch.uint8, "dispatch")):
+        if t is not None:
+            _need(t, dt, n)
+    if y is None:
+        y = torch.empty((m_tokens, hidden), dtype=torch.bfloat16, device=x.device)
+    if y_f32 is None and want_f32:
+        y_f32 = torch.empty((m_tokens, hidden), dtype=torch.float32, device=x.device)
+    _check(lib.moe_layer_mxfp4_noalloc(ctypes.byref(weights.desc), _ptr(x), _ptr(logits), m_tokens, k,
+                                       _ptr(ids), _ptr(topk_w), _ptr(dispatch), _ptr(y), _ptr(y_f32),
+                                       _stream(x)))
+    return y, y_f32
 
 
 def moe_layer_rmsnorm(weights, r_in, logits, k, workspace, r_out=None, eps=1e-6, x_out=None,

@@ -95,6 +95,8 @@ SIGNATURES = {
                                         ctypes.c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]),
     "moe_ffn_workspace_status": (c_int, [c_void_p, c_size_t, ctypes.POINTER(c_uint32), c_void_p]),
+    "moe_layer_mxfp4_noalloc": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "lmhead_quant_fp8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p,
                                  ctypes.POINTER(LMHeadFP8Desc), c_void_p]),
     "lmhead_gemv_fp8": (c_int, [ctypes.POINTER(LMHeadFP8Desc), c_void_p, c_int, c_void_p, c_void_p]),

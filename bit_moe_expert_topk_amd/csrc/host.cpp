@@ -220,15 +220,21 @@ int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const f
 int moe_ffn_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* flags_out,
                              moedec_stream_t stream) {
     if (flags_out) *flags_out = 0;
-    if (!workspace) return fail(MOEDEC_ERR_NULL, "workspace is NULL");
-    if (workspace_bytes < moedec::kWsStatusOffset + sizeof(uint32_t))
+    if (workspace && workspace_bytes < moedec::kWsStatusOffset + sizeof(uint32_t))
         return fail(MOEDEC_ERR_WORKSPACE, "workspace %zu bytes holds no status word (need > %zu)",
                     workspace_bytes, moedec::kWsStatusOffset);
-    if (!aligned(workspace, 16)) return fail(MOEDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (workspace && !aligned(workspace, 16)) return fail(MOEDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
     if (int st = check_device()) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const size_t bytes = workspace_bytes;
+    size_t bytes = workspace_bytes;
+    if (!ws) {
+        void* p = nullptr;
+        if (hipError_t e = moedec::noalloc_scratch(s, &p))
+            return fail(MOEDEC_ERR_LAUNCH, "no-alloc scratch: %s", hipGetErrorString(e));
+        ws = static_cast<uint8_t*>(p);
+        bytes = moedec::kNoAllocScratchBytes;
+    }
     uint32_t word = 0;
     if (hipMemcpyAsync(&word, ws + moedec::kWsStatusOffset, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
@@ -245,6 +251,29 @@ int moe_ffn_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* 
     }
     g_last_error[0] = '\0';
     return MOEDEC_OK;
+}
+
+int moe_layer_mxfp4_noalloc(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int M,
+                            int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
+                            uint16_t* y_bf16, float* y_f32, moedec_stream_t stream) {
+    // argument checks as moe_layer_mxfp4, the workspace being the fixed scratch
+    if (int st = check_moe_core(w, x_bf16, M, k, y_bf16, y_f32, false)) return st;
+    const size_t need = moedec::ffn_layout(M, k, w->H, w->I).total;
+    if (need > moedec::kNoAllocScratchBytes)
+        return fail(MOEDEC_ERR_WORKSPACE, "M=%d k=%d H=%d I=%d needs %zu bytes of scratch > the %zu-byte "
+                    "no-alloc limit", M, k, w->H, w->I, need, moedec::kNoAllocScratchBytes);
+    if (!logits) return fail(MOEDEC_ERR_NULL, "logits is NULL");
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+        return fail(MOEDEC_ERR_ALIGN, "logits/topk_ids/topk_w must be 4-byte aligned");
+    if (!aligned(dispatch, 16)) return fail(MOEDEC_ERR_ALIGN, "dispatch must be 16-byte aligned");
+    if (int st = check_device()) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    if (hipError_t e = moedec::noalloc_scratch(s, &ws))
+        return fail(MOEDEC_ERR_LAUNCH, "no-alloc scratch: %s", hipGetErrorString(e));
+    return launched(moedec::launch_moe(*w, x_bf16, M, k, nullptr, logits, topk_ids, topk_w, dispatch,
+                                       y_bf16, y_f32, ws, s),
+                    "moe_layer_mxfp4_noalloc");
 }
 
 int moe_layer_rmsnorm_mxfp4(const moedec_moe_weights* w, const float* r_in, const float* logits, int M,

@@ -41,6 +41,13 @@ FfnLayout ffn_layout(int M, int k_max, int H, int I);
 // reads and clears it.
 constexpr size_t kWsStatusOffset = 4096 * sizeof(uint32_t);
 
+// The file-scope scratch array behind moe_layer_mxfp4_noalloc (noalloc.hip):
+// its size, and this device's address of it (looked up with
+// hipGetSymbolAddress on the first call on a device, zero-filled then on `s`
+// unless `s` is capturing a graph).
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+hipError_t noalloc_scratch(hipStream_t s, void** ptr);
+
 // Residual stream of a decode stack: x = bf16(RMSNorm(r_in)) replaces the x
 // input, and r_out = r_in + y is written next to y.
 struct ResidualArgs {

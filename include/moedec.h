@@ -16,7 +16,9 @@
  *
  * Conventions for every call
  *   - All pointers are DEVICE pointers unless marked "host".  The caller owns
- *     every buffer; the library never allocates or frees device memory.
+ *     every buffer; the library never allocates or frees device memory (the
+ *     one array it holds is the scratch of moe_layer_mxfp4_noalloc, part of
+ *     the library image).
  *   - Work is enqueued on `stream` (a hipStream_t, NULL = null stream) and the
  *     call returns without waiting (moedec_selftest and
  *     moe_ffn_workspace_status are the two calls that wait for the stream).  The return value reports host-side
@@ -240,13 +242,34 @@ int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const f
  *   MOEDEC_ERR_TIMEOUT  at least one did: the results of those calls are
  *                       invalid.  The workspace is zero-filled again before
  *                       the call returns, so it can be used right away.
- * workspace        the workspace
+ * workspace        the workspace, or NULL for the current device's scratch
+ *                  of moe_layer_mxfp4_noalloc (workspace_bytes then ignored)
  * workspace_bytes  its size in bytes
  * flags_out        host, may be NULL: the raw status word (0 when clear)
  * Like moedec_selftest, this call waits for the stream.
  * ---------------------------------------------------------------------- */
 int moe_ffn_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* flags_out,
                              moedec_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_layer_mxfp4 without a caller workspace, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  Same arguments and results as moe_layer_mxfp4
+ * minus the workspace, and the same kernels: the workspace is a file-scope
+ * device array of 4 MiB (every GPU the library runs on holds its own copy
+ * until the process ends), looked up and zero-filled on the first call on a
+ * device.  Nothing is allocated by this call, ever.
+ *   - Sizes whose workspace (moe_ffn_workspace_bytes(M, k, H, I)) exceeds
+ *     4 MiB are refused with MOEDEC_ERR_WORKSPACE; a Ling-shaped layer
+ *     (H 2560, I 768, k 8) needs 1.6 MB at M = 4.
+ *   - All calls on one GPU share the array: calls that overlap in time on
+ *     one GPU (two streams, two threads) race and give wrong results.
+ *     Order them on one stream.
+ *   - moe_ffn_workspace_status(NULL, 0, ...) checks and clears its status.
+ * ---------------------------------------------------------------------- */
+int moe_layer_mxfp4_noalloc(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits,
+                            int M, int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
+                            uint16_t* y_bf16, float* y_f32, moedec_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * One MoE layer of a decode stack, on the residual stream.  The model the

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
                  "lmhead_quant_fp8", "lmhead_gemv_fp8",
                  "lmhead_gemv_bf16", "lmhead_gemv_fp8_argmax", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
-                 "moedec_last_error", "moedec_abi_version", "moe_ffn_workspace_status"):
+                 "moedec_last_error", "moedec_abi_version", "moe_ffn_workspace_status",
+                 "moe_layer_mxfp4_noalloc"):
         assert want in names
 
 
@@ -228,15 +229,21 @@ def test_lmhead_descriptor_guards_format(m):
     assert L.lmhead_gemv_bf16(FAKE, 10, 2560, None, 1, FAKE, None) == -1
 
 
-def test_workspace_status_argument_checks(m):
-    """The status call rejects a NULL workspace, one too small to hold the
-    status word and a misaligned one on the host, before any device work."""
+def test_workspace_status_and_noalloc_argument_checks(m):
+    """The status call and the no-alloc layer reject bad arguments on the host,
+    before any device work: a workspace too small to hold the status word, a
+    misaligned one, a NULL weights descriptor, and a shape whose workspace
+    exceeds the 4 MiB no-alloc scratch."""
     L = m.lib
     FAKE = ctypes.c_void_p(1 << 20)
     flags = ctypes.c_uint32(7)
     assert L.moe_ffn_workspace_status(FAKE, 64, ctypes.byref(flags), None) == m._lib.MOEDEC_ERR_WORKSPACE
     assert flags.value == 0
     assert b"status word" in L.moedec_last_error()
-    assert L.moe_ffn_workspace_status(None, 1 << 20, None, None) == -1
     assert L.moe_ffn_workspace_status(ctypes.c_void_p((1 << 20) + 8), 1 << 20, None, None) == -2
+    assert L.moe_layer_mxfp4_noalloc(None, FAKE, FAKE, 1, 8, None, None, None, FAKE, None, None) == -1
+    w = m.MoEWeights(m.MOE_MAGIC, 512, 4096, 2048, *([1 << 20] * 8))
+    # M = 4, k = 32 at H 4096, I 2048: a workspace far beyond 4 MiB
+    assert L.moe_layer_mxfp4_noalloc(ctypes.byref(w), FAKE, FAKE, 4, 32, None, None, None, FAKE, None, None) == -5
+    assert b"no-alloc limit" in L.moedec_last_error()
     assert m.lib.moedec_status_string(-9) != b"unknown status"
