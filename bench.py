@@ -38,7 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = "moe_ffn_kernel_ling_m1_hbm_traffic.md"
+TRAFFIC_FILE = "moe_ffn_kernel_ling_m{M}_hbm_traffic.md"
 COPY_PROBE_ELEMS = 1 << 28                 # float32: 1 GiB read and 1 GiB written
 PMC_KERNEL = "moe_ffn_kernel"
 EXPERT_BYTES_LING = 3 * (768 * 2560 // 2 + 768 * 2560 // 32)     # 3,133,440 B
@@ -65,11 +65,13 @@ def parse_args(argv=None):
                     help="only run a 1 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short eager run for rocprofv3 --pmc: a calibration copy of known size, "
-                         "then fused M=1 layers")
+                         "then fused layers of --pmc-m tokens")
+    ap.add_argument("--pmc-m", type=int, default=1, choices=(1, 4), help="tokens per layer in --pmc-run")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of --pmc-run (FETCH_SIZE, then WRITE_SIZE) "
                          "into the markdown file given by --traffic-out")
-    ap.add_argument("--traffic-out", default=os.path.join(ROOT, "profiles", TRAFFIC_FILE))
+    ap.add_argument("--traffic-out", default=None,
+                    help="default: profiles/" + TRAFFIC_FILE.format(M="<M>"))
     return ap.parse_args(argv)
 
 
@@ -524,10 +526,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def pmc_run(m, torch, synth, dev, n_layers=8, passes=2):
+def pmc_run(m, torch, synth, dev, M=1, n_layers=8, passes=2):
     """Dispatches for the counter runs: three float32 copies of COPY_PROBE_ELEMS
     elements (an elementwise kernel with known bytes), then `passes` eager
-    passes of the fused M=1 layer over n_layers layers."""
+    passes of the fused layer (M tokens) over n_layers layers."""
     a = torch.ones(COPY_PROBE_ELEMS, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     for _ in range(3):
@@ -536,14 +538,31 @@ def pmc_run(m, torch, synth, dev, n_layers=8, passes=2):
     del a, b
     layers = make_layers(m, synth, n_layers, dev)
     k = synth.LING.k
-    xs, lgs = layer_inputs(synth, n_layers, 1, dev)
-    ws = m.make_ffn_workspace(1, k, synth.LING.H, synth.LING.I, dev)
-    y = torch.empty((1, synth.LING.H), dtype=torch.bfloat16, device=dev)
+    xs, lgs = layer_inputs(synth, n_layers, M, dev)
+    ws = m.make_ffn_workspace(M, k, synth.LING.H, synth.LING.I, dev)
+    y = torch.empty((M, synth.LING.H), dtype=torch.bfloat16, device=dev)
     for _ in range(passes):
         for L in range(n_layers):
             m.moe_layer(layers[L], xs[L], lgs[L], k, ws, y=y, want_f32=False)
     torch.cuda.synchronize()
-    log(f"pmc run: {passes} x {n_layers} fused M=1 layers")
+    m.check_ffn_workspace(ws)
+    log(f"pmc run: {passes} x {n_layers} fused M={M} layers")
+
+
+def algorithmic_layer_bytes(synth, M, n_layers=8):
+    """Bytes a fused layer must move, per layer of the counter run: every
+    active expert's packed bytes once (the distinct top-k experts of the M
+    tokens, plus the shared expert), the logits, x and y.  The expert count
+    comes from the same seeded logits (top-k by value; ties have probability
+    zero for these inputs)."""
+    import numpy as np
+    shape = synth.LING
+    out = []
+    for layer in range(n_layers):
+        lg = synth.logits_f32(0, layer, M, shape.E)
+        active = np.unique(np.argsort(-lg, axis=1, kind="stable")[:, :shape.k])
+        out.append((len(active) + 1) * EXPERT_BYTES_LING + M * shape.E * 4 + 2 * M * shape.H * 2)
+    return out
 
 
 def _counter_rows(run_dir, counter):
@@ -560,10 +579,12 @@ def _counter_rows(run_dir, counter):
     return rows
 
 
-def traffic_summary(fetch_dir, write_dir, out_path):
-    """Per-dispatch HBM bytes of the fused M=1 kernel: FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch), each scaled by bytes / counter of the calibration copy."""
+def traffic_summary(fetch_dir, write_dir, out_path, M):
+    """Per-dispatch HBM bytes of the fused layer kernel (M tokens): FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by bytes / counter of the
+    calibration copy, against the algorithmic bytes of the same layers."""
     import statistics
+    import synth
     copy_bytes = COPY_PROBE_ELEMS * 4
     res = {}
     for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -577,19 +598,26 @@ def traffic_summary(fetch_dir, write_dir, out_path):
                         "calibration_kib": statistics.median(cal), "factor": factor,
                         "bytes_per_dispatch": 1024 * statistics.mean(ker) * factor}
     total = res["FETCH_SIZE"]["bytes_per_dispatch"] + res["WRITE_SIZE"]["bytes_per_dispatch"]
-    summary = {"kernel": PMC_KERNEL + " (fused M=1 Ling layer)", "source_hash": kernel_source_hash(),
+    algo = statistics.mean(algorithmic_layer_bytes(synth, M))
+    summary = {"kernel": f"{PMC_KERNEL} (fused M={M} Ling layer)", "M": M, "source_hash": kernel_source_hash(),
                "fetch_bytes": round(res["FETCH_SIZE"]["bytes_per_dispatch"]),
                "write_bytes": round(res["WRITE_SIZE"]["bytes_per_dispatch"]),
-               "traffic_bytes": round(total)}
+               "traffic_bytes": round(total), "algorithmic_bytes": round(algo),
+               "traffic_over_algorithmic": round(total / algo, 4)}
+    def rel(d):
+        d = os.path.abspath(d)
+        return os.path.relpath(d, ROOT) if d.startswith(ROOT + os.sep) else d
+
+    fetch_dir, write_dir = rel(fetch_dir), rel(write_dir)
     lines = [
-        "# HBM traffic of the fused MoE layer kernel, Ling-shaped layer, M = 1",
+        f"# HBM traffic of the fused MoE layer kernel, Ling-shaped layer, M = {M}",
         "",
-        "Commands (from the repository root on the GPU host):",
+        "Commands (R = the repository root on the GPU host; the profiler runs from /tmp):",
         "",
         "```",
-        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py --pmc-run",
-        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py --pmc-run",
-        f"python3 bench.py --traffic-from {fetch_dir} {write_dir} --traffic-out <this file>",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d R/{fetch_dir} -o run -- python3 R/bench.py --pmc-run --pmc-m {M}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d R/{write_dir} -o run -- python3 R/bench.py --pmc-run --pmc-m {M}",
+        f"python3 bench.py --traffic-from {fetch_dir} {write_dir} --pmc-m {M} --traffic-out <this file>",
         "```",
         "",
         "Calibration: an elementwise float32 copy of 2^28 elements (1 GiB read, 1 GiB written);",
@@ -602,17 +630,20 @@ def traffic_summary(fetch_dir, write_dir, out_path):
         r = res[c]
         lines.append(f"| {c} | {r['kib_per_dispatch']:.1f} | {r['dispatches']} | {r['calibration_kib']:.0f} | "
                      f"{r['factor']:.4f} | {r['bytes_per_dispatch']:.0f} |")
-    lines += ["", f"Algorithmic bytes per launch: 9 experts x {EXPERT_BYTES_LING} B + activations.", "",
+    lines += ["",
+              f"Algorithmic bytes per launch (mean over the {len(algorithmic_layer_bytes(synth, M))} layers): "
+              f"(distinct active experts + 1 shared) x {EXPERT_BYTES_LING} B + logits + x + y = {algo:.0f} B; "
+              f"measured / algorithmic = {total / algo:.4f}.", "",
               "```json", json.dumps(summary), "```", ""]
     with open(out_path, "w") as f:
         f.write("\n".join(lines))
     print(json.dumps(summary), flush=True)
 
 
-def stored_traffic():
-    """Traffic bytes per launch from the committed counter summary, or None when
-    there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
+def stored_traffic(M=1):
+    """Traffic bytes per launch from the committed counter summary for M tokens,
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(M=M))
     try:
         with open(path) as f:
             text = f.read()
@@ -628,7 +659,8 @@ def stored_traffic():
 def main(argv=None):
     args = parse_args(argv)
     if args.traffic_from:
-        traffic_summary(args.traffic_from[0], args.traffic_from[1], args.traffic_out)
+        out = args.traffic_out or os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(M=args.pmc_m))
+        traffic_summary(args.traffic_from[0], args.traffic_from[1], out, args.pmc_m)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -646,7 +678,7 @@ def main(argv=None):
     import bit_moe_expert_topk_amd as m
     import synth
     if args.pmc_run:
-        pmc_run(m, torch, synth, dev)
+        pmc_run(m, torch, synth, dev, M=args.pmc_m)
         return 0
 
     log(f"device: {torch.cuda.get_device_name(0)}; layers {args.layers}, steps {args.steps}, warmup {args.warmup}")
@@ -676,7 +708,8 @@ def main(argv=None):
         cpu = cpu_baseline(synth, args.cpu_layers)
         log("cpu:", json.dumps(cpu))
 
-    traffic = stored_traffic()
+    traffic = stored_traffic(1)
+    traffic4 = stored_traffic(4)
     line = {
         "metric": "µs/MoE layer + achieved HBM GB/s (% of peak) at M=1 and M=4; LM-head GEMV GB/s",
         "value": round(r1["gbs"], 1),
@@ -712,6 +745,8 @@ def main(argv=None):
             "avg_launch_us": round(r1["us_per_layer"], 3),
         },
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "traffic_m4": None if traffic4 is None else {k: traffic4[k] for k in (
+            "fetch_bytes", "write_bytes", "traffic_bytes", "algorithmic_bytes", "traffic_over_algorithmic")},
         "extra": {"m1": r1, "m4": r4, "stack": stack, "router": router, "lmhead": lm,
                   "cpu": cpu},
     }
