@@ -38,12 +38,12 @@ from .formats import (
 )
 from .route import route_topk, dispatch_table, router_logits
 from .moe import expert_ffn, moe_layer, rmsnorm
-from .lmhead import lmhead_quant_fp8, lmhead_gemv_fp8, lmhead_gemv_bf16, lmhead_argmax
+from .lmhead import lmhead_quant_fp8, lmhead_gemv_fp8, lmhead_gemv_bf16, lmhead_argmax, lmhead_sample
 
 __all__ = [
     "e2m1_value", "e8m0_value", "mxfp4_dequant", "e4m3_value",
     "e4m3_encode_rne_sat", "bf16_round", "bf16_bits",
     "route_topk", "dispatch_table", "router_logits",
     "expert_ffn", "moe_layer", "rmsnorm",
-    "lmhead_quant_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "lmhead_argmax",
+    "lmhead_quant_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "lmhead_argmax", "lmhead_sample",
 ]

@@ -16,12 +16,29 @@ Readings where the pages are silent:
   * logits[m, v] = s_v * sum_k x[m,k] * e4m3(q[v,k]), no bias, no soft-cap,
     float32 out; the bf16 comparator is logits = W x.
 
+Sampling (the decode step's draw on these logits; the pages give the settings
+only -- temperature 0.6, top-p 0.95, top-k 29 [card results]).  Readings:
+  * candidates: the top_k logits of the row, ordered by (logit desc, index
+    asc), the order the greedy argmax uses;
+  * probabilities: softmax of logit / temperature over the candidates
+    (temperature > 0);
+  * nucleus: the shortest prefix of the candidates whose cumulative
+    probability reaches top_p (at least one token);
+  * draw: the nucleus renormalised to sum 1; with a uniform u in [0, 1) the
+    token is the first nucleus entry whose cumulative renormalised
+    probability exceeds u (the inverse of the cumulative distribution).
+    u is an input: both sides take it from synth's counter-based generator.
+
 Parity status: quantisation pinned (tests/test_oracle_lmhead.py) by rows whose
 absmax is 448 (scale exactly 1, codes equal to the direct E4M3 encoding), an
 all-zero row, the per-element error bound of E4M3, and torch's float8_e4m3fn
 cast for in-range values; the GEMVs by one-hot activations selecting a single
 column times its row scale (orientation and scale) and x = 0; the greedy
-argmax by hand-worked rows with ties and signed zeros and by a library sort.
+argmax by hand-worked rows with ties and signed zeros and by a library sort;
+the sampling by hand-worked distributions (inverse-CDF boundaries, nucleus cut,
+top-k cut, temperature), the top_k = 1 and vanishing-temperature limits
+(argmax), and by the interval each token's draws occupy, which equals its
+renormalised probability computed by an independent loop.
 """
 
 import numpy as np
@@ -67,3 +84,33 @@ def lmhead_gemv_bf16(w, x):
     w = np.asarray(w, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     return x @ w.T
+
+
+def lmhead_sample(logits, u, temperature, top_p, top_k):
+    """Sampled token of each row of logits [M][V] (float64 arithmetic), int64 [M].
+
+    u [M] uniforms in [0, 1); temperature > 0; 0 < top_p <= 1; top_k >= 1.
+    Follows the readings in the module docstring: top_k candidates by
+    (logit desc, index asc), softmax of logit / temperature over them, the
+    shortest prefix reaching top_p, renormalised, inverse-CDF draw at u.
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    assert temperature > 0 and 0 < top_p <= 1 and top_k >= 1
+    out = np.empty(logits.shape[0], dtype=np.int64)
+    for m in range(logits.shape[0]):
+        row = logits[m]
+        idx = np.arange(row.shape[0])
+        order = np.lexsort((idx, -row))                    # logit desc, then index asc
+        cand = order[:min(top_k, row.shape[0])]
+        z = row[cand] / temperature
+        p = np.exp(z - z[0])                               # z[0] is the largest
+        p = p / p.sum()
+        cum = np.cumsum(p)
+        n_keep = int(np.searchsorted(cum, top_p, side="left")) + 1   # first cum >= top_p
+        n_keep = min(n_keep, cand.shape[0])
+        q = p[:n_keep] / cum[n_keep - 1]
+        cq = np.cumsum(q)
+        j = int(np.searchsorted(cq, u[m], side="right"))   # first cq > u
+        out[m] = cand[min(j, n_keep - 1)]
+    return out

@@ -20,7 +20,8 @@ Two generators are used:
   400M-element LM head), scaled, and rounded to bf16 by torch's RNE cast or
   kept as float32.
 
-Stream identifiers keep every tensor independent:
+Stream identifiers keep every tensor independent (the sampling draws of
+decode step t use stream 2^40 + t of the SplitMix64 generator):
   MXFP4 tensor (layer, expert, matrix, part):
       ((layer * 1025 + expert) * 3 + matrix) * 2 + part
   matrix 0 = gate, 1 = up, 2 = down; part 0 = codes, 1 = scales;
@@ -196,6 +197,18 @@ def lmhead_weight_bf16(seed, vocab, hidden, std=0.02, row_start=0, n_rows=None):
         if r1 >= row_start + n_rows:
             break
     return out
+
+
+SAMPLING_STREAM_BASE = 1 << 40
+
+
+def sampling_uniforms(seed, step, m_tokens):
+    """float32 [m_tokens] uniforms in [0, 1) for the draw of decode step `step`:
+    output m of SplitMix64 stream SAMPLING_STREAM_BASE + step, top 24 bits
+    divided by 2^24 (exact in float32, never 1.0)."""
+    state = stream_state(seed, SAMPLING_STREAM_BASE + step)
+    words = splitmix_outputs(state, np.arange(m_tokens, dtype=np.uint64))
+    return ((words >> np.uint64(40)).astype(np.float64) / float(1 << 24)).astype(np.float32)
 
 
 def lmhead_x_bf16(seed, m_tokens, hidden):

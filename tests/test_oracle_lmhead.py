@@ -86,3 +86,111 @@ def test_argmax_matches_a_stable_sort():
     lg = rng.integers(-3, 4, size=(6, 50)).astype(np.float64)      # many ties
     order = [np.lexsort((np.arange(50), -row))[0] for row in lg]   # largest, then lowest index
     np.testing.assert_array_equal(oracle.lmhead_argmax(lg), order)
+
+
+# ---------------------------------------------------------------- sampling
+
+LN1234 = np.log(np.array([[1.0, 2.0, 3.0, 4.0]]))       # softmax (T = 1): 0.1, 0.2, 0.3, 0.4
+
+
+def _sample(lg, u, t=1.0, p=1.0, k=4):
+    return int(oracle.lmhead_sample(lg, np.array([u]), t, p, k)[0])
+
+
+def test_sample_inverse_cdf_hand_worked():
+    # candidates in order 3, 2, 1, 0 with probabilities 0.4, 0.3, 0.2, 0.1:
+    # cumulative 0.4, 0.7, 0.9, 1.0
+    for u, tok in ((0.0, 3), (0.39, 3), (0.41, 2), (0.69, 2), (0.71, 1), (0.89, 1), (0.91, 0), (0.999, 0)):
+        assert _sample(LN1234, u) == tok, u
+
+
+def test_sample_nucleus_and_top_k_cuts():
+    # top_p 0.65: the prefix 0.4 + 0.3 reaches it; renormalised 4/7, 3/7
+    assert _sample(LN1234, 0.5, p=0.65) == 3
+    assert _sample(LN1234, 0.58, p=0.65) == 2
+    assert _sample(LN1234, 0.999, p=0.65) == 2
+    # top_p 0.35: the first token alone reaches it
+    for u in (0.0, 0.5, 0.999):
+        assert _sample(LN1234, u, p=0.35) == 3
+    # top_k 2 with top_p 1: the same two tokens, 4/7 and 3/7
+    assert _sample(LN1234, 0.5, k=2) == 3
+    assert _sample(LN1234, 0.58, k=2) == 2
+    assert _sample(LN1234, 0.999, k=2) == 2
+
+
+def test_sample_temperature():
+    # T = 0.5 squares the probabilities: 16, 9, 4, 1 over 30 -> cumulative 16/30, 25/30, 29/30
+    assert _sample(LN1234, 0.5, t=0.5) == 3
+    assert _sample(LN1234, 0.55, t=0.5) == 2
+    assert _sample(LN1234, 0.84, t=0.5) == 1
+    assert _sample(LN1234, 0.97, t=0.5) == 0
+    # T = 2 takes square roots: 2, 1.732, 1.414, 1 over their sum 6.146 ->
+    # cumulative 0.3254, 0.6072, 0.8373
+    assert _sample(LN1234, 0.32, t=2.0) == 3
+    assert _sample(LN1234, 0.33, t=2.0) == 2
+    assert _sample(LN1234, 0.60, t=2.0) == 2
+    assert _sample(LN1234, 0.61, t=2.0) == 1
+    assert _sample(LN1234, 0.84, t=2.0) == 0
+
+
+def test_sample_limits_reduce_to_argmax():
+    rng = np.random.default_rng(5)
+    lg = rng.normal(size=(5, 40))
+    am = oracle.lmhead_argmax(lg)
+    for u in (0.0, 0.3, 0.999):
+        uu = np.full(5, u)
+        np.testing.assert_array_equal(oracle.lmhead_sample(lg, uu, 0.6, 0.95, 1), am)        # top_k = 1
+        np.testing.assert_array_equal(oracle.lmhead_sample(lg, uu, 1e-6, 0.95, 29), am)     # T -> 0
+        np.testing.assert_array_equal(oracle.lmhead_sample(lg, uu, 1.0, 1e-9, 29), am)      # top_p -> 0
+
+
+def test_sample_ties_follow_index_order():
+    eq = np.array([[1.0, 1.0, 1.0, 1.0]])            # 0.25 each, candidates 0, 1, 2, 3
+    for u, tok in ((0.1, 0), (0.3, 1), (0.6, 2), (0.8, 3)):
+        assert _sample(eq, u) == tok
+    sz = np.array([[-0.0, 0.0, -1.0]])               # +0 and -0 tie: index 0 first
+    assert _sample(sz, 0.0, k=3) == 0
+
+
+def _expected_distribution(row, t, top_p, top_k):
+    """The renormalised nucleus written as a plain loop: (token, probability)
+    pairs in candidate order."""
+    cand = sorted(range(len(row)), key=lambda i: (-row[i], i))[:top_k]
+    w = [np.exp((row[i] - row[cand[0]]) / t) for i in cand]
+    tot = sum(w)
+    keep, acc = [], 0.0
+    for i, wi in zip(cand, w):
+        keep.append((i, wi / tot))
+        acc += wi / tot
+        if acc >= top_p:
+            break
+    s = sum(q for _, q in keep)
+    return [(i, q / s) for i, q in keep]
+
+
+def test_sample_draw_intervals_match_probabilities():
+    """Each token's draws form one interval of u whose length is its
+    renormalised probability: scan u on a grid and compare with the loop."""
+    rng = np.random.default_rng(11)
+    grid = (np.arange(200000) + 0.5) / 200000
+    for trial in range(4):
+        row = rng.normal(size=30) * 2
+        t, top_p, top_k = [(0.6, 0.95, 29), (1.0, 0.5, 10), (0.3, 0.99, 5), (2.0, 0.9, 30)][trial]
+        toks = oracle.lmhead_sample(np.repeat(row[None, :], grid.shape[0], axis=0), grid, t, top_p, top_k)
+        dist = _expected_distribution(row, t, top_p, top_k)
+        # tokens appear in candidate order, each over one run of u
+        runs = [toks[0]] + [b for a, b in zip(toks[:-1], toks[1:]) if a != b]
+        assert runs == [i for i, _ in dist]
+        for i, q in dist:
+            assert abs(np.mean(toks == i) - q) < 2e-5, (trial, i)
+
+
+def test_sampling_uniforms_are_in_range_and_counter_based():
+    u = synth.sampling_uniforms(3, 7, 4)
+    assert u.dtype == np.float32 and ((u >= 0) & (u < 1)).all()
+    np.testing.assert_array_equal(u, synth.sampling_uniforms(3, 7, 4))
+    assert not np.array_equal(u, synth.sampling_uniforms(3, 8, 4))
+    # u * 2^24 is the top 24 bits of the stream's outputs
+    st = synth.stream_state(3, synth.SAMPLING_STREAM_BASE + 7)
+    words = synth.splitmix_outputs(st, np.arange(4, dtype=np.uint64))
+    np.testing.assert_array_equal((u.astype(np.float64) * (1 << 24)).astype(np.uint64), words >> np.uint64(40))
