@@ -342,18 +342,27 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
         g8 = capture(torch, lambda: [m.lmhead_gemv_fp8(head, x, out=lo) for _ in range(reps)])
         gb = capture(torch, lambda: [m.lmhead_gemv_bf16(w, x, out=lo) for _ in range(reps)])
         # greedy decode: FP8 GEMV with the argmax epilogue, logits not written
-        aws = torch.empty(max(8, m.lib.lmhead_argmax_workspace_bytes(V, M)), dtype=torch.uint8, device=dev)
+        aws = m.make_lmhead_workspace(V, M, dev)
         ids = torch.empty(M, dtype=torch.int32, device=dev)
         m.lmhead_argmax_fp8(head, x, workspace=aws, ids=ids)
         ga = capture(torch, lambda: [m.lmhead_argmax_fp8(head, x, workspace=aws, ids=ids) for _ in range(reps)])
+        # sampled decode (temperature 0.6, top-p 0.95, top-k 29): logits written,
+        # candidates and draw in the same launch
+        u = torch.from_numpy(synth.sampling_uniforms(0, 0, M)).to(dev)
+        m.lmhead_sample_fp8(head, x, u, 0.6, 0.95, 29, workspace=aws, ids=ids, logits=lo)
+        gs = capture(torch, lambda: [m.lmhead_sample_fp8(head, x, u, 0.6, 0.95, 29, workspace=aws, ids=ids,
+                                                         logits=lo) for _ in range(reps)])
         g8.replay()
         gb.replay()
         ga.replay()
+        gs.replay()
         ms8 = t.run(g8.replay) / reps
         msb = t.run(gb.replay) / reps
         msa = t.run(ga.replay) / reps
+        mss = t.run(gs.replay) / reps
         out[f"fp8_argmax_m{M}_us"] = 1e3 * msa
         out[f"fp8_argmax_m{M}_gbs"] = (V * H + V * 4 + M * H * 2) / (1e6 * msa)
+        out[f"fp8_sample_m{M}_us"] = 1e3 * mss
         b8 = V * H + V * 4 + M * H * 2 + M * V * 4
         bb = V * H * 2 + M * H * 2 + M * V * 4
         out[f"fp8_m{M}_us"] = 1e3 * ms8
@@ -363,7 +372,7 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
         out[f"bf16_m{M}_us"] = 1e3 * msb
         out[f"bf16_m{M}_gbs"] = bb / (1e6 * msb)
         out[f"bf16_m{M}_frac_of_peak"] = bb / (1e6 * msb) / PEAK_HBM_GBS
-        del g8, gb, ga
+        del g8, gb, ga, gs
     del head, w
     torch.cuda.empty_cache()
     return out
@@ -514,15 +523,26 @@ def copy_probe(torch, dev):
 # HBM traffic from rocprofv3 counters
 
 def kernel_source_hash():
-    """Hash of the HIP sources and ABI header that define the measured kernel."""
+    """Hash of what defines the measured kernel's code: its source file, the
+    device headers it includes and the structure definitions of the ABI
+    header that it reads (declarations of other entry points do not count)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_moe_expert_topk_amd", "csrc")
-    paths = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
-    paths.append(os.path.join(ROOT, "include", "moedec.h"))
-    for path in paths:
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    used = set()
+    for name in ("ffn_mxfp4.hip", "device_common.h", "route_device.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            text = f.read()
+        h.update(name.encode() + b"\0" + text)
+        used.update(re.findall(r"MOEDEC_\w+", text.decode()))
+    with open(os.path.join(ROOT, "include", "moedec.h")) as f:
+        header = f.read()
+    for block in re.findall(r"typedef struct[^}]*\}[^;]*;", header):
+        h.update(block.encode() + b"\0")
+    for name, value in sorted(re.findall(r"#define (MOEDEC_\w+)\s+([^\n/]*)", header)):
+        if name in used:
+            h.update(f"{name}={value.strip()}".encode() + b"\0")
     return h.hexdigest()[:16]
 
 
@@ -763,6 +783,8 @@ def main(argv=None):
     if lm is not None:
         line["lmhead_fp8_gbs_m1"] = round(lm["fp8_m1_gbs"], 1)
         line["lmhead_fp8_argmax_us_m1"] = round(lm["fp8_argmax_m1_us"], 2)
+        line["lmhead_fp8_sample_us_m1"] = round(lm["fp8_sample_m1_us"], 2)
+        line["lmhead_fp8_sample_us_m4"] = round(lm["fp8_sample_m4_us"], 2)
         line["lmhead_fp8_gbs_m4"] = round(lm["fp8_m4_gbs"], 1)
         line["lmhead_bf16_gbs_m1"] = round(lm["bf16_m1_gbs"], 1)
     print(json.dumps(line), flush=True)

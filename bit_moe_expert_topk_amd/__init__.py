@@ -319,22 +319,64 @@ def lmhead_gemv_fp8(head, x, out=None):
     return out
 
 
+def make_lmhead_workspace(V, m_tokens, device):
+    """Zero-filled workspace for lmhead_argmax_fp8 / lmhead_sample_fp8 of one
+    head (per-block launch counts and the published keys; every call leaves it
+    ready for the next)."""
+    need = lib.lmhead_argmax_workspace_bytes(V, m_tokens)
+    if need == 0:
+        raise MoedecError(-3, f"no LM-head workspace for V={V}, M={m_tokens}")
+    return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
 def lmhead_argmax_fp8(head, x, workspace=None, ids=None, logits=None):
     """Greedy token ids [M] int32 from the FP8 head (lmhead_gemv_fp8_argmax);
-    logits [M][V] float32 are written too when a tensor is given."""
+    logits [M][V] float32 are written too when a tensor is given.  A workspace
+    passed in must come from make_lmhead_workspace (zero-filled once)."""
     _need(x, torch.bfloat16, "x", 2)
     m_tokens = x.shape[0]
-    need = lib.lmhead_argmax_workspace_bytes(head.V, m_tokens)
     if workspace is None:
-        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
+        workspace = make_lmhead_workspace(head.V, m_tokens, x.device)
     _need(workspace, torch.uint8, "workspace", 1)
     if ids is None:
         ids = torch.empty(m_tokens, dtype=torch.int32, device=x.device)
+    _need(ids, torch.int32, "ids", 1)
     if logits is not None:
         _need(logits, torch.float32, "logits", 2)
+    if ids.numel() != m_tokens or (logits is not None and tuple(logits.shape) != (m_tokens, head.V)):
+        raise ValueError(f"ids [{m_tokens}] and logits [{m_tokens}][{head.V}] needed")
     _check(lib.lmhead_gemv_fp8_argmax(ctypes.byref(head.desc), _ptr(x), m_tokens, _ptr(logits), _ptr(ids),
                                       _ptr(workspace), workspace.numel(), _stream(x)))
     return ids
+
+
+def lmhead_sample_fp8(head, x, u, temperature=0.6, top_p=0.95, top_k=29, workspace=None, ids=None,
+                      logits=None, want_logits=True):
+    """Sampled token ids [M] int32 from the FP8 head (lmhead_gemv_fp8_sample):
+    top_k candidates, softmax at `temperature`, the top_p nucleus, drawn at the
+    uniforms u [M] float32 (device).  Returns (ids, logits [M][V] float32, or
+    None when want_logits is false and no logits tensor is given)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(u, torch.float32, "u", 1)
+    m_tokens = x.shape[0]
+    if workspace is None:
+        workspace = make_lmhead_workspace(head.V, m_tokens, x.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    if ids is None:
+        ids = torch.empty(m_tokens, dtype=torch.int32, device=x.device)
+    if logits is None and want_logits:
+        logits = torch.empty((m_tokens, head.V), dtype=torch.float32, device=x.device)
+    if logits is not None:
+        _need(logits, torch.float32, "logits", 2)
+        if tuple(logits.shape) != (m_tokens, head.V):
+            raise ValueError(f"logits [{m_tokens}][{head.V}] needed")
+    _need(ids, torch.int32, "ids", 1)
+    if u.numel() != m_tokens or ids.numel() != m_tokens:
+        raise ValueError(f"u [{m_tokens}] and ids [{m_tokens}] needed")
+    _check(lib.lmhead_gemv_fp8_sample(ctypes.byref(head.desc), _ptr(x), m_tokens, float(temperature),
+                                      float(top_p), int(top_k), _ptr(u), _ptr(logits), _ptr(ids),
+                                      _ptr(workspace), workspace.numel(), _stream(x)))
+    return ids, logits
 
 
 def selftest(device="cuda"):

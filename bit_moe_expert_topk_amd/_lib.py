@@ -21,6 +21,9 @@ MOEDEC_ERR_LAUNCH = -6
 MOEDEC_ERR_DEVICE = -7
 MOEDEC_ERR_SELFTEST = -8
 MOEDEC_ERR_TIMEOUT = -9
+MOEDEC_ERR_ARG = -10
+MOEDEC_MAX_SAMPLE_K = 32
+MOEDEC_MAX_EPILOGUE_V = 1 << 18
 
 MAX_M = 4
 MAX_K = 32
@@ -34,6 +37,7 @@ FMT_E4M3FN_ROWSCALE_F32 = 1
 c_void_p = ctypes.c_void_p
 c_int = ctypes.c_int
 c_size_t = ctypes.c_size_t
+c_float = ctypes.c_float
 c_uint32 = ctypes.c_uint32
 c_int32 = ctypes.c_int32
 
@@ -81,6 +85,8 @@ SIGNATURES = {
     "lmhead_argmax_workspace_bytes": (c_size_t, [c_int, c_int]),
     "lmhead_gemv_fp8_argmax": (c_int, [ctypes.POINTER(LMHeadFP8Desc), c_void_p, c_int, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
+    "lmhead_gemv_fp8_sample": (c_int, [ctypes.POINTER(LMHeadFP8Desc), c_void_p, c_int, c_float, c_float, c_int,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_router_logits_bf16": (c_int, [c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p]),
     "moedec_mxfp4_packed_sizes": (c_int, [c_int, c_int, ctypes.POINTER(MXFP4Sizes)]),
     "moe_pack_gateup_mxfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,

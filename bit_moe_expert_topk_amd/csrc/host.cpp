@@ -78,6 +78,7 @@ const char* moedec_status_string(int status) {
         case MOEDEC_ERR_LAUNCH: return "kernel launch failed";
         case MOEDEC_ERR_DEVICE: return "device is not gfx950";
         case MOEDEC_ERR_SELFTEST: return "self-test mismatch";
+        case MOEDEC_ERR_ARG: return "argument out of range";
         case MOEDEC_ERR_TIMEOUT: return "a cross-block wait gave up (results invalid)";
         default: return "unknown status";
     }
@@ -359,13 +360,15 @@ int lmhead_gemv_bf16(const uint16_t* w_bf16, int V, int H, const uint16_t* x_bf1
 }
 
 size_t lmhead_argmax_workspace_bytes(int V, int M) {
-    if (V < 1 || M < 1 || M > MOEDEC_MAX_M) return 0;
-    return moedec::lmhead_argmax_keys_bytes(V, M);
+    if (V < 1 || V > MOEDEC_MAX_EPILOGUE_V || M < 1 || M > MOEDEC_MAX_M) return 0;
+    return moedec::lmhead_epilogue_bytes(V, M);
 }
 
-int lmhead_gemv_fp8_argmax(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M, float* logits,
-                           int32_t* token_ids, void* workspace, size_t workspace_bytes,
-                           moedec_stream_t stream) {
+namespace {
+
+// Checks shared by the greedy and the sampling epilogue calls.
+int check_epilogue(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M, const float* logits,
+                   const int32_t* token_ids, const void* workspace, size_t workspace_bytes) {
     if (!head) return fail(MOEDEC_ERR_NULL, "head descriptor is NULL");
     if (head->magic != MOEDEC_LMHEAD_MAGIC)
         return fail(MOEDEC_ERR_FORMAT, "head magic 0x%08x is not an FP8 LM-head descriptor",
@@ -376,21 +379,50 @@ int lmhead_gemv_fp8_argmax(const moedec_lmhead_fp8* head, const uint16_t* x_bf16
     if (!head->codes || !head->row_scale || !x_bf16 || !token_ids || !workspace)
         return fail(MOEDEC_ERR_NULL, "codes, row_scale, x, token_ids or workspace is NULL");
     if (M < 1 || M > MOEDEC_MAX_M) return fail(MOEDEC_ERR_SHAPE, "M=%d not in 1..%d", M, MOEDEC_MAX_M);
-    if (head->V < 1) return fail(MOEDEC_ERR_SHAPE, "V=%d < 1", head->V);
+    if (head->V < 1 || head->V > MOEDEC_MAX_EPILOGUE_V)
+        return fail(MOEDEC_ERR_SHAPE, "V=%d not in 1..%d", head->V, MOEDEC_MAX_EPILOGUE_V);
     if (head->H < 16 || head->H > 4096 || head->H % 16)
         return fail(MOEDEC_ERR_SHAPE, "H=%d: need 16 <= H <= 4096 and H %% 16 == 0", head->H);
     if (!aligned(head->codes, 16) || !aligned(head->row_scale, 4) || !aligned(x_bf16, 4) ||
         !aligned(logits, 4) || !aligned(token_ids, 4) || !aligned(workspace, 8))
         return fail(MOEDEC_ERR_ALIGN,
                     "codes 16-byte, row_scale/x/logits/token_ids 4-byte, workspace 8-byte alignment needed");
-    const size_t need = moedec::lmhead_argmax_keys_bytes(head->V, M);
+    const size_t need = moedec::lmhead_epilogue_bytes(head->V, M);
     if (workspace_bytes < need)
         return fail(MOEDEC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    return MOEDEC_OK;
+}
+
+}  // namespace
+
+int lmhead_gemv_fp8_argmax(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M, float* logits,
+                           int32_t* token_ids, void* workspace, size_t workspace_bytes,
+                           moedec_stream_t stream) {
+    if (int st = check_epilogue(head, x_bf16, M, logits, token_ids, workspace, workspace_bytes)) return st;
     if (int st = check_device()) return st;
+    const moedec::Fp8Epilogue ep{workspace, token_ids, nullptr, 1.f, 1.f, 1};
     return launched(moedec::launch_gemv_fp8(head->codes, head->row_scale, head->V, head->H, x_bf16, M,
-                                            logits, static_cast<hipStream_t>(stream),
-                                            static_cast<uint64_t*>(workspace), token_ids),
+                                            logits, static_cast<hipStream_t>(stream), &ep),
                     "lmhead_gemv_fp8_argmax");
+}
+
+int lmhead_gemv_fp8_sample(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M,
+                           float temperature, float top_p, int top_k, const float* u, float* logits,
+                           int32_t* token_ids, void* workspace, size_t workspace_bytes,
+                           moedec_stream_t stream) {
+    if (int st = check_epilogue(head, x_bf16, M, logits, token_ids, workspace, workspace_bytes)) return st;
+    if (!u) return fail(MOEDEC_ERR_NULL, "u is NULL");
+    if (!aligned(u, 4)) return fail(MOEDEC_ERR_ALIGN, "u must be 4-byte aligned");
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return fail(MOEDEC_ERR_ARG, "temperature %g: need a finite value > 0", (double)temperature);
+    if (!(top_p > 0.f && top_p <= 1.f)) return fail(MOEDEC_ERR_ARG, "top_p %g not in (0, 1]", (double)top_p);
+    if (top_k < 1 || top_k > MOEDEC_MAX_SAMPLE_K || top_k > head->V)
+        return fail(MOEDEC_ERR_ARG, "top_k=%d not in 1..min(%d, V=%d)", top_k, MOEDEC_MAX_SAMPLE_K, head->V);
+    if (int st = check_device()) return st;
+    const moedec::Fp8Epilogue ep{workspace, token_ids, u, temperature, top_p, top_k};
+    return launched(moedec::launch_gemv_fp8(head->codes, head->row_scale, head->V, head->H, x_bf16, M,
+                                            logits, static_cast<hipStream_t>(stream), &ep),
+                    "lmhead_gemv_fp8_sample");
 }
 
 int moe_router_logits_bf16(const uint16_t* w_router, int E, int H, const uint16_t* x_bf16, int M,
@@ -448,7 +480,7 @@ StLayout st_layout() {
     L.ws = take(moedec::ffn_layout(1, kStK, kStH, kStI).total);
     L.lw = take(kStV * kStHv * 2); L.lcodes = take(kStV * kStHv); L.lscale = take(kStV * 4);
     L.lx = take(kStHv * 2); L.llogits = take(kStV * 4); L.lid = take(4);
-    L.lws = take(moedec::lmhead_argmax_keys_bytes(kStV, 1));
+    L.lws = take(moedec::lmhead_epilogue_bytes(kStV, 1));
     L.total = (off + 255) & ~(size_t)255;
     return L;
 }
@@ -496,7 +528,8 @@ int moedec_selftest(void* scratch, size_t scratch_bytes, moedec_stream_t stream)
     for (const Copy& c : copies)
         if (hipMemcpyAsync(d + c.at, c.p, c.n, hipMemcpyHostToDevice, s) != hipSuccess)
             return fail(MOEDEC_ERR_LAUNCH, "self-test: copy to scratch failed");
-    if (hipMemsetAsync(d + L.ws, 0, moedec::ffn_layout(1, kStK, kStH, kStI).total, s) != hipSuccess)
+    if (hipMemsetAsync(d + L.ws, 0, moedec::ffn_layout(1, kStK, kStH, kStI).total, s) != hipSuccess ||
+        hipMemsetAsync(d + L.lws, 0, moedec::lmhead_epilogue_bytes(kStV, 1), s) != hipSuccess)
         return fail(MOEDEC_ERR_LAUNCH, "self-test: workspace clear failed");
     int st;
     if ((st = moe_pack_gateup_mxfp4(d + L.gate_c, d + L.gate_s, d + L.up_c, d + L.up_s, kStE, kStH, kStI,
@@ -519,7 +552,7 @@ int moedec_selftest(void* scratch, size_t scratch_bytes, moedec_stream_t stream)
                                reinterpret_cast<float*>(d + L.lscale), &head, stream)) ||
         (st = lmhead_gemv_fp8_argmax(&head, reinterpret_cast<uint16_t*>(d + L.lx), 1,
                                      reinterpret_cast<float*>(d + L.llogits), reinterpret_cast<int32_t*>(d + L.lid),
-                                     d + L.lws, moedec::lmhead_argmax_keys_bytes(kStV, 1), stream)))
+                                     d + L.lws, moedec::lmhead_epilogue_bytes(kStV, 1), stream)))
         return st;
     int32_t ids[kStK], lid = -1;
     float wts[kStK], y32[kStH], lsc[kStV], llg[kStV];

@@ -69,12 +69,21 @@ hipError_t launch_expert_ffn(const moedec_moe_weights& w, const uint16_t* x, int
 
 hipError_t launch_lmhead_quant(const uint16_t* w, int V, int H, uint8_t* codes, float* rs,
                                hipStream_t s);
-// keys / ids non-null: the greedy epilogue (per-wave argmax keys, then one
-// reducing block writes ids[M]); logits may then be null.
+// The FP8 GEMV's epilogue, run by the block launched last: the greedy token
+// (u null or top_k = 1) or a sampled one (temperature, top_p, top_k <= 32,
+// u[M] in [0, 1)).  V <= 2^18.  workspace: lmhead_epilogue_bytes(V, M) bytes,
+// zero-filled before the first call, left ready for the next.
+struct Fp8Epilogue {
+    void* workspace;
+    int32_t* ids;
+    const float* u;
+    float temperature, top_p;
+    int top_k;
+};
 hipError_t launch_gemv_fp8(const uint8_t* codes, const float* rs, int V, int H,
                            const uint16_t* x, int M, float* logits, hipStream_t s,
-                           uint64_t* keys = nullptr, int32_t* ids = nullptr);
-size_t lmhead_argmax_keys_bytes(int V, int M);
+                           const Fp8Epilogue* ep = nullptr);
+size_t lmhead_epilogue_bytes(int V, int M);
 hipError_t launch_gemv_bf16(const uint16_t* w, int V, int H, const uint16_t* x, int M,
                             float* logits, hipStream_t s);
 

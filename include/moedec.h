@@ -56,6 +56,7 @@ typedef void* moedec_stream_t;
 #define MOEDEC_ERR_DEVICE    -7   /* the current device is not a gfx950 GPU */
 #define MOEDEC_ERR_SELFTEST  -8   /* moedec_selftest: a result differs from its closed form */
 #define MOEDEC_ERR_TIMEOUT   -9   /* moe_ffn_workspace_status: a cross-block wait gave up */
+#define MOEDEC_ERR_ARG      -10   /* a scalar argument is outside its range (sampling settings) */
 
 /* Limits. */
 #define MOEDEC_MAX_M      4       /* tokens per call: 1, or the 4-token verify window [card #3] */
@@ -337,19 +338,61 @@ int lmhead_gemv_fp8(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M
 /*
  * Greedy decode on the FP8 head [card results: the measured decode samples
  * the next token from these logits with temperature 0.6, top-p 0.95, top-k 29;
- * greedy choice is the temperature-0 case]: the GEMV of lmhead_gemv_fp8 followed by
+ * greedy choice is the temperature-0 case]: the GEMV of lmhead_gemv_fp8 and
  * token_ids[m] = the row v of the largest logits[m][v], the lowest such row
  * on ties (+0.0 and -0.0 are equal), without a pass over the logits: each
- * wave keeps the best (logit, row) of its rows and one reducing block picks
- * among the waves.  Two launches on `stream`.
+ * block publishes the best (logit, row) of its rows, and the block launched
+ * last waits for the others' and picks among them.  One launch on `stream`.
+ * V <= MOEDEC_MAX_EPILOGUE_V, else MOEDEC_ERR_SHAPE.
  * logits      [M][V] float32, optional (NULL: not written)
- * token_ids   [M] int32, 4-byte aligned
- * workspace   >= lmhead_argmax_workspace_bytes(V, M) bytes, 8-byte aligned
- *             (per-wave keys; no initial contents needed)
+ * token_ids   [M] int32, 4-byte aligned.  -1 means the polling block gave up
+ *             waiting for another block's words (not expected on a working
+ *             device; the call's tokens are then invalid).
+ * workspace   >= lmhead_argmax_workspace_bytes(V, M) bytes, 8-byte aligned,
+ *             ZERO-FILLED ONCE before its first use; every call leaves it
+ *             ready for the next (launch counts, then words tagged with
+ *             them).  One workspace serves one head (one V); calls sharing
+ *             it must not overlap.  Layout: 8 KiB of per-block launch
+ *             counts, then per token 2,048 block-key slots, 8,192 wave-key
+ *             slots and V row-key slots of 8 bytes (the last two written by
+ *             the sampling call).
  * Other arguments and limits as lmhead_gemv_fp8.
  */
+#define MOEDEC_MAX_EPILOGUE_V (1 << 18)
 size_t lmhead_argmax_workspace_bytes(int V, int M);   /* 0 for sizes out of range */
 int lmhead_gemv_fp8_argmax(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M, float* logits,
+                           int32_t* token_ids, void* workspace, size_t workspace_bytes,
+                           moedec_stream_t stream);
+
+/*
+ * Sampled decode on the FP8 head [card results: temperature 0.6, top-p 0.95,
+ * top-k 29 in the measured decode]: the GEMV of lmhead_gemv_fp8, then per
+ * token m
+ *   - candidates: the top_k largest logits[m][v], ordered by (logit desc, row
+ *     asc);
+ *   - p_i = softmax(logit_i / temperature) over the candidates (float32);
+ *   - the nucleus: the shortest prefix of the candidates whose cumulative
+ *     probability reaches top_p;
+ *   - token_ids[m] = the first nucleus entry whose cumulative probability,
+ *     renormalised over the nucleus, exceeds u[m].
+ * Every wave publishes its rows' (logit, row) keys in the workspace; the block
+ * launched last selects the candidates exactly (radix selects over the
+ * block maxima, the waves of the top_k blocks, then the rows of the top_k
+ * waves) and draws.
+ * top_k = 1 gives the greedy token.  One launch on `stream`.
+ * temperature > 0 and finite; 0 < top_p <= 1; 1 <= top_k <= min(32, V), else
+ * MOEDEC_ERR_ARG.
+ * u           [M] float32 uniforms in [0, 1) (the caller's random draw),
+ *             4-byte aligned
+ * logits      [M][V] float32, optional (NULL: not written)
+ * token_ids   [M] int32, as for lmhead_gemv_fp8_argmax (-1: a wait gave up)
+ * workspace   as for lmhead_gemv_fp8_argmax (same size function, zero-filled
+ *             once; the two calls may share one workspace if they do not
+ *             overlap).
+ */
+#define MOEDEC_MAX_SAMPLE_K 32
+int lmhead_gemv_fp8_sample(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M,
+                           float temperature, float top_p, int top_k, const float* u, float* logits,
                            int32_t* token_ids, void* workspace, size_t workspace_bytes,
                            moedec_stream_t stream);
 

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("moe_route_topk", "moe_expert_ffn_mxfp4", "moe_layer_mxfp4", "moe_layer_rmsnorm_mxfp4",
                  "lmhead_quant_fp8", "lmhead_gemv_fp8",
-                 "lmhead_gemv_bf16", "lmhead_gemv_fp8_argmax", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
+                 "lmhead_gemv_bf16", "lmhead_gemv_fp8_argmax", "lmhead_gemv_fp8_sample", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
                  "moedec_last_error", "moedec_abi_version", "moe_ffn_workspace_status",
                  "moe_layer_mxfp4_noalloc"):
@@ -80,10 +80,15 @@ def test_route_argument_checks(m):
 
 
 def test_argmax_workspace_and_argument_checks(m):
+    """Workspace = 2,048 per-block 4-byte launch counts, then 8-byte keys per
+    token: 2,048 block slots, 8,192 wave slots (the most 2^18 rows need at 32
+    rows per wave and 4 waves per block) and one per row."""
     L = m.lib
-    assert L.lmhead_argmax_workspace_bytes(157184, 1) == 4 * ((4912 + 3) // 4) * 1 * 8
-    assert L.lmhead_argmax_workspace_bytes(157184, 4) == 4 * ((4912 + 3) // 4) * 4 * 8
+    for M in (1, 4):
+        assert L.lmhead_argmax_workspace_bytes(157184, M) == 8192 + (2048 + 8192 + 157184) * M * 8
     assert L.lmhead_argmax_workspace_bytes(0, 1) == 0 and L.lmhead_argmax_workspace_bytes(10, 5) == 0
+    assert L.lmhead_argmax_workspace_bytes((1 << 18) + 1, 1) == 0
+    assert L.lmhead_argmax_workspace_bytes(1 << 18, 1) > 0
     desc = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32, 157184, 2560, FAKE, FAKE)
     ws = L.lmhead_argmax_workspace_bytes(157184, 1)
     assert L.lmhead_gemv_fp8_argmax(None, FAKE, 1, None, FAKE, FAKE, ws, None) == -1
@@ -93,6 +98,34 @@ def test_argmax_workspace_and_argument_checks(m):
     assert L.lmhead_gemv_fp8_argmax(ctypes.byref(desc), FAKE, 1, None, ODD, FAKE, ws, None) == -2
     bad = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, 7, 157184, 2560, FAKE, FAKE)
     assert L.lmhead_gemv_fp8_argmax(ctypes.byref(bad), FAKE, 1, None, FAKE, FAKE, ws, None) == -4
+    huge = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32, (1 << 18) + 1, 2560, FAKE, FAKE)
+    assert L.lmhead_gemv_fp8_argmax(ctypes.byref(huge), FAKE, 1, None, FAKE, FAKE, 1 << 40, None) == -3
+
+
+def test_sample_argument_checks(m):
+    """The sampling call rejects its settings on the host before any device
+    work: temperature <= 0 or not finite, top_p outside (0, 1], top_k outside
+    1..min(32, V); u is required (logits are optional)."""
+    L = m.lib
+    desc = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32, 157184, 2560, FAKE, FAKE)
+    ws = L.lmhead_argmax_workspace_bytes(157184, 1)
+    d = ctypes.byref(desc)
+
+    def call(T=0.6, p=0.95, k=29, u=FAKE, logits=FAKE, ids=FAKE, wsb=ws, head=d, M=1):
+        return L.lmhead_gemv_fp8_sample(head, FAKE, M, T, p, k, u, logits, ids, FAKE, wsb, None)
+
+    ARG = m._lib.MOEDEC_ERR_ARG
+    assert call(T=0.0) == ARG and b"temperature" in L.moedec_last_error()
+    assert call(T=-1.0) == ARG and call(T=float("inf")) == ARG and call(T=float("nan")) == ARG
+    assert call(p=0.0) == ARG and call(p=1.0000001) == ARG and call(p=float("nan")) == ARG
+    assert call(k=0) == ARG and call(k=33) == ARG
+    assert b"top_k=33" in L.moedec_last_error()
+    small = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32, 5, 2560, FAKE, FAKE)
+    assert call(k=6, head=ctypes.byref(small), wsb=L.lmhead_argmax_workspace_bytes(5, 1)) == ARG
+    assert call(u=None) == -1 and call(ids=None) == -1
+    assert call(u=ODD) == -2
+    assert call(M=5) == -3 and call(wsb=ws - 8) == -5
+    assert L.moedec_status_string(ARG) == b"argument out of range"
 
 
 def test_selftest_argument_checks(m):

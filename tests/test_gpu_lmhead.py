@@ -219,7 +219,7 @@ def test_argmax_graph_replays(m):
     head = m.lmhead_quant_fp8(bf16_tensor(wb))
     x = bf16_tensor(synth.lmhead_x_bf16(3, 4, 256))
     ref = m.lmhead_argmax_fp8(head, x).cpu().numpy()
-    ws = torch.empty(m.lib.lmhead_argmax_workspace_bytes(3000, 4), dtype=torch.uint8, device="cuda")
+    ws = m.make_lmhead_workspace(3000, 4, "cuda")
     ids = torch.empty(4, dtype=torch.int32, device="cuda")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -230,3 +230,202 @@ def test_argmax_graph_replays(m):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(ids.cpu().numpy(), ref)
         np.testing.assert_array_equal(m.lmhead_argmax_fp8(head, x).cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------
+# Sampling epilogue (lmhead_gemv_fp8_sample)
+
+SETTINGS = [(0.6, 0.95, 29), (1.0, 1.0, 32), (0.6, 0.5, 5), (2.0, 0.9, 17), (0.3, 0.99, 2)]
+DELTA = 1e-5      # float32 softmax + scan against float64: decisions this close to a boundary may go either way
+
+
+def _sample_ok(row, u, T, p, k, tok):
+    """The sampled token is the oracle's draw on the same float32 logits, or,
+    when u or the nucleus cut lies within DELTA of a boundary of the
+    cumulative distribution, the draw at a perturbed u or top_p (the kernel's
+    float32 softmax and scan may land on either side).  Returns (ok, exact)."""
+    row = np.asarray(row, np.float64)[None, :]
+    ref = int(oracle.lmhead_sample(row, [u], T, p, k)[0])
+    if tok == ref:
+        return True, True
+    for du in (-DELTA, 0.0, DELTA):
+        for dp in (-DELTA, 0.0, DELTA):
+            uu = min(max(u + du, 0.0), np.nextafter(1.0, 0.0))
+            pp = min(max(p + dp, 1e-9), 1.0)
+            if int(oracle.lmhead_sample(row, [uu], T, pp, k)[0]) == tok:
+                return True, False
+    return False, False
+
+
+def _check_sample(m, head, xb, u, T, p, k, what):
+    """Kernel ids against the oracle's draw on the kernel's own logits (which
+    must equal the plain GEMV's bit for bit); returns the number of draws that
+    needed the boundary allowance."""
+    x = bf16_tensor(xb)
+    M = x.shape[0]
+    u_dev = torch.from_numpy(np.asarray(u, np.float32)).cuda()
+    ids, lg = m.lmhead_sample_fp8(head, x, u_dev, T, p, k)
+    ids_only, none = m.lmhead_sample_fp8(head, x, u_dev, T, p, k, want_logits=False)
+    plain = m.lmhead_gemv_fp8(head, x)
+    torch.cuda.synchronize()
+    assert none is None
+    lg_np = lg.cpu().numpy()
+    np.testing.assert_array_equal(lg_np.view(np.uint32), plain.cpu().numpy().view(np.uint32))
+    got = ids.cpu().numpy()
+    np.testing.assert_array_equal(got, ids_only.cpu().numpy())
+    loose = 0
+    for mm in range(M):
+        ok, exact = _sample_ok(lg_np[mm], float(u[mm]), T, p, k, int(got[mm]))
+        assert ok, f"{what} token {mm}: kernel {got[mm]}, oracle " \
+                   f"{oracle.lmhead_sample(lg_np[mm:mm + 1].astype(np.float64), u[mm:mm + 1], T, p, k)}"
+        loose += not exact
+    return loose
+
+
+@pytest.mark.parametrize("V,H", [(300, 2560), (77, 256), (4097, 64), (33, 16), (1100, 128)])
+@pytest.mark.parametrize("M", [1, 3, 4])
+def test_sample_small(m, V, H, M):
+    """Several vocabulary sizes (one wave, a ragged last wave, many blocks)
+    and every setting, at uniforms from the counter-based stream."""
+    wb = _weights(V, H, seed=V + 11)
+    head = _check_quant(m, wb)
+    loose = 0
+    for i, (T, p, k) in enumerate(SETTINGS):
+        k = min(k, V)
+        say("sample", V, H, M, T, p, k)
+        xb = synth.lmhead_x_bf16(100 + i, M, H)
+        loose += _check_sample(m, head, xb, synth.sampling_uniforms(V, i, M), T, p, k,
+                               f"V={V} H={H} M={M} T={T} p={p} k={k}")
+    assert loose <= 1
+
+
+def test_sample_tiny_vocabulary_all_candidates(m):
+    """V = 5 < top_k bound: the candidates are every row (one wave holds
+    them all); a grid of uniforms visits every token with top_p = 1."""
+    V, H = 5, 64
+    wb = _weights(V, H, seed=41)
+    head = _check_quant(m, wb)
+    xb = synth.lmhead_x_bf16(41, 4, H)
+    seen = set()
+    for j in range(32):
+        u = (np.arange(4, dtype=np.float32) + 4 * j) / 128.0
+        _check_sample(m, head, xb, u, 3.0, 1.0, 5, f"tiny grid {j}")
+        ids, _ = m.lmhead_sample_fp8(head, bf16_tensor(xb), torch.from_numpy(u).cuda(), 3.0, 1.0, 5)
+        seen.update(int(t) for t in ids.cpu().numpy())
+    assert seen == set(range(V))
+
+
+def test_sample_frequencies_follow_the_nucleus(m):
+    """Fixed logits, uniforms on a fine grid: how often each token is drawn
+    equals its renormalised nucleus probability times the grid size, up to
+    the two grid points at each interval's ends."""
+    V, H, M = 2000, 256, 4
+    wb = _weights(V, H, seed=12)
+    head = _check_quant(m, wb)
+    xb = synth.lmhead_x_bf16(12, M, H)
+    x = bf16_tensor(xb)
+    T, p, k, n = 0.6, 0.95, 29, 512
+    counts = [dict() for _ in range(M)]
+    lg_np = None
+    for j in range(n):
+        u = np.full(M, (j + 0.5) / n, np.float32)
+        ids, lg = m.lmhead_sample_fp8(head, x, torch.from_numpy(u).cuda(), T, p, k)
+        for mm, t in enumerate(ids.cpu().numpy()):
+            counts[mm][int(t)] = counts[mm].get(int(t), 0) + 1
+        lg_np = lg.cpu().numpy()
+    for mm in range(M):
+        row = lg_np[mm].astype(np.float64)
+        order = np.lexsort((np.arange(V), -row))[:k]
+        z = row[order] / T
+        pr = np.exp(z - z[0])
+        pr /= pr.sum()
+        cum = np.cumsum(pr)
+        n_keep = min(int(np.searchsorted(cum, p, side="left")) + 1, k)
+        q = pr[:n_keep] / cum[n_keep - 1]
+        for i in range(n_keep):
+            assert abs(counts[mm].get(int(order[i]), 0) - q[i] * n) <= 2, f"token {mm} cand {i}"
+        assert sum(counts[mm].values()) == n
+        assert set(counts[mm]) <= set(int(t) for t in order[:n_keep])
+
+
+def test_sample_candidates_clustered_and_tied(m):
+    """The top logits packed into one wave's rows (stage A must keep that
+    wave), and an exact tie straddling the top_k cut (identical rows: the
+    lower row is a candidate, the higher one is not)."""
+    V, H = 3000, 256
+    wb = _weights(V, H, seed=21)
+    xb = synth.lmhead_x_bf16(21, 2, H)
+    sign = np.sign(synth.bf16_values(xb[0])).astype(np.float32)
+    for i, row in enumerate(range(640, 671)):            # 31 of one wave's 32 rows, graded
+        wb[row] = synth.bf16_bits_from_f32((0.02 + 0.0005 * i) * sign)
+    tie = synth.bf16_bits_from_f32(0.0195 * sign)
+    wb[2999] = tie                                        # ties with row 5 for the last place
+    wb[5] = tie
+    head = _check_quant(m, wb)
+    x = bf16_tensor(xb)
+    lg = m.lmhead_gemv_fp8(head, x).cpu().numpy()
+    assert lg[0, 5] == lg[0, 2999]
+    top = np.lexsort((np.arange(V), -lg[0].astype(np.float64)))[:33]
+    assert set(range(640, 671)) == set(top[:31])
+    k = 32                                                # row 5 is the last candidate, row 2999 the first one cut
+    assert top[31] == 5 and top[32] == 2999
+    hits = set()
+    for j in range(64):
+        u = np.float32([(j + 0.5) / 64, 0.999])
+        _check_sample(m, head, xb, u, 50.0, 1.0, k, f"cluster/tie grid {j}")
+        ids, _ = m.lmhead_sample_fp8(head, x, torch.from_numpy(u).cuda(), 50.0, 1.0, k)
+        hits.add(int(ids.cpu().numpy()[0]))
+    assert 5 in hits and 2999 not in hits and hits <= set(int(t) for t in top[:k])
+
+
+def test_sample_greedy_limits(m):
+    """top_k = 1, and a vanishing temperature, give the greedy token."""
+    V, H, M = 5000, 512, 4
+    wb = _weights(V, H, seed=31)
+    head = _check_quant(m, wb)
+    x = bf16_tensor(synth.lmhead_x_bf16(31, M, H))
+    greedy = m.lmhead_argmax_fp8(head, x).cpu().numpy()
+    u = torch.from_numpy(synth.sampling_uniforms(31, 0, M)).cuda()
+    for T, p, k in ((0.6, 0.95, 1), (1e-6, 0.95, 29), (1.0, 1e-6, 32)):
+        ids, _ = m.lmhead_sample_fp8(head, x, u, T, p, k)
+        np.testing.assert_array_equal(ids.cpu().numpy(), greedy, err_msg=f"T={T} p={p} k={k}")
+
+
+def test_sample_full_size(m, full_head):
+    """157,184 x 2,560 at M = 1 and 4 with the pages' settings: several decode
+    steps of uniforms, each draw against the oracle on the kernel's logits."""
+    head = m.lmhead_quant_fp8(bf16_tensor(full_head))
+    loose = 0
+    for M in (1, 4):
+        for step in range(4):
+            xb = synth.lmhead_x_bf16(50 + step, M, synth.LMHEAD_H)
+            say("full sample", M, step)
+            loose += _check_sample(m, head, xb, synth.sampling_uniforms(0, step, M), 0.6, 0.95, 29,
+                                   f"full M={M} step={step}")
+    assert loose <= 1
+
+
+def test_sample_graph_replays_and_shared_workspace(m):
+    """Sampling captured in a HIP graph: new uniforms written into the
+    captured tensor before each replay give the eager draw; greedy and
+    sampling calls share one workspace in between."""
+    V, H, M = 3000, 256, 4
+    wb = _weights(V, H, seed=9)
+    head = m.lmhead_quant_fp8(bf16_tensor(wb))
+    x = bf16_tensor(synth.lmhead_x_bf16(4, M, H))
+    ws = m.make_lmhead_workspace(V, M, "cuda")
+    u = torch.zeros(M, dtype=torch.float32, device="cuda")
+    ids = torch.empty(M, dtype=torch.int32, device="cuda")
+    lg = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.lmhead_sample_fp8(head, x, u, 0.6, 0.95, 29, workspace=ws, ids=ids, logits=lg)
+    for step in range(4):
+        u.copy_(torch.from_numpy(synth.sampling_uniforms(9, step, M)))
+        ids.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        ref, _ = m.lmhead_sample_fp8(head, x, u.clone(), 0.6, 0.95, 29)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ref.cpu().numpy())
+        greedy = m.lmhead_argmax_fp8(head, x, workspace=ws).cpu().numpy()
+        np.testing.assert_array_equal(greedy, m.lmhead_argmax_fp8(head, x).cpu().numpy())
