@@ -221,48 +221,67 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
 
 def stack_bench(m, torch, synth, layers, passes, eager_passes, dev):
     """Passes over all layers in order at M = 1, each layer on the residual
-    stream (moe_layer_rmsnorm_mxfp4: x = bf16(RMSNorm(r)), r += MoE layer(x)),
-    so every layer's input depends on the previous layer's output.  Timed as a
-    HIP graph of `passes` passes and eagerly (one launch per layer from Python)."""
+    stream, so every layer's input depends on the previous layer's output.
+    Two forms: routed from pre-drawn logits (moe_layer_rmsnorm_mxfp4: x =
+    bf16(RMSNorm(r)), r += MoE layer(x)), and routed from its own data
+    (moe_layer_rmsnorm_router_mxfp4: the same with the router logits x W_router^T
+    of each layer's own bf16 router [512][2560] in front).  Each is timed as a
+    HIP graph of `passes` passes and eagerly (from Python)."""
+    import numpy as np
     n_layers = len(layers)
     shape = synth.LING
     k = shape.k
     _, lgs = layer_inputs(synth, n_layers, 1, dev)
+    wrs = [torch.from_numpy(synth.router_weight_bf16(0, L, shape.E, shape.H).view(np.int16))
+           .view(torch.bfloat16).to(dev) for L in range(n_layers)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
     r0 = torch.randn((1, shape.H), generator=gen, device=dev, dtype=torch.float32)
     bufs = [r0.clone(), torch.empty_like(r0)]
+    lg_own = torch.empty((1, shape.E), dtype=torch.float32, device=dev)
     ws = m.make_ffn_workspace(1, k, shape.H, shape.I, dev)
 
-    def one_pass():
+    def pass_given():
         for L in range(n_layers):
             m.moe_layer_rmsnorm(layers[L], bufs[L % 2], lgs[L], k, ws, r_out=bufs[(L + 1) % 2])
         if n_layers % 2:
             bufs.reverse()
 
-    one_pass()
-    torch.cuda.synchronize()
+    def pass_routed():
+        for L in range(n_layers):
+            m.moe_layer_rmsnorm_router(layers[L], wrs[L], bufs[L % 2], k, ws, r_out=bufs[(L + 1) % 2],
+                                       logits=lg_own)
+        if n_layers % 2:
+            bufs.reverse()
+
     t = Timer(torch)
-    g = capture(torch, lambda: [one_pass() for _ in range(passes)])
-    g.replay()
-    ms_graph = t.run(g.replay)
-    del g
-    one_pass()
-    ms_eager = t.run(lambda: [one_pass() for _ in range(eager_passes)])
-    m.check_ffn_workspace(ws)
-    finite = bool(torch.isfinite(bufs[0]).all().item())
     steps_g, steps_e = passes * n_layers, eager_passes * n_layers
-    layer_bytes = (shape.k + 1) * EXPERT_BYTES_LING + shape.E * 4 + 2 * shape.H * 4   # + r in, r out
-    return {
-        "layers": n_layers, "passes_graph": passes, "passes_eager": eager_passes,
-        "us_per_layer_graph": 1e3 * ms_graph / steps_g,
-        "us_per_layer_eager": 1e3 * ms_eager / steps_e,
-        "us_per_pass_graph": 1e3 * ms_graph / passes,
-        "bytes_per_layer": layer_bytes,
-        "gbs_graph": layer_bytes * steps_g / (1e6 * ms_graph),
-        "frac_of_peak_graph": layer_bytes * steps_g / (1e6 * ms_graph) / PEAK_HBM_GBS,
-        "residual_finite": finite,
-    }
+    out = {"layers": n_layers, "passes_graph": passes, "passes_eager": eager_passes}
+    for name, one_pass in (("", pass_given), ("routed_", pass_routed)):
+        bufs[0].copy_(r0)
+        one_pass()
+        torch.cuda.synchronize()
+        g = capture(torch, lambda: [one_pass() for _ in range(passes)])
+        g.replay()
+        ms_graph = t.run(g.replay)
+        del g
+        one_pass()
+        ms_eager = t.run(lambda: [one_pass() for _ in range(eager_passes)])
+        m.check_ffn_workspace(ws)
+        layer_bytes = (shape.k + 1) * EXPERT_BYTES_LING + shape.E * 4 + 2 * shape.H * 4   # + r in, r out
+        if name:
+            layer_bytes += shape.E * shape.H * 2                                         # the router
+        out.update({
+            name + "us_per_layer_graph": 1e3 * ms_graph / steps_g,
+            name + "us_per_layer_eager": 1e3 * ms_eager / steps_e,
+            name + "us_per_pass_graph": 1e3 * ms_graph / passes,
+            name + "bytes_per_layer": layer_bytes,
+            name + "gbs_graph": layer_bytes * steps_g / (1e6 * ms_graph),
+            name + "frac_of_peak_graph": layer_bytes * steps_g / (1e6 * ms_graph) / PEAK_HBM_GBS,
+            name + "residual_finite": bool(torch.isfinite(bufs[0]).all().item()),
+        })
+    del wrs
+    return out
 
 
 def router_bench(m, torch, synth, layers, steps, dev, n_router=128):
@@ -780,6 +799,7 @@ def main(argv=None):
     if stack is not None:
         line["stack_us_per_layer_graph"] = round(stack["us_per_layer_graph"], 3)
         line["stack_us_per_layer_eager"] = round(stack["us_per_layer_eager"], 3)
+        line["stack_norm_router_layer_us_graph"] = round(stack["routed_us_per_layer_graph"], 3)
     if lm is not None:
         line["lmhead_fp8_gbs_m1"] = round(lm["fp8_m1_gbs"], 1)
         line["lmhead_fp8_argmax_us_m1"] = round(lm["fp8_argmax_m1_us"], 2)

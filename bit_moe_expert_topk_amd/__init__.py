@@ -287,6 +287,36 @@ def moe_layer_rmsnorm(weights, r_in, logits, k, workspace, r_out=None, eps=1e-6,
     return r_out
 
 
+def moe_layer_rmsnorm_router(weights, w_router, r_in, k, workspace, r_out=None, eps=1e-6, logits=None,
+                             x_out=None, y_f32=None):
+    """One layer on the residual stream with its router in front, in two
+    launches: x = bf16(RMSNorm(r_in)), logits = x W_router^T, then the layer of
+    moe_layer_rmsnorm on those logits.  w_router: [E][H] bfloat16.  Returns
+    (r_out, logits); x_out (bf16) and y_f32 are filled when given."""
+    _need(r_in, torch.float32, "r_in", 2)
+    _need(w_router, torch.bfloat16, "w_router", 2)
+    _need(workspace, torch.uint8, "workspace", 1)
+    m_tokens, hidden = r_in.shape
+    if tuple(w_router.shape) != (weights.E, weights.H) or hidden != weights.H:
+        raise ValueError(f"w_router must be [{weights.E}][{weights.H}] and r_in [M][{weights.H}]")
+    if logits is None:
+        logits = torch.empty((m_tokens, weights.E), dtype=torch.float32, device=r_in.device)
+    _need(logits, torch.float32, "logits", 2)
+    if tuple(logits.shape) != (m_tokens, weights.E):
+        raise ValueError(f"logits must be [{m_tokens}][{weights.E}], got {tuple(logits.shape)}")
+    if r_out is None:
+        r_out = torch.empty_like(r_in)
+    _need(r_out, torch.float32, "r_out", 2)
+    if x_out is not None:
+        _need(x_out, torch.bfloat16, "x_out", 2)
+    if y_f32 is not None:
+        _need(y_f32, torch.float32, "y_f32", 2)
+    _check(lib.moe_layer_rmsnorm_router_mxfp4(ctypes.byref(weights.desc), _ptr(w_router), _ptr(r_in), m_tokens,
+                                              k, float(eps), _ptr(logits), _ptr(r_out), _ptr(x_out),
+                                              _ptr(y_f32), _ptr(workspace), workspace.numel(), _stream(r_in)))
+    return r_out, logits
+
+
 # --------------------------------------------------------------------------
 # LM head
 

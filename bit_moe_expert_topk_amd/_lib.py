@@ -100,6 +100,9 @@ SIGNATURES = {
     "moe_layer_rmsnorm_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int,
                                         ctypes.c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]),
+    "moe_layer_rmsnorm_router_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int,
+                                               ctypes.c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                                               c_void_p, c_size_t, c_void_p]),
     "moe_ffn_workspace_status": (c_int, [c_void_p, c_size_t, ctypes.POINTER(c_uint32), c_void_p]),
     "moe_layer_mxfp4_noalloc": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

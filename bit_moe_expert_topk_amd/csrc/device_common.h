@@ -194,4 +194,44 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
 }
 
+// RMSNorm factors inv[m] = 1 / sqrt(mean(r_m^2) + eps) of M_T tokens of H
+// float32 values, by a block of 256 threads that holds the residual as
+// 16-byte pieces: piece p = threadIdx.x + 256 i (held in xv[i], p <
+// n_pieces) is elements 4p'..4p'+3 of token p / per_tok, p' = p mod per_tok.
+// Order: per-thread sums of ((a^2 + b^2) + (c^2 + d^2)) per piece, a wave
+// sum, then the four waves' sums added pairwise.  Every kernel that forms
+// x = bf16(r * inv) from r takes its factors from here, so all of them form
+// the same x bit for bit.  Contains a block barrier.
+template <int M_T, int P>
+__device__ __forceinline__ void rmsnorm_factors(const u32x4 (&xv)[P], int n_pieces, int per_tok, int H,
+                                                float eps, float (&inv)[M_T]) {
+    __shared__ float s_ss[4][M_T];
+    const int tid = threadIdx.x;
+    float ss[M_T];
+#pragma unroll
+    for (int m = 0; m < M_T; ++m) ss[m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int p = tid + 256 * i;
+        if (p < n_pieces) {
+            const int pm = p / per_tok;
+            const float v0 = __uint_as_float(xv[i][0]), v1 = __uint_as_float(xv[i][1]);
+            const float v2 = __uint_as_float(xv[i][2]), v3 = __uint_as_float(xv[i][3]);
+            const float sq = (v0 * v0 + v1 * v1) + (v2 * v2 + v3 * v3);
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) ss[m] += (m == pm) ? sq : 0.f;
+        }
+    }
+    const int w = tid / kWave;
+#pragma unroll
+    for (int m = 0; m < M_T; ++m) {
+        const float t = wave_sum_f32(ss[m]);
+        if ((tid & (kWave - 1)) == 0) s_ss[w][m] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M_T; ++m)
+        inv[m] = 1.0f / sqrtf(((s_ss[0][m] + s_ss[1][m]) + (s_ss[2][m] + s_ss[3][m])) / (float)H + eps);
+}
+
 }  // namespace moedec

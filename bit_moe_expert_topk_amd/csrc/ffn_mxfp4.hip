@@ -864,33 +864,9 @@ __device__ void x_stage(const FfnArgs& a, const u32x4 (&xv)[x_pieces<M_T, NORM>(
     const int xtok = a.kbh4 * 4 * kXBlock;
     if constexpr (NORM) {
         // piece p holds elements 4r..4r+3
-        __shared__ float s_ss[kWaves][MOEDEC_MAX_M];
-        float ss[M_T];
-#pragma unroll
-        for (int m = 0; m < M_T; ++m) ss[m] = 0.f;
-#pragma unroll
-        for (int i = 0; i < kPieces; ++i) {
-            const int p = tid + kThreads * i;
-            if (p < n_pieces) {
-                const int pm = p / per_tok;
-                const float v0 = __uint_as_float(xv[i][0]), v1 = __uint_as_float(xv[i][1]);
-                const float v2 = __uint_as_float(xv[i][2]), v3 = __uint_as_float(xv[i][3]);
-                const float sq = (v0 * v0 + v1 * v1) + (v2 * v2 + v3 * v3);
-#pragma unroll
-                for (int m = 0; m < M_T; ++m) ss[m] += (m == pm) ? sq : 0.f;
-            }
-        }
-        const int w = tid / kWave;
-#pragma unroll
-        for (int m = 0; m < M_T; ++m) {
-            const float t = wave_sum_f32(ss[m]);
-            if ((tid & (kWave - 1)) == 0) s_ss[w][m] = t;
-        }
-        __syncthreads();
+        static_assert(kThreads == 256 && kWaves == 4, "rmsnorm_factors takes a block of 256 threads");
         float inv[M_T];
-#pragma unroll
-        for (int m = 0; m < M_T; ++m)
-            inv[m] = 1.0f / sqrtf(((s_ss[0][m] + s_ss[1][m]) + (s_ss[2][m] + s_ss[3][m])) / (float)a.H + a.eps);
+        rmsnorm_factors<M_T>(xv, n_pieces, per_tok, a.H, a.eps, inv);
         const bool export_x = (int)blockIdx.x == a.writer && a.x_out != nullptr;
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) {

@@ -277,9 +277,10 @@ int moe_layer_mxfp4_noalloc(const moedec_moe_weights* w, const uint16_t* x_bf16,
                     "moe_layer_mxfp4_noalloc");
 }
 
-int moe_layer_rmsnorm_mxfp4(const moedec_moe_weights* w, const float* r_in, const float* logits, int M,
-                            int k, float eps, float* r_out, uint16_t* x_bf16, float* y_f32,
-                            void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+// Checks of the layer steps that start from the residual stream.
+static int check_residual_layer(const moedec_moe_weights* w, const float* r_in, const float* logits, int M,
+                                int k, float eps, float* r_out, uint16_t* x_bf16, float* y_f32,
+                                void* workspace, size_t workspace_bytes) {
     if (int st = check_moe_args(w, x_bf16, M, k, nullptr, y_f32, workspace, workspace_bytes, true))
         return st;
     if (!r_in || !r_out || !logits) return fail(MOEDEC_ERR_NULL, "r_in, r_out or logits is NULL");
@@ -290,11 +291,41 @@ int moe_layer_rmsnorm_mxfp4(const moedec_moe_weights* w, const float* r_in, cons
     const auto lo_in = reinterpret_cast<uintptr_t>(r_in), lo_out = reinterpret_cast<uintptr_t>(r_out);
     if (lo_in < lo_out + bytes && lo_out < lo_in + bytes)
         return fail(MOEDEC_ERR_SHAPE, "r_out overlaps r_in (use two buffers)");
+    return MOEDEC_OK;
+}
+
+int moe_layer_rmsnorm_mxfp4(const moedec_moe_weights* w, const float* r_in, const float* logits, int M,
+                            int k, float eps, float* r_out, uint16_t* x_bf16, float* y_f32,
+                            void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+    if (int st = check_residual_layer(w, r_in, logits, M, k, eps, r_out, x_bf16, y_f32, workspace,
+                                      workspace_bytes))
+        return st;
     if (int st = check_device()) return st;
     moedec::ResidualArgs res{r_in, r_out, x_bf16, eps};
     return launched(moedec::launch_moe(*w, nullptr, M, k, nullptr, logits, nullptr, nullptr, nullptr,
                                        nullptr, y_f32, workspace, static_cast<hipStream_t>(stream), &res),
                     "moe_layer_rmsnorm_mxfp4");
+}
+
+int moe_layer_rmsnorm_router_mxfp4(const moedec_moe_weights* w, const uint16_t* w_router, const float* r_in,
+                                   int M, int k, float eps, float* logits, float* r_out, uint16_t* x_bf16,
+                                   float* y_f32, void* workspace, size_t workspace_bytes,
+                                   moedec_stream_t stream) {
+    if (int st = check_residual_layer(w, r_in, logits, M, k, eps, r_out, x_bf16, y_f32, workspace,
+                                      workspace_bytes))
+        return st;
+    if (!w_router) return fail(MOEDEC_ERR_NULL, "w_router is NULL");
+    if (!aligned(w_router, 16)) return fail(MOEDEC_ERR_ALIGN, "w_router must be 16-byte aligned");
+    if (w->H % 8 || w->H > 4096) return fail(MOEDEC_ERR_SHAPE, "H=%d: the router needs H %% 8 == 0, H <= 4096", w->H);
+    if (int st = check_device()) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int st = launched(moedec::launch_norm_router_bf16(w_router, w->E, w->H, r_in, eps, M, logits, s),
+                          "moe_layer_rmsnorm_router_mxfp4 (router)"))
+        return st;
+    moedec::ResidualArgs res{r_in, r_out, x_bf16, eps};
+    return launched(moedec::launch_moe(*w, nullptr, M, k, nullptr, logits, nullptr, nullptr, nullptr,
+                                       nullptr, y_f32, workspace, s, &res),
+                    "moe_layer_rmsnorm_router_mxfp4");
 }
 
 int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H, uint8_t* codes, float* row_scale,

@@ -86,5 +86,9 @@ hipError_t launch_gemv_fp8(const uint8_t* codes, const float* rs, int V, int H,
 size_t lmhead_epilogue_bytes(int V, int M);
 hipError_t launch_gemv_bf16(const uint16_t* w, int V, int H, const uint16_t* x, int M,
                             float* logits, hipStream_t s);
+// Router logits [M][E] = bf16(RMSNorm(r)) W^T, the norm as the fused layer forms it.
+// r [M][H] float32 16-byte aligned, H % 8 == 0, H <= 4096.
+hipError_t launch_norm_router_bf16(const uint16_t* w, int E, int H, const float* r, float eps, int M,
+                                   float* logits, hipStream_t s);
 
 }  // namespace moedec

@@ -690,26 +690,15 @@ void gemv_fp8_kernel(const uint8_t* __restrict__ codes,
     }
 }
 
+// The rows of the bf16 GEMV for this wave: rows_per_wave rows from row
+// wave * rows_per_wave, R per step, against the lane's x chunks xr.
 template <int M_T, int T, int R>
-__global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restrict__ wt, int V,
-                                                        int H, const uint32_t* __restrict__ x,
-                                                        float* __restrict__ logits,
-                                                        int rows_per_wave) {
+__device__ __forceinline__ void gemv_bf16_rows(const uint16_t* __restrict__ wt, int V, int H,
+                                               const uint32_t (&xr)[M_T][T][4], float* __restrict__ logits,
+                                               int rows_per_wave) {
     const int lane = lane_id();
     const int n_ch = H / 8;
     const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    uint32_t xr[M_T][T][4];
-#pragma unroll
-    for (int m = 0; m < M_T; ++m)
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int ch = lane + 64 * t;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t xv = x[(size_t)m * (H / 2) + min(ch, n_ch - 1) * 4 + j];
-                xr[m][t][j] = (ch < n_ch) ? xv : 0u;
-            }
-        }
     const uint8_t* base = reinterpret_cast<const uint8_t*>(wt);
     const int v0 = gw * rows_per_wave;
     const int v1 = min(V, v0 + rows_per_wave);
@@ -745,11 +734,79 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
     }
 }
 
+template <int M_T, int T, int R>
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restrict__ wt, int V,
+                                                        int H, const uint32_t* __restrict__ x,
+                                                        float* __restrict__ logits,
+                                                        int rows_per_wave) {
+    const int lane = lane_id();
+    const int n_ch = H / 8;
+    uint32_t xr[M_T][T][4];
+#pragma unroll
+    for (int m = 0; m < M_T; ++m)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int ch = lane + 64 * t;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t xv = x[(size_t)m * (H / 2) + min(ch, n_ch - 1) * 4 + j];
+                xr[m][t][j] = (ch < n_ch) ? xv : 0u;
+            }
+        }
+    gemv_bf16_rows<M_T, T, R>(wt, V, H, xr, logits, rows_per_wave);
+}
+
+// Router logits from the residual stream: x = bf16(RMSNorm(r)) with unit gain,
+// formed in every block from the float32 r [M_T][H] with the factors of
+// rmsnorm_factors (the fused layer's order, so this x is the layer's x bit for
+// bit), then the rows of gemv_bf16_rows.  H % 8 == 0, H <= 4096.
+template <int M_T, int T, int R>
+__global__ __launch_bounds__(256) void norm_gemv_bf16_kernel(const uint16_t* __restrict__ wt, int V,
+                                                             int H, const float* __restrict__ r,
+                                                             float eps, float* __restrict__ logits,
+                                                             int rows_per_wave) {
+    const int lane = lane_id();
+    const int n_ch = H / 8;
+    constexpr int kPieces = 4 * M_T;                   // 16-byte pieces per thread: H / 4 <= 4 * 256
+    const int per_tok = H / 4, n_pieces = M_T * per_tok;
+    const u32x4* r4 = reinterpret_cast<const u32x4*>(r);
+    u32x4 rv[kPieces];
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) rv[i] = r4[min((int)threadIdx.x + 256 * i, n_pieces - 1)];
+    float inv[M_T];
+    rmsnorm_factors<M_T>(rv, n_pieces, per_tok, H, eps, inv);
+    // this lane's chunks of x: chunk ch = 8 elements, from r's pieces 2ch and 2ch + 1
+    uint32_t xr[M_T][T][4];
+#pragma unroll
+    for (int m = 0; m < M_T; ++m)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int ch = lane + 64 * t;
+            const int cc = min(ch, n_ch - 1);
+            const u32x4 lo = r4[m * per_tok + 2 * cc], hi = r4[m * per_tok + 2 * cc + 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t a = j < 2 ? lo[2 * j] : hi[2 * j - 4];
+                const uint32_t b = j < 2 ? lo[2 * j + 1] : hi[2 * j - 3];
+                const uint32_t pair = (uint32_t)f32_to_bf16_rne(__uint_as_float(a) * inv[m]) |
+                                      ((uint32_t)f32_to_bf16_rne(__uint_as_float(b) * inv[m]) << 16);
+                xr[m][t][j] = (ch < n_ch) ? pair : 0u;
+            }
+        }
+    gemv_bf16_rows<M_T, T, R>(wt, V, H, xr, logits, rows_per_wave);
+}
+
 // bf16 GEMV: 16 rows per wave, 4 per step, for a vocabulary-sized matrix; a
 // short one (a router's 512 rows) takes one row per wave so that its few
 // megabytes spread over as many waves as it has rows (latency-bound).
 constexpr int kRowsPerWave = 16;
 constexpr int kShortRows = 16384;
+
+template <int M_T, int T>
+void launch_norm_bf16_t(const uint16_t* w, int V, int H, const float* r, float eps, float* logits, hipStream_t s) {
+    const dim3 grid((V + 3) / 4), blk(256);                // one row per wave, as for a short matrix
+    hipLaunchKernelGGL((norm_gemv_bf16_kernel<M_T, T, 1>), grid, blk, 0, s, w, V, H, r, eps, logits, 1);
+}
 
 template <int M_T, int T>
 void launch_bf16_t(const uint16_t* w, int V, int H, const uint32_t* x, float* logits, hipStream_t s) {
@@ -836,6 +893,22 @@ hipError_t gemv_bf16_m(const uint16_t* w, int V, int H, const uint32_t* x, float
     return hipGetLastError();
 }
 
+template <int M_T>
+hipError_t norm_gemv_bf16_m(const uint16_t* w, int V, int H, const float* r, float eps, float* logits,
+                            hipStream_t s) {
+    switch ((H / 8 + 63) / 64) {
+        case 1: launch_norm_bf16_t<M_T, 1>(w, V, H, r, eps, logits, s); break;
+        case 2: launch_norm_bf16_t<M_T, 2>(w, V, H, r, eps, logits, s); break;
+        case 3: launch_norm_bf16_t<M_T, 3>(w, V, H, r, eps, logits, s); break;
+        case 4: launch_norm_bf16_t<M_T, 4>(w, V, H, r, eps, logits, s); break;
+        case 5: launch_norm_bf16_t<M_T, 5>(w, V, H, r, eps, logits, s); break;
+        case 6: launch_norm_bf16_t<M_T, 6>(w, V, H, r, eps, logits, s); break;
+        case 7: launch_norm_bf16_t<M_T, 7>(w, V, H, r, eps, logits, s); break;
+        default: launch_norm_bf16_t<M_T, 8>(w, V, H, r, eps, logits, s); break;
+    }
+    return hipGetLastError();
+}
+
 // Rows are handed out grid-stride, so the grid is sized to what is resident
 // at once (occupancy of the instantiation times the CU count), not beyond.
 template <int T>
@@ -902,6 +975,16 @@ hipError_t launch_gemv_bf16(const uint16_t* w, int V, int H, const uint16_t* x, 
         case 2: return gemv_bf16_m<2>(w, V, H, x32, logits, s);
         case 3: return gemv_bf16_m<3>(w, V, H, x32, logits, s);
         default: return gemv_bf16_m<4>(w, V, H, x32, logits, s);
+    }
+}
+
+hipError_t launch_norm_router_bf16(const uint16_t* w, int E, int H, const float* r, float eps, int M,
+                                   float* logits, hipStream_t s) {
+    switch (M) {
+        case 1: return norm_gemv_bf16_m<1>(w, E, H, r, eps, logits, s);
+        case 2: return norm_gemv_bf16_m<2>(w, E, H, r, eps, logits, s);
+        case 3: return norm_gemv_bf16_m<3>(w, E, H, r, eps, logits, s);
+        default: return norm_gemv_bf16_m<4>(w, E, H, r, eps, logits, s);
     }
 }
 

@@ -297,6 +297,29 @@ int moe_layer_rmsnorm_mxfp4(const moedec_moe_weights* w, const float* r_in, cons
                             int M, int k, float eps, float* r_out, uint16_t* x_bf16, float* y_f32,
                             void* workspace, size_t workspace_bytes, moedec_stream_t stream);
 
+/*
+ * The same layer with its router in front [card background: a router picks
+ * 8 of the 512 experts for each token from its hidden state]: from the
+ * residual stream alone,
+ *     x      = bf16(RMSNorm(r_in))                      (as above)
+ *     logits = x W_router^T                             (float32, no bias)
+ *     then moe_layer_rmsnorm_mxfp4 on those logits: top-k routing, the
+ *     routed + shared experts, r_out = r_in + y.
+ * Two launches on `stream`: the norm and the router GEMV (one router row per
+ * wave; every block forms x from r_in in the fused layer's summation order,
+ * so both launches use the same x bit for bit), then the fused layer.
+ * w_router    [E][H] bf16 (E = w->E, H = w->H), row-major, 16-byte aligned
+ * logits      [M][E] float32 output (the second launch reads it), 4-byte
+ *             aligned
+ * Other arguments, limits and the workspace as moe_layer_rmsnorm_mxfp4.  If
+ * the second launch is refused (MOEDEC_ERR_LAUNCH), the first has already
+ * been enqueued and writes logits.
+ */
+int moe_layer_rmsnorm_router_mxfp4(const moedec_moe_weights* w, const uint16_t* w_router, const float* r_in,
+                                   int M, int k, float eps, float* logits, float* r_out, uint16_t* x_bf16,
+                                   float* y_f32, void* workspace, size_t workspace_bytes,
+                                   moedec_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * LM head with online FP8 weights.  [news where the speed comes from; card
  * #2: the 157,184 x 2,560 vocabulary projection is read whole for every

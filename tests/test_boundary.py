@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
                  "lmhead_gemv_bf16", "lmhead_gemv_fp8_argmax", "lmhead_gemv_fp8_sample", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
                  "moedec_last_error", "moedec_abi_version", "moe_ffn_workspace_status",
-                 "moe_layer_mxfp4_noalloc"):
+                 "moe_layer_mxfp4_noalloc", "moe_layer_rmsnorm_router_mxfp4"):
         assert want in names
 
 
@@ -240,6 +240,28 @@ def test_residual_layer_argument_checks(m):
     assert call(_weights(m), r_out=ctypes.c_void_p((1 << 24) + 4)) == -2
     assert call(_weights(m), x=ctypes.c_void_p((1 << 22) + 8)) == -2
     assert call(_weights(m), M=5) == -3
+    assert call(_weights(m), n=ws - 1) == -5
+
+
+def test_router_chain_argument_checks(m):
+    """The layer with its router in front checks what the residual layer
+    checks, plus the router matrix, before any device work."""
+    L = m.lib
+    ws = m.ffn_workspace_bytes(1, 8, 2560, 768)
+    far = ctypes.c_void_p(1 << 24)
+
+    def call(w, wr=FAKE, r_in=FAKE, r_out=far, lg=FAKE, eps=1e-6, M=1, k=8, n=ws):
+        return L.moe_layer_rmsnorm_router_mxfp4(ctypes.byref(w), wr, r_in, M, k, eps, lg, r_out, None, None,
+                                                FAKE, n, None)
+
+    assert call(_weights(m), wr=None) == -1 and b"w_router" in L.moedec_last_error()
+    assert call(_weights(m), wr=ctypes.c_void_p((1 << 20) + 8)) == -2
+    assert call(_weights(m), r_in=None) == -1
+    assert call(_weights(m), lg=None) == -1
+    assert call(_weights(m, magic=1)) == -4
+    assert call(_weights(m), eps=2.0) == -3
+    assert call(_weights(m), r_out=ctypes.c_void_p((1 << 20) + 4096)) == -3     # overlaps r_in
+    assert call(_weights(m), M=0) == -3 and call(_weights(m), k=0) == -3
     assert call(_weights(m), n=ws - 1) == -5
 
 

@@ -529,6 +529,71 @@ def test_residual_layer_ling_m1(m, ling_layer):
                     "residual ling M=1")
 
 
+def _router_chain_stack(m, layers, routers, r0, k, expert_fns, shareds, what, eps=1e-6):
+    """Layers routed from their own data (moe_layer_rmsnorm_router): per
+    layer, x = bf16(RMSNorm(r)); the router logits equal the router GEMV on
+    that exported x bit for bit (so the router and the layer used one x) and
+    the float64 oracle's within the float32 tolerance; the experts chosen are
+    a valid top-k of the oracle logits under the near-tie rule; y equals the
+    layer on (x, logits) bit for bit and the oracle within tolerance; r
+    advances by exactly y."""
+    M, H = r0.shape
+    W0 = layers[0]
+    ws = m.make_ffn_workspace(M, k, W0.H, W0.I, "cuda")
+    r = torch.from_numpy(r0).cuda()
+    for L, (W, wr_bits) in enumerate(zip(layers, routers)):
+        say(f"{what} layer {L}")
+        wr = bf16_tensor(wr_bits)
+        x_out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        y32 = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        r_out, lg = m.moe_layer_rmsnorm_router(W, wr, r, k, ws, eps=eps, x_out=x_out, y_f32=y32)
+        lg_plain = m.router_logits(wr, x_out)
+        ids, w, _ = m.route_topk(lg, k)
+        _, y32_plain = m.moe_layer(W, x_out, lg, k, ws)
+        torch.cuda.synchronize()
+        assert m.check_ffn_workspace(ws) == 0
+        r_in_h, r_out_h, y_h, lg_h = r.cpu().numpy(), r_out.cpu().numpy(), y32.cpu().numpy(), lg.cpu().numpy()
+        xb = bits_of(x_out)
+        _check_rmsnorm_x(xb, r_in_h, eps, f"{what} layer {L}")
+        np.testing.assert_array_equal(lg_h.view(np.uint32), lg_plain.cpu().numpy().view(np.uint32))
+        ref_lg = oracle.router_logits(synth.bf16_values(wr_bits), synth.bf16_values(xb))
+        check_acc(lg_h, ref_lg, f"{what} layer {L} router logits")
+        _check_route_from_router(ids.cpu().numpy(), w.cpu().numpy(), ref_lg, k, f"{what} layer {L}")
+        np.testing.assert_array_equal(y_h, y32_plain.cpu().numpy())
+        _, _, ref_y = oracle_layer(xb, lg_h, k, expert_fns[L], shareds[L])
+        check_acc(y_h, ref_y, f"{what} layer {L}")
+        np.testing.assert_array_equal(r_out_h, r_in_h + y_h)
+        r = r_out
+
+
+@pytest.mark.parametrize("M,scale,eps", [(1, 3.0, 1e-6), (4, 3.0, 1e-6), (3, 1e-3, 2e-6), (2, 1.0, 0.5)])
+def test_router_chain_stack_tiny(m, M, scale, eps):
+    """Three tiny layers, each with its own router, routed from the residual
+    stream alone."""
+    shape = synth.TINY
+    layers, efs, shs, wrs = [], [], [], []
+    for L in range(3):
+        W, _, _, ef, sh, k = _host_layer_case(m, shape, M, seed=6, layer=L,
+                                              logits=synth.logits_f32(6, L, M, shape.E))
+        layers.append(W)
+        efs.append(ef)
+        shs.append(sh)
+        wrs.append(synth.router_weight_bf16(6, L, shape.E, shape.H))
+    r0 = (np.random.default_rng(9).standard_normal((M, shape.H)) * scale).astype(np.float32)
+    _router_chain_stack(m, layers, wrs, r0, k, efs, shs, f"router chain tiny M={M} scale={scale}", eps=eps)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_router_chain_ling(m, ling_layer, M):
+    """The Ling-shaped layer (512 experts, top-8, H = 2560) behind a 512 x 2560
+    router, two steps on the residual stream."""
+    wrs = [synth.router_weight_bf16(1, L, synth.LING.E, synth.LING.H) for L in range(2)]
+    r0 = np.random.default_rng(10 + M).standard_normal((M, synth.LING.H)).astype(np.float32)
+    ef = [_ling_expert] * 2
+    sh = [_ling_expert(synth.LING.E)] * 2
+    _router_chain_stack(m, [ling_layer, ling_layer], wrs, r0, 8, ef, sh, f"router chain ling M={M}")
+
+
 def test_paths_share_one_workspace(m):
     """The fused and two-call paths alternate on one workspace with different
     M; every call still matches the oracle (launch generations stay in step)."""
