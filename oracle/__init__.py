@@ -47,3 +47,4 @@ __all__ = [
     "expert_ffn", "moe_layer", "rmsnorm",
     "lmhead_quant_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "lmhead_argmax", "lmhead_sample",
 ]
+from .shared_fp8 import quant_fp8_rows, dequant_fp8_rows, shared_fp8_dense

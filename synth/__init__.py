@@ -136,6 +136,7 @@ def _rng(seed, stream):
 # Stream numbers for Gaussian tensors.
 GAUSS_X, GAUSS_LOGITS, GAUSS_ROUTER, GAUSS_LMHEAD_W, GAUSS_LMHEAD_X = 1, 2, 3, 4, 5
 GAUSS_ROUTER_W = 6
+GAUSS_SHARED_W = 7
 
 
 def bf16_bits_from_f32(v):
@@ -178,6 +179,18 @@ def router_weight_bf16(seed, layer, n_experts, hidden):
     that with N(0,1) activations the logits are about N(0,1)."""
     g = _rng(seed, GAUSS_ROUTER_W * 1000 + layer).standard_normal((n_experts, hidden), dtype=np.float32)
     return bf16_bits_from_f32(g * np.float32(1.0 / np.sqrt(hidden)))
+
+
+def shared_expert_bf16(seed, layer, hidden, inter):
+    """bf16 source weights of a shared expert stored in FP8 (uint16 patterns):
+    W_gate, W_up [inter][hidden] ~ N(0, 1/hidden) and W_down [hidden][inter]
+    ~ N(0, 1/inter), so that with N(0,1) activations g, u and y are about
+    N(0,1)."""
+    rng = _rng(seed, GAUSS_SHARED_W * 1000 + layer)
+    g = rng.standard_normal((inter, hidden), dtype=np.float32) * np.float32(1.0 / np.sqrt(hidden))
+    u = rng.standard_normal((inter, hidden), dtype=np.float32) * np.float32(1.0 / np.sqrt(hidden))
+    d = rng.standard_normal((hidden, inter), dtype=np.float32) * np.float32(1.0 / np.sqrt(inter))
+    return bf16_bits_from_f32(g), bf16_bits_from_f32(u), bf16_bits_from_f32(d)
 
 
 def lmhead_weight_bf16(seed, vocab, hidden, std=0.02, row_start=0, n_rows=None):
