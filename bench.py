@@ -216,6 +216,54 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
     return res
 
 
+def shared_fp8_bench(m, torch, synth, layers, steps, dev):
+    """The fused layer with its shared expert stored in FP8 (E4M3, float32 row
+    scales; pack_shared_fp8 of seeded bf16 weights per layer) instead of MXFP4,
+    the routed experts unchanged, at M = 1 and 4 (steps cycle over the layers)."""
+    import numpy as np
+    n_layers = len(layers)
+    shape = synth.LING
+    E, H, I, k = shape.E, shape.H, shape.I, shape.k
+    s8 = m.shared_fp8_sizes(H, I)
+    sh_bytes = s8.gu_codes + s8.gu_scales + s8.dn_codes + s8.dn_scales
+    fp8_layers = []
+    for L, W in enumerate(layers):
+        g, u, d = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+                   for a in synth.shared_expert_bf16(0, L, H, I))
+        sh8 = m.pack_shared_fp8(g, u, d)
+        fp8_layers.append(m.MoELayerWeights(E, H, I, W.gu_codes, W.gu_scales, W.dn_codes, W.dn_scales,
+                                            shared_fp8=sh8))
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    out = {"shared_bytes_fp8": sh_bytes, "shared_bytes_mxfp4": EXPERT_BYTES_LING}
+    for M in (1, 4):
+        xs, lgs = layer_inputs(synth, n_layers, M, dev)
+        ws = m.make_ffn_workspace(M, k, H, I, dev)
+        ys = [torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
+        disp = [torch.zeros(m.DISPATCH_BYTES, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+
+        def step(i):
+            L = i % n_layers
+            m.moe_layer(fp8_layers[L], xs[L], lgs[L], k, ws, y=ys[L], want_f32=False, dispatch=disp[L])
+
+        for i in range(n_layers):
+            step(i)
+        torch.cuda.synchronize()
+        n_routed = [m.decode_dispatch(dd)["n_slots"] - 1 for dd in disp]
+        act = M * E * 4 + 2 * M * H * 2
+        step_bytes = sum(n_routed[i % n_layers] * EXPERT_BYTES_LING + sh_bytes + act for i in range(steps)) / steps
+        g_main = capture(torch, lambda: [step(i) for i in range(steps)])
+        g_main.replay()
+        ms = t.run(g_main.replay)
+        m.check_ffn_workspace(ws)
+        out[f"m{M}_us_per_layer"] = 1e3 * ms / steps
+        out[f"m{M}_bytes_per_layer"] = step_bytes
+        out[f"m{M}_gbs"] = step_bytes / (1e6 * ms / steps)
+        del g_main
+    del fp8_layers
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Cold stack: the layers in sequence on a residual stream
 
@@ -728,6 +776,8 @@ def main(argv=None):
     if not args.no_m4:
         r4 = moe_bench(m, torch, synth, layers, 4, args.steps, args.warmup, dev)
         log("M=4:", json.dumps(r4))
+    sh8 = shared_fp8_bench(m, torch, synth, layers, args.steps, dev)
+    log("FP8 shared:", json.dumps(sh8))
     stack = None
     if not args.no_stack:
         stack = stack_bench(m, torch, synth, layers, args.stack_passes, max(1, args.stack_passes // 10), dev)
@@ -786,7 +836,7 @@ def main(argv=None):
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "traffic_m4": None if traffic4 is None else {k: traffic4[k] for k in (
             "fetch_bytes", "write_bytes", "traffic_bytes", "algorithmic_bytes", "traffic_over_algorithmic")},
-        "extra": {"m1": r1, "m4": r4, "stack": stack, "router": router, "lmhead": lm,
+        "extra": {"m1": r1, "m4": r4, "stack": stack, "router": router, "lmhead": lm, "fp8_shared": sh8,
                   "cpu": cpu},
     }
     if router is not None:
@@ -800,6 +850,8 @@ def main(argv=None):
         line["stack_us_per_layer_graph"] = round(stack["us_per_layer_graph"], 3)
         line["stack_us_per_layer_eager"] = round(stack["us_per_layer_eager"], 3)
         line["stack_norm_router_layer_us_graph"] = round(stack["routed_us_per_layer_graph"], 3)
+    line["fp8_shared_us_per_layer_m1"] = round(sh8["m1_us_per_layer"], 3)
+    line["fp8_shared_us_per_layer_m4"] = round(sh8["m4_us_per_layer"], 3)
     if lm is not None:
         line["lmhead_fp8_gbs_m1"] = round(lm["fp8_m1_gbs"], 1)
         line["lmhead_fp8_argmax_us_m1"] = round(lm["fp8_argmax_m1_us"], 2)

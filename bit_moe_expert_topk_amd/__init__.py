@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 from ._lib import (Dispatch, LMHeadFP8Desc, MoEWeights, MXFP4Sizes, MAX_E, MAX_K, MAX_M,
-                   MAX_SLOTS, MOE_MAGIC, LMHEAD_MAGIC, FMT_E4M3FN_ROWSCALE_F32)
+                   MAX_SLOTS, MOE_MAGIC, MOE_MAGIC_SHARED_FP8, LMHEAD_MAGIC, FMT_E4M3FN_ROWSCALE_F32)
 
 lib = _lib.lib
 LIB_PATH = _lib.LIB_PATH
@@ -134,29 +134,44 @@ def pack_down(down_codes, down_scales, out_codes=None, out_scales=None):
 
 
 class MoELayerWeights:
-    """Packed MXFP4 weights of one MoE layer: E routed experts + 1 shared.
+    """Packed weights of one MoE layer: E routed MXFP4 experts + 1 shared.
 
-    The four packed arrays hold E+1 consecutive experts; the last one is the
-    shared expert.  Tensors are kept alive by this object.
+    The four packed arrays hold E+1 consecutive MXFP4 experts; the last one is
+    the shared expert -- unless shared_fp8 (the four tensors of
+    pack_shared_fp8) is given, which then is the shared expert (the arrays
+    need only E experts).  Tensors are kept alive by this object.
     """
 
-    def __init__(self, E, H, I, gu_codes, gu_scales, dn_codes, dn_scales):
+    def __init__(self, E, H, I, gu_codes, gu_scales, dn_codes, dn_scales, shared_fp8=None):
         self.E, self.H, self.I = E, H, I
         self.sizes = packed_sizes(H, I)
         sz = self.sizes
+        n_mx = E if shared_fp8 is not None else E + 1
         for t, per in ((gu_codes, sz.gu_codes), (gu_scales, sz.gu_scales),
                        (dn_codes, sz.dn_codes), (dn_scales, sz.dn_scales)):
             _need(t, torch.uint8, "packed weights")
-            if t.numel() < (E + 1) * per:
-                raise ValueError(f"packed array has {t.numel()} bytes, need {(E + 1) * per}")
+            if t.numel() < n_mx * per:
+                raise ValueError(f"packed array has {t.numel()} bytes, need {n_mx * per}")
         self.gu_codes, self.gu_scales = gu_codes, gu_scales
         self.dn_codes, self.dn_scales = dn_codes, dn_scales
+        self.shared_fp8 = shared_fp8
         base = lambda t: t.data_ptr()
-        self.desc = MoEWeights(
-            MOE_MAGIC, E, H, I,
-            base(gu_codes), base(gu_scales), base(dn_codes), base(dn_scales),
-            base(gu_codes) + E * sz.gu_codes, base(gu_scales) + E * sz.gu_scales,
-            base(dn_codes) + E * sz.dn_codes, base(dn_scales) + E * sz.dn_scales)
+        if shared_fp8 is None:
+            magic = MOE_MAGIC
+            shared = (base(gu_codes) + E * sz.gu_codes, base(gu_scales) + E * sz.gu_scales,
+                      base(dn_codes) + E * sz.dn_codes, base(dn_scales) + E * sz.dn_scales)
+        else:
+            s8 = shared_fp8_sizes(H, I)
+            sgc, sgs, sdc, sds = shared_fp8
+            for t, dt, n in ((sgc, torch.uint8, s8.gu_codes), (sgs, torch.float32, s8.gu_scales // 4),
+                             (sdc, torch.uint8, s8.dn_codes), (sds, torch.float32, s8.dn_scales // 4)):
+                _need(t, dt, "FP8 shared expert")
+                if t.numel() != n:
+                    raise ValueError(f"FP8 shared expert array has {t.numel()} elements, need {n}")
+            magic = MOE_MAGIC_SHARED_FP8
+            shared = (base(sgc), base(sgs), base(sdc), base(sds))
+        self.desc = MoEWeights(magic, E, H, I, base(gu_codes), base(gu_scales), base(dn_codes),
+                               base(dn_scales), *shared)
 
     @classmethod
     def from_canonical(cls, gate, up, down, E):
@@ -167,6 +182,32 @@ class MoELayerWeights:
         H = 2 * gate[0].shape[2]
         I = gate[0].shape[1]
         return cls(E, H, I, gu_c, gu_s, dn_c, dn_s)
+
+
+def shared_fp8_sizes(H, I):
+    out = MXFP4Sizes()
+    _check(lib.moedec_shared_fp8_packed_sizes(H, I, ctypes.byref(out)))
+    return out
+
+
+def pack_shared_fp8(gate, up, down):
+    """Quantise a shared expert's bf16 W_gate, W_up [I][H] and W_down [H][I] to
+    E4M3 with a float32 scale per row, in the FP8 streaming layout: returns
+    (gu_codes uint8, gu_scales float32 [2I], dn_codes uint8, dn_scales float32 [H])."""
+    for t, n in ((gate, "gate"), (up, "up"), (down, "down")):
+        _need(t, torch.bfloat16, n, 2)
+    I, H = gate.shape
+    if tuple(up.shape) != (I, H) or tuple(down.shape) != (H, I):
+        raise ValueError("gate, up must be [I][H] and down [H][I]")
+    sz = shared_fp8_sizes(H, I)
+    dev = gate.device
+    gu_c = torch.empty(sz.gu_codes, dtype=torch.uint8, device=dev)
+    gu_s = torch.empty(2 * I, dtype=torch.float32, device=dev)
+    dn_c = torch.empty(sz.dn_codes, dtype=torch.uint8, device=dev)
+    dn_s = torch.empty(H, dtype=torch.float32, device=dev)
+    _check(lib.moe_pack_shared_fp8(_ptr(gate), _ptr(up), _ptr(down), H, I, _ptr(gu_c), _ptr(gu_s), _ptr(dn_c),
+                                   _ptr(dn_s), _stream(gate)))
+    return gu_c, gu_s, dn_c, dn_s
 
 
 def ffn_workspace_bytes(M, k_max, H, I):

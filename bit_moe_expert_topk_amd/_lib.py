@@ -31,6 +31,7 @@ MAX_E = 1024
 MAX_SLOTS = MAX_M * MAX_K + 1
 
 MOE_MAGIC = 0x4D4F4534
+MOE_MAGIC_SHARED_FP8 = 0x4D4F4538
 LMHEAD_MAGIC = 0x4C4D4838
 FMT_E4M3FN_ROWSCALE_F32 = 1
 
@@ -92,6 +93,9 @@ SIGNATURES = {
     "moe_pack_gateup_mxfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                       c_void_p, c_void_p, c_void_p]),
     "moe_pack_down_mxfp4": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "moedec_shared_fp8_packed_sizes": (c_int, [c_int, c_int, ctypes.POINTER(MXFP4Sizes)]),
+    "moe_pack_shared_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p]),
     "moe_ffn_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
     "moe_expert_ffn_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_int, c_void_p, c_int,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -188,10 +188,30 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_c
 #define MOEDEC_FP4X2_F32(w, scale, sel) __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((w), (scale), (sel))
 // Two E4M3 codes (16-bit half `hi` of `w`, low byte first) as a bf16 pair.
 #define MOEDEC_FP8X2_BF16(w, hi) __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((w), 1.0f, (hi))
+// Two E4M3 codes (bytes 0-1, or 2-3 when hi) to exact float32 values.
+#define MOEDEC_FP8X2_F32(w, hi) __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((w), 1.0f, (hi))
 
 // acc + a.x*b.x + a.y*b.y with bf16 inputs, float32 accumulate.
 __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
+
+// E4M3 magnitude code (0x00..0x7E) of a non-negative float32 q: nearest
+// value, ties to the even code, saturating at 448.  At and above 2^-6 the code
+// keeps 3 of the 23 mantissa bits (round to nearest even on the 20 dropped
+// bits) and rebiases the exponent from 127 to 7; below 2^-6 it is q / 2^-9
+// rounded to the nearest even integer, read from the low bits of q + 2^14
+// (whose float32 spacing is 2^-9).  Values above 448 and NaN give codes above
+// 0x7E and are clamped to it; CLAMP = false leaves that out for quotients
+// known to stay below 464, the midpoint above 448.
+template <bool CLAMP = true>
+__device__ __forceinline__ uint32_t e4m3_mag_code(float q) {
+    const uint32_t b = __float_as_uint(q);
+    const uint32_t nrm = (b + (0x7FFFFu - (120u << 23)) + ((b >> 20) & 1u)) >> 20;
+    const uint32_t sub = __float_as_uint(q + 16384.0f) - 0x46800000u;
+    const uint32_t c = b >= 0x3C800000u ? nrm : sub;
+    if constexpr (CLAMP) return c < 0x7Eu ? c : 0x7Eu;
+    return c;
 }
 
 // RMSNorm factors inv[m] = 1 / sqrt(mean(r_m^2) + eps) of M_T tokens of H

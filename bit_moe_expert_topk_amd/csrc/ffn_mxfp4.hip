@@ -149,6 +149,10 @@ struct FfnArgs {
     int h_bytes;                     // size of h (device-coherent buffer loads)
     uint16_t* y_bf16;                // [M][H] or null
     float* y_f32;                    // [M][H] or null
+    // The shared expert in FP8 (instantiations with SH8): sh_gu_codes and
+    // sh_dn_codes then hold the FP8 layout of pack.hip and these its row scales.
+    const float* sh8_gu_scale;       // gate [I], then up [I]
+    const float* sh8_dn_scale;       // [H]
 };
 
 struct SlotTable {
@@ -437,14 +441,79 @@ __device__ __forceinline__ void gateup_issue_e(const FfnArgs& a, int e, int rg, 
     }
 }
 
-template <int M_T, int NB>
+// FP8 shared expert (SH8): a wave's chunks (64 values per row each, 16 codes
+// per lane) go in rounds of NB; this issues round `round` of unit rg.
+template <int NB>
+__device__ __forceinline__ void gateup_fp8_issue(const FfnArgs& a, int rg, int round, GuLoads<NB>& L) {
+    const int w = wave_id_uniform();
+    const int lane = lane_id();
+    const int kh8 = 2 * a.kbh4;
+    const int cpw = (kh8 + kWaves - 1) / kWaves;
+    const int c_begin = w * cpw;
+    const int c_end = min(kh8, c_begin + cpw);
+    const uint8_t* ub = a.sh_gu_codes + (size_t)rg * kh8 * 2048 + lane * 16;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int c = max(0, min(c_begin + round * NB + i, c_end - 1));   // clamped; extra loads unused
+        L.cg[i] = load_stream16(ub + (size_t)c * 2048);
+        L.cu[i] = load_stream16(ub + (size_t)c * 2048 + 1024);
+    }
+}
+
+template <int M_T, int NB, bool SH8 = false>
 __device__ __forceinline__ void gateup_issue(const FfnArgs& a, const SlotTable& T, int u, GuLoads<NB>& L) {
     const int s = u / a.gu_units;
     const int rg = u - s * a.gu_units;
     if (s >= T.n_slots) return;
     const int e = T.expert[s];
     if (e < 0) return;
+    if (SH8 && e == a.E) {
+        gateup_fp8_issue<NB>(a, rg, 0, L);
+        return;
+    }
     gateup_issue_e<M_T, NB>(a, e, rg, L);
+}
+
+// The end of a gate/up unit: sum the four 16-lane rows (cross-lane), then the
+// four waves (LDS); with SCALED, times the row scales sg, su (wave 0's lanes);
+// h = silu(g) * u, published as tagged words.
+template <int M_T, bool SCALED>
+__device__ __forceinline__ void gateup_finish(const FfnArgs& a, uint8_t* lds, int s, int rg, uint32_t mask,
+                                              const float (&accg)[M_T], const float (&accu)[M_T], uint32_t gen,
+                                              float sg, float su) {
+    const int w = wave_id_uniform();
+    const int lane = lane_id();
+    float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][2][16]
+#pragma unroll
+    for (int m = 0; m < M_T; ++m) {
+        const float g = row_sum_f32(accg[m]);
+        const float uu = row_sum_f32(accu[m]);
+        if (lane < kUnitRows) {
+            red[((w * M_T + m) * 2 + 0) * kUnitRows + lane] = g;
+            red[((w * M_T + m) * 2 + 1) * kUnitRows + lane] = uu;
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        if (lane < kUnitRows) {
+#pragma unroll
+            for (int m = 0; m < M_T; ++m) {
+                if (!((mask >> m) & 1u)) continue;
+                float g = 0.f, uu = 0.f;
+#pragma unroll
+                for (int v = 0; v < kWaves; ++v) {
+                    g += red[((v * M_T + m) * 2 + 0) * kUnitRows + lane];
+                    uu += red[((v * M_T + m) * 2 + 1) * kUnitRows + lane];
+                }
+                if constexpr (SCALED) {
+                    g *= sg;
+                    uu *= su;
+                }
+                const float hv = g / (1.f + expf(-g)) * uu;
+                store_tagged(&a.h[((size_t)s * M_T + m) * a.I + kUnitRows * rg + lane], gen, hv);
+            }
+        }
+    }
 }
 
 // Finish a gate/up unit whose loads gateup_issue put in L: the dot products
@@ -502,40 +571,70 @@ __device__ void gateup_compute(const FfnArgs& a, const SlotTable& T, uint8_t* ld
         if (M_T > 2) __builtin_amdgcn_sched_barrier(0);
     }
 
-    // sum the four 16-lane rows (cross-lane), then the four waves (LDS)
-    float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][2][16]
-#pragma unroll
-    for (int m = 0; m < M_T; ++m) {
-        const float g = row_sum_f32(accg[m]);
-        const float uu = row_sum_f32(accu[m]);
-        if (lane < kUnitRows) {
-            red[((w * M_T + m) * 2 + 0) * kUnitRows + lane] = g;
-            red[((w * M_T + m) * 2 + 1) * kUnitRows + lane] = uu;
-        }
+    gateup_finish<M_T, false>(a, lds, s, rg, mask, accg, accu, gen, 1.f, 1.f);
+}
+
+// The shared expert's gate/up unit rg in FP8 (SH8): round 0 of its loads is in
+// L (gateup_fp8_issue), later rounds are issued here; codes become exact bf16
+// pairs that meet x (LDS) in float32 dot products, and the row scales multiply
+// the finished sums.
+template <int M_T, int NB>
+__device__ void gateup_fp8_unit(const FfnArgs& a, const SlotTable& T, uint8_t* lds, int rg, uint32_t gen,
+                                GuLoads<NB> L) {
+    const uint32_t mask = T.mask[0];
+    const int w = wave_id_uniform();
+    const int lane = lane_id();
+    const int kh8 = 2 * a.kbh4;
+    const int cpw = (kh8 + kWaves - 1) / kWaves;
+    const int c_begin = w * cpw;
+    const int n_c = min(kh8, c_begin + cpw) - c_begin;
+    float sg = 1.f, su = 1.f;                           // row scales, needed by wave 0's lanes < 16
+    if (w == 0 && lane < kUnitRows) {
+        sg = a.sh8_gu_scale[kUnitRows * rg + lane];
+        su = a.sh8_gu_scale[a.I + kUnitRows * rg + lane];
     }
-    __syncthreads();
-    if (w == 0) {
-        if (lane < kUnitRows) {
+    const int xtok = a.kbh4 * 4 * kXBlock;
+    const int quarter = lane >> 4;
+    float accg[M_T], accu[M_T];
 #pragma unroll
-            for (int m = 0; m < M_T; ++m) {
-                if (!((mask >> m) & 1u)) continue;
-                float g = 0.f, uu = 0.f;
+    for (int m = 0; m < M_T; ++m) accg[m] = accu[m] = 0.f;
+    for (int round = 0; round * NB < n_c; ++round) {
+        if (round > 0) gateup_fp8_issue<NB>(a, rg, round, L);
 #pragma unroll
-                for (int v = 0; v < kWaves; ++v) {
-                    g += red[((v * M_T + m) * 2 + 0) * kUnitRows + lane];
-                    uu += red[((v * M_T + m) * 2 + 1) * kUnitRows + lane];
+        for (int i = 0; i < NB; ++i) {
+            if (round * NB + i < n_c) {
+                const int c = c_begin + round * NB + i;
+                bf16x2 wg[8], wu[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    wg[j] = (j & 1) ? MOEDEC_FP8X2_BF16(L.cg[i][j >> 1], true) : MOEDEC_FP8X2_BF16(L.cg[i][j >> 1], false);
+                    wu[j] = (j & 1) ? MOEDEC_FP8X2_BF16(L.cu[i][j >> 1], true) : MOEDEC_FP8X2_BF16(L.cu[i][j >> 1], false);
                 }
-                const float hv = g / (1.f + expf(-g)) * uu;
-                store_tagged(&a.h[((size_t)s * M_T + m) * a.I + kUnitRows * rg + lane], gen, hv);
+                // the lane's 16 values of x: block 2c + quarter / 2, half quarter % 2
+                const uint8_t* xq = lds + (2 * c + (quarter >> 1)) * kXBlock + (quarter & 1) * 32;
+#pragma unroll
+                for (int m = 0; m < M_T; ++m) {
+                    if (M_T > 1 && !((mask >> m) & 1u)) continue;
+                    const u32x4* xp = reinterpret_cast<const u32x4*>(xq + m * xtok);
+                    const u32x4 xr[2] = {xp[0], xp[1]};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const bf16x2 xx = as_bf16x2(xr[j >> 2][j & 3]);
+                        accg[m] = dot2_bf16(wg[j], xx, accg[m]);
+                        accu[m] = dot2_bf16(wu[j], xx, accu[m]);
+                    }
+                }
             }
+            if (M_T > 2) __builtin_amdgcn_sched_barrier(0);
         }
     }
+    gateup_finish<M_T, true>(a, lds, 0, rg, mask, accg, accu, gen, sg, su);
 }
 
 // ---------------------------------------------------------------------------
 // down unit
 
-template <int M_T, bool ONE>
+template <int M_T, bool ONE, bool SH8 = false>
 __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, uint32_t gen) {
     const int n_nc = (a.max_groups - 1) * a.dn_units;    // units of groups 1.. come first
     int grp, g;
@@ -555,8 +654,25 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     const int pbase = T.start[sb];
     const int n_pairs = T.start[se] - pbase;
 
-    // this wave's items: (slot, chunk), chunk fastest, over the group's slots
-    const int n_items = (se - sb) * a.kbi4;
+    // this wave's items: (slot, chunk), chunk fastest, over the group's slots.
+    // With SH8 the shared expert (slot 0, first in group 0) is FP8: its chunks
+    // hold 64 values per row, so it has twice the chunks (kbi8) of a slot.
+    const bool sh8g = SH8 && grp == 0;
+    const int kbi8 = 2 * a.kbi4;
+    const int n_items = (se - sb) * a.kbi4 + (sh8g ? a.kbi4 : 0);
+    auto item_pos = [&](int i, int& ls, int& ch) {
+        if (sh8g && i >= kbi8) {
+            ls = 1 + (i - kbi8) / a.kbi4;
+            ch = (i - kbi8) - (ls - 1) * a.kbi4;
+        } else if (sh8g) {
+            ls = 0;
+            ch = i;
+        } else {
+            ls = i / a.kbi4;
+            ch = i - ls * a.kbi4;
+        }
+    };
+    auto item_len = [&](int ls) { return (sh8g && ls == 0) ? kbi8 : a.kbi4; };
     const int i_begin = (w * n_items) / kWaves;
     const int i_end = ((w + 1) * n_items) / kWaves;
     constexpr int SUB = dn_sub<M_T, ONE>();
@@ -574,23 +690,33 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     // items past i_end load the last item again (unused); the walk over
     // (slot, chunk) is branch-free so that no per-item state is carried
     auto load_batch = [&](int i0, u32x4 (&cw)[kDnBatch][SUB], uint32_t (&scw)[kDnBatch][SUB]) {
-        int ls = i0 / a.kbi4;
-        int ch = i0 - ls * a.kbi4;
+        int ls, ch;
+        item_pos(i0, ls, ch);
 #pragma unroll
         for (int k = 0; k < kDnBatch; ++k) {
             const int e = max(T.expert[sb + ls], 0);
             const bool shared = e == a.E;
-            const size_t ce = shared ? 0 : (size_t)e * a.dn_codes_stride;
-            const size_t se = shared ? 0 : (size_t)e * a.dn_scales_stride;
-            const uint8_t* cp = (shared ? a.sh_dn_codes : a.dn_codes) + ce + rg_codes + ch * 1024 + lane * 16;
-            const uint8_t* sp = (shared ? a.sh_dn_scales : a.dn_scales) + se + rg_scales + ch * 64 + lane;
+            if (SH8 && shared) {
+                // FP8 layout: row block rb, chunk ch at (rb * kbi8 + ch) KiB
+                const uint8_t* cp = a.sh_dn_codes + ((size_t)(SUB * g) * kbi8 + ch) * 1024 + lane * 16;
 #pragma unroll
-            for (int j = 0; j < SUB; ++j) {
-                cw[k][j] = load_stream16(cp + j * sub_codes);
-                scw[k][j] = sp[j * sub_scales];
+                for (int j = 0; j < SUB; ++j) {
+                    cw[k][j] = load_stream16(cp + (size_t)j * kbi8 * 1024);
+                    scw[k][j] = 0u;
+                }
+            } else {
+                const size_t ce = shared ? 0 : (size_t)e * a.dn_codes_stride;
+                const size_t se = shared ? 0 : (size_t)e * a.dn_scales_stride;
+                const uint8_t* cp = (shared ? a.sh_dn_codes : a.dn_codes) + ce + rg_codes + ch * 1024 + lane * 16;
+                const uint8_t* sp = (shared ? a.sh_dn_scales : a.dn_scales) + se + rg_scales + ch * 64 + lane;
+#pragma unroll
+                for (int j = 0; j < SUB; ++j) {
+                    cw[k][j] = load_stream16(cp + j * sub_codes);
+                    scw[k][j] = sp[j * sub_scales];
+                }
             }
             const bool adv = i0 + k + 1 < i_end;
-            const bool wrap = ch + 1 == a.kbi4;
+            const bool wrap = ch + 1 == item_len(ls);
             ls += (adv && wrap) ? 1 : 0;
             ch = adv ? (wrap ? 0 : ch + 1) : ch;
         }
@@ -599,6 +725,11 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
     // loaded now (ahead of the weights) rather than after the combine.
     constexpr int kRowsU = SUB * kUnitRows;                     // output rows of this unit
     float rin[M_T];
+    // SH8: the FP8 shared expert's row scales of this unit's rows (group 0),
+    // loaded now by the first SUB * 16 threads and kept in the reduction
+    // area of LDS (unused until the end of the unit) once h is staged
+    float sd_own = 0.f;
+    if (sh8g && tid < SUB * kUnitRows) sd_own = a.sh8_dn_scale[kUnitRows * SUB * g + tid];
     if (grp == 0 && a.r_out != nullptr && w == 0) {
         const int row = kRowsU * g + (lane & (kRowsU - 1));
 #pragma unroll
@@ -688,6 +819,8 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
             }
         }
     }
+    float* sd_lds = reinterpret_cast<float*>(lds + a.red_off);   // [SUB][16] (SH8, group 0)
+    if (sh8g && tid < SUB * kUnitRows) sd_lds[tid] = sd_own;
     __syncthreads();
 
     const int quarter = lane >> 4;
@@ -700,11 +833,40 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
 #pragma unroll
             for (int m = 0; m < M_T; ++m) acc[c][j][m] = 0.f;
     auto compute_batch = [&](int i0, const u32x4 (&cw)[kDnBatch][SUB], const uint32_t (&scw)[kDnBatch][SUB]) {
-        int ls = i0 / a.kbi4;
-        int ch = i0 - ls * a.kbi4;
+        int ls, ch;
+        item_pos(i0, ls, ch);
 #pragma unroll
         for (int k = 0; k < kDnBatch; ++k) {
-            if (i0 + k < i_end) {
+            if (SH8 && sh8g && ls == 0 && i0 + k < i_end) {
+                // FP8 item: the lane's 16 values of h (block 2ch + quarter / 2,
+                // half quarter % 2) against 16 codes per row block, each code's
+                // exact value times its row's scale
+                const uint8_t* hq = lds + (2 * ch + (quarter >> 1)) * kHBlock + (quarter & 1) * 64;
+                const uint32_t msk = (M_T == 1) ? 1u : T.mask[sb];
+                int p = 0;
+#pragma unroll
+                for (int m = 0; m < M_T; ++m) {
+                    if (M_T > 1 && !((msk >> m) & 1u)) continue;
+                    const float4* hp = reinterpret_cast<const float4*>(hq + p * a.pair_bytes);
+                    ++p;
+                    float4 hv[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) hv[v] = hp[v];
+#pragma unroll
+                    for (int j = 0; j < SUB; ++j) {
+                        const float sj = sd_lds[j * kUnitRows + (lane & 15)];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const f32x2 w0 = MOEDEC_FP8X2_F32(cw[k][j][v], false);
+                            const f32x2 w1 = MOEDEC_FP8X2_F32(cw[k][j][v], true);
+                            acc[0][j][m] = fmaf(w0.x * sj, hv[v].x, acc[0][j][m]);
+                            acc[1 % kCh][j][m] = fmaf(w0.y * sj, hv[v].y, acc[1 % kCh][j][m]);
+                            acc[2 % kCh][j][m] = fmaf(w1.x * sj, hv[v].z, acc[2 % kCh][j][m]);
+                            acc[3 % kCh][j][m] = fmaf(w1.y * sj, hv[v].w, acc[3 % kCh][j][m]);
+                        }
+                    }
+                }
+            } else if (i0 + k < i_end) {
                 const int s = sb + ls;
                 // one token: every slot serves it, so slot sb + j holds pair j
                 // (no table lookups on the way to the LDS reads)
@@ -747,7 +909,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
                     }
                 }
             }
-            if (++ch == a.kbi4) {
+            if (++ch == item_len(ls)) {
                 ch = 0;
                 ++ls;
             }
@@ -768,6 +930,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
         }
     }
 
+    if (sh8g) __syncthreads();                                  // every wave is done with sd_lds
     float* red = reinterpret_cast<float*>(lds + a.red_off);    // [waves][M_T][SUB][16]
 #pragma unroll
     for (int m = 0; m < M_T; ++m)
@@ -915,7 +1078,18 @@ __device__ __forceinline__ uint32_t gens_advance(const FfnArgs& a) {
     return g;
 }
 
-template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE>
+// A gate/up unit whose round-0 loads are in L: the FP8 shared expert's units
+// (slot 0 with SH8) or an MXFP4 unit.
+template <int M_T, int NB, bool SH8>
+__device__ __forceinline__ void gateup_run(const FfnArgs& a, const SlotTable& T, uint8_t* lds, int u, uint32_t gen,
+                                           const GuLoads<NB>& L) {
+    if (SH8 && u < a.gu_units)
+        gateup_fp8_unit<M_T, NB>(a, T, lds, u, gen, L);
+    else
+        gateup_compute<M_T, NB>(a, T, lds, u, gen, L);
+}
+
+template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE, bool SH8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(blocks_per_cu<ONE>())))
 void moe_ffn_kernel(FfnArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -933,7 +1107,10 @@ void moe_ffn_kernel(FfnArgs a) {
         // while the other blocks select their experts.
         if (unit0 < a.gu_units) {
             GuLoads<NB> cur;
-            gateup_issue_e<M_T, NB>(a, a.E, unit0, cur);
+            if constexpr (SH8)
+                gateup_fp8_issue<NB>(a, unit0, 0, cur);
+            else
+                gateup_issue_e<M_T, NB>(a, a.E, unit0, cur);
             u32x4 xv[kPieces];
             x_issue<M_T, NORM>(a, xv);
             if (tid == kThreads - kWave) s_gen = gens_advance(a);
@@ -944,7 +1121,7 @@ void moe_ffn_kernel(FfnArgs a) {
             }
             x_stage<M_T, NORM>(a, xv, lds);
             __syncthreads();
-            gateup_compute<M_T, NB>(a, T, lds, unit0, s_gen, cur);
+            gateup_run<M_T, NB, SH8>(a, T, lds, unit0, s_gen, cur);
             return;
         }
     }
@@ -994,8 +1171,8 @@ void moe_ffn_kernel(FfnArgs a) {
     if (ONE) {
         for (; u < a.n_gu; u += gridDim.x) {
             GuLoads<NB> cur;
-            gateup_issue<M_T, NB>(a, T, u, cur);
-            gateup_compute<M_T, NB>(a, T, lds, u, gen, cur);
+            gateup_issue<M_T, NB, SH8>(a, T, u, cur);
+            gateup_run<M_T, NB, SH8>(a, T, lds, u, gen, cur);
             __syncthreads();
         }
     } else if (u < a.n_gu) {
@@ -1003,22 +1180,22 @@ void moe_ffn_kernel(FfnArgs a) {
         // instead was slower at 4 tokens, 34.3 against 32.4 us: they compete
         // with the gate/up stream that every down unit waits for.)
         GuLoads<NB> cur, nxt;
-        gateup_issue<M_T, NB>(a, T, u, cur);
+        gateup_issue<M_T, NB, SH8>(a, T, u, cur);
         bool groups_pending = groups_late;
         for (; u < a.n_gu; u += gridDim.x) {
             const int un = u + gridDim.x;
-            if (un < a.n_gu) gateup_issue<M_T, NB>(a, T, un, nxt);
+            if (un < a.n_gu) gateup_issue<M_T, NB, SH8>(a, T, un, nxt);
             if (groups_pending) {                          // wave 0; published by the unit's barrier
                 table_groups(a, T);
                 groups_pending = false;
             }
-            gateup_compute<M_T, NB>(a, T, lds, u, gen, cur);
+            gateup_run<M_T, NB, SH8>(a, T, lds, u, gen, cur);
             cur = nxt;
             __syncthreads();
         }
     }
     for (; u < a.n_units; u += gridDim.x) {
-        down_unit<M_T, ONE>(a, T, lds, u - a.n_gu, gen);
+        down_unit<M_T, ONE, SH8>(a, T, lds, u - a.n_gu, gen);
         __syncthreads();
     }
 }
@@ -1049,7 +1226,7 @@ int device_cus() {
     return d.cus;
 }
 
-template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE>
+template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE, bool SH8>
 hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) {
     constexpr int kBlocksPerCU = blocks_per_cu<ONE>();
     // ONE: a block per unit (the host picks ONE only when they all fit)
@@ -1061,30 +1238,30 @@ hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) 
     if (v == 0) {
         int blocks = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE>), kThreads, lds);
+            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE, SH8>), kThreads, lds);
         if (e != hipSuccess) return e;
         v = (blocks >= kBlocksPerCU) ? 1 : 2;
         occ_ok[cls].store(v, std::memory_order_relaxed);
     }
     if (v != 1) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE, SH8>), dim3(grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
-template <int M_T, bool ROUTE, bool NORM, bool ONE>
+template <int M_T, bool ROUTE, bool NORM, bool ONE, bool SH8>
 hipError_t launch_nb(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     switch (nb) {
-        case 1: return launch_variant<M_T, 1, ROUTE, NORM, ONE>(a, cus, lds, s);
-        case 2: return launch_variant<M_T, 2, ROUTE, NORM, ONE>(a, cus, lds, s);
-        case 4: return launch_variant<M_T, 4, ROUTE, NORM, ONE>(a, cus, lds, s);
-        case 5: return launch_variant<M_T, 5, ROUTE, NORM, ONE>(a, cus, lds, s);
-        default: return launch_variant<M_T, 8, ROUTE, NORM, ONE>(a, cus, lds, s);
+        case 1: return launch_variant<M_T, 1, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
+        case 2: return launch_variant<M_T, 2, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
+        case 4: return launch_variant<M_T, 4, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
+        case 5: return launch_variant<M_T, 5, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
+        default: return launch_variant<M_T, 8, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
     }
 }
 
 // One token: a block per unit when the units fit four blocks per CU (and the
 // variant's occupancy allows it), else the general three-block grid.
-template <int M_T, bool ROUTE, bool NORM>
+template <int M_T, bool ROUTE, bool NORM, bool SH8>
 hipError_t launch_one(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     if constexpr (M_T == 1) {
         FfnArgs b = a;                                  // the down units of the ONE form
@@ -1092,19 +1269,23 @@ hipError_t launch_one(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t
         b.n_units = b.n_gu + b.max_groups * b.dn_units;
         b.writer = b.gu_units;                          // slot 1's first gate/up block routes; slot 0's do not
         if (b.n_units <= std::min(kMaxGrid, blocks_per_cu<true>() * cus)) {
-            const hipError_t e = launch_nb<M_T, ROUTE, NORM, true>(b, nb, cus, lds, s);
+            const hipError_t e = launch_nb<M_T, ROUTE, NORM, true, SH8>(b, nb, cus, lds, s);
             if (e != hipErrorInvalidConfiguration) return e;
         }
     }
-    return launch_nb<M_T, ROUTE, NORM, false>(a, nb, cus, lds, s);
+    return launch_nb<M_T, ROUTE, NORM, false, SH8>(a, nb, cus, lds, s);
 }
 
 // routing from logits with or without the residual stream, or from a table
-template <int M_T>
+// (the table form takes an MXFP4 shared expert only)
+template <int M_T, bool SH8>
 hipError_t launch_m(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
-    if (a.r_in) return launch_one<M_T, true, true>(a, nb, cus, lds, s);
-    if (a.logits) return launch_one<M_T, true, false>(a, nb, cus, lds, s);
-    return launch_one<M_T, false, false>(a, nb, cus, lds, s);
+    if (a.r_in) return launch_one<M_T, true, true, SH8>(a, nb, cus, lds, s);
+    if (a.logits) return launch_one<M_T, true, false, SH8>(a, nb, cus, lds, s);
+    if constexpr (SH8)
+        return hipErrorInvalidValue;
+    else
+        return launch_one<M_T, false, false, false>(a, nb, cus, lds, s);
 }
 
 }  // namespace
@@ -1217,11 +1398,22 @@ hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int
     const int cpw = (a.kbh4 + kWaves - 1) / kWaves;   // chunk pairs per wave, <= 8 for H <= 4096
     const int nb = cpw <= 1 ? 1 : cpw <= 2 ? 2 : cpw <= 4 ? 4 : cpw <= 5 ? 5 : 8;
     if (a.r_in && !a.logits) return hipErrorInvalidValue;     // the residual form routes from logits
+    const bool sh8 = w.magic == MOEDEC_MOE_MAGIC_SHARED_FP8;
+    a.sh8_gu_scale = sh8 ? reinterpret_cast<const float*>(w.sh_gu_scales) : nullptr;
+    a.sh8_dn_scale = sh8 ? reinterpret_cast<const float*>(w.sh_dn_scales) : nullptr;
+    if (sh8) {
+        switch (M) {
+            case 1: return launch_m<1, true>(a, nb, cus, L.lds_bytes, s);
+            case 2: return launch_m<2, true>(a, nb, cus, L.lds_bytes, s);
+            case 3: return launch_m<3, true>(a, nb, cus, L.lds_bytes, s);
+            default: return launch_m<4, true>(a, nb, cus, L.lds_bytes, s);
+        }
+    }
     switch (M) {
-        case 1: return launch_m<1>(a, nb, cus, L.lds_bytes, s);
-        case 2: return launch_m<2>(a, nb, cus, L.lds_bytes, s);
-        case 3: return launch_m<3>(a, nb, cus, L.lds_bytes, s);
-        default: return launch_m<4>(a, nb, cus, L.lds_bytes, s);
+        case 1: return launch_m<1, false>(a, nb, cus, L.lds_bytes, s);
+        case 2: return launch_m<2, false>(a, nb, cus, L.lds_bytes, s);
+        case 3: return launch_m<3, false>(a, nb, cus, L.lds_bytes, s);
+        default: return launch_m<4, false>(a, nb, cus, L.lds_bytes, s);
     }
 }
 

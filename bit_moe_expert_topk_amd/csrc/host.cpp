@@ -146,6 +146,29 @@ int moe_pack_down_mxfp4(const uint8_t* down_codes, const uint8_t* down_scales, i
                     "moe_pack_down_mxfp4");
 }
 
+int moedec_shared_fp8_packed_sizes(int H, int I, moedec_mxfp4_sizes* out) {
+    if (!out) return fail(MOEDEC_ERR_NULL, "out is NULL");
+    if (int st = check_mxfp4_shape(H, I)) return st;
+    moedec::shared_fp8_sizes(H, I, out);
+    g_last_error[0] = '\0';
+    return MOEDEC_OK;
+}
+
+int moe_pack_shared_fp8(const uint16_t* gate_bf16, const uint16_t* up_bf16, const uint16_t* down_bf16, int H,
+                        int I, uint8_t* gu_codes, float* gu_scales, uint8_t* dn_codes, float* dn_scales,
+                        moedec_stream_t stream) {
+    if (!gate_bf16 || !up_bf16 || !down_bf16 || !gu_codes || !gu_scales || !dn_codes || !dn_scales)
+        return fail(MOEDEC_ERR_NULL, "a pack pointer is NULL");
+    if (int st = check_mxfp4_shape(H, I)) return st;
+    if (!aligned(gate_bf16, 2) || !aligned(up_bf16, 2) || !aligned(down_bf16, 2) || !aligned(gu_codes, 16) ||
+        !aligned(dn_codes, 16) || !aligned(gu_scales, 4) || !aligned(dn_scales, 4))
+        return fail(MOEDEC_ERR_ALIGN, "code arrays 16-byte, scales 4-byte, bf16 inputs 2-byte alignment needed");
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_pack_shared_fp8(gate_bf16, up_bf16, down_bf16, H, I, gu_codes, gu_scales,
+                                                   dn_codes, dn_scales, static_cast<hipStream_t>(stream)),
+                    "moe_pack_shared_fp8");
+}
+
 size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I) {
     if (M < 1 || M > MOEDEC_MAX_M || k_max < 1 || k_max > MOEDEC_MAX_K || H < 64 || H > 4096 ||
         H % 64 || I < 32 || I > 2048 || I % 32)
@@ -157,9 +180,9 @@ size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I) {
 static int check_moe_core(const moedec_moe_weights* w, const uint16_t* x_bf16, int M, int k,
                           uint16_t* y_bf16, float* y_f32, bool residual) {
     if (!w) return fail(MOEDEC_ERR_NULL, "weights descriptor is NULL");
-    if (w->magic != MOEDEC_MOE_MAGIC)
-        return fail(MOEDEC_ERR_FORMAT, "weights descriptor magic 0x%08x != 0x%08x", w->magic,
-                    MOEDEC_MOE_MAGIC);
+    if (w->magic != MOEDEC_MOE_MAGIC && w->magic != MOEDEC_MOE_MAGIC_SHARED_FP8)
+        return fail(MOEDEC_ERR_FORMAT, "weights descriptor magic 0x%08x is neither 0x%08x nor 0x%08x", w->magic,
+                    MOEDEC_MOE_MAGIC, MOEDEC_MOE_MAGIC_SHARED_FP8);
     if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales || !w->sh_gu_codes ||
         !w->sh_gu_scales || !w->sh_dn_codes || !w->sh_dn_scales)
         return fail(MOEDEC_ERR_NULL, "a weight pointer is NULL");
@@ -174,6 +197,8 @@ static int check_moe_core(const moedec_moe_weights* w, const uint16_t* x_bf16, i
         return fail(MOEDEC_ERR_ALIGN, "packed code arrays must be 16-byte aligned");
     if (!aligned(w->gu_scales, 2) || !aligned(w->sh_gu_scales, 2))
         return fail(MOEDEC_ERR_ALIGN, "packed gate/up scale arrays must be 2-byte aligned");
+    if (w->magic == MOEDEC_MOE_MAGIC_SHARED_FP8 && (!aligned(w->sh_gu_scales, 4) || !aligned(w->sh_dn_scales, 4)))
+        return fail(MOEDEC_ERR_ALIGN, "the FP8 shared expert's float32 scale arrays must be 4-byte aligned");
     if (!aligned(x_bf16, 16) || !aligned(y_bf16, 4) || !aligned(y_f32, 4))
         return fail(MOEDEC_ERR_ALIGN, "x must be 16-byte aligned, y_bf16 and y_f32 4-byte");
     return MOEDEC_OK;
@@ -195,6 +220,9 @@ int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, in
                          const moedec_dispatch* dispatch, int k_max, uint16_t* y_bf16, float* y_f32,
                          void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
     if (int st = check_moe_args(w, x_bf16, M, k_max, y_bf16, y_f32, workspace, workspace_bytes)) return st;
+    if (w->magic == MOEDEC_MOE_MAGIC_SHARED_FP8)
+        return fail(MOEDEC_ERR_FORMAT, "the dispatch-table FFN takes an MXFP4 shared expert; "
+                                       "use moe_layer_mxfp4 for an FP8 one");
     if (!dispatch) return fail(MOEDEC_ERR_NULL, "dispatch is NULL");
     if (!aligned(dispatch, 16)) return fail(MOEDEC_ERR_ALIGN, "dispatch must be 16-byte aligned");
     if (int st = check_device()) return st;

@@ -21,6 +21,10 @@ hipError_t launch_pack_down(const uint8_t* dc, const uint8_t* ds, int n_exp, int
 
 // Per-expert packed MXFP4 sizes (bytes) for hidden H and intermediate I.
 void packed_sizes(int H, int I, moedec_mxfp4_sizes* out);
+// The FP8 shared expert's packed sizes and its one-time quantise-and-pack.
+void shared_fp8_sizes(int H, int I, moedec_mxfp4_sizes* out);
+hipError_t launch_pack_shared_fp8(const uint16_t* g, const uint16_t* u, const uint16_t* d, int H, int I,
+                                  uint8_t* gu_c, float* gu_s, uint8_t* dn_c, float* dn_s, hipStream_t s);
 
 // Workspace and launch layout of the fused FFN kernel.
 struct FfnLayout {

@@ -22,24 +22,6 @@ namespace moedec {
 
 namespace {
 
-// E4M3 magnitude code (0x00..0x7E) of a non-negative float32 q: nearest
-// value, ties to the even code, saturating at 448.  At and above 2^-6 the code
-// keeps 3 of the 23 mantissa bits (round to nearest even on the 20 dropped
-// bits) and rebiases the exponent from 127 to 7; below 2^-6 it is q / 2^-9
-// rounded to the nearest even integer, read from the low bits of q + 2^14
-// (whose float32 spacing is 2^-9).  Values above 448 and NaN give codes above
-// 0x7E and are clamped to it; CLAMP = false leaves that out for quotients
-// known to stay below 464, the midpoint above 448.
-template <bool CLAMP = true>
-__device__ __forceinline__ uint32_t e4m3_mag_code(float q) {
-    const uint32_t b = __float_as_uint(q);
-    const uint32_t nrm = (b + (0x7FFFFu - (120u << 23)) + ((b >> 20) & 1u)) >> 20;
-    const uint32_t sub = __float_as_uint(q + 16384.0f) - 0x46800000u;
-    const uint32_t c = b >= 0x3C800000u ? nrm : sub;
-    if constexpr (CLAMP) return c < 0x7Eu ? c : 0x7Eu;
-    return c;
-}
-
 // Quotient |w| / s of a bf16 magnitude (its 15 low bits, placed in the top of
 // a float) by the row scale.  FAST replaces the division by the product with
 // the rounded reciprocal y = 1/s and one correction with the exact remainder

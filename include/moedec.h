@@ -153,12 +153,44 @@ int moe_pack_down_mxfp4(const uint8_t* down_codes, const uint8_t* down_scales,
                         int n_experts, int H, int I,
                         uint8_t* dn_codes, uint8_t* dn_scales, moedec_stream_t stream);
 
-#define MOEDEC_MOE_MAGIC 0x4D4F4534u   /* "MOE4" */
+/* ------------------------------------------------------------------------
+ * The shared expert in FP8.  [ic three scalpels: the shared projections keep
+ * a higher-precision format than the MXFP4 routed experts; card #2 and news
+ * where the speed comes from: an FP8 copy built when the model is loaded
+ * halves what bf16 weights cost to read]  Each of W_gate, W_up [I][H] and
+ * W_down [H][I] (bf16) is quantised per output row as the LM head is: s =
+ * absmax / 448 (1 for an all-zero row), code = E4M3 nearest-even,
+ * saturating, of fl32(w / s).  Layout (16-byte lanes of 16 codes):
+ *     gate/up codes [I/16][KH8][2][64][16]: unit rg, chunk c, half (0 gate,
+ *              1 up), lane l = row 16rg + (l & 15), k = 64c + 16(l >> 4) + b
+ *     down codes    [H/16][KI8][64][16]:    row block rb, chunk c, lane l =
+ *              row 16rb + (l & 15), k = 64c + 16(l >> 4) + b
+ *     scales   gate/up: float32 [2][I] (gate rows, then up rows); down:
+ *              float32 [H]
+ * KH8 = 2 * KBH4, KI8 = 2 * KBI4 (as above); codes past H or I are zero.
+ * The shapes are those of moedec_mxfp4_packed_sizes.
+ * ---------------------------------------------------------------------- */
+int moedec_shared_fp8_packed_sizes(int H, int I, moedec_mxfp4_sizes* out);
+
+/* Quantise and pack once.  gate_bf16, up_bf16 [I][H] and down_bf16 [H][I]
+ * row-major bf16; codes 16-byte aligned, scales 4-byte aligned.  Two launches
+ * on `stream` (the row scales, then the codes). */
+int moe_pack_shared_fp8(const uint16_t* gate_bf16, const uint16_t* up_bf16, const uint16_t* down_bf16,
+                        int H, int I, uint8_t* gu_codes, float* gu_scales, uint8_t* dn_codes,
+                        float* dn_scales, moedec_stream_t stream);
+
+#define MOEDEC_MOE_MAGIC 0x4D4F4534u             /* "MOE4": every expert MXFP4 */
+#define MOEDEC_MOE_MAGIC_SHARED_FP8 0x4D4F4538u  /* "MOE8": routed MXFP4, shared FP8 */
 
 /* Packed weights of one MoE layer.  Routed expert e starts at e * (per-expert
- * size) in each routed array; the shared expert has its own pointers. */
+ * size) in each routed array; the shared expert has its own pointers, in the
+ * MXFP4 layout (MOEDEC_MOE_MAGIC) or in the FP8 layout of
+ * moe_pack_shared_fp8 (MOEDEC_MOE_MAGIC_SHARED_FP8: sh_gu_scales and
+ * sh_dn_scales then point to the float32 row scales, 4-byte aligned).  The
+ * fused layer calls take both; moe_expert_ffn_mxfp4 takes the first only
+ * (MOEDEC_ERR_FORMAT). */
 typedef struct {
-    uint32_t magic;                    /* MOEDEC_MOE_MAGIC */
+    uint32_t magic;                    /* MOEDEC_MOE_MAGIC or MOEDEC_MOE_MAGIC_SHARED_FP8 */
     int32_t  E, H, I;
     const uint8_t* gu_codes;           /* [E] packed gate/up codes (16-byte aligned) */
     const uint8_t* gu_scales;          /* [E] packed gate/up scales (2-byte aligned) */

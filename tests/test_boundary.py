@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
                  "lmhead_gemv_bf16", "lmhead_gemv_fp8_argmax", "lmhead_gemv_fp8_sample", "moe_router_logits_bf16", "moe_pack_gateup_mxfp4", "moe_pack_down_mxfp4",
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
                  "moedec_last_error", "moedec_abi_version", "moe_ffn_workspace_status",
-                 "moe_layer_mxfp4_noalloc", "moe_layer_rmsnorm_router_mxfp4"):
+                 "moe_layer_mxfp4_noalloc", "moe_layer_rmsnorm_router_mxfp4",
+                 "moe_pack_shared_fp8", "moedec_shared_fp8_packed_sizes"):
         assert want in names
 
 
@@ -241,6 +242,41 @@ def test_residual_layer_argument_checks(m):
     assert call(_weights(m), x=ctypes.c_void_p((1 << 22) + 8)) == -2
     assert call(_weights(m), M=5) == -3
     assert call(_weights(m), n=ws - 1) == -5
+
+
+def test_shared_fp8_sizes_and_argument_checks(m):
+    """FP8 shared expert: packed sizes (16 codes per 16-byte lane, chunks of
+    64 values per row, twice the MXFP4 chunk counts), pack argument checks,
+    and descriptor rules -- the fused layer takes the FP8 magic, the
+    dispatch-table FFN refuses it, and its float32 scales must be 4-byte
+    aligned."""
+    L = m.lib
+    sz = m.shared_fp8_sizes(2560, 768)
+    assert sz.gu_codes == 768 // 16 * 40 * 2 * 1024 == 2 * 768 * 2560
+    assert sz.dn_codes == 2560 // 16 * 12 * 1024 == 2560 * 768
+    assert sz.gu_scales == 2 * 768 * 4 and sz.dn_scales == 2560 * 4
+    ragged = m.shared_fp8_sizes(192, 96)               # 6 and 3 MX blocks: chunk counts padded to 4 and 2
+    assert ragged.gu_codes == 96 // 16 * 4 * 2 * 1024 and ragged.dn_codes == 192 // 16 * 2 * 1024
+    out = m.MXFP4Sizes()
+    assert L.moedec_shared_fp8_packed_sizes(100, 768, ctypes.byref(out)) == -3
+    args = [FAKE, FAKE, FAKE, 2560, 768, FAKE, FAKE, FAKE, FAKE, None]
+    bad = list(args); bad[0] = None
+    assert L.moe_pack_shared_fp8(*bad) == -1
+    bad = list(args); bad[5] = ctypes.c_void_p((1 << 20) + 8)
+    assert L.moe_pack_shared_fp8(*bad) == -2
+    bad = list(args); bad[6] = ctypes.c_void_p((1 << 20) + 2)
+    assert L.moe_pack_shared_fp8(*bad) == -2
+    bad = list(args); bad[3] = 2500
+    assert L.moe_pack_shared_fp8(*bad) == -3
+    ws = m.ffn_workspace_bytes(1, 8, 2560, 768)
+    w8 = _weights(m, magic=m.MOE_MAGIC_SHARED_FP8)
+    assert L.moe_expert_ffn_mxfp4(ctypes.byref(w8), FAKE, 1, FAKE, 8, FAKE, None, FAKE, ws, None) == -4
+    assert b"MXFP4 shared" in L.moedec_last_error()
+    w8.sh_dn_scales = (1 << 20) + 2
+    assert L.moe_layer_mxfp4(ctypes.byref(w8), FAKE, FAKE, 1, 8, None, None, None, FAKE, None, FAKE, ws,
+                             None) == -2
+    assert L.moe_layer_mxfp4(ctypes.byref(_weights(m, magic=0x4D4F4539)), FAKE, FAKE, 1, 8, None, None, None,
+                             FAKE, None, FAKE, ws, None) == -4
 
 
 def test_router_chain_argument_checks(m):
