@@ -56,6 +56,7 @@ def parse_args(argv=None):
     ap.add_argument("--layers", type=int, default=42, help="distinct layers the steps cycle through")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head measurements")
+    ap.add_argument("--no-fp8-shared", action="store_true", help="skip the FP8 shared-expert layer")
     ap.add_argument("--no-m4", action="store_true", help="skip the M = 4 measurement")
     ap.add_argument("--no-stack", action="store_true", help="skip the residual-stack measurement")
     ap.add_argument("--no-router", action="store_true", help="skip the router-logits measurement")
@@ -776,8 +777,10 @@ def main(argv=None):
     if not args.no_m4:
         r4 = moe_bench(m, torch, synth, layers, 4, args.steps, args.warmup, dev)
         log("M=4:", json.dumps(r4))
-    sh8 = shared_fp8_bench(m, torch, synth, layers, args.steps, dev)
-    log("FP8 shared:", json.dumps(sh8))
+    sh8 = None
+    if not args.no_fp8_shared:
+        sh8 = shared_fp8_bench(m, torch, synth, layers, args.steps, dev)
+        log("FP8 shared:", json.dumps(sh8))
     stack = None
     if not args.no_stack:
         stack = stack_bench(m, torch, synth, layers, args.stack_passes, max(1, args.stack_passes // 10), dev)
@@ -850,8 +853,9 @@ def main(argv=None):
         line["stack_us_per_layer_graph"] = round(stack["us_per_layer_graph"], 3)
         line["stack_us_per_layer_eager"] = round(stack["us_per_layer_eager"], 3)
         line["stack_norm_router_layer_us_graph"] = round(stack["routed_us_per_layer_graph"], 3)
-    line["fp8_shared_us_per_layer_m1"] = round(sh8["m1_us_per_layer"], 3)
-    line["fp8_shared_us_per_layer_m4"] = round(sh8["m4_us_per_layer"], 3)
+    if sh8 is not None:
+        line["fp8_shared_us_per_layer_m1"] = round(sh8["m1_us_per_layer"], 3)
+        line["fp8_shared_us_per_layer_m4"] = round(sh8["m4_us_per_layer"], 3)
     if lm is not None:
         line["lmhead_fp8_gbs_m1"] = round(lm["fp8_m1_gbs"], 1)
         line["lmhead_fp8_argmax_us_m1"] = round(lm["fp8_argmax_m1_us"], 2)
