@@ -20,6 +20,9 @@ sums every expert under a routing mask in a different loop order, by k = E
 giving the dense softmax mixture, by x = 0 giving y = 0 exactly, and by a
 hand-computed closed-form layer (constant codes, known silu value).
 rmsnorm: pinned by a hand-computed constant vector and scale invariance.
+moe_layer_by_expert: pinned against moe_layer (to float64 rounding) on tiny
+shapes, including an expert every token chose, ragged token counts and a token
+subset (tests/test_oracle_moe.py).
 """
 
 import numpy as np
@@ -53,6 +56,46 @@ def moe_layer(x, ids, w, expert_weights, shared_weights):
             wg, wu, wd = expert_weights(int(ids[m, j]))
             y[m] += w[m, j] * expert_ffn(wg, wu, wd, x[m])
         y[m] += expert_ffn(*shared_weights, x[m])
+    return y
+
+
+def moe_layer_by_expert(x, ids, w, expert_weights, shared_weights, tokens=None):
+    """moe_layer's sum evaluated expert by expert, for many tokens.
+
+    Each active expert's dense weights are formed once and applied to all the
+    tokens that chose it (one matrix product per expert); each token's terms
+    are then added in moe_layer's order: w[t][0] * FFN_0 + ... + w[t][k-1] *
+    FFN_{k-1}, then the shared expert.  Only the float64 rounding of the
+    products may differ from moe_layer.
+
+    tokens  optional ascending token indices; only their rows are evaluated
+            (the returned array has one row per listed token)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(ids)
+    if tokens is None:
+        tokens = np.arange(x.shape[0])
+    tokens = np.asarray(tokens, dtype=np.int64)
+    k = ids.shape[1]
+    terms = np.zeros((len(tokens), k, x.shape[1]))
+    for e in sorted(set(int(v) for v in ids[tokens].flatten())):
+        rows, slots = np.nonzero(ids[tokens] == e)
+        wg, wu, wd = expert_weights(e)
+        xs = x[tokens[rows]]                      # [n][H]
+        g = xs @ wg.T
+        u = xs @ wu.T
+        h = g / (1.0 + np.exp(-g)) * u
+        terms[rows, slots] = h @ wd.T
+    wg, wu, wd = shared_weights
+    xs = x[tokens]
+    g = xs @ wg.T
+    u = xs @ wu.T
+    shared = (g / (1.0 + np.exp(-g)) * u) @ wd.T
+    y = np.zeros((len(tokens), x.shape[1]))
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            y[i] += w[t, j] * terms[i, j]
+        y[i] += shared[i]
     return y
 
 

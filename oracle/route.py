@@ -14,13 +14,20 @@ Readings where the pages are silent (stated, not derived from them):
   * no group limit, no expert bias, routed scaling factor 1;
   * the grouped table lists the distinct selected experts in ascending id, each
     with the set of tokens that chose it and their weights, followed by the
-    shared expert serving every token with weight 1.
+    shared expert serving every token with weight 1;
+  * for many tokens (a prefill chunk, a long verify window) the same grouping
+    is kept as one token list per expert, tokens ascending, the shared
+    expert's list (every token) last [card §method #3: each active expert is
+    read once for all the tokens it serves].
 
 Parity status: pinned (tests/test_oracle_route.py) by the invariant that the
 selection equals the first k entries of a stable full sort done by a library
 routine (numpy lexsort) on random and tie-heavy logits, by k = E, by the
 softmax-over-selected closed form (scipy), by sum(w) = 1 and k = 1 -> w = 1, and
-by a hand-worked tie fixture under tests/golden/.  The router logits are pinned
+by a hand-worked tie fixture under tests/golden/.  expert_groups is pinned
+against dispatch_table (same membership, for M <= 32), by its counting
+invariants (every token in exactly k routed lists and the shared one), and by
+a hand-worked fixture under tests/golden/.  The router logits are pinned
 by a hand-worked 3 x 2 example, one-hot activations selecting one column of the
 router matrix per expert (orientation), x = 0, and linearity in x.
 """
@@ -97,3 +104,22 @@ def dispatch_table(ids, w, n_experts):
     weights.append(np.ones(m_tokens, dtype=np.float64))
     return (np.array(experts, dtype=np.int32), np.array(masks, dtype=np.uint32),
             np.array(weights, dtype=np.float64))
+
+
+def expert_groups(ids, n_experts):
+    """Token lists of the E routed experts and the shared expert.
+
+    ids  int [T][k], the k distinct experts of each token
+    returns a list of n_experts + 1 int64 arrays: entry e holds, ascending, the
+    tokens t with e among ids[t]; entry n_experts (the shared expert) holds
+    every token.  len(entry) is the number of rows expert e multiplies.
+    """
+    ids = np.asarray(ids)
+    t_tokens = ids.shape[0]
+    lists = [[] for _ in range(n_experts)]
+    for t in range(t_tokens):
+        for e in ids[t]:
+            lists[int(e)].append(t)
+    groups = [np.array(sorted(lst), dtype=np.int64) for lst in lists]
+    groups.append(np.arange(t_tokens, dtype=np.int64))
+    return groups

@@ -144,3 +144,28 @@ def test_library_selftest_cases_agree_with_the_oracle():
     logits = oracle.lmhead_gemv_fp8(codes, scale, np.eye(16)[1:2])
     np.testing.assert_allclose(logits, [[-2.0, 0.25]], rtol=1e-6)
     assert oracle.lmhead_argmax(logits)[0] == 1
+
+
+@pytest.mark.parametrize("m_tokens,forced", [(37, False), (64, True)])
+def test_by_expert_equals_moe_layer(m_tokens, forced):
+    """The expert-by-expert evaluation equals the per-token definition up to
+    float64 rounding: ragged token counts, and a case where every token chose
+    expert 5 (one expert multiplying the whole batch)."""
+    shape = synth.TINY
+    deq = _dense_experts(shape)
+    xb, lg = synth.moe_inputs(synth.Workload("t", shape, m_tokens, router_matrix=True))
+    if forced:
+        lg = lg.copy()
+        lg[:, 5] = 100.0
+    x = synth.bf16_values(xb).astype(np.float64)
+    ids, w = oracle.route_topk(lg, shape.k)
+    if forced:
+        assert (ids[:, 0] == 5).all()
+    fn = lambda e: (deq["gate"][e], deq["up"][e], deq["down"][e])
+    shared = (deq["gate"][shape.E], deq["up"][shape.E], deq["down"][shape.E])
+    ref = oracle.moe_layer(x, ids, w, fn, shared)
+    y = oracle.moe_layer_by_expert(x, ids, w, fn, shared)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    sub = np.array([0, 3, m_tokens - 1])
+    ys = oracle.moe_layer_by_expert(x, ids, w, fn, shared, tokens=sub)
+    assert np.max(np.abs(ys - ref[sub])) <= 1e-12 * np.max(np.abs(ref))

@@ -107,3 +107,38 @@ def test_router_logits_linear_in_x():
     x2 = rng.integers(-8, 8, size=(3, 16)).astype(np.float64)
     np.testing.assert_array_equal(oracle.router_logits(w, x1 + x2),
                                   oracle.router_logits(w, x1) + oracle.router_logits(w, x2))
+
+
+def test_expert_groups_hand_worked(golden):
+    case = golden("expert_groups.json")
+    groups = oracle.expert_groups(np.array(case["ids"]), case["n_experts"])
+    assert [g.tolist() for g in groups] == case["groups"]
+    assert [len(g) for g in groups] == case["counts"]
+
+
+@pytest.mark.parametrize("m,e,k", [(4, 512, 8), (32, 16, 2), (7, 33, 5)])
+def test_expert_groups_match_dispatch_table(m, e, k):
+    rng = np.random.default_rng(40 + m)
+    ids, w = oracle.route_topk(rng.standard_normal((m, e)).astype(np.float32), k)
+    groups = oracle.expert_groups(ids, e)
+    experts, masks, _ = oracle.dispatch_table(ids, w, e)
+    active = [x for x in range(e) if len(groups[x])]
+    assert active == experts[:-1].tolist()
+    for x, mask in zip(experts, masks):
+        assert groups[x].tolist() == [t for t in range(m) if (int(mask) >> t) & 1]
+
+
+def test_expert_groups_counting_invariants():
+    rng = np.random.default_rng(41)
+    t_tokens, e, k = 1000, 512, 8
+    ids, _ = oracle.route_topk(rng.standard_normal((t_tokens, e)).astype(np.float32), k)
+    groups = oracle.expert_groups(ids, e)
+    assert len(groups) == e + 1
+    assert sum(len(g) for g in groups) == t_tokens * k + t_tokens
+    assert groups[e].tolist() == list(range(t_tokens))
+    seen = np.zeros((t_tokens, e), dtype=np.int64)
+    for x in range(e):
+        assert (np.diff(groups[x]) > 0).all()            # ascending, no repeats
+        seen[groups[x], x] += 1
+    for t in range(t_tokens):
+        assert np.nonzero(seen[t])[0].tolist() == sorted(ids[t].tolist())
