@@ -263,6 +263,46 @@ def moe_layer(weights, x, logits, k, workspace, y=None, y_f32=None, want_f32=Tru
     return y, y_f32
 
 
+def prefill_workspace_bytes(T, E, k, H, I):
+    n = lib.moe_prefill_workspace_bytes(T, E, k, H, I)
+    if n == 0:
+        raise ValueError(f"no many-token workspace for T={T} E={E} k={k} H={H} I={I}")
+    return n
+
+
+def make_prefill_workspace(T, E, k, H, I, device):
+    """Workspace of moe_layer_prefill (no initial contents needed)."""
+    return torch.empty(prefill_workspace_bytes(T, E, k, H, I), dtype=torch.uint8, device=device)
+
+
+def moe_layer_prefill(weights, x, logits, k, workspace=None, y=None, y_f32=None, want_f32=True,
+                      ids=None, topk_w=None, counts=None):
+    """The layer for many tokens (moe_layer_mxfp4_prefill): x [T][H] bfloat16,
+    logits [T][E] float32.  Returns (y bf16, y_f32 or None); ids [T][k],
+    topk_w [T][k] and counts [E + 1] (int32, tokens per expert, then T) are
+    filled when given."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(logits, torch.float32, "logits", 2)
+    t_tokens, hidden = x.shape
+    if logits.shape[0] != t_tokens or logits.shape[1] != weights.E:
+        raise ValueError(f"logits must be [{t_tokens}][{weights.E}], got {tuple(logits.shape)}")
+    for t, dt, n in ((ids, torch.int32, "ids"), (topk_w, torch.float32, "topk_w"),
+                     (counts, torch.int32, "counts")):
+        if t is not None:
+            _need(t, dt, n)
+    if workspace is None:
+        workspace = make_prefill_workspace(t_tokens, weights.E, k, weights.H, weights.I, x.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    if y is None:
+        y = torch.empty((t_tokens, hidden), dtype=torch.bfloat16, device=x.device)
+    if y_f32 is None and want_f32:
+        y_f32 = torch.empty((t_tokens, hidden), dtype=torch.float32, device=x.device)
+    _check(lib.moe_layer_mxfp4_prefill(ctypes.byref(weights.desc), _ptr(x), _ptr(logits), t_tokens, k,
+                                       _ptr(ids), _ptr(topk_w), _ptr(counts), _ptr(y), _ptr(y_f32),
+                                       _ptr(workspace), workspace.numel(), _stream(x)))
+    return y, y_f32
+
+
 def check_ffn_workspace(workspace=None, device=None):
     """Wait for the stream and raise MoedecError (MOEDEC_ERR_TIMEOUT) when a
     cross-block wait of any FFN call on `workspace` gave up since the last

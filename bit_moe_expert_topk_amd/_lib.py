@@ -24,6 +24,7 @@ MOEDEC_ERR_TIMEOUT = -9
 MOEDEC_ERR_ARG = -10
 MOEDEC_MAX_SAMPLE_K = 32
 MOEDEC_MAX_EPILOGUE_V = 1 << 18
+MOEDEC_MAX_PREFILL_T = 65536
 
 MAX_M = 4
 MAX_K = 32
@@ -107,6 +108,9 @@ SIGNATURES = {
     "moe_layer_rmsnorm_router_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int,
                                                ctypes.c_float, c_void_p, c_void_p, c_void_p, c_void_p,
                                                c_void_p, c_size_t, c_void_p]),
+    "moe_prefill_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "moe_layer_mxfp4_prefill": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_ffn_workspace_status": (c_int, [c_void_p, c_size_t, ctypes.POINTER(c_uint32), c_void_p]),
     "moe_layer_mxfp4_noalloc": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -356,6 +356,38 @@ int moe_layer_rmsnorm_router_mxfp4(const moedec_moe_weights* w, const uint16_t* 
                     "moe_layer_rmsnorm_router_mxfp4");
 }
 
+size_t moe_prefill_workspace_bytes(int T, int E, int k, int H, int I) {
+    if (T < 1 || T > MOEDEC_MAX_PREFILL_T || E < 1 || E > MOEDEC_MAX_E || k < 1 || k > MOEDEC_MAX_K || k > E)
+        return 0;
+    if (H < 64 || H > 4096 || H % 64 || I < 32 || I > 2048 || I % 32) return 0;
+    return moedec::prefill_layout(T, E, k, H, I).total;
+}
+
+int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int T,
+                            int k, int32_t* topk_ids, float* topk_w, int32_t* group_counts, uint16_t* y_bf16,
+                            float* y_f32, void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+    if (!w) return fail(MOEDEC_ERR_NULL, "weights descriptor is NULL");
+    if (w->magic == MOEDEC_MOE_MAGIC_SHARED_FP8)
+        return fail(MOEDEC_ERR_FORMAT, "the many-token layer takes an MXFP4 shared expert");
+    if (int st = check_moe_core(w, x_bf16, 1, k, y_bf16, y_f32, false)) return st;
+    if (!logits) return fail(MOEDEC_ERR_NULL, "logits is NULL");
+    if (T < 1 || T > MOEDEC_MAX_PREFILL_T)
+        return fail(MOEDEC_ERR_SHAPE, "T=%d not in 1..%d", T, MOEDEC_MAX_PREFILL_T);
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(group_counts, 4))
+        return fail(MOEDEC_ERR_ALIGN, "logits/topk_ids/topk_w/group_counts must be 4-byte aligned");
+    if (!aligned(y_bf16, 8) || !aligned(y_f32, 16))
+        return fail(MOEDEC_ERR_ALIGN, "y_bf16 must be 8-byte aligned, y_f32 16-byte");
+    if (!workspace) return fail(MOEDEC_ERR_NULL, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(MOEDEC_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const size_t need = moedec::prefill_layout(T, w->E, k, w->H, w->I).total;
+    if (workspace_bytes < need)
+        return fail(MOEDEC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    return launched(moedec::launch_prefill(*w, x_bf16, logits, T, k, topk_ids, topk_w, group_counts, y_bf16,
+                                           y_f32, workspace, static_cast<hipStream_t>(stream)),
+                    "moe_layer_mxfp4_prefill");
+}
+
 int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H, uint8_t* codes, float* row_scale,
                      moedec_lmhead_fp8* out_desc, moedec_stream_t stream) {
     if (!w_bf16 || !codes || !row_scale) return fail(MOEDEC_ERR_NULL, "w, codes or row_scale is NULL");

@@ -95,4 +95,17 @@ hipError_t launch_gemv_bf16(const uint16_t* w, int V, int H, const uint16_t* x, 
 hipError_t launch_norm_router_bf16(const uint16_t* w, int E, int H, const float* r, float eps, int M,
                                    float* logits, hipStream_t s);
 
+// Many-token layer (prefill.hip): workspace layout and the launch sequence.
+struct PrefillLayout {
+    int ns;             // 32-token column blocks per tile
+    int max_tiles;      // tiles at most: (T*k + T) / (32*ns) + E + 1
+    size_t counts_off, cursor_off, off_off, n_tiles_off, tiles_off, ids_off, w_off, pos_off, tok_of_off,
+        h_hi_off, h_lo_off, y_pair_off, total;
+};
+int prefill_sub_tiles(int T, int E, int k);
+PrefillLayout prefill_layout(int T, int E, int k, int H, int I);
+hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const float* logits, int T, int k,
+                          int32_t* ids_out, float* w_out, int32_t* counts_out, uint16_t* y_bf16, float* y_f32,
+                          void* ws, hipStream_t s);
+
 }  // namespace moedec

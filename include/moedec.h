@@ -353,6 +353,55 @@ int moe_layer_rmsnorm_router_mxfp4(const moedec_moe_weights* w, const uint16_t* 
                                    moedec_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Many tokens at once: a prefill chunk or a long verify window.  [news "two
+ * easily missed details": filling a long prompt is bound by matrix
+ * arithmetic, decoding by bandwidth; card #3: each active expert is read once
+ * for every token that chose it]
+ *
+ * The same layer as moe_layer_mxfp4 for T tokens,
+ *     y[t] = sum_j w[t][j] FFN_{ids[t][j]}(x[t]) + FFN_shared(x[t]),
+ * computed as a grouped GEMM on bf16 matrix cores: routing with per-expert
+ * token counts, one token list per expert (the shared expert's list holds all
+ * T), then gate/up, down and a combine.  The MXFP4 weights are used in the
+ * packed layout above (the same buffers the decode calls read), dequantised
+ * exactly to bf16 in registers; x is bf16; products accumulate in float32.
+ * h = silu(g) * u is carried into the down product as the sum of two bf16
+ * values (hi = bf16(h), lo = bf16(h - hi)), 16 significant bits, relative
+ * error at most 2^-17 per element.  Each token's terms are added in float32 in
+ * the order j = 0 .. k-1 then the shared expert, and rounded once to bf16.
+ * Results do not depend on scheduling: every output is formed from its own
+ * row and column only, in a fixed order.
+ *
+ * Six launches on `stream`: counts reset, routing, plan (one block), scatter,
+ * gate/up, down, combine.
+ * w             MOEDEC_MOE_MAGIC weights (an FP8 shared expert is refused
+ *               with MOEDEC_ERR_FORMAT)
+ * x_bf16        [T][H] bf16, 16-byte aligned
+ * logits        [T][E] float32 router logits, 4-byte aligned
+ * T             1 .. MOEDEC_MAX_PREFILL_T tokens
+ * k             1 .. min(E, MOEDEC_MAX_K)
+ * topk_ids      [T][k] int32 output (selection order) or NULL
+ * topk_w        [T][k] float32 output or NULL
+ * group_counts  [E + 1] int32 output or NULL: tokens of each routed expert,
+ *               then T for the shared expert
+ * y_bf16        [T][H] bf16 output, 8-byte aligned
+ * y_f32         [T][H] float32 output before rounding, or NULL; 16-byte
+ *               aligned
+ * workspace     moe_prefill_workspace_bytes(T, E, k, H, I) bytes, 256-byte
+ *               aligned, owned by the caller; no initial contents needed.
+ *               About T*(k+1)*(4H + 4I) bytes: the per-pair h and down
+ *               outputs.  One call at a time per workspace.
+ * Returns MOEDEC_OK, or an error code with nothing enqueued.
+ */
+#define MOEDEC_MAX_PREFILL_T 65536
+
+size_t moe_prefill_workspace_bytes(int T, int E, int k, int H, int I);
+
+int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int T,
+                            int k, int32_t* topk_ids, float* topk_w, int32_t* group_counts, uint16_t* y_bf16,
+                            float* y_f32, void* workspace, size_t workspace_bytes, moedec_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * LM head with online FP8 weights.  [news where the speed comes from; card
  * #2: the 157,184 x 2,560 vocabulary projection is read whole for every
  * token; a dynamic FP8 config applied when the head is built halves that

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                  "moe_ffn_workspace_bytes", "moedec_mxfp4_packed_sizes", "moedec_status_string",
                  "moedec_last_error", "moedec_abi_version", "moe_ffn_workspace_status",
                  "moe_layer_mxfp4_noalloc", "moe_layer_rmsnorm_router_mxfp4",
-                 "moe_pack_shared_fp8", "moedec_shared_fp8_packed_sizes"):
+                 "moe_pack_shared_fp8", "moedec_shared_fp8_packed_sizes",
+                 "moe_layer_mxfp4_prefill", "moe_prefill_workspace_bytes"):
         assert want in names
 
 
@@ -338,3 +339,30 @@ def test_workspace_status_and_noalloc_argument_checks(m):
     assert L.moe_layer_mxfp4_noalloc(ctypes.byref(w), FAKE, FAKE, 4, 32, None, None, None, FAKE, None, None) == -5
     assert b"no-alloc limit" in L.moedec_last_error()
     assert m.lib.moedec_status_string(-9) != b"unknown status"
+
+
+def test_prefill_workspace_and_argument_checks(m):
+    L = m.lib
+    for T, E, k, H, I in ((8192, 512, 8, 2560, 768), (1, 16, 2, 256, 64), (37, 16, 2, 256, 64)):
+        n = L.moe_prefill_workspace_bytes(T, E, k, H, I)
+        pairs = T * (k + 1)
+        body = pairs * (4 * H + 4 * I)                    # y_pair float32 + h as two bf16
+        assert body <= n <= body + pairs * 4 + 3 * T * k * 4 + (3 * (E + 2) * 4) + ((pairs // 32 + E + 1) * 8) + 4096
+    assert L.moe_prefill_workspace_bytes(0, 512, 8, 2560, 768) == 0
+    assert L.moe_prefill_workspace_bytes(m._lib.MOEDEC_MAX_PREFILL_T + 1, 512, 8, 2560, 768) == 0
+    assert L.moe_prefill_workspace_bytes(64, 512, 33, 2560, 768) == 0
+    assert L.moe_prefill_workspace_bytes(64, 512, 8, 2560 + 32, 768) == 0
+    ws = L.moe_prefill_workspace_bytes(64, 512, 8, 2560, 768)
+    call = lambda w, lg=FAKE, T=64, k=8, n=ws, work=FAKE, y32=None: L.moe_layer_mxfp4_prefill(
+        ctypes.byref(w), FAKE, lg, T, k, None, None, None, FAKE, y32, work, n, None)
+    assert call(_weights(m), lg=None) == -1
+    assert call(_weights(m, magic=1)) == -4
+    assert call(_weights(m, magic=m._lib.MOE_MAGIC_SHARED_FP8)) == -4
+    assert call(_weights(m), k=33) == -3
+    assert call(_weights(m), T=0) == -3
+    assert call(_weights(m), T=m._lib.MOEDEC_MAX_PREFILL_T + 1) == -3
+    assert call(_weights(m), lg=ODD) == -2
+    assert call(_weights(m), y32=ctypes.c_void_p((1 << 20) + 8)) == -2
+    assert call(_weights(m), work=ctypes.c_void_p((1 << 20) + 16)) == -2
+    assert call(_weights(m), work=None) == -1
+    assert call(_weights(m), n=ws - 1) == -5
