@@ -370,6 +370,9 @@ int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16,
     if (w->magic == MOEDEC_MOE_MAGIC_SHARED_FP8)
         return fail(MOEDEC_ERR_FORMAT, "the many-token layer takes an MXFP4 shared expert");
     if (int st = check_moe_core(w, x_bf16, 1, k, y_bf16, y_f32, false)) return st;
+    if (!aligned(w->gu_scales, 4) || !aligned(w->dn_scales, 4) || !aligned(w->sh_gu_scales, 4) ||
+        !aligned(w->sh_dn_scales, 4))
+        return fail(MOEDEC_ERR_ALIGN, "the many-token layer needs 4-byte aligned scale arrays");
     if (!logits) return fail(MOEDEC_ERR_NULL, "logits is NULL");
     if (T < 1 || T > MOEDEC_MAX_PREFILL_T)
         return fail(MOEDEC_ERR_SHAPE, "T=%d not in 1..%d", T, MOEDEC_MAX_PREFILL_T);

@@ -19,7 +19,8 @@
 //   gate/up  per (tile, 128 intermediate rows): g = W_gate x, u = W_up x on
 //            MFMA 32x32x16 bf16 with float32 accumulation, h = silu(g) * u,
 //            stored as h = hi + lo (two bf16, 16 significant bits)
-//   down     per (tile, 128 output rows): y_pair = W_down hi + W_down lo
+//   down     per (up to 64 tokens of a tile, 256 output rows): y_pair =
+//            W_down hi + W_down lo
 //   combine  y[t] = sum_j w[t][j] * y_pair[row(t, j)] + y_pair[T*k + t] in
 //            float32 in that order, then rounded once to bf16
 //
@@ -48,10 +49,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = 128;   // 4 waves x 32 weight rows
 constexpr int kSub = 32;             // tokens per MFMA column block
 constexpr int kSlab = 64;            // k per pipeline step: two MX blocks
-constexpr int kLdsRow = kSlab + 8;   // bf16 per LDS row, 16 B of padding
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -64,10 +63,6 @@ __device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float scale) {
     const bf16x2 a = MOEDEC_FP4X2_BF16(w, scale, 0), b = MOEDEC_FP4X2_BF16(w, scale, 1);
     const bf16x2 c = MOEDEC_FP4X2_BF16(w, scale, 2), d = MOEDEC_FP4X2_BF16(w, scale, 3);
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-__device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
 // The work item of this block, or false when it has none.  Items are (tile,
@@ -196,72 +191,185 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
 }
 
 // ----------------------------------------------------------------------------
-// gate/up: block = (tile of up to 32*NS tokens of one group, 128 intermediate
-// rows); wave w owns rows 32w..32w+31 of that block for both W_gate and W_up.
+// Pipeline shared by both products.  Everything a step multiplies flows
+// through a ring of LDS slots filled by direct global->LDS loads, each
+// slot holding one 64-k slab: the B operand (activations, or the two halves of
+// h) and each wave's own A-operand codes and scales.  A wave's load
+// instruction writes 64 lanes x 16 B (or 4 B) contiguously, lane l at 16 l
+// (4 l).  B rows are 128 B; inside a row the eight 16-byte units sit at slot
+// u ^ ((row >> 1) & 7), so the 16 lanes that read one unit of 16 consecutive
+// rows hit 16 distinct bank groups.
+//
+// With S slots, step j (j = 1 - S .. n_slabs - 1; the first S - 1 only
+// fill): for j >= 0 wait until this thread's loads of slab j are done (loads
+// retire in order, and only those of slabs j + 1 .. j + S - 2 were issued
+// after them) and barrier (every thread's part of slab j is in LDS, every
+// wave is done with slab j - 1); then load slab j + S - 1 into the slot slab
+// j - 1 used and multiply slab j.  Loads past the last slab repeat the last
+// one into that free slot, keeping every count fixed.  The step takes the slot it writes and the slot it reads as restrict
+// pointers: that tells the compiler the ring write does not feed this step's
+// LDS reads, so it adds no wait of its own between them.  No register is
+// loaded from global memory inside the loop, so every vmcnt wait there is
+// the one written here.
 
-template <int NS>
-struct GateUpLds {
-    uint16_t x[2][NS * kSub][kLdsRow];
+constexpr int kGuWaveBytes = 2048 + 256;    // gate codes, up codes, scale dwords
+constexpr int kDnWaveBytes = 2048 + 512;    // codes of two row tiles, their scale dwords
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt at their no-wait values).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void lds_load16(const void* src, uint8_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void lds_load4(const void* src, uint8_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+
+__device__ __forceinline__ int lds_slot(int row, int unit) { return row * 128 + ((unit ^ ((row >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ bf16x8 lds_b(const uint8_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+template <int S>
+__device__ __forceinline__ int next_slot(int s) { return s + 1 == S ? 0 : s + 1; }
+
+// ----------------------------------------------------------------------------
+// gate/up: block = (tile of up to 32*NS tokens of one group, 32*W intermediate
+// rows); wave w owns rows 32w..32w+31 of that block for both W_gate and W_up.
+// Each of the block's ceil(I / 32W) row blocks reads the tile's activations
+// again (from L2), so wider blocks cut that traffic.
+
+template <int NS, int W>
+struct GuCtx {
+    static constexpr int kX = NS * kSub * 128 / (8 * 128 * W);   // ring-fill instructions per wave
+    const uint16_t* xsrc[kX];   // token row of this lane's ring unit, instruction v
+    int xk[kX];                 // its k offset inside a slab
+    const uint8_t* codes;       // this lane's 16 code bytes of MX block q = half of chunk 0
+    const uint8_t* scales;      // the scale dword holding this lane's 16-bit gate/up scale pair, chunk 0
+    int n_slabs, H, wv, lane;
+    int sc_shift;               // 0 or 16: this lane's half of the scale dword
+    bool has_rows;
+    int boff[4];                // LDS offsets of this lane's B operand, steps 0..3
 };
 
-template <int NS>
-__global__ __launch_bounds__(kThreads, 2) void gateup_kernel(
-    const uint8_t* __restrict__ gu_codes, const uint16_t* __restrict__ gu_scales, size_t e_codes,
-    size_t e_scales, const uint8_t* __restrict__ sh_codes, const uint16_t* __restrict__ sh_scales,
+template <int NS, int W, int S, int NSUB>
+__device__ __forceinline__ void gu_step(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd,
+                                        const GuCtx<NS, W>& c, int j, f32x16 (&acc_g)[NS], f32x16 (&acc_u)[NS]) {
+    constexpr int kX = NS * kSub * 128;
+    {
+        const int sl = min(j + S - 1, c.n_slabs - 1);
+#pragma unroll
+        for (int v = 0; v < GuCtx<NS, W>::kX; ++v) {
+            const int k = sl * kSlab + c.xk[v];
+            lds_load16(c.xsrc[v] + (k < c.H ? k : 0), wr + (W * v + c.wv) * 1024);
+        }
+        if (c.has_rows) {
+            uint8_t* wb = wr + kX + c.wv * kGuWaveBytes;
+            const uint8_t* p = c.codes + (size_t)(sl >> 1) * 2048 + (sl & 1) * 512;
+            lds_load16(p, wb);
+            lds_load16(p + 1024, wb + 1024);
+            lds_load4(c.scales + (size_t)(sl >> 1) * 128 + (sl & 1) * 64, wb + 2048);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (c.has_rows && j >= 0) {
+        // every LDS read of the slab first (weights, then B in the order the
+        // products use them), so the matrix core never waits on one
+        const uint8_t* wb = rd + kX + c.wv * kGuWaveBytes;
+        const u32x4 cg = *reinterpret_cast<const u32x4*>(wb + c.lane * 16);
+        const u32x4 cu = *reinterpret_cast<const u32x4*>(wb + 1024 + c.lane * 16);
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(wb + 2048 + c.lane * 4) >> c.sc_shift;
+        bf16x8 b[4][NSUB];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) b[st][s] = lds_b(rd + s * kSub * 128 + c.boff[st]);
+        const float sg = e8m0_to_f32(sc & 0xFF), su = e8m0_to_f32((sc >> 8) & 0xFF);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const bf16x8 ag = fp4x8_bf16(cg[st], sg), au = fp4x8_bf16(cu[st], su);
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+                acc_g[s] = mfma_bf16(ag, b[st][s], acc_g[s]);
+                acc_u[s] = mfma_bf16(au, b[st][s], acc_u[s]);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NS, int W>
+constexpr int gu_slot_bytes() { return NS * kSub * 128 + W * kGuWaveBytes; }
+
+template <int NS, int W, int S, int NSUB>
+__device__ __forceinline__ void gu_main(uint8_t (&ring)[S][(gu_slot_bytes<NS, W>())], const GuCtx<NS, W>& c,
+                                        f32x16 (&acc_g)[NS], f32x16 (&acc_u)[NS]) {
+    constexpr int kG = GuCtx<NS, W>::kX;   // loads per fill without weights
+    int ws = 0, rs = 1;                    // slot written, slot read (nothing read before j = 0)
+    for (int j = 1 - S; j < c.n_slabs; ++j) {
+        if (j >= 0) {
+            if (c.has_rows) wait_vm<(S - 2) * (kG + 3)>(); else wait_vm<(S - 2) * kG>();
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        gu_step<NS, W, S, NSUB>(&ring[ws][0], &ring[rs][0], c, j, acc_g, acc_u);
+        ws = next_slot<S>(ws);
+        rs = next_slot<S>(rs);
+    }
+    wait_vm<0>();    // no ring write may land after the block's LDS is released
+}
+
+template <int NS, int W, int S>
+__global__ __launch_bounds__(64 * W) void gateup_kernel(
+    const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales, size_t e_codes,
+    size_t e_scales, const uint8_t* __restrict__ sh_codes, const uint8_t* __restrict__ sh_scales,
     const uint16_t* __restrict__ x, int H, int I, int E, const int32_t* __restrict__ n_tiles,
     const int2* __restrict__ tiles, const int32_t* __restrict__ counts, const int32_t* __restrict__ off,
     const int32_t* __restrict__ tok_of, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
     constexpr int TT = NS * kSub;
-    constexpr int kUnits = TT * (kSlab / 8) / kThreads;   // 16-byte x units per thread per slab
-    __shared__ __align__(16) GateUpLds<NS> L;
+    static_assert(GuCtx<NS, W>::kX >= 1, "every wave fills part of each slab");
+    __shared__ __align__(1024) uint8_t ring[S][(gu_slot_bytes<NS, W>())];
 
     Item it;
-    if (!block_item(n_tiles, tiles, counts, (I + kRowsPerBlock - 1) / kRowsPerBlock, TT, it)) return;
+    if (!block_item(n_tiles, tiles, counts, (I + 32 * W - 1) / (32 * W), TT, it)) return;
 
-    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id_uniform();
-    const int kb4 = (H / 32 + 3) / 4, n_slabs = 2 * kb4;
+    const int lane = lane_id(), wv = wave_id_uniform();
     const int n_sub = (it.rows + kSub - 1) / kSub;
     const int pair0 = off[it.group] + it.start;
-
-    // activations: unit u = tid + 256 v covers row u >> 3, 8 bf16 at (u & 7) * 8
-    const uint16_t* xrow[kUnits];
-#pragma unroll
-    for (int v = 0; v < kUnits; ++v) {
-        const int u = tid + kThreads * v, row = u >> 3;
-        xrow[v] = row < it.rows ? x + (size_t)tok_of[pair0 + row] * H + (u & 7) * 8 : nullptr;
-    }
-    auto load_x = [&](int slab, u32x4 (&r)[kUnits]) {
-#pragma unroll
-        for (int v = 0; v < kUnits; ++v) {
-            const int k0 = slab * kSlab + ((tid + kThreads * v) & 7) * 8;
-            r[v] = (xrow[v] && k0 < H) ? *reinterpret_cast<const u32x4*>(xrow[v] + slab * kSlab)
-                                       : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store_x = [&](int buf, const u32x4 (&r)[kUnits]) {
-#pragma unroll
-        for (int v = 0; v < kUnits; ++v) {
-            const int u = tid + kThreads * v;
-            *reinterpret_cast<u32x4*>(&L.x[buf][u >> 3][(u & 7) * 8]) = r[v];
-        }
-    };
-
-    // weights of this wave: rows n0 .. n0 + 31
-    const int n0 = it.rb * kRowsPerBlock + 32 * wv;
-    const bool has_rows = n0 < I;
-    const uint8_t* cbase = it.group < E ? gu_codes + (size_t)it.group * e_codes : sh_codes;
-    const uint16_t* sbase = it.group < E ? gu_scales + (size_t)it.group * e_scales / 2 : sh_scales;
     const int r = lane & 31, half = lane >> 5;
-    const size_t unit = (size_t)(n0 / 16 + (r >> 4));
-    const int li0 = (r & 15) + 16 * half;     // lane inside the unit for MX block q = half (+ 32 per p)
-    auto load_w = [&](int slab, u32x4& g, u32x4& u, uint32_t& sc) {
-        if (!has_rows) return;
-        const int c = slab >> 1, li = li0 + 32 * (slab & 1);
-        const uint8_t* p = cbase + ((unit * kb4 + c) * 2) * 1024 + li * 16;
-        g = load_stream16(p);
-        u = load_stream16(p + 1024);
-        sc = sbase[(unit * kb4 + c) * 64 + li];
-    };
+    const int kb4 = (H / 32 + 3) / 4;
+
+    GuCtx<NS, W> c;
+    c.n_slabs = 2 * kb4;
+    c.H = H;
+    c.wv = wv;
+    c.lane = lane;
+#pragma unroll
+    for (int v = 0; v < GuCtx<NS, W>::kX; ++v) {
+        const int row = 8 * (W * v + wv) + (lane >> 3);
+        c.xsrc[v] = x + (size_t)tok_of[pair0 + min(row, it.rows - 1)] * H;
+        c.xk[v] = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    }
+    const int n0 = it.rb * 32 * W + 32 * wv;
+    c.has_rows = n0 < I;
+    {
+        const uint8_t* cb = it.group < E ? gu_codes + (size_t)it.group * e_codes : sh_codes;
+        const uint8_t* sb = it.group < E ? gu_scales + (size_t)it.group * e_scales : sh_scales;
+        const size_t unit = (size_t)(n0 / 16 + (r >> 4));
+        const int li0 = (r & 15) + 16 * half;
+        c.codes = cb + unit * kb4 * 2048 + li0 * 16;
+        c.scales = sb + unit * kb4 * 128 + ((2 * li0) & ~3);   // 16-bit scale pairs, dword holding li0
+        c.sc_shift = 16 * (li0 & 1);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) c.boff[st] = lds_slot(r, 4 * half + st);
 
     f32x16 acc_g[NS], acc_u[NS];
 #pragma unroll
@@ -269,46 +377,12 @@ __global__ __launch_bounds__(kThreads, 2) void gateup_kernel(
         acc_g[s] = f32x16{};
         acc_u[s] = f32x16{};
     }
+    if (NS == 4 && n_sub == 4) gu_main<NS, W, S, (NS >= 4 ? 4 : 1)>(ring, c, acc_g, acc_u);
+    else if (NS >= 3 && n_sub == 3) gu_main<NS, W, S, (NS >= 3 ? 3 : 1)>(ring, c, acc_g, acc_u);
+    else if (NS >= 2 && n_sub == 2) gu_main<NS, W, S, (NS >= 2 ? 2 : 1)>(ring, c, acc_g, acc_u);
+    else gu_main<NS, W, S, 1>(ring, c, acc_g, acc_u);
 
-    u32x4 xr[kUnits];
-    u32x4 wg = {0u, 0u, 0u, 0u}, wu = {0u, 0u, 0u, 0u};
-    uint32_t ws = 0x7F7Fu;
-    load_x(0, xr);
-    load_w(0, wg, wu, ws);
-    store_x(0, xr);
-    __syncthreads();
-
-    for (int slab = 0; slab < n_slabs; ++slab) {
-        const int buf = slab & 1;
-        u32x4 ng = {0u, 0u, 0u, 0u}, nu = {0u, 0u, 0u, 0u};
-        uint32_t ns = 0x7F7Fu;
-        if (slab + 1 < n_slabs) {
-            load_x(slab + 1, xr);
-            load_w(slab + 1, ng, nu, ns);
-        }
-        if (has_rows) {
-            const float sg = e8m0_to_f32(ws & 0xFF), su = e8m0_to_f32((ws >> 8) & 0xFF);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const bf16x8 ag = fp4x8_bf16(wg[st], sg), au = fp4x8_bf16(wu[st], su);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    if (s < n_sub) {
-                        const bf16x8 b = lds_bf16x8(&L.x[buf][s * kSub + r][32 * half + 8 * st]);
-                        acc_g[s] = mfma_bf16(ag, b, acc_g[s]);
-                        acc_u[s] = mfma_bf16(au, b, acc_u[s]);
-                    }
-                }
-            }
-        }
-        if (slab + 1 < n_slabs) store_x(buf ^ 1, xr);
-        __syncthreads();
-        wg = ng;
-        wu = nu;
-        ws = ns;
-    }
-
-    if (!has_rows) return;
+    if (!c.has_rows) return;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int row = s * kSub + r;
@@ -338,123 +412,181 @@ __global__ __launch_bounds__(kThreads, 2) void gateup_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// down: block = (tile, 128 output rows); wave w owns output rows 32w..32w+31.
-// Both halves of h go through the same weights into one accumulator.
+// down: block = (32*ND tokens of a gate/up tile, 64*W output rows); wave w
+// owns output rows 64w..64w+63 as two 32-row MFMA tiles.  A gate/up tile of TT
+// tokens splits into TT / (32 ND) parts.  Both halves of h go through the same
+// weights into one accumulator.
 
-template <int NS>
-struct DownLds {
-    uint16_t h[2][2][NS * kSub][kLdsRow];   // [buffer][hi, lo][token][k]
+template <int ND, int W>
+struct DnCtx {
+    static constexpr int kX = ND * kSub * 128 / (8 * 128 * W);   // ring-fill instructions per wave and plane
+    size_t hrow[kX];
+    int hk[kX];
+    const uint16_t* h_hi;
+    const uint16_t* h_lo;
+    const uint8_t* codes0;    // row tile 0; tile 1 is two units (2 * kb4 chunks) further
+    const uint8_t* scales0;   // the scale dword holding this lane's byte, chunk 0
+    size_t t1_codes, t1_scales;
+    int n_slabs, I, wv, lane;
+    int sc_shift;
+    bool has_rows;
+    int boff[4];
 };
 
-template <int NS>
-__global__ __launch_bounds__(kThreads, 2) void down_kernel(
+template <int ND, int W>
+constexpr int dn_slot_bytes() { return 2 * ND * kSub * 128 + W * kDnWaveBytes; }
+
+template <int ND, int W, int S, int NSUB>
+__device__ __forceinline__ void dn_step(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd,
+                                        const DnCtx<ND, W>& c, int j, f32x16 (&acc)[2][ND]) {
+    constexpr int kPlane = ND * kSub * 128;
+    {
+        const int sl = min(j + S - 1, c.n_slabs - 1);
+#pragma unroll
+        for (int v = 0; v < DnCtx<ND, W>::kX; ++v) {
+            const int k = sl * kSlab + c.hk[v];
+            const size_t o = c.hrow[v] + (k < c.I ? k : 0);
+            lds_load16(c.h_hi + o, wr + (W * v + c.wv) * 1024);
+            lds_load16(c.h_lo + o, wr + kPlane + (W * v + c.wv) * 1024);
+        }
+        if (c.has_rows) {
+            uint8_t* wb = wr + 2 * kPlane + c.wv * kDnWaveBytes;
+            const uint8_t* p = c.codes0 + (size_t)(sl >> 1) * 1024 + (sl & 1) * 512;
+            const uint8_t* s = c.scales0 + (size_t)(sl >> 1) * 64 + (sl & 1) * 32;
+            lds_load16(p, wb);
+            lds_load16(p + c.t1_codes, wb + 1024);
+            lds_load4(s, wb + 2048);
+            lds_load4(s + c.t1_scales, wb + 2304);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (c.has_rows && j >= 0) {
+        const uint8_t* wb = rd + 2 * kPlane + c.wv * kDnWaveBytes;
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + c.lane * 16);
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + 1024 + c.lane * 16);
+        const uint32_t w0 = *reinterpret_cast<const uint32_t*>(wb + 2048 + c.lane * 4);
+        const uint32_t w1 = *reinterpret_cast<const uint32_t*>(wb + 2304 + c.lane * 4);
+        bf16x8 bh[4][NSUB], bl[4][NSUB];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+                const uint8_t* p = rd + s * kSub * 128 + c.boff[st];
+                bh[st][s] = lds_b(p);
+                bl[st][s] = lds_b(p + kPlane);
+            }
+        const float s0 = e8m0_to_f32((w0 >> c.sc_shift) & 0xFF), s1 = e8m0_to_f32((w1 >> c.sc_shift) & 0xFF);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const bf16x8 a0 = fp4x8_bf16(c0[st], s0), a1 = fp4x8_bf16(c1[st], s1);
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+                acc[0][s] = mfma_bf16(a0, bh[st][s], acc[0][s]);
+                acc[1][s] = mfma_bf16(a1, bh[st][s], acc[1][s]);
+                acc[0][s] = mfma_bf16(a0, bl[st][s], acc[0][s]);
+                acc[1][s] = mfma_bf16(a1, bl[st][s], acc[1][s]);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int ND, int W, int S, int NSUB>
+__device__ __forceinline__ void dn_main(uint8_t (&ring)[S][(dn_slot_bytes<ND, W>())], const DnCtx<ND, W>& c,
+                                        f32x16 (&acc)[2][ND]) {
+    constexpr int kG = 2 * DnCtx<ND, W>::kX;
+    int ws = 0, rs = 1;
+    for (int j = 1 - S; j < c.n_slabs; ++j) {
+        if (j >= 0) {
+            if (c.has_rows) wait_vm<(S - 2) * (kG + 4)>(); else wait_vm<(S - 2) * kG>();
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dn_step<ND, W, S, NSUB>(&ring[ws][0], &ring[rs][0], c, j, acc);
+        ws = next_slot<S>(ws);
+        rs = next_slot<S>(rs);
+    }
+    wait_vm<0>();
+}
+
+template <int ND, int W, int S>
+__global__ __launch_bounds__(64 * W) void down_kernel(
     const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales, size_t e_codes,
     size_t e_scales, const uint8_t* __restrict__ sh_codes, const uint8_t* __restrict__ sh_scales,
-    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int H, int I, int E,
+    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int H, int I, int E, int tile_tokens,
     const int32_t* __restrict__ n_tiles, const int2* __restrict__ tiles, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ off, float* __restrict__ y_pair) {
-    constexpr int TT = NS * kSub;
-    constexpr int kUnits = TT * (kSlab / 8) / kThreads;
-    __shared__ __align__(16) DownLds<NS> L;
+    constexpr int TD = ND * kSub;
+    static_assert(DnCtx<ND, W>::kX >= 1, "every wave fills part of each slab");
+    __shared__ __align__(1024) uint8_t ring[S][(dn_slot_bytes<ND, W>())];
 
+    const int parts = tile_tokens / TD, n_rb = (H + 64 * W - 1) / (64 * W);
     Item it;
-    if (!block_item(n_tiles, tiles, counts, (H + kRowsPerBlock - 1) / kRowsPerBlock, TT, it)) return;
+    if (!block_item(n_tiles, tiles, counts, parts * n_rb, tile_tokens, it)) return;
+    const int part = it.rb / n_rb;
+    it.rb -= part * n_rb;
+    it.rows = min(it.rows - part * TD, TD);
+    if (it.rows <= 0) return;
+    it.start += part * TD;
 
-    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id_uniform();
-    const int kb4 = (I / 32 + 3) / 4, n_slabs = 2 * kb4;
+    const int lane = lane_id(), wv = wave_id_uniform();
     const int n_sub = (it.rows + kSub - 1) / kSub;
     const int pair0 = off[it.group] + it.start;
-
-    auto load_h = [&](int slab, u32x4 (&rh)[kUnits], u32x4 (&rl)[kUnits]) {
-#pragma unroll
-        for (int v = 0; v < kUnits; ++v) {
-            const int u = tid + kThreads * v, row = u >> 3;
-            const int k0 = slab * kSlab + (u & 7) * 8;
-            if (row < it.rows && k0 < I) {
-                const size_t o = (size_t)(pair0 + row) * I + k0;
-                rh[v] = *reinterpret_cast<const u32x4*>(h_hi + o);
-                rl[v] = *reinterpret_cast<const u32x4*>(h_lo + o);
-            } else {
-                rh[v] = u32x4{0u, 0u, 0u, 0u};
-                rl[v] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto store_h = [&](int buf, const u32x4 (&rh)[kUnits], const u32x4 (&rl)[kUnits]) {
-#pragma unroll
-        for (int v = 0; v < kUnits; ++v) {
-            const int u = tid + kThreads * v;
-            *reinterpret_cast<u32x4*>(&L.h[buf][0][u >> 3][(u & 7) * 8]) = rh[v];
-            *reinterpret_cast<u32x4*>(&L.h[buf][1][u >> 3][(u & 7) * 8]) = rl[v];
-        }
-    };
-
-    const int n0 = it.rb * kRowsPerBlock + 32 * wv;
-    const bool has_rows = n0 < H;
-    const uint8_t* cbase = it.group < E ? dn_codes + (size_t)it.group * e_codes : sh_codes;
-    const uint8_t* sbase = it.group < E ? dn_scales + (size_t)it.group * e_scales : sh_scales;
     const int r = lane & 31, half = lane >> 5;
-    const size_t unit = (size_t)(n0 / 16 + (r >> 4));
-    const int li0 = (r & 15) + 16 * half;
-    auto load_w = [&](int slab, u32x4& w, uint32_t& sc) {
-        if (!has_rows) return;
-        const int c = slab >> 1, li = li0 + 32 * (slab & 1);
-        w = load_stream16(cbase + (unit * kb4 + c) * 1024 + li * 16);
-        sc = sbase[(unit * kb4 + c) * 64 + li];
-    };
+    const int kb4 = (I / 32 + 3) / 4;
 
-    f32x16 acc[NS];
+    DnCtx<ND, W> c;
+    c.n_slabs = 2 * kb4;
+    c.I = I;
+    c.wv = wv;
+    c.lane = lane;
+    c.h_hi = h_hi;
+    c.h_lo = h_lo;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc[s] = f32x16{};
-
-    u32x4 hr[kUnits], lr[kUnits];
-    u32x4 w = {0u, 0u, 0u, 0u};
-    uint32_t ws = 0x7Fu;
-    load_h(0, hr, lr);
-    load_w(0, w, ws);
-    store_h(0, hr, lr);
-    __syncthreads();
-
-    for (int slab = 0; slab < n_slabs; ++slab) {
-        const int buf = slab & 1;
-        u32x4 nw = {0u, 0u, 0u, 0u};
-        uint32_t ns = 0x7Fu;
-        if (slab + 1 < n_slabs) {
-            load_h(slab + 1, hr, lr);
-            load_w(slab + 1, nw, ns);
-        }
-        if (has_rows) {
-            const float sc = e8m0_to_f32(ws & 0xFF);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const bf16x8 a = fp4x8_bf16(w[st], sc);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    if (s < n_sub) {
-                        const bf16x8 bh = lds_bf16x8(&L.h[buf][0][s * kSub + r][32 * half + 8 * st]);
-                        const bf16x8 bl = lds_bf16x8(&L.h[buf][1][s * kSub + r][32 * half + 8 * st]);
-                        acc[s] = mfma_bf16(a, bh, acc[s]);
-                        acc[s] = mfma_bf16(a, bl, acc[s]);
-                    }
-                }
-            }
-        }
-        if (slab + 1 < n_slabs) store_h(buf ^ 1, hr, lr);
-        __syncthreads();
-        w = nw;
-        ws = ns;
+    for (int v = 0; v < DnCtx<ND, W>::kX; ++v) {
+        const int row = 8 * (W * v + wv) + (lane >> 3);
+        c.hrow[v] = (size_t)(pair0 + min(row, it.rows - 1)) * I;
+        c.hk[v] = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
     }
+    const int n0 = it.rb * 64 * W + 64 * wv;
+    c.has_rows = n0 < H;
+    {
+        const uint8_t* cb = it.group < E ? dn_codes + (size_t)it.group * e_codes : sh_codes;
+        const uint8_t* sb = it.group < E ? dn_scales + (size_t)it.group * e_scales : sh_scales;
+        const size_t unit = (size_t)(n0 / 16 + (r >> 4));
+        const int li0 = (r & 15) + 16 * half;
+        c.codes0 = cb + unit * kb4 * 1024 + li0 * 16;
+        c.scales0 = sb + unit * kb4 * 64 + (li0 & ~3);
+        c.sc_shift = 8 * (li0 & 3);
+        c.t1_codes = (size_t)2 * kb4 * 1024;
+        c.t1_scales = (size_t)2 * kb4 * 64;
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) c.boff[st] = lds_slot(r, 4 * half + st);
 
-    if (!has_rows) return;
+    f32x16 acc[2][ND];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int row = s * kSub + r;
-        if (s >= n_sub || row >= it.rows) continue;
-        float* dst = y_pair + (size_t)(pair0 + row) * H + n0 + 4 * half;
+    for (int s = 0; s < ND; ++s) {
+        acc[0][s] = f32x16{};
+        acc[1][s] = f32x16{};
+    }
+    if (ND == 2 && n_sub == 2) dn_main<ND, W, S, (ND >= 2 ? 2 : 1)>(ring, c, acc);
+    else dn_main<ND, W, S, 1>(ring, c, acc);
+
+    if (!c.has_rows) return;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            *reinterpret_cast<float4*>(dst + 8 * r4) =
-                float4{acc[s][4 * r4], acc[s][4 * r4 + 1], acc[s][4 * r4 + 2], acc[s][4 * r4 + 3]};
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int s = 0; s < ND; ++s) {
+            const int row = s * kSub + r;
+            if (s >= n_sub || row >= it.rows) continue;
+            float* dst = y_pair + (size_t)(pair0 + row) * H + n0 + 32 * t + 4 * half;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<float4*>(dst + 8 * r4) =
+                    float4{acc[t][s][4 * r4], acc[t][s][4 * r4 + 1], acc[t][s][4 * r4 + 2], acc[t][s][4 * r4 + 3]};
+        }
     }
 }
 
@@ -513,20 +645,25 @@ hipError_t launch_gemms(const moedec_moe_weights& w, const uint16_t* x, const Pr
     uint16_t* h_lo = reinterpret_cast<uint16_t*>(base + lay.h_lo_off);
     float* y_pair = reinterpret_cast<float*>(base + lay.y_pair_off);
 
-    const size_t gu_items = (size_t)lay.max_tiles * ((w.I + kRowsPerBlock - 1) / kRowsPerBlock);
-    hipLaunchKernelGGL(gateup_kernel<NS>, dim3((unsigned)(kXcds * ((gu_items + kXcds - 1) / kXcds))),
-                       dim3(kThreads), 0, s, static_cast<const uint8_t*>(w.gu_codes),
-                       reinterpret_cast<const uint16_t*>(w.gu_scales), sz.gu_codes, sz.gu_scales,
-                       static_cast<const uint8_t*>(w.sh_gu_codes), reinterpret_cast<const uint16_t*>(w.sh_gu_scales),
+    // Wider blocks for the larger tiles: 8 waves (one block per CU, a 4-slot
+    // ring) where every wave still fills part of each slab.
+    constexpr int WG = NS >= 2 ? 8 : 4, SG = NS >= 2 ? 4 : 3;
+    const size_t gu_items = (size_t)lay.max_tiles * ((w.I + 32 * WG - 1) / (32 * WG));
+    hipLaunchKernelGGL((gateup_kernel<NS, WG, SG>), dim3((unsigned)(kXcds * ((gu_items + kXcds - 1) / kXcds))),
+                       dim3(64 * WG), 0, s, static_cast<const uint8_t*>(w.gu_codes),
+                       static_cast<const uint8_t*>(w.gu_scales), sz.gu_codes, sz.gu_scales,
+                       static_cast<const uint8_t*>(w.sh_gu_codes), static_cast<const uint8_t*>(w.sh_gu_scales),
                        x, w.H, w.I, w.E, n_tiles, tiles, counts, off, tok_of, h_hi, h_lo);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t dn_items = (size_t)lay.max_tiles * ((w.H + kRowsPerBlock - 1) / kRowsPerBlock);
-    hipLaunchKernelGGL(down_kernel<NS>, dim3((unsigned)(kXcds * ((dn_items + kXcds - 1) / kXcds))),
-                       dim3(kThreads), 0, s, static_cast<const uint8_t*>(w.dn_codes),
+    constexpr int ND = NS >= 2 ? 2 : 1;
+    constexpr int WD = ND >= 2 ? 8 : 4, SD = ND >= 2 ? 4 : 3;
+    const size_t dn_items = (size_t)lay.max_tiles * (NS / ND) * ((w.H + 64 * WD - 1) / (64 * WD));
+    hipLaunchKernelGGL((down_kernel<ND, WD, SD>), dim3((unsigned)(kXcds * ((dn_items + kXcds - 1) / kXcds))),
+                       dim3(64 * WD), 0, s, static_cast<const uint8_t*>(w.dn_codes),
                        static_cast<const uint8_t*>(w.dn_scales), sz.dn_codes, sz.dn_scales,
                        static_cast<const uint8_t*>(w.sh_dn_codes), static_cast<const uint8_t*>(w.sh_dn_scales),
-                       h_hi, h_lo, w.H, w.I, w.E, n_tiles, tiles, counts, off, y_pair);
+                       h_hi, h_lo, w.H, w.I, w.E, NS * kSub, n_tiles, tiles, counts, off, y_pair);
     return hipGetLastError();
 }
 

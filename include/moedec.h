@@ -375,7 +375,8 @@ int moe_layer_rmsnorm_router_mxfp4(const moedec_moe_weights* w, const uint16_t* 
  * Six launches on `stream`: counts reset, routing, plan (one block), scatter,
  * gate/up, down, combine.
  * w             MOEDEC_MOE_MAGIC weights (an FP8 shared expert is refused
- *               with MOEDEC_ERR_FORMAT)
+ *               with MOEDEC_ERR_FORMAT); the four scale arrays 4-byte
+ *               aligned (they are read as 32-bit words)
  * x_bf16        [T][H] bf16, 16-byte aligned
  * logits        [T][E] float32 router logits, 4-byte aligned
  * T             1 .. MOEDEC_MAX_PREFILL_T tokens

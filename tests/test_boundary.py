@@ -359,6 +359,7 @@ def test_prefill_workspace_and_argument_checks(m):
     assert call(_weights(m, magic=1)) == -4
     assert call(_weights(m, magic=m._lib.MOE_MAGIC_SHARED_FP8)) == -4
     assert call(_weights(m), k=33) == -3
+    assert call(_weights(m, dn_scales=(1 << 20) + 2)) == -2
     assert call(_weights(m), T=0) == -3
     assert call(_weights(m), T=m._lib.MOEDEC_MAX_PREFILL_T + 1) == -3
     assert call(_weights(m), lg=ODD) == -2
