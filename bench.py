@@ -18,6 +18,10 @@ Reported next to the headline (M = 1) figure, each measured the same way:
     layer's output, as a HIP graph and eagerly;
   * the LM head 157,184 x 2,560: one-off FP8 quantisation, FP8 GEMV at M = 1
     and 4, and the bf16 GEMV comparator;
+  * the many-token layer (moe_layer_mxfp4_prefill: a prefill chunk or a long
+    verify window, grouped GEMM on bf16 matrix cores) on one layer's experts
+    at T = 512 .. 32,768 tokens: µs per layer and algorithmic TFLOP/s against
+    the 2.5 PFLOP/s dense bf16 peak;
   * the CPU oracle on a bounded sample of the same layers (cpu_baseline).
 
 Bytes are algorithmic: the weights a step must read (codes + E8M0 scales of
@@ -38,6 +42,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PREFILL_TOKENS = (512, 2048, 8192, 32768)
 TRAFFIC_FILE = "moe_ffn_kernel_ling_m{M}_hbm_traffic.md"
 COPY_PROBE_ELEMS = 1 << 28                 # float32: 1 GiB read and 1 GiB written
 PMC_KERNEL = "moe_ffn_kernel"
@@ -58,6 +64,9 @@ def parse_args(argv=None):
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head measurements")
     ap.add_argument("--no-fp8-shared", action="store_true", help="skip the FP8 shared-expert layer")
     ap.add_argument("--no-m4", action="store_true", help="skip the M = 4 measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the many-token (prefill) layer")
+    ap.add_argument("--prefill-tokens", type=int, nargs="+", default=list(PREFILL_TOKENS),
+                    help="token counts of the many-token layer measurement")
     ap.add_argument("--no-stack", action="store_true", help="skip the residual-stack measurement")
     ap.add_argument("--no-router", action="store_true", help="skip the router-logits measurement")
     ap.add_argument("--stack-passes", type=int, default=100, help="graph passes over the layers (stack)")
@@ -262,6 +271,48 @@ def shared_fp8_bench(m, torch, synth, layers, steps, dev):
         out[f"m{M}_gbs"] = step_bytes / (1e6 * ms / steps)
         del g_main
     del fp8_layers
+    return out
+
+
+def prefill_bench(m, torch, synth, layers, dev, tokens=PREFILL_TOKENS):
+    """The many-token layer on layer 0's experts: T tokens of N(0,1) bf16
+    activations with N(0,1) router logits, routed top-8 of 512 plus the shared
+    expert.  Algorithmic flops per (token, expert) pair: 2 * (2 I H) for
+    gate/up and 2 H I for down, over the T * (k + 1) pairs (the kernels
+    carry h as two bf16 halves, so the down product runs twice on the
+    matrix cores; that is not counted)."""
+    shape = synth.LING
+    E, H, I, k = shape.E, shape.H, shape.I, shape.k
+    W = layers[0]
+    t = Timer(torch)
+    out = {}
+    for T in tokens:
+        x = torch.from_numpy(synth.activations_bf16(0, 0, T, H).view("int16")).view(torch.bfloat16).to(dev)
+        lg = torch.from_numpy(synth.logits_f32(0, 0, T, E)).to(dev)
+        ws = m.make_prefill_workspace(T, E, k, H, I, dev)
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        counts = torch.empty(E + 1, dtype=torch.int32, device=dev)
+
+        def call():
+            m.moe_layer_prefill(W, x, lg, k, workspace=ws, y=y, want_f32=False, counts=counts)
+
+        call()
+        call()
+        reps = max(5, min(50, 80000 // T))
+        ms = t.run(lambda: [call() for _ in range(reps)])
+        us = 1e3 * ms / reps
+        flops = T * (k + 1) * 6 * H * I
+        active = int((counts[:E] > 0).sum().item()) + 1
+        out[str(T)] = {
+            "us_per_layer": us,
+            "tflops": flops / us / 1e6,
+            "frac_of_bf16_peak": flops / us / 1e6 / PEAK_BF16_TFLOPS,
+            "active_experts": active,
+            "weight_gbs": active * EXPERT_BYTES_LING / us / 1e3,
+            "reps": reps,
+        }
+        del ws, x, lg, y
+        torch.cuda.empty_cache()
     return out
 
 
@@ -789,6 +840,10 @@ def main(argv=None):
     if not args.no_router:
         router = router_bench(m, torch, synth, layers, min(args.steps, 2100), dev)
         log("router:", json.dumps(router))
+    pf = None
+    if not args.no_prefill:
+        pf = prefill_bench(m, torch, synth, layers, dev, tuple(args.prefill_tokens))
+        log("prefill:", json.dumps(pf))
     del layers
     torch.cuda.empty_cache()
     lm = None
@@ -840,7 +895,7 @@ def main(argv=None):
         "traffic_m4": None if traffic4 is None else {k: traffic4[k] for k in (
             "fetch_bytes", "write_bytes", "traffic_bytes", "algorithmic_bytes", "traffic_over_algorithmic")},
         "extra": {"m1": r1, "m4": r4, "stack": stack, "router": router, "lmhead": lm, "fp8_shared": sh8,
-                  "cpu": cpu},
+                  "prefill": pf, "cpu": cpu},
     }
     if router is not None:
         line["router_us_m1"] = round(router["us_m1"], 3)
@@ -856,6 +911,10 @@ def main(argv=None):
     if sh8 is not None:
         line["fp8_shared_us_per_layer_m1"] = round(sh8["m1_us_per_layer"], 3)
         line["fp8_shared_us_per_layer_m4"] = round(sh8["m4_us_per_layer"], 3)
+    if pf is not None:
+        for T, r in pf.items():
+            line[f"prefill_us_t{T}"] = round(r["us_per_layer"], 1)
+            line[f"prefill_tflops_t{T}"] = round(r["tflops"], 1)
     if lm is not None:
         line["lmhead_fp8_gbs_m1"] = round(lm["fp8_m1_gbs"], 1)
         line["lmhead_fp8_argmax_us_m1"] = round(lm["fp8_argmax_m1_us"], 2)
