@@ -38,13 +38,15 @@ from .formats import (
 )
 from .route import route_topk, dispatch_table, router_logits, expert_groups
 from .moe import expert_ffn, moe_layer, moe_layer_by_expert, rmsnorm
-from .lmhead import lmhead_quant_fp8, lmhead_gemv_fp8, lmhead_gemv_bf16, lmhead_argmax, lmhead_sample
+from .lmhead import (lmhead_quant_fp8, lmhead_gemv_fp8, lmhead_gemv_fp8_dynact, lmhead_gemv_bf16, lmhead_argmax,
+                     lmhead_sample)
 
 __all__ = [
     "e2m1_value", "e8m0_value", "mxfp4_dequant", "e4m3_value",
     "e4m3_encode_rne_sat", "bf16_round", "bf16_bits",
     "route_topk", "dispatch_table", "router_logits", "expert_groups",
     "expert_ffn", "moe_layer", "moe_layer_by_expert", "rmsnorm",
-    "lmhead_quant_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "lmhead_argmax", "lmhead_sample",
+    "lmhead_quant_fp8", "lmhead_gemv_fp8", "lmhead_gemv_fp8_dynact", "lmhead_gemv_bf16", "lmhead_argmax",
+    "lmhead_sample",
 ]
 from .shared_fp8 import quant_fp8_rows, dequant_fp8_rows, shared_fp8_dense

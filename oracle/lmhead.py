@@ -16,6 +16,13 @@ Readings where the pages are silent:
   * logits[m, v] = s_v * sum_k x[m,k] * e4m3(q[v,k]), no bias, no soft-cap,
     float32 out; the bf16 comparator is logits = W x.
 
+Dynamic FP8 activations (the other half of a dynamic FP8 configuration: the
+activations quantised per token when the layer runs, as the weights were per
+row when it was built).  Reading: each token row x[m] gets the weights' rule,
+t_m = fl32(max_k |x[m,k]| / 448) (1 for a zero row), p[m,k] = E4M3
+nearest-even, saturating, of fl32(x[m,k] / t_m); then logits[m, v] =
+s_v * t_m * sum_k e4m3(p[m,k]) * e4m3(q[v,k]).
+
 Sampling (the decode step's draw on these logits; the pages give the settings
 only -- temperature 0.6, top-p 0.95, top-k 29 [card results]).  Readings:
   * candidates: the top_k logits of the row, ordered by (logit desc, index
@@ -35,7 +42,11 @@ all-zero row, the per-element error bound of E4M3, and torch's float8_e4m3fn
 cast for in-range values; the GEMVs by one-hot activations selecting a single
 column times its row scale (orientation and scale) and x = 0; the greedy
 argmax by hand-worked rows with ties and signed zeros and by a library sort;
-the sampling by hand-worked distributions (inverse-CDF boundaries, nucleus cut,
+the dynamic-activation GEMV by activations that are already E4M3 values times
+a per-token power of two with absmax 448 * 2^j (quantised without loss, so the
+logits equal the weight-only GEMV's), by a hand-worked two-element case, by x =
+0 and by scaling a token by a power of two (same codes, logits scaled); the
+sampling by hand-worked distributions (inverse-CDF boundaries, nucleus cut,
 top-k cut, temperature), the top_k = 1 and vanishing-temperature limits
 (argmax), and by the interval each token's draws occupy, which equals its
 renormalised probability computed by an independent loop.
@@ -68,6 +79,15 @@ def lmhead_gemv_fp8(codes, row_scale, x):
     x = np.asarray(x, dtype=np.float64)                       # [M][H]
     s = np.asarray(row_scale, dtype=np.float64)               # [V]
     return (x @ wq.T) * s[None, :]
+
+
+def lmhead_gemv_fp8_dynact(codes, row_scale, x):
+    """logits [M][V] float64 with dynamic per-token FP8 activations:
+    row_scale[v] * t[m] * sum_k e4m3(p[m,k]) * e4m3(codes[v,k]), where (p, t)
+    is the weights' per-row quantisation applied to each token row of x."""
+    p, t = lmhead_quant_fp8(x)
+    xq = e4m3_value(p) * np.asarray(t, dtype=np.float64)[:, None]
+    return lmhead_gemv_fp8(codes, row_scale, xq)
 
 
 def lmhead_argmax(logits):

@@ -194,3 +194,46 @@ def test_sampling_uniforms_are_in_range_and_counter_based():
     st = synth.stream_state(3, synth.SAMPLING_STREAM_BASE + 7)
     words = synth.splitmix_outputs(st, np.arange(4, dtype=np.uint64))
     np.testing.assert_array_equal((u.astype(np.float64) * (1 << 24)).astype(np.uint64), words >> np.uint64(40))
+
+
+def test_dynact_lossless_activations_equal_weight_only_gemv():
+    """Token rows that are E4M3 values times 2^j with absmax 448 * 2^j quantise
+    without loss (t = 2^j exactly), so the dynamic-activation logits equal the
+    weight-only FP8 logits bit for bit."""
+    rng = np.random.default_rng(31)
+    w = rng.standard_normal((40, 64)).astype(np.float32)
+    codes, s = oracle.lmhead_quant_fp8(w)
+    vals = oracle.formats.e4m3_value(rng.integers(0, 0x7F, size=(3, 64)))
+    vals *= np.where(rng.random((3, 64)) < 0.5, -1.0, 1.0)
+    vals[:, 5] = 448.0
+    x = vals * np.array([[2.0 ** -3], [1.0], [2.0 ** 4]])
+    p, t = oracle.lmhead_quant_fp8(x)
+    np.testing.assert_array_equal(t, np.float32([2.0 ** -3, 1.0, 2.0 ** 4]))
+    np.testing.assert_array_equal(oracle.lmhead_gemv_fp8_dynact(codes, s, x),
+                                  oracle.lmhead_gemv_fp8(codes, s, x))
+
+
+def test_dynact_hand_worked():
+    # W = [1, 2]: s_w = fl32(2/448), codes 224 -> 0x76, 448 -> 0x7E.
+    # x = [3, -1]: t = fl32(3/448), x / t = [448, -149.33] -> codes 0x7E, 0xF1 (-144).
+    # sum of code products 224*448 + 448*(-144) = 35840.
+    codes, s = oracle.lmhead_quant_fp8(np.float32([[1.0, 2.0]]))
+    assert codes.tolist() == [[0x76, 0x7E]]
+    x = np.float32([[3.0, -1.0]])
+    p, t = oracle.lmhead_quant_fp8(x)
+    assert p.tolist() == [[0x7E, 0xF1]]
+    want = 35840.0 * float(np.float32(2.0) / np.float32(448.0)) * float(np.float32(3.0) / np.float32(448.0))
+    np.testing.assert_allclose(oracle.lmhead_gemv_fp8_dynact(codes, s, x), [[want]], rtol=1e-15)
+    assert abs(want - 15.0 / 14.0) < 1e-6      # the quantised x is [3, -0.964]
+
+
+def test_dynact_zero_and_power_of_two_scaling():
+    rng = np.random.default_rng(32)
+    w = rng.standard_normal((20, 32)).astype(np.float32)
+    codes, s = oracle.lmhead_quant_fp8(w)
+    assert (oracle.lmhead_gemv_fp8_dynact(codes, s, np.zeros((2, 32))) == 0).all()
+    x = synth.bf16_values(synth.bf16_bits_from_f32(rng.standard_normal((2, 32)).astype(np.float32)))
+    base = oracle.lmhead_gemv_fp8_dynact(codes, s, x)
+    for j in (-5, 3):
+        np.testing.assert_array_equal(oracle.lmhead_quant_fp8(x * 2.0 ** j)[0], oracle.lmhead_quant_fp8(x)[0])
+        np.testing.assert_array_equal(oracle.lmhead_gemv_fp8_dynact(codes, s, x * 2.0 ** j), base * 2.0 ** j)
