@@ -17,7 +17,8 @@ Reported next to the headline (M = 1) figure, each measured the same way:
     (moe_layer_rmsnorm_mxfp4), each layer's input formed from the previous
     layer's output, as a HIP graph and eagerly;
   * the LM head 157,184 x 2,560: one-off FP8 quantisation, FP8 GEMV at M = 1
-    and 4, and the bf16 GEMV comparator;
+    and 4 (weight-only, and with dynamic per-token FP8 activations), and the
+    bf16 GEMV comparator;
   * the many-token layer (moe_layer_mxfp4_prefill: a prefill chunk or a long
     verify window, grouped GEMM on bf16 matrix cores) on one layer's experts
     at T = 512 .. 32,768 tokens: µs per layer and algorithmic TFLOP/s against
@@ -460,6 +461,10 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
         m.lmhead_gemv_bf16(w, x, out=lo)
         g8 = capture(torch, lambda: [m.lmhead_gemv_fp8(head, x, out=lo) for _ in range(reps)])
         gb = capture(torch, lambda: [m.lmhead_gemv_bf16(w, x, out=lo) for _ in range(reps)])
+        # the same head with dynamic per-token FP8 activations
+        dyn = m.lmhead_dynamic_act(head)
+        m.lmhead_gemv_fp8(dyn, x, out=lo)
+        gd = capture(torch, lambda: [m.lmhead_gemv_fp8(dyn, x, out=lo) for _ in range(reps)])
         # greedy decode: FP8 GEMV with the argmax epilogue, logits not written
         aws = m.make_lmhead_workspace(V, M, dev)
         ids = torch.empty(M, dtype=torch.int32, device=dev)
@@ -475,6 +480,8 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
         gb.replay()
         ga.replay()
         gs.replay()
+        gd.replay()
+        msd = t.run(gd.replay) / reps
         ms8 = t.run(g8.replay) / reps
         msb = t.run(gb.replay) / reps
         msa = t.run(ga.replay) / reps
@@ -484,6 +491,8 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
         out[f"fp8_sample_m{M}_us"] = 1e3 * mss
         b8 = V * H + V * 4 + M * H * 2 + M * V * 4
         bb = V * H * 2 + M * H * 2 + M * V * 4
+        out[f"fp8_dynact_m{M}_us"] = 1e3 * msd
+        out[f"fp8_dynact_m{M}_gbs"] = b8 / (1e6 * msd)
         out[f"fp8_m{M}_us"] = 1e3 * ms8
         out[f"fp8_m{M}_bytes"] = b8
         out[f"fp8_m{M}_gbs"] = b8 / (1e6 * ms8)
@@ -491,7 +500,7 @@ def lmhead_bench(m, torch, synth, dev, reps=50):
         out[f"bf16_m{M}_us"] = 1e3 * msb
         out[f"bf16_m{M}_gbs"] = bb / (1e6 * msb)
         out[f"bf16_m{M}_frac_of_peak"] = bb / (1e6 * msb) / PEAK_HBM_GBS
-        del g8, gb, ga, gs
+        del g8, gb, ga, gs, gd
     del head, w
     torch.cuda.empty_cache()
     return out
@@ -921,6 +930,8 @@ def main(argv=None):
         line["lmhead_fp8_sample_us_m1"] = round(lm["fp8_sample_m1_us"], 2)
         line["lmhead_fp8_sample_us_m4"] = round(lm["fp8_sample_m4_us"], 2)
         line["lmhead_fp8_gbs_m4"] = round(lm["fp8_m4_gbs"], 1)
+        line["lmhead_fp8_dynact_gbs_m1"] = round(lm["fp8_dynact_m1_gbs"], 1)
+        line["lmhead_fp8_dynact_gbs_m4"] = round(lm["fp8_dynact_m4_gbs"], 1)
         line["lmhead_bf16_gbs_m1"] = round(lm["bf16_m1_gbs"], 1)
     print(json.dumps(line), flush=True)
     return 0

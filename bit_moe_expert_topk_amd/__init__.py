@@ -13,7 +13,8 @@ import torch
 
 from . import _lib
 from ._lib import (Dispatch, LMHeadFP8Desc, MoEWeights, MXFP4Sizes, MAX_E, MAX_K, MAX_M,
-                   MAX_SLOTS, MOE_MAGIC, MOE_MAGIC_SHARED_FP8, LMHEAD_MAGIC, FMT_E4M3FN_ROWSCALE_F32)
+                   MAX_SLOTS, MOE_MAGIC, MOE_MAGIC_SHARED_FP8, LMHEAD_MAGIC, FMT_E4M3FN_ROWSCALE_F32,
+                   FMT_E4M3FN_ROWSCALE_F32_DYNACT)
 
 lib = _lib.lib
 LIB_PATH = _lib.LIB_PATH
@@ -408,6 +409,15 @@ class LMHeadFP8:
     def __init__(self, codes, row_scale, desc):
         self.codes, self.row_scale, self.desc = codes, row_scale, desc
         self.V, self.H = codes.shape
+
+
+def lmhead_dynamic_act(head):
+    """The same FP8 head with dynamic per-token FP8 activations
+    (MOEDEC_FMT_E4M3FN_ROWSCALE_F32_DYNACT): shares the codes and scales."""
+    desc = LMHeadFP8Desc()
+    ctypes.memmove(ctypes.byref(desc), ctypes.byref(head.desc), ctypes.sizeof(LMHeadFP8Desc))
+    desc.format = FMT_E4M3FN_ROWSCALE_F32_DYNACT
+    return LMHeadFP8(head.codes, head.row_scale, desc)
 
 
 def lmhead_quant_fp8(w_bf16):

@@ -35,6 +35,7 @@ MOE_MAGIC = 0x4D4F4534
 MOE_MAGIC_SHARED_FP8 = 0x4D4F4538
 LMHEAD_MAGIC = 0x4C4D4838
 FMT_E4M3FN_ROWSCALE_F32 = 1
+FMT_E4M3FN_ROWSCALE_F32_DYNACT = 2
 
 c_void_p = ctypes.c_void_p
 c_int = ctypes.c_int

@@ -420,7 +420,7 @@ int lmhead_gemv_fp8(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M
     if (head->magic != MOEDEC_LMHEAD_MAGIC)
         return fail(MOEDEC_ERR_FORMAT, "head magic 0x%08x is not an FP8 LM-head descriptor",
                     head->magic);
-    if (head->format != MOEDEC_FMT_E4M3FN_ROWSCALE_F32)
+    if (head->format != MOEDEC_FMT_E4M3FN_ROWSCALE_F32 && head->format != MOEDEC_FMT_E4M3FN_ROWSCALE_F32_DYNACT)
         return fail(MOEDEC_ERR_FORMAT, "head format %u is not E4M3 with per-row float32 scales",
                     head->format);
     if (!head->codes || !head->row_scale || !x_bf16 || !logits)
@@ -434,7 +434,8 @@ int lmhead_gemv_fp8(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M
         return fail(MOEDEC_ERR_ALIGN, "codes 16-byte, row_scale/x/logits 4-byte alignment needed");
     if (int st = check_device()) return st;
     return launched(moedec::launch_gemv_fp8(head->codes, head->row_scale, head->V, head->H, x_bf16,
-                                            M, logits, static_cast<hipStream_t>(stream)),
+                                            M, logits, static_cast<hipStream_t>(stream), nullptr,
+                                            head->format == MOEDEC_FMT_E4M3FN_ROWSCALE_F32_DYNACT),
                     "lmhead_gemv_fp8");
 }
 
@@ -467,7 +468,7 @@ int check_epilogue(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M,
     if (head->magic != MOEDEC_LMHEAD_MAGIC)
         return fail(MOEDEC_ERR_FORMAT, "head magic 0x%08x is not an FP8 LM-head descriptor",
                     head->magic);
-    if (head->format != MOEDEC_FMT_E4M3FN_ROWSCALE_F32)
+    if (head->format != MOEDEC_FMT_E4M3FN_ROWSCALE_F32 && head->format != MOEDEC_FMT_E4M3FN_ROWSCALE_F32_DYNACT)
         return fail(MOEDEC_ERR_FORMAT, "head format %u is not E4M3 with per-row float32 scales",
                     head->format);
     if (!head->codes || !head->row_scale || !x_bf16 || !token_ids || !workspace)
@@ -496,7 +497,8 @@ int lmhead_gemv_fp8_argmax(const moedec_lmhead_fp8* head, const uint16_t* x_bf16
     if (int st = check_device()) return st;
     const moedec::Fp8Epilogue ep{workspace, token_ids, nullptr, 1.f, 1.f, 1};
     return launched(moedec::launch_gemv_fp8(head->codes, head->row_scale, head->V, head->H, x_bf16, M,
-                                            logits, static_cast<hipStream_t>(stream), &ep),
+                                            logits, static_cast<hipStream_t>(stream), &ep,
+                                            head->format == MOEDEC_FMT_E4M3FN_ROWSCALE_F32_DYNACT),
                     "lmhead_gemv_fp8_argmax");
 }
 
@@ -515,7 +517,8 @@ int lmhead_gemv_fp8_sample(const moedec_lmhead_fp8* head, const uint16_t* x_bf16
     if (int st = check_device()) return st;
     const moedec::Fp8Epilogue ep{workspace, token_ids, u, temperature, top_p, top_k};
     return launched(moedec::launch_gemv_fp8(head->codes, head->row_scale, head->V, head->H, x_bf16, M,
-                                            logits, static_cast<hipStream_t>(stream), &ep),
+                                            logits, static_cast<hipStream_t>(stream), &ep,
+                                            head->format == MOEDEC_FMT_E4M3FN_ROWSCALE_F32_DYNACT),
                     "lmhead_gemv_fp8_sample");
 }
 

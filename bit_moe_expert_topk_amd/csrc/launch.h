@@ -84,9 +84,11 @@ struct Fp8Epilogue {
     float temperature, top_p;
     int top_k;
 };
+// act8: quantise each token's activations to E4M3 on the fly (per-token
+// float32 scale, the weights' rule) and multiply FP8 by FP8.
 hipError_t launch_gemv_fp8(const uint8_t* codes, const float* rs, int V, int H,
                            const uint16_t* x, int M, float* logits, hipStream_t s,
-                           const Fp8Epilogue* ep = nullptr);
+                           const Fp8Epilogue* ep = nullptr, bool act8 = false);
 size_t lmhead_epilogue_bytes(int V, int M);
 hipError_t launch_gemv_bf16(const uint16_t* w, int V, int H, const uint16_t* x, int M,
                             float* logits, hipStream_t s);

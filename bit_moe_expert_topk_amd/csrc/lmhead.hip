@@ -566,9 +566,10 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
 // Waves per SIMD the FP8 GEMV asks the register allocator for: with an
 // epilogue at up to 3 chunks per lane the kernel fits the 168 registers of
 // three waves (without the hint the M = 4 variant takes one more and drops
-// to two); M = 3 would spill there and keeps the default.
-template <int M_T, int T, bool KEYS>
-constexpr int kFp8WavesPerSimd = (KEYS && T <= 3 && M_T != 3) ? 3 : 1;
+// to two); M = 3, and the dynamic-activation variants (their quantised x
+// takes more registers), would spill there and keep the default.
+template <int M_T, int T, bool KEYS, bool ACT8>
+constexpr int kFp8WavesPerSimd = (KEYS && T <= 3 && M_T != 3 && !ACT8) ? 3 : 1;
 
 // FP8 GEMV.  T = 16-byte chunks per lane per row (ceil(H / 16 / 64)), R rows
 // per wave step.  Each lane keeps its slice of x (every token) in registers
@@ -577,8 +578,14 @@ constexpr int kFp8WavesPerSimd = (KEYS && T <= 3 && M_T != 3) ? 3 : 1;
 // KEYS (the greedy or sampling epilogue; 32 rows per wave): the row sums go
 // to LDS, the block then writes the logits (if any), derives the keys of its
 // rows and wave groups (publishing them when sampling) and runs gemv_tail.
-template <int M_T, int T, int R, bool KEYS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFp8WavesPerSimd<M_T, T, KEYS>)))
+// ACT8 (dynamic FP8 activations): each block quantises every token row with
+// the weights' rule (t = absmax / 448 over the whole row, a wave maximum;
+// codes = E4M3 nearest-even of x / t), one wave per token, into LDS; the
+// waves keep the E4M3 values as exact bf16 pairs in place of x and multiply
+// each finished sum by t.  Every block forms the same codes, so no block
+// depends on another.
+template <int M_T, int T, int R, bool KEYS, bool ACT8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFp8WavesPerSimd<M_T, T, KEYS, ACT8>)))
 void gemv_fp8_kernel(const uint8_t* __restrict__ codes,
                                                        const float* __restrict__ rs, int V, int H,
                                                        const uint32_t* __restrict__ x,
@@ -603,6 +610,47 @@ void gemv_fp8_kernel(const uint8_t* __restrict__ codes,
                 xr[m][t][j] = (ch < n_ch) ? xv : 0u;     // chunks past H multiply by zero
             }
         }
+    float tok_scale[M_T];
+    if constexpr (ACT8) {
+        // wave m quantises token m (its slice of every token is already in
+        // registers) into LDS; after one barrier every wave reads all tokens'
+        // codes back as exact bf16 pairs
+        __shared__ uint32_t s_xq[M_T][64 * T * 8];
+        __shared__ float s_ts[M_T];
+        const int wv = threadIdx.x >> 6;
+#pragma unroll
+        for (int m = 0; m < M_T; ++m) {
+            if ((m & 3) != wv) continue;                        // wave-uniform
+            uint32_t am = 0;
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) am = max(am, max(xr[m][t][j] & 0x7FFFu, (xr[m][t][j] >> 16) & 0x7FFFu));
+            const float a = bf16_to_f32(wave_max_u32(am));
+            const float ts = (a == 0.f) ? 1.0f : a / 448.0f;
+            const float ty = 1.0f / ts;
+            const bool fast = ts >= 0x1p-90f && ts <= 0x1.fffffep127f;   // wave-uniform, as in quant_fp8_kernel
+            if (lane == 0) s_ts[m] = ts;
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const uint32_t q = fast ? quant4<true>(xr[m][t][j], xr[m][t][j + 1], ts, ty)
+                                            : quant4<false>(xr[m][t][j], xr[m][t][j + 1], ts, ty);
+                    s_xq[m][(lane + 64 * t) * 8 + j] = __builtin_bit_cast(uint32_t, MOEDEC_FP8X2_BF16(q, false));
+                    s_xq[m][(lane + 64 * t) * 8 + j + 1] = __builtin_bit_cast(uint32_t, MOEDEC_FP8X2_BF16(q, true));
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < M_T; ++m) {
+            tok_scale[m] = s_ts[m];
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) xr[m][t][j] = s_xq[m][(lane + 64 * t) * 8 + j];
+        }
+    }
     const int v0 = gw * rows_per_wave;
     const int v1 = min(V, v0 + rows_per_wave);
     __shared__ float s_rows[KEYS ? M_T : 1][kBlockRows];
@@ -634,6 +682,12 @@ void gemv_fp8_kernel(const uint8_t* __restrict__ codes,
                     for (int m = 0; m < M_T; ++m)
                         acc[r][m] = dot2_bf16(wp, as_bf16x2(xr[m][t][j]), acc[r][m]);
                 }
+        if constexpr (ACT8) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M_T; ++m) acc[r][m] *= tok_scale[m];
+        }
         store_row_sums<R, M_T, KEYS>(acc, v, v1, V, logits, [&](int row) { return rs[row]; }, &s_rows[0][0],
                                      wrow + (v - v0));
     }
@@ -819,13 +873,13 @@ int fp8_waves(int V) {                              // waves launched (4 per blo
 // [M][V].
 constexpr size_t kGenBytes = kMaxBlocks * sizeof(uint32_t);
 
-template <int M_T, int T>
+template <int M_T, int T, bool ACT8>
 hipError_t gemv_fp8_t(const uint8_t* codes, const float* rs, int V, int H, const uint32_t* x,
                       float* logits, const Fp8Epilogue* ep, hipStream_t s) {
     const int n_waves = fp8_waves(V);
     const dim3 grid(n_waves / 4), blk(256);
     if (!ep) {
-        hipLaunchKernelGGL((gemv_fp8_kernel<M_T, T, kFp8Rows, false>), grid, blk, 0, s, codes, rs, V, H, x,
+        hipLaunchKernelGGL((gemv_fp8_kernel<M_T, T, kFp8Rows, false, ACT8>), grid, blk, 0, s, codes, rs, V, H, x,
                            logits, kFp8RowsPerWave, TailArgs{});
         return hipGetLastError();
     }
@@ -843,19 +897,30 @@ hipError_t gemv_fp8_t(const uint8_t* codes, const float* rs, int V, int H, const
     ta.top_p = ep->top_p;
     ta.top_k = ep->top_k;
     ta.n_row_waves = (V + kFp8RowsPerWave - 1) / kFp8RowsPerWave;
-    hipLaunchKernelGGL((gemv_fp8_kernel<M_T, T, kFp8Rows, true>), grid, blk, 0, s, codes, rs, V, H, x, logits,
-                       kFp8RowsPerWave, ta);
+    hipLaunchKernelGGL((gemv_fp8_kernel<M_T, T, kFp8Rows, true, ACT8>), grid, blk, 0, s, codes, rs, V, H, x,
+                       logits, kFp8RowsPerWave, ta);
     return hipGetLastError();
 }
 
-template <int M_T>
+template <int M_T, bool ACT8>
 hipError_t gemv_fp8_m(const uint8_t* codes, const float* rs, int V, int H, const uint32_t* x,
                       float* logits, const Fp8Epilogue* ep, hipStream_t s) {
     switch ((H / 16 + 63) / 64) {
-        case 1: return gemv_fp8_t<M_T, 1>(codes, rs, V, H, x, logits, ep, s);
-        case 2: return gemv_fp8_t<M_T, 2>(codes, rs, V, H, x, logits, ep, s);
-        case 3: return gemv_fp8_t<M_T, 3>(codes, rs, V, H, x, logits, ep, s);
-        default: return gemv_fp8_t<M_T, 4>(codes, rs, V, H, x, logits, ep, s);
+        case 1: return gemv_fp8_t<M_T, 1, ACT8>(codes, rs, V, H, x, logits, ep, s);
+        case 2: return gemv_fp8_t<M_T, 2, ACT8>(codes, rs, V, H, x, logits, ep, s);
+        case 3: return gemv_fp8_t<M_T, 3, ACT8>(codes, rs, V, H, x, logits, ep, s);
+        default: return gemv_fp8_t<M_T, 4, ACT8>(codes, rs, V, H, x, logits, ep, s);
+    }
+}
+
+template <bool ACT8>
+hipError_t gemv_fp8_any(const uint8_t* codes, const float* rs, int V, int H, const uint32_t* x, int M,
+                        float* logits, const Fp8Epilogue* ep, hipStream_t s) {
+    switch (M) {
+        case 1: return gemv_fp8_m<1, ACT8>(codes, rs, V, H, x, logits, ep, s);
+        case 2: return gemv_fp8_m<2, ACT8>(codes, rs, V, H, x, logits, ep, s);
+        case 3: return gemv_fp8_m<3, ACT8>(codes, rs, V, H, x, logits, ep, s);
+        default: return gemv_fp8_m<4, ACT8>(codes, rs, V, H, x, logits, ep, s);
     }
 }
 
@@ -935,14 +1000,10 @@ hipError_t launch_lmhead_quant(const uint16_t* w, int V, int H, uint8_t* codes, 
 
 hipError_t launch_gemv_fp8(const uint8_t* codes, const float* rs, int V, int H,
                            const uint16_t* x, int M, float* logits, hipStream_t s,
-                           const Fp8Epilogue* ep) {
+                           const Fp8Epilogue* ep, bool act8) {
     const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
-    switch (M) {
-        case 1: return gemv_fp8_m<1>(codes, rs, V, H, x32, logits, ep, s);
-        case 2: return gemv_fp8_m<2>(codes, rs, V, H, x32, logits, ep, s);
-        case 3: return gemv_fp8_m<3>(codes, rs, V, H, x32, logits, ep, s);
-        default: return gemv_fp8_m<4>(codes, rs, V, H, x32, logits, ep, s);
-    }
+    return act8 ? gemv_fp8_any<true>(codes, rs, V, H, x32, M, logits, ep, s)
+                : gemv_fp8_any<false>(codes, rs, V, H, x32, M, logits, ep, s);
 }
 
 size_t lmhead_epilogue_bytes(int V, int M) {

@@ -411,10 +411,19 @@ int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16,
  * ---------------------------------------------------------------------- */
 #define MOEDEC_LMHEAD_MAGIC 0x4C4D4838u         /* "LMH8" */
 #define MOEDEC_FMT_E4M3FN_ROWSCALE_F32 1u       /* OCP E4M3, one float32 scale per row */
+/* The same weights with dynamic FP8 activations [card #2: the head gets a
+ * dynamic FP8 configuration]: every GEMV call quantises each token row of x
+ * with the weights' rule, t_m = max_k |x[m][k]| / 448 (float32 division, 1
+ * for a zero row), p = E4M3 nearest-even, saturating, of x / t_m, and
+ * computes logits[m][v] = s_v * t_m * sum_k e4m3(p[m][k]) * e4m3(codes[v][k])
+ * in float32.  Set desc.format to it after lmhead_quant_fp8; the GEMV, greedy
+ * and sampling calls all take it.  Reads the same bytes as the weight-only
+ * head (x is a few KiB). */
+#define MOEDEC_FMT_E4M3FN_ROWSCALE_F32_DYNACT 2u
 
 typedef struct {
     uint32_t magic;                    /* MOEDEC_LMHEAD_MAGIC */
-    uint32_t format;                   /* MOEDEC_FMT_E4M3FN_ROWSCALE_F32 */
+    uint32_t format;                   /* MOEDEC_FMT_E4M3FN_ROWSCALE_F32 or ..._DYNACT */
     int32_t  V, H;
     const uint8_t* codes;              /* [V][H] E4M3 codes, row-major, 16-byte aligned */
     const float* row_scale;            /* [V] */
@@ -433,8 +442,9 @@ int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H,
 
 /*
  * logits[m][v] = s_v * sum_k x[m][k] * e4m3(codes[v][k]), float32 accumulation.
- * head (host) must carry the LM-head magic and the E4M3 format tag, else
- * MOEDEC_ERR_FORMAT.  x_bf16 [M][H] 4-byte aligned; logits [M][V] float32.
+ * head (host) must carry the LM-head magic and an E4M3 format tag, else
+ * MOEDEC_ERR_FORMAT; with MOEDEC_FMT_E4M3FN_ROWSCALE_F32_DYNACT the
+ * activations are quantised per token first (see there).  x_bf16 [M][H] 4-byte aligned; logits [M][V] float32.
  * 1 <= M <= 4, H % 16 == 0, H <= 4096.
  */
 int lmhead_gemv_fp8(const moedec_lmhead_fp8* head, const uint16_t* x_bf16, int M,

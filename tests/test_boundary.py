@@ -308,7 +308,9 @@ def test_lmhead_descriptor_guards_format(m):
     L = m.lib
     good = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32, 157184, 2560, 1 << 20, 1 << 20)
     wrong_magic = m.LMHeadFP8Desc(0, m.FMT_E4M3FN_ROWSCALE_F32, 157184, 2560, 1 << 20, 1 << 20)
-    wrong_fmt = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, 2, 157184, 2560, 1 << 20, 1 << 20)
+    wrong_fmt = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, 3, 157184, 2560, 1 << 20, 1 << 20)
+    dyn = m.LMHeadFP8Desc(m.LMHEAD_MAGIC, m.FMT_E4M3FN_ROWSCALE_F32_DYNACT, 157184, 2560, 1 << 20, 1 << 20)
+    assert L.lmhead_gemv_fp8(ctypes.byref(dyn), FAKE, 5, FAKE, None) == -3      # format accepted, M checked
     assert L.lmhead_gemv_fp8(ctypes.byref(wrong_magic), FAKE, 1, FAKE, None) == -4
     assert L.lmhead_gemv_fp8(ctypes.byref(wrong_fmt), FAKE, 1, FAKE, None) == -4
     assert L.lmhead_gemv_fp8(None, FAKE, 1, FAKE, None) == -1

@@ -429,3 +429,65 @@ def test_sample_graph_replays_and_shared_workspace(m):
         np.testing.assert_array_equal(ids.cpu().numpy(), ref.cpu().numpy())
         greedy = m.lmhead_argmax_fp8(head, x, workspace=ws).cpu().numpy()
         np.testing.assert_array_equal(greedy, m.lmhead_argmax_fp8(head, x).cpu().numpy())
+
+
+# ---------------------------------------------------------------- dynamic FP8 activations
+
+def _dynact_ref(head, x_bits):
+    return oracle.lmhead_gemv_fp8_dynact(head.codes.cpu().numpy(), head.row_scale.cpu().numpy(),
+                                         synth.bf16_values(x_bits))
+
+
+@pytest.mark.parametrize("V,H", [(300, 2560), (77, 256), (129, 4096), (5, 16)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_dynact_gemv_small(m, V, H, M):
+    """Per-token FP8 activations (the weights' rule per token row) against
+    the oracle: an all-zero token (scale 1), a token of tiny values (scale far
+    below 2^-90: the division path), a token whose absmax is negative."""
+    wb = _weights(V, H, seed=V + 21)
+    head = m.lmhead_dynamic_act(_check_quant(m, wb))
+    assert head.desc.format == m.FMT_E4M3FN_ROWSCALE_F32_DYNACT
+    xb = synth.lmhead_x_bf16(M + 40, M, H)
+    if M >= 2:
+        xb[1] = 0
+    if M >= 3:
+        rng = np.random.default_rng(V)
+        xb[2] = synth.bf16_bits_from_f32((rng.standard_normal(H) * 2.0 ** -110).astype(np.float32))
+    if M >= 4:
+        xb[3, 7] = synth.bf16_bits_from_f32(np.float32([-50.0]))[0]
+    got = _check_gemv(m, head, xb, None, f"dynact gemv V={V} H={H} M={M}")
+    check_acc(got, _dynact_ref(head, xb), f"dynact gemv V={V} H={H} M={M}")
+    if M >= 2:
+        assert (got[1] == 0).all()
+
+
+def test_dynact_full_size(m, full_head, full_oracle):
+    """157,184 x 2,560 with dynamic activations at M = 1 and 4 (every logit),
+    the greedy token and a sampled token from the same head."""
+    say("full dynact head")
+    head = m.lmhead_dynamic_act(m.lmhead_quant_fp8(bf16_tensor(full_head)))
+    torch.cuda.synchronize()
+    for key in ("gemv_m1", "gemv_m4"):
+        xb = full_oracle["x_bits"][key]
+        M = xb.shape[0]
+        ref = oracle.lmhead_gemv_fp8_dynact(full_oracle["codes"], full_oracle["scale"], synth.bf16_values(xb))
+        got = _check_gemv(m, head, xb, None, f"full dynact gemv M={M}")
+        check_acc(got, ref, f"full dynact M={M}")
+        _check_argmax(m, head, xb, f"full dynact argmax M={M}", ref_logits=ref)
+    xb = full_oracle["x_bits"]["gemv_m4"]
+    loose = _check_sample(m, head, xb, synth.sampling_uniforms(synth.LMHEAD_V, 7, 4), 0.6, 0.95, 29,
+                          "full dynact sample")
+    assert loose <= 1
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_dynact_argmax_and_sample_small(m, M):
+    V, H = 4097, 64
+    head = m.lmhead_dynamic_act(_check_quant(m, _weights(V, H, seed=91)))
+    xb = synth.lmhead_x_bf16(92, M, H)
+    _check_argmax(m, head, xb, f"dynact argmax M={M}", ref_logits=_dynact_ref(head, xb))
+    loose = 0
+    for i, (T, p, k) in enumerate(SETTINGS):
+        loose += _check_sample(m, head, synth.lmhead_x_bf16(93 + i, M, H), synth.sampling_uniforms(V, 50 + i, M),
+                               T, p, min(k, V), f"dynact sample M={M} T={T} p={p} k={k}")
+    assert loose <= 1
