@@ -44,6 +44,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0      # dense fp8 (and fp4 x fp8) matrix peak
 PREFILL_TOKENS = (512, 2048, 8192, 32768)
 TRAFFIC_FILE = "moe_ffn_kernel_ling_m{M}_hbm_traffic.md"
 COPY_PROBE_ELEMS = 1 << 28                 # float32: 1 GiB read and 1 GiB written
@@ -279,9 +280,11 @@ def prefill_bench(m, torch, synth, layers, dev, tokens=PREFILL_TOKENS):
     """The many-token layer on layer 0's experts: T tokens of N(0,1) bf16
     activations with N(0,1) router logits, routed top-8 of 512 plus the shared
     expert.  Algorithmic flops per (token, expert) pair: 2 * (2 I H) for
-    gate/up and 2 H I for down, over the T * (k + 1) pairs (the kernels
+    gate/up and 2 H I for down, over the T * (k + 1) pairs (the bf16 kernels
     carry h as two bf16 halves, so the down product runs twice on the
-    matrix cores; that is not counted)."""
+    matrix cores; that is not counted).  Each T is timed for both variants:
+    bf16 activations (moe_layer_mxfp4_prefill) and MXFP8 activations
+    (moe_layer_mxfp4_prefill_a8, keys suffixed _a8)."""
     shape = synth.LING
     E, H, I, k = shape.E, shape.H, shape.I, shape.k
     W = layers[0]
@@ -294,24 +297,27 @@ def prefill_bench(m, torch, synth, layers, dev, tokens=PREFILL_TOKENS):
         y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         counts = torch.empty(E + 1, dtype=torch.int32, device=dev)
 
-        def call():
-            m.moe_layer_prefill(W, x, lg, k, workspace=ws, y=y, want_f32=False, counts=counts)
-
-        call()
-        call()
         reps = max(5, min(50, 80000 // T))
-        ms = t.run(lambda: [call() for _ in range(reps)])
-        us = 1e3 * ms / reps
         flops = T * (k + 1) * 6 * H * I
-        active = int((counts[:E] > 0).sum().item()) + 1
-        out[str(T)] = {
-            "us_per_layer": us,
-            "tflops": flops / us / 1e6,
-            "frac_of_bf16_peak": flops / us / 1e6 / PEAK_BF16_TFLOPS,
-            "active_experts": active,
-            "weight_gbs": active * EXPERT_BYTES_LING / us / 1e3,
-            "reps": reps,
-        }
+        r = {"reps": reps}
+        for sfx, act8 in (("", False), ("_a8", True)):
+            def call():
+                m.moe_layer_prefill(W, x, lg, k, workspace=ws, y=y, want_f32=False, counts=counts, act8=act8)
+
+            call()
+            call()
+            ms = t.run(lambda: [call() for _ in range(reps)])
+            us = 1e3 * ms / reps
+            active = int((counts[:E] > 0).sum().item()) + 1
+            r.update({
+                "us_per_layer" + sfx: us,
+                "tflops" + sfx: flops / us / 1e6,
+                "weight_gbs" + sfx: active * EXPERT_BYTES_LING / us / 1e3,
+            })
+        r["frac_of_bf16_peak"] = r["tflops"] / PEAK_BF16_TFLOPS
+        r["frac_of_fp8_peak_a8"] = r["tflops_a8"] / PEAK_FP8_TFLOPS
+        r["active_experts"] = active
+        out[str(T)] = r
         del ws, x, lg, y
         torch.cuda.empty_cache()
     return out
@@ -924,6 +930,8 @@ def main(argv=None):
         for T, r in pf.items():
             line[f"prefill_us_t{T}"] = round(r["us_per_layer"], 1)
             line[f"prefill_tflops_t{T}"] = round(r["tflops"], 1)
+            line[f"prefill_a8_us_t{T}"] = round(r["us_per_layer_a8"], 1)
+            line[f"prefill_a8_tflops_t{T}"] = round(r["tflops_a8"], 1)
     if lm is not None:
         line["lmhead_fp8_gbs_m1"] = round(lm["fp8_m1_gbs"], 1)
         line["lmhead_fp8_argmax_us_m1"] = round(lm["fp8_argmax_m1_us"], 2)

@@ -276,12 +276,21 @@ def make_prefill_workspace(T, E, k, H, I, device):
     return torch.empty(prefill_workspace_bytes(T, E, k, H, I), dtype=torch.uint8, device=device)
 
 
+def prefill_workspace_layout(T, E, k, H, I):
+    """Byte offsets of the many-token intermediates in the workspace
+    (moe_prefill_workspace_layout), as a dict."""
+    out = _lib.PrefillLayout()
+    _check(lib.moe_prefill_workspace_layout(T, E, k, H, I, ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in _lib.PrefillLayout._fields_}
+
+
 def moe_layer_prefill(weights, x, logits, k, workspace=None, y=None, y_f32=None, want_f32=True,
-                      ids=None, topk_w=None, counts=None):
+                      ids=None, topk_w=None, counts=None, act8=False):
     """The layer for many tokens (moe_layer_mxfp4_prefill): x [T][H] bfloat16,
     logits [T][E] float32.  Returns (y bf16, y_f32 or None); ids [T][k],
     topk_w [T][k] and counts [E + 1] (int32, tokens per expert, then T) are
-    filled when given."""
+    filled when given.  act8 = True runs the W4A8 variant
+    (moe_layer_mxfp4_prefill_a8: MXFP8 activations into both products)."""
     _need(x, torch.bfloat16, "x", 2)
     _need(logits, torch.float32, "logits", 2)
     t_tokens, hidden = x.shape
@@ -298,9 +307,9 @@ def moe_layer_prefill(weights, x, logits, k, workspace=None, y=None, y_f32=None,
         y = torch.empty((t_tokens, hidden), dtype=torch.bfloat16, device=x.device)
     if y_f32 is None and want_f32:
         y_f32 = torch.empty((t_tokens, hidden), dtype=torch.float32, device=x.device)
-    _check(lib.moe_layer_mxfp4_prefill(ctypes.byref(weights.desc), _ptr(x), _ptr(logits), t_tokens, k,
-                                       _ptr(ids), _ptr(topk_w), _ptr(counts), _ptr(y), _ptr(y_f32),
-                                       _ptr(workspace), workspace.numel(), _stream(x)))
+    fn = lib.moe_layer_mxfp4_prefill_a8 if act8 else lib.moe_layer_mxfp4_prefill
+    _check(fn(ctypes.byref(weights.desc), _ptr(x), _ptr(logits), t_tokens, k, _ptr(ids), _ptr(topk_w),
+              _ptr(counts), _ptr(y), _ptr(y_f32), _ptr(workspace), workspace.numel(), _stream(x)))
     return y, y_f32
 
 

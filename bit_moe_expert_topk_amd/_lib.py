@@ -70,6 +70,14 @@ class MoEWeights(ctypes.Structure):
     ]
 
 
+class PrefillLayout(ctypes.Structure):
+    """moedec_prefill_layout: byte offsets of the many-token intermediates."""
+    _fields_ = [("total_bytes", ctypes.c_uint64), ("pos", ctypes.c_uint64), ("y_pair", ctypes.c_uint64),
+                ("x_codes", ctypes.c_uint64), ("x_scales", ctypes.c_uint64), ("h_codes", ctypes.c_uint64),
+                ("h_scales", ctypes.c_uint64), ("x_scale_stride", ctypes.c_int32),
+                ("h_scale_stride", ctypes.c_int32)]
+
+
 class LMHeadFP8Desc(ctypes.Structure):
     _fields_ = [
         ("magic", c_uint32), ("format", c_uint32), ("V", c_int32), ("H", c_int32),
@@ -112,6 +120,10 @@ SIGNATURES = {
     "moe_prefill_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_layer_mxfp4_prefill": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_layer_mxfp4_prefill_a8": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                           c_void_p]),
+    "moe_prefill_workspace_layout": (c_int, [c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(PrefillLayout)]),
     "moe_ffn_workspace_status": (c_int, [c_void_p, c_size_t, ctypes.POINTER(c_uint32), c_void_p]),
     "moe_layer_mxfp4_noalloc": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

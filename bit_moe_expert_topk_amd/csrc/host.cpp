@@ -363,9 +363,27 @@ size_t moe_prefill_workspace_bytes(int T, int E, int k, int H, int I) {
     return moedec::prefill_layout(T, E, k, H, I).total;
 }
 
-int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int T,
-                            int k, int32_t* topk_ids, float* topk_w, int32_t* group_counts, uint16_t* y_bf16,
-                            float* y_f32, void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+int moe_prefill_workspace_layout(int T, int E, int k, int H, int I, moedec_prefill_layout* out) {
+    if (!out) return fail(MOEDEC_ERR_NULL, "out is NULL");
+    if (!moe_prefill_workspace_bytes(T, E, k, H, I))
+        return fail(MOEDEC_ERR_SHAPE, "T=%d E=%d k=%d H=%d I=%d out of range", T, E, k, H, I);
+    const moedec::PrefillLayout l = moedec::prefill_layout(T, E, k, H, I);
+    out->total_bytes = l.total;
+    out->pos = l.pos_off;
+    out->y_pair = l.y_pair_off;
+    out->x_codes = l.x8_off;
+    out->x_scales = l.xs_off;
+    out->h_codes = l.h8_off;
+    out->h_scales = l.hs_off;
+    out->x_scale_stride = l.sb;
+    out->h_scale_stride = l.sbi;
+    return MOEDEC_OK;
+}
+
+static int prefill_call(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int T, int k,
+                        int32_t* topk_ids, float* topk_w, int32_t* group_counts, uint16_t* y_bf16, float* y_f32,
+                        void* workspace, size_t workspace_bytes, moedec_stream_t stream, bool a8,
+                        const char* name) {
     if (!w) return fail(MOEDEC_ERR_NULL, "weights descriptor is NULL");
     if (w->magic == MOEDEC_MOE_MAGIC_SHARED_FP8)
         return fail(MOEDEC_ERR_FORMAT, "the many-token layer takes an MXFP4 shared expert");
@@ -387,8 +405,22 @@ int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16,
         return fail(MOEDEC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
     if (int st = check_device()) return st;
     return launched(moedec::launch_prefill(*w, x_bf16, logits, T, k, topk_ids, topk_w, group_counts, y_bf16,
-                                           y_f32, workspace, static_cast<hipStream_t>(stream)),
-                    "moe_layer_mxfp4_prefill");
+                                           y_f32, workspace, static_cast<hipStream_t>(stream), a8),
+                    name);
+}
+
+int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int T,
+                            int k, int32_t* topk_ids, float* topk_w, int32_t* group_counts, uint16_t* y_bf16,
+                            float* y_f32, void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+    return prefill_call(w, x_bf16, logits, T, k, topk_ids, topk_w, group_counts, y_bf16, y_f32, workspace,
+                        workspace_bytes, stream, false, "moe_layer_mxfp4_prefill");
+}
+
+int moe_layer_mxfp4_prefill_a8(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int T,
+                               int k, int32_t* topk_ids, float* topk_w, int32_t* group_counts, uint16_t* y_bf16,
+                               float* y_f32, void* workspace, size_t workspace_bytes, moedec_stream_t stream) {
+    return prefill_call(w, x_bf16, logits, T, k, topk_ids, topk_w, group_counts, y_bf16, y_f32, workspace,
+                        workspace_bytes, stream, true, "moe_layer_mxfp4_prefill_a8");
 }
 
 int lmhead_quant_fp8(const uint16_t* w_bf16, int V, int H, uint8_t* codes, float* row_scale,

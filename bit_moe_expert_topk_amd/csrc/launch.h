@@ -103,11 +103,15 @@ struct PrefillLayout {
     int max_tiles;      // tiles at most: (T*k + T) / (32*ns) + E + 1
     size_t counts_off, cursor_off, off_off, n_tiles_off, tiles_off, ids_off, w_off, pos_off, tok_of_off,
         h_hi_off, h_lo_off, y_pair_off, total;
+    // MXFP8-activation variant: scale bytes per token row of x (sb) and of h
+    // (sbi), x's codes and scales, h's codes and scales (inside h_hi / h_lo)
+    int sb, sbi;
+    size_t x8_off, xs_off, h8_off, hs_off;
 };
 int prefill_sub_tiles(int T, int E, int k);
 PrefillLayout prefill_layout(int T, int E, int k, int H, int I);
 hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const float* logits, int T, int k,
                           int32_t* ids_out, float* w_out, int32_t* counts_out, uint16_t* y_bf16, float* y_f32,
-                          void* ws, hipStream_t s);
+                          void* ws, hipStream_t s, bool a8);
 
 }  // namespace moedec

@@ -591,6 +591,427 @@ __global__ __launch_bounds__(64 * W) void down_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// W4A8: MXFP8 activations (E4M3 elements, one E8M0 scale per 32 values along
+// the reduction axis) into v_mfma_scale_f32_32x32x64_f8f6f4, A = the MXFP4
+// weights as stored (E2M1 codes and their E8M0 bytes, no conversion), B = the
+// activations.  Operand lanes (checked with an in-bounds probe): A lane l =
+// row l % 32 with the 32 codes of MX block l / 32 of the 64-k step (the packed
+// layout's 16-byte lane chunk) and that block's scale; B lane l = column
+// l % 32 with k 16 (l/32) .. +15 and 32 + 16 (l/32) .. +15, and the scale of
+// block l / 32.  D as for the bf16 MFMA.
+//
+// x is quantised by quant_x8 ([T][H] codes, [T][SB] scale bytes, SB = 4 *
+// ceil(H/128), padding blocks 127); h by the gate/up epilogue ([P][I] codes,
+// [P][SBI] scale bytes): the 32 rows of a wave's MFMA tile are one MX block of
+// h for each token, split over lanes l and l ^ 32.  Per slab the ring carries
+// the activation codes (64 B per token row, one 1 KB load per wave: a block
+// of W waves holds 16 W tokens) and each wave's weights; the activation scales
+// of the whole reduction are loaded into LDS once per block.
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// E8M0 byte of a block whose largest magnitude is amax: 2^(floor(log2 amax) - 8),
+// the exponent clamped at -127 (byte 0, also for an all-zero block).
+__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+    return (uint32_t)max((int)((__float_as_uint(amax) >> 23) & 0xFFu) - 8, 0);
+}
+// 2^(127 - byte): the exact reciprocal of the block scale (byte <= 246).
+__device__ __forceinline__ float mx8_inv(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
+// E4M3 code of v / X (an exact product), nearest-even, saturating, sign kept.
+__device__ __forceinline__ uint32_t mx8_code(float v, float inv) {
+    const float q = v * inv;
+    return e4m3_mag_code<true>(fabsf(q)) | ((__float_as_uint(q) >> 24) & 0x80u);
+}
+
+__device__ __forceinline__ f32x16 mfma_a4b8(const u32x4& a, const i32x8& b, uint32_t sa, uint32_t sb, f32x16 c) {
+    const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, b, c, 4, 0, 0, (int)sa, 0, (int)sb);
+}
+
+// One thread per 32-value block of one token.
+__global__ __launch_bounds__(kThreads) void quant_x8_kernel(const uint16_t* __restrict__ x, int T, int H, int sb,
+                                                           uint8_t* __restrict__ x8, uint8_t* __restrict__ xs) {
+    const int nb = H / 32;
+    for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < (size_t)T * sb;
+         i += (size_t)gridDim.x * kThreads) {
+        const int t = (int)(i / sb), b = (int)(i - (size_t)t * sb);
+        if (b >= nb) {
+            xs[i] = 127;
+            continue;
+        }
+        const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)t * H + b * 32);
+        u32x4 d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[q] = src[q];
+        uint32_t am = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) am = max(am, max(d[q][e] & 0x7FFFu, (d[q][e] >> 16) & 0x7FFFu));
+        const uint32_t sbyte = mx8_scale_byte(bf16_to_f32(am));
+        const float inv = mx8_inv(sbyte);
+        u32x4 o[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                const uint32_t w0 = d[q][e], w1 = d[q][e + 1];
+                const uint32_t c = mx8_code(bf16_to_f32(w0 & 0xFFFFu), inv) |
+                                   (mx8_code(bf16_to_f32(w0 >> 16), inv) << 8) |
+                                   (mx8_code(bf16_to_f32(w1 & 0xFFFFu), inv) << 16) |
+                                   (mx8_code(bf16_to_f32(w1 >> 16), inv) << 24);
+                o[q >> 1][(q & 1) * 2 + (e >> 1)] = c;
+            }
+        u32x4* dst = reinterpret_cast<u32x4*>(x8 + (size_t)t * H + b * 32);
+        dst[0] = o[0];
+        dst[1] = o[1];
+        xs[i] = (uint8_t)sbyte;
+    }
+}
+
+// Activation rows in a ring slot: 64 B per row, 16-byte unit u at u ^ ((row >> 2) & 3).
+__device__ __forceinline__ int a8_slot(int row, int unit) { return row * 64 + ((unit ^ ((row >> 2) & 3)) << 4); }
+
+// The B operand of row `row`: units h and 2 + h.
+__device__ __forceinline__ i32x8 a8_b(const uint8_t* base, int row, int half) {
+    const u32x4 p = *reinterpret_cast<const u32x4*>(base + a8_slot(row, half));
+    const u32x4 q = *reinterpret_cast<const u32x4*>(base + a8_slot(row, 2 + half));
+    return i32x8{(int)p[0], (int)p[1], (int)p[2], (int)p[3], (int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+}
+
+// Ring slot of the W4A8 products: the activation codes (64 B per token row:
+// 16-byte unit u at u ^ ((row >> 2) & 3)), the rows' scale dwords of the
+// slab's 128-k chunk (row r at 4 r; kScW waves load them, 64 rows each),
+// then each wave's weights.  A wave's fill is 1 code load, 1 scale load if
+// it is one of the first kScW waves, and its weight loads.
+template <int TR>
+struct A8Ring {
+    static constexpr int kCodes = TR * 64;
+    static constexpr int kScales = TR * 4 < 256 ? 256 : TR * 4;
+    static constexpr int kScW = kScales / 256;
+};
+
+// s_waitcnt for `per` loads per fill and S - 2 fills in flight (per <= 6).
+template <int S>
+__device__ __forceinline__ void wait_fills(int per) {
+    switch (per) {
+        case 1: wait_vm<(S - 2) * 1>(); break;
+        case 2: wait_vm<(S - 2) * 2>(); break;
+        case 3: wait_vm<(S - 2) * 3>(); break;
+        case 4: wait_vm<(S - 2) * 4>(); break;
+        case 5: wait_vm<(S - 2) * 5>(); break;
+        default: wait_vm<(S - 2) * 6>(); break;
+    }
+}
+
+// gate/up, W4A8: block = (32*NS tokens, 32*W intermediate rows), W = 2*NS
+// waves (each fills one 1 KB piece of every activation slab).
+template <int NS, int NSUB, int S>
+__device__ __forceinline__ void ga8_step(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd,
+                                         const uint8_t* xsrc, int xk, const uint8_t* ssrc, const uint8_t* codes,
+                                         const uint8_t* scales, int sc_shift, int n_slabs, int H, int wv, int lane,
+                                         bool has_rows, int j, f32x16 (&acc_g)[NS], f32x16 (&acc_u)[NS]) {
+    using R = A8Ring<NS * kSub>;
+    constexpr int kW = R::kCodes + R::kScales;
+    {
+        const int sl = min(j + S - 1, n_slabs - 1);
+        const int k = sl * kSlab + xk;
+        lds_load16(xsrc + (k < H ? k : 0), wr + wv * 1024);
+        if (wv < R::kScW) lds_load4(ssrc + 4 * (sl >> 1), wr + R::kCodes + wv * 256);
+        if (has_rows) {
+            uint8_t* wb = wr + kW + wv * kGuWaveBytes;
+            const uint8_t* p = codes + (size_t)(sl >> 1) * 2048 + (sl & 1) * 512;
+            lds_load16(p, wb);
+            lds_load16(p + 1024, wb + 1024);
+            lds_load4(scales + (size_t)(sl >> 1) * 128 + (sl & 1) * 64, wb + 2048);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_rows && j >= 0) {
+        const int r = lane & 31, half = lane >> 5;
+        const uint8_t* wb = rd + kW + wv * kGuWaveBytes;
+        const u32x4 cg = *reinterpret_cast<const u32x4*>(wb + lane * 16);
+        const u32x4 cu = *reinterpret_cast<const u32x4*>(wb + 1024 + lane * 16);
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(wb + 2048 + lane * 4) >> sc_shift;
+        const int sbyte = 2 * (j & 1) + half;
+        i32x8 b[NSUB];
+        uint32_t bs[NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            b[s] = a8_b(rd, s * kSub + r, half);
+            bs[s] = rd[R::kCodes + 4 * (s * kSub + r) + sbyte];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            acc_g[s] = mfma_a4b8(cg, b[s], sc & 0xFF, bs[s], acc_g[s]);
+            acc_u[s] = mfma_a4b8(cu, b[s], (sc >> 8) & 0xFF, bs[s], acc_u[s]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NS>
+constexpr int ga8_slot_bytes() {
+    return A8Ring<NS * kSub>::kCodes + A8Ring<NS * kSub>::kScales + 2 * NS * kGuWaveBytes;
+}
+
+template <int NS, int NSUB, int S>
+__device__ __forceinline__ void ga8_main(uint8_t (&ring)[S][(ga8_slot_bytes<NS>())], const uint8_t* xsrc, int xk,
+                                         const uint8_t* ssrc, const uint8_t* codes, const uint8_t* scales,
+                                         int sc_shift, int n_slabs, int H, int wv, int lane, bool has_rows,
+                                         f32x16 (&acc_g)[NS], f32x16 (&acc_u)[NS]) {
+    const int per = 1 + (wv < A8Ring<NS * kSub>::kScW) + (has_rows ? 3 : 0);
+    int ws = 0, rs = 1;
+    for (int j = 1 - S; j < n_slabs; ++j) {
+        if (j >= 0) {
+            wait_fills<S>(per);
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        ga8_step<NS, NSUB, S>(&ring[ws][0], &ring[rs][0], xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv,
+                              lane, has_rows, j, acc_g, acc_u);
+        ws = next_slot<S>(ws);
+        rs = next_slot<S>(rs);
+    }
+    wait_vm<0>();
+}
+
+template <int NS, int S>
+__global__ __launch_bounds__(64 * 2 * NS) void gateup_a8_kernel(
+    const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales, size_t e_codes,
+    size_t e_scales, const uint8_t* __restrict__ sh_codes, const uint8_t* __restrict__ sh_scales,
+    const uint8_t* __restrict__ x8, const uint8_t* __restrict__ xs, int H, int I, int E, int sb,
+    const int32_t* __restrict__ n_tiles, const int2* __restrict__ tiles, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ tok_of, uint8_t* __restrict__ h8,
+    uint8_t* __restrict__ hs, int sbi) {
+    constexpr int W = 2 * NS, TT = NS * kSub, kRows = 32 * W;
+    __shared__ __align__(1024) uint8_t ring[S][(ga8_slot_bytes<NS>())];
+
+    Item it;
+    if (!block_item(n_tiles, tiles, counts, (I + kRows - 1) / kRows, TT, it)) return;
+    const int lane = lane_id(), wv = wave_id_uniform();
+    const int n_sub = (it.rows + kSub - 1) / kSub;
+    const int pair0 = off[it.group] + it.start;
+    const int r = lane & 31, half = lane >> 5;
+    const int kb4 = (H / 32 + 3) / 4, n_slabs = 2 * kb4;
+
+    // code fill: wave wv covers rows 16 wv .. 16 wv + 15, lane l row 16 wv + l / 4
+    const int frow = 16 * wv + (lane >> 2);
+    const uint8_t* xsrc = x8 + (size_t)tok_of[pair0 + min(frow, it.rows - 1)] * H;
+    const int xk = ((lane & 3) ^ ((frow >> 2) & 3)) * 16;
+    // scale fill (first waves): lane l row 64 wv + l
+    const uint8_t* ssrc = xs + (size_t)tok_of[pair0 + min(64 * wv + lane, it.rows - 1)] * sb;
+
+    const int n0 = it.rb * kRows + 32 * wv;
+    const bool has_rows = n0 < I;
+    const uint8_t* cb = it.group < E ? gu_codes + (size_t)it.group * e_codes : sh_codes;
+    const uint8_t* sbp = it.group < E ? gu_scales + (size_t)it.group * e_scales : sh_scales;
+    const size_t unit = (size_t)((has_rows ? n0 : 0) / 16 + (r >> 4));
+    const int li0 = (r & 15) + 16 * half;
+    const uint8_t* codes = cb + unit * kb4 * 2048 + li0 * 16;
+    const uint8_t* scales = sbp + unit * kb4 * 128 + ((2 * li0) & ~3);
+    const int sc_shift = 16 * (li0 & 1);
+
+    f32x16 acc_g[NS], acc_u[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        acc_g[s] = f32x16{};
+        acc_u[s] = f32x16{};
+    }
+    if (NS == 4 && n_sub == 4)
+        ga8_main<NS, (NS >= 4 ? 4 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
+                                           has_rows, acc_g, acc_u);
+    else if (NS >= 3 && n_sub == 3)
+        ga8_main<NS, (NS >= 3 ? 3 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
+                                           has_rows, acc_g, acc_u);
+    else if (NS >= 2 && n_sub == 2)
+        ga8_main<NS, (NS >= 2 ? 2 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
+                                           has_rows, acc_g, acc_u);
+    else
+        ga8_main<NS, 1, S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane, has_rows, acc_g,
+                           acc_u);
+
+    if (!has_rows) return;
+    // h = silu(g) * u, then its MXFP8: rows n0 .. n0 + 31 of one token are one
+    // block, held by lanes r and r + 32
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (s >= n_sub) continue;                               // block-uniform
+        float hv[16];
+        uint32_t am = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float g = acc_g[s][e], u = acc_u[s][e];
+            hv[e] = g / (1.f + expf(-g)) * u;
+            am = max(am, __float_as_uint(hv[e]) & 0x7FFFFFFFu);
+        }
+        const u32x2 pr = swap32(am);
+        const uint32_t sbyte = mx8_scale_byte(__uint_as_float(max(pr[0], pr[1])));
+        const float inv = mx8_inv(sbyte);
+        const int row = s * kSub + r;
+        if (row >= it.rows) continue;
+        const size_t pp = (size_t)(pair0 + row);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const uint32_t c = mx8_code(hv[4 * r4], inv) | (mx8_code(hv[4 * r4 + 1], inv) << 8) |
+                               (mx8_code(hv[4 * r4 + 2], inv) << 16) | (mx8_code(hv[4 * r4 + 3], inv) << 24);
+            *reinterpret_cast<uint32_t*>(h8 + pp * I + n0 + 8 * r4 + 4 * half) = c;
+        }
+        if (half == 0) hs[pp * sbi + n0 / 32] = (uint8_t)sbyte;
+    }
+}
+
+// down, W4A8: block = (32*ND tokens of a gate/up tile, 64*W output rows), W =
+// 2*ND waves; wave w owns rows 64 w .. 64 w + 63 as two 32-row tiles.  Scale
+// bytes of h past I/32 are never written and are read as 127 (1.0) instead:
+// their codes meet zero weights.
+template <int ND, int NSUB, int S>
+__device__ __forceinline__ void da8_step(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd,
+                                         const uint8_t* hsrc, int hk, const uint8_t* ssrc, const uint8_t* codes0,
+                                         const uint8_t* scales0, size_t t1c, size_t t1s, int sc_shift, int n_slabs,
+                                         int I, int wv, int lane, bool has_rows, int j, f32x16 (&acc)[2][ND]) {
+    using R = A8Ring<ND * kSub>;
+    constexpr int kW = R::kCodes + R::kScales;
+    {
+        const int sl = min(j + S - 1, n_slabs - 1);
+        const int k = sl * kSlab + hk;
+        lds_load16(hsrc + (k < I ? k : 0), wr + wv * 1024);
+        if (wv < R::kScW) lds_load4(ssrc + 4 * (sl >> 1), wr + R::kCodes + wv * 256);
+        if (has_rows) {
+            uint8_t* wb = wr + kW + wv * kDnWaveBytes;
+            const uint8_t* p = codes0 + (size_t)(sl >> 1) * 1024 + (sl & 1) * 512;
+            const uint8_t* sp = scales0 + (size_t)(sl >> 1) * 64 + (sl & 1) * 32;
+            lds_load16(p, wb);
+            lds_load16(p + t1c, wb + 1024);
+            lds_load4(sp, wb + 2048);
+            lds_load4(sp + t1s, wb + 2304);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_rows && j >= 0) {
+        const int r = lane & 31, half = lane >> 5;
+        const uint8_t* wb = rd + kW + wv * kDnWaveBytes;
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + lane * 16);
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + 1024 + lane * 16);
+        const uint32_t s0 = (*reinterpret_cast<const uint32_t*>(wb + 2048 + lane * 4) >> sc_shift) & 0xFF;
+        const uint32_t s1 = (*reinterpret_cast<const uint32_t*>(wb + 2304 + lane * 4) >> sc_shift) & 0xFF;
+        const int sbyte = 2 * (j & 1) + half;
+        const bool real = 2 * j + half < I / 32;
+        i32x8 b[NSUB];
+        uint32_t bs[NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            b[s] = a8_b(rd, s * kSub + r, half);
+            bs[s] = real ? (uint32_t)rd[R::kCodes + 4 * (s * kSub + r) + sbyte] : 127u;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            acc[0][s] = mfma_a4b8(c0, b[s], s0, bs[s], acc[0][s]);
+            acc[1][s] = mfma_a4b8(c1, b[s], s1, bs[s], acc[1][s]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int ND>
+constexpr int da8_slot_bytes() {
+    return A8Ring<ND * kSub>::kCodes + A8Ring<ND * kSub>::kScales + 2 * ND * kDnWaveBytes;
+}
+
+template <int ND, int NSUB, int S>
+__device__ __forceinline__ void da8_main(uint8_t (&ring)[S][(da8_slot_bytes<ND>())], const uint8_t* hsrc, int hk,
+                                         const uint8_t* ssrc, const uint8_t* codes0, const uint8_t* scales0,
+                                         size_t t1c, size_t t1s, int sc_shift, int n_slabs, int I, int wv, int lane,
+                                         bool has_rows, f32x16 (&acc)[2][ND]) {
+    const int per = 1 + (wv < A8Ring<ND * kSub>::kScW) + (has_rows ? 4 : 0);
+    int ws = 0, rs = 1;
+    for (int j = 1 - S; j < n_slabs; ++j) {
+        if (j >= 0) {
+            wait_fills<S>(per);
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        da8_step<ND, NSUB, S>(&ring[ws][0], &ring[rs][0], hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift,
+                              n_slabs, I, wv, lane, has_rows, j, acc);
+        ws = next_slot<S>(ws);
+        rs = next_slot<S>(rs);
+    }
+    wait_vm<0>();
+}
+
+template <int ND, int S>
+__global__ __launch_bounds__(64 * 2 * ND) void down_a8_kernel(
+    const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales, size_t e_codes,
+    size_t e_scales, const uint8_t* __restrict__ sh_codes, const uint8_t* __restrict__ sh_scales,
+    const uint8_t* __restrict__ h8, const uint8_t* __restrict__ hs, int H, int I, int E, int sbi,
+    int tile_tokens, const int32_t* __restrict__ n_tiles, const int2* __restrict__ tiles,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ off, float* __restrict__ y_pair) {
+    constexpr int W = 2 * ND, TD = ND * kSub, kRows = 64 * W;
+    __shared__ __align__(1024) uint8_t ring[S][(da8_slot_bytes<ND>())];
+
+    const int parts = tile_tokens / TD, n_rb = (H + kRows - 1) / kRows;
+    Item it;
+    if (!block_item(n_tiles, tiles, counts, parts * n_rb, tile_tokens, it)) return;
+    const int part = it.rb / n_rb;
+    it.rb -= part * n_rb;
+    it.rows = min(it.rows - part * TD, TD);
+    if (it.rows <= 0) return;
+    it.start += part * TD;
+
+    const int lane = lane_id(), wv = wave_id_uniform();
+    const int n_sub = (it.rows + kSub - 1) / kSub;
+    const int pair0 = off[it.group] + it.start;
+    const int r = lane & 31, half = lane >> 5;
+    const int kb4 = (I / 32 + 3) / 4, n_slabs = 2 * kb4;
+
+    const int frow = 16 * wv + (lane >> 2);
+    const uint8_t* hsrc = h8 + (size_t)(pair0 + min(frow, it.rows - 1)) * I;
+    const int hk = ((lane & 3) ^ ((frow >> 2) & 3)) * 16;
+    const uint8_t* ssrc = hs + (size_t)(pair0 + min(64 * wv + lane, it.rows - 1)) * sbi;
+
+    const int n0 = it.rb * kRows + 64 * wv;
+    const bool has_rows = n0 < H;
+    const uint8_t* cb = it.group < E ? dn_codes + (size_t)it.group * e_codes : sh_codes;
+    const uint8_t* sbp = it.group < E ? dn_scales + (size_t)it.group * e_scales : sh_scales;
+    const size_t unit = (size_t)((has_rows ? n0 : 0) / 16 + (r >> 4));
+    const int li0 = (r & 15) + 16 * half;
+    const uint8_t* codes0 = cb + unit * kb4 * 1024 + li0 * 16;
+    const uint8_t* scales0 = sbp + unit * kb4 * 64 + (li0 & ~3);
+    const size_t t1c = (size_t)2 * kb4 * 1024, t1s = (size_t)2 * kb4 * 64;
+    const int sc_shift = 8 * (li0 & 3);
+
+    f32x16 acc[2][ND];
+#pragma unroll
+    for (int s = 0; s < ND; ++s) {
+        acc[0][s] = f32x16{};
+        acc[1][s] = f32x16{};
+    }
+    if (ND == 2 && n_sub == 2)
+        da8_main<ND, (ND >= 2 ? 2 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
+                                           lane, has_rows, acc);
+    else
+        da8_main<ND, 1, S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv, lane,
+                           has_rows, acc);
+
+    if (!has_rows) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int s = 0; s < ND; ++s) {
+            const int row = s * kSub + r;
+            if (s >= n_sub || row >= it.rows) continue;
+            float* dst = y_pair + (size_t)(pair0 + row) * H + n0 + 32 * t + 4 * half;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<float4*>(dst + 8 * r4) =
+                    float4{acc[t][s][4 * r4], acc[t][s][4 * r4 + 1], acc[t][s][4 * r4 + 2], acc[t][s][4 * r4 + 3]};
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
 // combine: one thread per 4 consecutive outputs of one token.
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y_pair,
@@ -667,6 +1088,40 @@ hipError_t launch_gemms(const moedec_moe_weights& w, const uint16_t* x, const Pr
     return hipGetLastError();
 }
 
+template <int NS>
+hipError_t launch_gemms_a8(const moedec_moe_weights& w, const PrefillLayout& lay, uint8_t* base, hipStream_t s) {
+    moedec_mxfp4_sizes sz;
+    packed_sizes(w.H, w.I, &sz);
+    const int32_t* n_tiles = reinterpret_cast<const int32_t*>(base + lay.n_tiles_off);
+    const int2* tiles = reinterpret_cast<const int2*>(base + lay.tiles_off);
+    const int32_t* counts = reinterpret_cast<const int32_t*>(base + lay.counts_off);
+    const int32_t* off = reinterpret_cast<const int32_t*>(base + lay.off_off);
+    const int32_t* tok_of = reinterpret_cast<const int32_t*>(base + lay.tok_of_off);
+    uint8_t* h8 = base + lay.h8_off;
+    uint8_t* hs = base + lay.hs_off;
+
+    constexpr int WG = 2 * NS, SG = NS >= 2 ? 4 : 3;
+    const size_t gu_items = (size_t)lay.max_tiles * ((w.I + 32 * WG - 1) / (32 * WG));
+    hipLaunchKernelGGL((gateup_a8_kernel<NS, SG>), dim3((unsigned)(kXcds * ((gu_items + kXcds - 1) / kXcds))),
+                       dim3(64 * WG), 0, s, static_cast<const uint8_t*>(w.gu_codes),
+                       static_cast<const uint8_t*>(w.gu_scales), sz.gu_codes, sz.gu_scales,
+                       static_cast<const uint8_t*>(w.sh_gu_codes), static_cast<const uint8_t*>(w.sh_gu_scales),
+                       base + lay.x8_off, base + lay.xs_off, w.H, w.I, w.E, lay.sb, n_tiles, tiles, counts, off,
+                       tok_of, h8, hs, lay.sbi);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    constexpr int ND = NS >= 2 ? 2 : 1;
+    constexpr int WD = 2 * ND, SD = ND >= 2 ? 4 : 3;
+    const size_t dn_items = (size_t)lay.max_tiles * (NS / ND) * ((w.H + 64 * WD - 1) / (64 * WD));
+    hipLaunchKernelGGL((down_a8_kernel<ND, SD>), dim3((unsigned)(kXcds * ((dn_items + kXcds - 1) / kXcds))),
+                       dim3(64 * WD), 0, s, static_cast<const uint8_t*>(w.dn_codes),
+                       static_cast<const uint8_t*>(w.dn_scales), sz.dn_codes, sz.dn_scales,
+                       static_cast<const uint8_t*>(w.sh_dn_codes), static_cast<const uint8_t*>(w.sh_dn_scales), h8,
+                       hs, w.H, w.I, w.E, lay.sbi, NS * kSub, n_tiles, tiles, counts, off,
+                       reinterpret_cast<float*>(base + lay.y_pair_off));
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int prefill_sub_tiles(int T, int E, int k) {
@@ -693,13 +1148,20 @@ PrefillLayout prefill_layout(int T, int E, int k, int H, int I) {
     l.h_hi_off = o;     o = align256(o + P * I * 2);
     l.h_lo_off = o;     o = align256(o + P * I * 2);
     l.y_pair_off = o;   o = align256(o + P * H * 4);
+    // MXFP8 path: x's codes and scales, and h's in the space of h_hi / h_lo
+    l.sb = 4 * ((H / 32 + 3) / 4);
+    l.sbi = 4 * ((I / 32 + 3) / 4);
+    l.x8_off = o;       o = align256(o + (size_t)T * H);
+    l.xs_off = o;       o = align256(o + (size_t)T * l.sb);
+    l.h8_off = l.h_hi_off;
+    l.hs_off = align256(l.h8_off + P * I);
     l.total = o;
     return l;
 }
 
 hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const float* logits, int T, int k,
                           int32_t* ids_out, float* w_out, int32_t* counts_out, uint16_t* y_bf16, float* y_f32,
-                          void* ws, hipStream_t s) {
+                          void* ws, hipStream_t s, bool a8) {
     const PrefillLayout lay = prefill_layout(T, w.E, k, w.H, w.I);
     uint8_t* base = static_cast<uint8_t*>(ws);
     int32_t* counts = reinterpret_cast<int32_t*>(base + lay.counts_off);
@@ -727,10 +1189,21 @@ hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const 
                        off, cursor, reinterpret_cast<int32_t*>(base + lay.tok_of_off), pos, w.E);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
-    switch (lay.ns) {
-        case 4: err = launch_gemms<4>(w, x, lay, base, s); break;
-        case 2: err = launch_gemms<2>(w, x, lay, base, s); break;
-        default: err = launch_gemms<1>(w, x, lay, base, s); break;
+    if (a8) {
+        hipLaunchKernelGGL(quant_x8_kernel, dim3(grid_cap((size_t)T * lay.sb, 8192)), dim3(kThreads), 0, s, x, T,
+                           w.H, lay.sb, base + lay.x8_off, base + lay.xs_off);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        switch (lay.ns) {
+            case 4: err = launch_gemms_a8<4>(w, lay, base, s); break;
+            case 2: err = launch_gemms_a8<2>(w, lay, base, s); break;
+            default: err = launch_gemms_a8<1>(w, lay, base, s); break;
+        }
+    } else {
+        switch (lay.ns) {
+            case 4: err = launch_gemms<4>(w, x, lay, base, s); break;
+            case 2: err = launch_gemms<2>(w, x, lay, base, s); break;
+            default: err = launch_gemms<1>(w, x, lay, base, s); break;
+        }
     }
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(combine_kernel, dim3(grid_cap((size_t)T * (w.H / 4), 8192)), dim3(kThreads), 0, s,

@@ -402,6 +402,48 @@ int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16,
                             int k, int32_t* topk_ids, float* topk_w, int32_t* group_counts, uint16_t* y_bf16,
                             float* y_f32, void* workspace, size_t workspace_bytes, moedec_stream_t stream);
 
+/* The same layer with 8-bit activations (W4A8).  [news "boundary": the
+ * measured baseline serves the model in its W4A8 configuration; MX
+ * Specification v1.0 §5.2 and §6.3: MXFP8 = E4M3 elements sharing one E8M0
+ * scale per 32 values]
+ *
+ * Both products take MXFP8 activations along their reduction axis and the
+ * MXFP4 weights as stored, on the block-scaled fp4 x fp8 matrix instruction
+ * (products of the scaled values are exact; they accumulate in float32):
+ *     x_q = MXFP8(x) per token over H, h = silu(W_gate x_q) * (W_up x_q),
+ *     h_q = MXFP8(h) per (token, expert) over I, y_pair = W_down h_q,
+ * then the combine of moe_layer_mxfp4_prefill.  A block's scale is
+ * 2^(floor(log2 max|v|) - 8), 2^-127 for an all-zero block; each element is
+ * v / scale rounded to the nearest E4M3 value, ties to even, saturating at
+ * +-448.  Seven launches: the six above plus the quantisation of x.
+ * Arguments, alignment, errors and workspace (moe_prefill_workspace_bytes,
+ * the same size) as for moe_layer_mxfp4_prefill.
+ */
+int moe_layer_mxfp4_prefill_a8(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int T,
+                               int k, int32_t* topk_ids, float* topk_w, int32_t* group_counts, uint16_t* y_bf16,
+                               float* y_f32, void* workspace, size_t workspace_bytes, moedec_stream_t stream);
+
+/* Where the many-token calls leave their intermediates in the workspace, as
+ * byte offsets from its start; for inspecting a call after it has finished
+ * (the stream synchronised).  P = T*(k+1) (token, expert) pairs.
+ *   pos       int32 [T][k]: pair row of token t's choice j; the shared
+ *             expert's row of token t is T*k + t
+ *   y_pair    float32 [P][H]: each pair's down output
+ *   x_codes   uint8 [T][H], x_scales uint8 [T][x_scale_stride]: MXFP8 x
+ *             (W4A8 call only; scale bytes past H/32 are padding)
+ *   h_codes   uint8 [P][I], h_scales uint8 [P][h_scale_stride]: MXFP8 h
+ *             (W4A8 call only; scale bytes past I/32 are not written)
+ * Same argument ranges as moe_prefill_workspace_bytes; returns MOEDEC_OK or
+ * MOEDEC_ERR_NULL / MOEDEC_ERR_SHAPE with *out untouched.
+ */
+typedef struct moedec_prefill_layout {
+    uint64_t total_bytes;
+    uint64_t pos, y_pair, x_codes, x_scales, h_codes, h_scales;
+    int32_t x_scale_stride, h_scale_stride;
+} moedec_prefill_layout;
+
+int moe_prefill_workspace_layout(int T, int E, int k, int H, int I, moedec_prefill_layout* out);
+
 /* ------------------------------------------------------------------------
  * LM head with online FP8 weights.  [news where the speed comes from; card
  * #2: the 157,184 x 2,560 vocabulary projection is read whole for every

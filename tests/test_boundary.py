@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                  "moedec_last_error", "moedec_abi_version", "moe_ffn_workspace_status",
                  "moe_layer_mxfp4_noalloc", "moe_layer_rmsnorm_router_mxfp4",
                  "moe_pack_shared_fp8", "moedec_shared_fp8_packed_sizes",
-                 "moe_layer_mxfp4_prefill", "moe_prefill_workspace_bytes"):
+                 "moe_layer_mxfp4_prefill", "moe_prefill_workspace_bytes", "moe_layer_mxfp4_prefill_a8",
+                 "moe_prefill_workspace_layout"):
         assert want in names
 
 
@@ -349,13 +350,20 @@ def test_prefill_workspace_and_argument_checks(m):
         n = L.moe_prefill_workspace_bytes(T, E, k, H, I)
         pairs = T * (k + 1)
         body = pairs * (4 * H + 4 * I)                    # y_pair float32 + h as two bf16
-        assert body <= n <= body + pairs * 4 + 3 * T * k * 4 + (3 * (E + 2) * 4) + ((pairs // 32 + E + 1) * 8) + 4096
+        x8 = T * H + T * (H // 32 + 4)                     # MXFP8 x of the W4A8 call
+        assert body <= n <= (body + pairs * 4 + 3 * T * k * 4 + (3 * (E + 2) * 4) + ((pairs // 32 + E + 1) * 8)
+                             + x8 + 4096)
     assert L.moe_prefill_workspace_bytes(0, 512, 8, 2560, 768) == 0
     assert L.moe_prefill_workspace_bytes(m._lib.MOEDEC_MAX_PREFILL_T + 1, 512, 8, 2560, 768) == 0
     assert L.moe_prefill_workspace_bytes(64, 512, 33, 2560, 768) == 0
     assert L.moe_prefill_workspace_bytes(64, 512, 8, 2560 + 32, 768) == 0
     ws = L.moe_prefill_workspace_bytes(64, 512, 8, 2560, 768)
-    call = lambda w, lg=FAKE, T=64, k=8, n=ws, work=FAKE, y32=None: L.moe_layer_mxfp4_prefill(
+    for fn in (L.moe_layer_mxfp4_prefill, L.moe_layer_mxfp4_prefill_a8):
+        _prefill_argument_checks(m, fn, ws)
+
+
+def _prefill_argument_checks(m, fn, ws):
+    call = lambda w, lg=FAKE, T=64, k=8, n=ws, work=FAKE, y32=None: fn(
         ctypes.byref(w), FAKE, lg, T, k, None, None, None, FAKE, y32, work, n, None)
     assert call(_weights(m), lg=None) == -1
     assert call(_weights(m, magic=1)) == -4
@@ -369,3 +377,26 @@ def test_prefill_workspace_and_argument_checks(m):
     assert call(_weights(m), work=ctypes.c_void_p((1 << 20) + 16)) == -2
     assert call(_weights(m), work=None) == -1
     assert call(_weights(m), n=ws - 1) == -5
+
+
+def test_prefill_workspace_layout(m):
+    """The layout query: regions inside the workspace, disjoint, aligned, with
+    the scale strides of 128-value chunks; errors for NULL and bad shapes."""
+    L = m.lib
+    out = m._lib.PrefillLayout()
+    assert L.moe_prefill_workspace_layout(64, 512, 8, 2560, 768, None) == -1
+    assert L.moe_prefill_workspace_layout(0, 512, 8, 2560, 768, ctypes.byref(out)) == -3
+    assert L.moe_prefill_workspace_layout(64, 512, 8, 2560 + 32, 768, ctypes.byref(out)) == -3
+    for T, E, k, H, I in ((8192, 512, 8, 2560, 768), (1, 16, 2, 256, 64), (129, 24, 3, 320, 96),
+                          (m._lib.MOEDEC_MAX_PREFILL_T, 1024, 32, 4096, 2048)):
+        lay = m.prefill_workspace_layout(T, E, k, H, I)
+        assert lay["total_bytes"] == L.moe_prefill_workspace_bytes(T, E, k, H, I)
+        sb, sbi = lay["x_scale_stride"], lay["h_scale_stride"]
+        assert sb == 4 * -(-H // 128) and sbi == 4 * -(-I // 128)
+        P = T * (k + 1)
+        regions = sorted([(lay["pos"], T * k * 4), (lay["y_pair"], P * H * 4), (lay["x_codes"], T * H),
+                          (lay["x_scales"], T * sb), (lay["h_codes"], P * I), (lay["h_scales"], P * sbi)])
+        for (a, n), (b, _) in zip(regions, regions[1:]):
+            assert a + n <= b
+        assert regions[-1][0] + regions[-1][1] <= lay["total_bytes"]
+        assert all(off % 256 == 0 for off, _ in regions)
