@@ -988,7 +988,13 @@ __global__ __launch_bounds__(64 * 2 * ND) void down_a8_kernel(
         acc[0][s] = f32x16{};
         acc[1][s] = f32x16{};
     }
-    if (ND == 2 && n_sub == 2)
+    if (ND == 4 && n_sub == 4)
+        da8_main<ND, (ND >= 4 ? 4 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
+                                           lane, has_rows, acc);
+    else if (ND >= 3 && n_sub == 3)
+        da8_main<ND, (ND >= 3 ? 3 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
+                                           lane, has_rows, acc);
+    else if (ND >= 2 && n_sub == 2)
         da8_main<ND, (ND >= 2 ? 2 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
                                            lane, has_rows, acc);
     else
@@ -1110,7 +1116,7 @@ hipError_t launch_gemms_a8(const moedec_moe_weights& w, const PrefillLayout& lay
                        tok_of, h8, hs, lay.sbi);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    constexpr int ND = NS >= 2 ? 2 : 1;
+    constexpr int ND = NS;
     constexpr int WD = 2 * ND, SD = ND >= 2 ? 4 : 3;
     const size_t dn_items = (size_t)lay.max_tiles * (NS / ND) * ((w.H + 64 * WD - 1) / (64 * WD));
     hipLaunchKernelGGL((down_a8_kernel<ND, SD>), dim3((unsigned)(kXcds * ((dn_items + kXcds - 1) / kXcds))),

@@ -372,8 +372,8 @@ int moe_layer_rmsnorm_router_mxfp4(const moedec_moe_weights* w, const uint16_t* 
  * Results do not depend on scheduling: every output is formed from its own
  * row and column only, in a fixed order.
  *
- * Six launches on `stream`: counts reset, routing, plan (one block), scatter,
- * gate/up, down, combine.
+ * Seven launches on `stream`: counts reset, routing, plan (one block),
+ * scatter, gate/up, down, combine.
  * w             MOEDEC_MOE_MAGIC weights (an FP8 shared expert is refused
  *               with MOEDEC_ERR_FORMAT); the four scale arrays 4-byte
  *               aligned (they are read as 32-bit words)
@@ -390,8 +390,9 @@ int moe_layer_rmsnorm_router_mxfp4(const moedec_moe_weights* w, const uint16_t* 
  *               aligned
  * workspace     moe_prefill_workspace_bytes(T, E, k, H, I) bytes, 256-byte
  *               aligned, owned by the caller; no initial contents needed.
- *               About T*(k+1)*(4H + 4I) bytes: the per-pair h and down
- *               outputs.  One call at a time per workspace.
+ *               About T*(k+1)*(4H + 4I) + T*H bytes: the per-pair h and down
+ *               outputs, and the W4A8 call's 8-bit x.  One call at a time per
+ *               workspace.
  * Returns MOEDEC_OK, or an error code with nothing enqueued.
  */
 #define MOEDEC_MAX_PREFILL_T 65536
@@ -415,7 +416,7 @@ int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16,
  * then the combine of moe_layer_mxfp4_prefill.  A block's scale is
  * 2^(floor(log2 max|v|) - 8), 2^-127 for an all-zero block; each element is
  * v / scale rounded to the nearest E4M3 value, ties to even, saturating at
- * +-448.  Seven launches: the six above plus the quantisation of x.
+ * +-448.  Eight launches: the seven above plus the quantisation of x.
  * Arguments, alignment, errors and workspace (moe_prefill_workspace_bytes,
  * the same size) as for moe_layer_mxfp4_prefill.
  */
