@@ -658,8 +658,9 @@ def copy_probe(torch, dev):
 
 def kernel_source_hash():
     """Hash of what defines the measured kernel's code: its source file, the
-    device headers it includes and the structure definitions of the ABI
-    header that it reads (declarations of other entry points do not count)."""
+    device headers it includes and the ABI header's structure definitions and
+    constants that those files name (other entry points' declarations and
+    structures do not count)."""
     import hashlib
     import re
     h = hashlib.sha256()
@@ -669,11 +670,13 @@ def kernel_source_hash():
         with open(os.path.join(csrc, name), "rb") as f:
             text = f.read()
         h.update(name.encode() + b"\0" + text)
-        used.update(re.findall(r"MOEDEC_\w+", text.decode()))
+        used.update(re.findall(r"MOEDEC_\w+|moedec_\w+", text.decode()))
     with open(os.path.join(ROOT, "include", "moedec.h")) as f:
         header = f.read()
     for block in re.findall(r"typedef struct[^}]*\}[^;]*;", header):
-        h.update(block.encode() + b"\0")
+        name = re.search(r"\}\s*(\w+)\s*;", block).group(1)
+        if name in used:
+            h.update(block.encode() + b"\0")
     for name, value in sorted(re.findall(r"#define (MOEDEC_\w+)\s+([^\n/]*)", header)):
         if name in used:
             h.update(f"{name}={value.strip()}".encode() + b"\0")

@@ -691,7 +691,7 @@ struct A8Ring {
     static constexpr int kScW = kScales / 256;
 };
 
-// s_waitcnt for `per` loads per fill and S - 2 fills in flight (per <= 6).
+// s_waitcnt for `per` loads per fill and S - 2 fills in flight (per <= 8).
 template <int S>
 __device__ __forceinline__ void wait_fills(int per) {
     switch (per) {
@@ -700,23 +700,30 @@ __device__ __forceinline__ void wait_fills(int per) {
         case 3: wait_vm<(S - 2) * 3>(); break;
         case 4: wait_vm<(S - 2) * 4>(); break;
         case 5: wait_vm<(S - 2) * 5>(); break;
-        default: wait_vm<(S - 2) * 6>(); break;
+        case 6: wait_vm<(S - 2) * 6>(); break;
+        case 7: wait_vm<(S - 2) * 7>(); break;
+        default: wait_vm<(S - 2) * 8>(); break;
     }
 }
 
-// gate/up, W4A8: block = (32*NS tokens, 32*W intermediate rows), W = 2*NS
-// waves (each fills one 1 KB piece of every activation slab).
-template <int NS, int NSUB, int S>
+// gate/up, W4A8: block = (32*NS tokens, 32*W intermediate rows), W waves;
+// an activation slab is 2*NS pieces of 1 KB (16 token rows each), wave wv
+// filling pieces wv, wv + W, ...
+template <int NS, int W, int NSUB, int S>
 __device__ __forceinline__ void ga8_step(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd,
-                                         const uint8_t* xsrc, int xk, const uint8_t* ssrc, const uint8_t* codes,
+                                         const uint8_t* const (&xsrc)[2 * NS / W], const int (&xk)[2 * NS / W],
+                                         const uint8_t* ssrc, const uint8_t* codes,
                                          const uint8_t* scales, int sc_shift, int n_slabs, int H, int wv, int lane,
                                          bool has_rows, int j, f32x16 (&acc_g)[NS], f32x16 (&acc_u)[NS]) {
     using R = A8Ring<NS * kSub>;
     constexpr int kW = R::kCodes + R::kScales;
     {
         const int sl = min(j + S - 1, n_slabs - 1);
-        const int k = sl * kSlab + xk;
-        lds_load16(xsrc + (k < H ? k : 0), wr + wv * 1024);
+#pragma unroll
+        for (int v = 0; v < 2 * NS / W; ++v) {
+            const int k = sl * kSlab + xk[v];
+            lds_load16(xsrc[v] + (k < H ? k : 0), wr + (W * v + wv) * 1024);
+        }
         if (wv < R::kScW) lds_load4(ssrc + 4 * (sl >> 1), wr + R::kCodes + wv * 256);
         if (has_rows) {
             uint8_t* wb = wr + kW + wv * kGuWaveBytes;
@@ -751,17 +758,18 @@ __device__ __forceinline__ void ga8_step(uint8_t* __restrict__ wr, const uint8_t
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NS>
+template <int NS, int W>
 constexpr int ga8_slot_bytes() {
-    return A8Ring<NS * kSub>::kCodes + A8Ring<NS * kSub>::kScales + 2 * NS * kGuWaveBytes;
+    return A8Ring<NS * kSub>::kCodes + A8Ring<NS * kSub>::kScales + W * kGuWaveBytes;
 }
 
-template <int NS, int NSUB, int S>
-__device__ __forceinline__ void ga8_main(uint8_t (&ring)[S][(ga8_slot_bytes<NS>())], const uint8_t* xsrc, int xk,
+template <int NS, int W, int NSUB, int S>
+__device__ __forceinline__ void ga8_main(uint8_t (&ring)[S][(ga8_slot_bytes<NS, W>())],
+                                         const uint8_t* const (&xsrc)[2 * NS / W], const int (&xk)[2 * NS / W],
                                          const uint8_t* ssrc, const uint8_t* codes, const uint8_t* scales,
                                          int sc_shift, int n_slabs, int H, int wv, int lane, bool has_rows,
                                          f32x16 (&acc_g)[NS], f32x16 (&acc_u)[NS]) {
-    const int per = 1 + (wv < A8Ring<NS * kSub>::kScW) + (has_rows ? 3 : 0);
+    const int per = 2 * NS / W + (wv < A8Ring<NS * kSub>::kScW) + (has_rows ? 3 : 0);
     int ws = 0, rs = 1;
     for (int j = 1 - S; j < n_slabs; ++j) {
         if (j >= 0) {
@@ -769,7 +777,7 @@ __device__ __forceinline__ void ga8_main(uint8_t (&ring)[S][(ga8_slot_bytes<NS>(
             __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        ga8_step<NS, NSUB, S>(&ring[ws][0], &ring[rs][0], xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv,
+        ga8_step<NS, W, NSUB, S>(&ring[ws][0], &ring[rs][0], xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv,
                               lane, has_rows, j, acc_g, acc_u);
         ws = next_slot<S>(ws);
         rs = next_slot<S>(rs);
@@ -777,16 +785,17 @@ __device__ __forceinline__ void ga8_main(uint8_t (&ring)[S][(ga8_slot_bytes<NS>(
     wait_vm<0>();
 }
 
-template <int NS, int S>
-__global__ __launch_bounds__(64 * 2 * NS) void gateup_a8_kernel(
+template <int NS, int W, int S>
+__global__ __launch_bounds__(64 * W) void gateup_a8_kernel(
     const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales, size_t e_codes,
     size_t e_scales, const uint8_t* __restrict__ sh_codes, const uint8_t* __restrict__ sh_scales,
     const uint8_t* __restrict__ x8, const uint8_t* __restrict__ xs, int H, int I, int E, int sb,
     const int32_t* __restrict__ n_tiles, const int2* __restrict__ tiles, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ off, const int32_t* __restrict__ tok_of, uint8_t* __restrict__ h8,
     uint8_t* __restrict__ hs, int sbi) {
-    constexpr int W = 2 * NS, TT = NS * kSub, kRows = 32 * W;
-    __shared__ __align__(1024) uint8_t ring[S][(ga8_slot_bytes<NS>())];
+    constexpr int TT = NS * kSub, kRows = 32 * W, XL = 2 * NS / W;
+    static_assert(XL >= 1 && XL * W == 2 * NS, "every wave fills whole 1 KB pieces of each slab");
+    __shared__ __align__(1024) uint8_t ring[S][(ga8_slot_bytes<NS, W>())];
 
     Item it;
     if (!block_item(n_tiles, tiles, counts, (I + kRows - 1) / kRows, TT, it)) return;
@@ -796,10 +805,15 @@ __global__ __launch_bounds__(64 * 2 * NS) void gateup_a8_kernel(
     const int r = lane & 31, half = lane >> 5;
     const int kb4 = (H / 32 + 3) / 4, n_slabs = 2 * kb4;
 
-    // code fill: wave wv covers rows 16 wv .. 16 wv + 15, lane l row 16 wv + l / 4
-    const int frow = 16 * wv + (lane >> 2);
-    const uint8_t* xsrc = x8 + (size_t)tok_of[pair0 + min(frow, it.rows - 1)] * H;
-    const int xk = ((lane & 3) ^ ((frow >> 2) & 3)) * 16;
+    // code fill: piece q = W v + wv covers rows 16 q .. 16 q + 15, lane l row 16 q + l / 4
+    const uint8_t* xsrc[XL];
+    int xk[XL];
+#pragma unroll
+    for (int v = 0; v < XL; ++v) {
+        const int frow = 16 * (W * v + wv) + (lane >> 2);
+        xsrc[v] = x8 + (size_t)tok_of[pair0 + min(frow, it.rows - 1)] * H;
+        xk[v] = ((lane & 3) ^ ((frow >> 2) & 3)) * 16;
+    }
     // scale fill (first waves): lane l row 64 wv + l
     const uint8_t* ssrc = xs + (size_t)tok_of[pair0 + min(64 * wv + lane, it.rows - 1)] * sb;
 
@@ -820,16 +834,16 @@ __global__ __launch_bounds__(64 * 2 * NS) void gateup_a8_kernel(
         acc_u[s] = f32x16{};
     }
     if (NS == 4 && n_sub == 4)
-        ga8_main<NS, (NS >= 4 ? 4 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
+        ga8_main<NS, W, (NS >= 4 ? 4 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
                                            has_rows, acc_g, acc_u);
     else if (NS >= 3 && n_sub == 3)
-        ga8_main<NS, (NS >= 3 ? 3 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
+        ga8_main<NS, W, (NS >= 3 ? 3 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
                                            has_rows, acc_g, acc_u);
     else if (NS >= 2 && n_sub == 2)
-        ga8_main<NS, (NS >= 2 ? 2 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
+        ga8_main<NS, W, (NS >= 2 ? 2 : 1), S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane,
                                            has_rows, acc_g, acc_u);
     else
-        ga8_main<NS, 1, S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane, has_rows, acc_g,
+        ga8_main<NS, W, 1, S>(ring, xsrc, xk, ssrc, codes, scales, sc_shift, n_slabs, H, wv, lane, has_rows, acc_g,
                            acc_u);
 
     if (!has_rows) return;
@@ -866,17 +880,21 @@ __global__ __launch_bounds__(64 * 2 * NS) void gateup_a8_kernel(
 // 2*ND waves; wave w owns rows 64 w .. 64 w + 63 as two 32-row tiles.  Scale
 // bytes of h past I/32 are never written and are read as 127 (1.0) instead:
 // their codes meet zero weights.
-template <int ND, int NSUB, int S>
+template <int ND, int W, int NSUB, int S>
 __device__ __forceinline__ void da8_step(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd,
-                                         const uint8_t* hsrc, int hk, const uint8_t* ssrc, const uint8_t* codes0,
+                                         const uint8_t* const (&hsrc)[2 * ND / W], const int (&hk)[2 * ND / W],
+                                         const uint8_t* ssrc, const uint8_t* codes0,
                                          const uint8_t* scales0, size_t t1c, size_t t1s, int sc_shift, int n_slabs,
                                          int I, int wv, int lane, bool has_rows, int j, f32x16 (&acc)[2][ND]) {
     using R = A8Ring<ND * kSub>;
     constexpr int kW = R::kCodes + R::kScales;
     {
         const int sl = min(j + S - 1, n_slabs - 1);
-        const int k = sl * kSlab + hk;
-        lds_load16(hsrc + (k < I ? k : 0), wr + wv * 1024);
+#pragma unroll
+        for (int v = 0; v < 2 * ND / W; ++v) {
+            const int k = sl * kSlab + hk[v];
+            lds_load16(hsrc[v] + (k < I ? k : 0), wr + (W * v + wv) * 1024);
+        }
         if (wv < R::kScW) lds_load4(ssrc + 4 * (sl >> 1), wr + R::kCodes + wv * 256);
         if (has_rows) {
             uint8_t* wb = wr + kW + wv * kDnWaveBytes;
@@ -915,17 +933,18 @@ __device__ __forceinline__ void da8_step(uint8_t* __restrict__ wr, const uint8_t
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int ND>
+template <int ND, int W>
 constexpr int da8_slot_bytes() {
-    return A8Ring<ND * kSub>::kCodes + A8Ring<ND * kSub>::kScales + 2 * ND * kDnWaveBytes;
+    return A8Ring<ND * kSub>::kCodes + A8Ring<ND * kSub>::kScales + W * kDnWaveBytes;
 }
 
-template <int ND, int NSUB, int S>
-__device__ __forceinline__ void da8_main(uint8_t (&ring)[S][(da8_slot_bytes<ND>())], const uint8_t* hsrc, int hk,
+template <int ND, int W, int NSUB, int S>
+__device__ __forceinline__ void da8_main(uint8_t (&ring)[S][(da8_slot_bytes<ND, W>())],
+                                         const uint8_t* const (&hsrc)[2 * ND / W], const int (&hk)[2 * ND / W],
                                          const uint8_t* ssrc, const uint8_t* codes0, const uint8_t* scales0,
                                          size_t t1c, size_t t1s, int sc_shift, int n_slabs, int I, int wv, int lane,
                                          bool has_rows, f32x16 (&acc)[2][ND]) {
-    const int per = 1 + (wv < A8Ring<ND * kSub>::kScW) + (has_rows ? 4 : 0);
+    const int per = 2 * ND / W + (wv < A8Ring<ND * kSub>::kScW) + (has_rows ? 4 : 0);
     int ws = 0, rs = 1;
     for (int j = 1 - S; j < n_slabs; ++j) {
         if (j >= 0) {
@@ -933,7 +952,7 @@ __device__ __forceinline__ void da8_main(uint8_t (&ring)[S][(da8_slot_bytes<ND>(
             __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        da8_step<ND, NSUB, S>(&ring[ws][0], &ring[rs][0], hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift,
+        da8_step<ND, W, NSUB, S>(&ring[ws][0], &ring[rs][0], hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift,
                               n_slabs, I, wv, lane, has_rows, j, acc);
         ws = next_slot<S>(ws);
         rs = next_slot<S>(rs);
@@ -941,15 +960,16 @@ __device__ __forceinline__ void da8_main(uint8_t (&ring)[S][(da8_slot_bytes<ND>(
     wait_vm<0>();
 }
 
-template <int ND, int S>
-__global__ __launch_bounds__(64 * 2 * ND) void down_a8_kernel(
+template <int ND, int W, int S>
+__global__ __launch_bounds__(64 * W) void down_a8_kernel(
     const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales, size_t e_codes,
     size_t e_scales, const uint8_t* __restrict__ sh_codes, const uint8_t* __restrict__ sh_scales,
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ hs, int H, int I, int E, int sbi,
     int tile_tokens, const int32_t* __restrict__ n_tiles, const int2* __restrict__ tiles,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ off, float* __restrict__ y_pair) {
-    constexpr int W = 2 * ND, TD = ND * kSub, kRows = 64 * W;
-    __shared__ __align__(1024) uint8_t ring[S][(da8_slot_bytes<ND>())];
+    constexpr int TD = ND * kSub, kRows = 64 * W, XL = 2 * ND / W;
+    static_assert(XL >= 1 && XL * W == 2 * ND, "every wave fills whole 1 KB pieces of each slab");
+    __shared__ __align__(1024) uint8_t ring[S][(da8_slot_bytes<ND, W>())];
 
     const int parts = tile_tokens / TD, n_rb = (H + kRows - 1) / kRows;
     Item it;
@@ -966,9 +986,14 @@ __global__ __launch_bounds__(64 * 2 * ND) void down_a8_kernel(
     const int r = lane & 31, half = lane >> 5;
     const int kb4 = (I / 32 + 3) / 4, n_slabs = 2 * kb4;
 
-    const int frow = 16 * wv + (lane >> 2);
-    const uint8_t* hsrc = h8 + (size_t)(pair0 + min(frow, it.rows - 1)) * I;
-    const int hk = ((lane & 3) ^ ((frow >> 2) & 3)) * 16;
+    const uint8_t* hsrc[XL];
+    int hk[XL];
+#pragma unroll
+    for (int v = 0; v < XL; ++v) {
+        const int frow = 16 * (W * v + wv) + (lane >> 2);
+        hsrc[v] = h8 + (size_t)(pair0 + min(frow, it.rows - 1)) * I;
+        hk[v] = ((lane & 3) ^ ((frow >> 2) & 3)) * 16;
+    }
     const uint8_t* ssrc = hs + (size_t)(pair0 + min(64 * wv + lane, it.rows - 1)) * sbi;
 
     const int n0 = it.rb * kRows + 64 * wv;
@@ -989,16 +1014,16 @@ __global__ __launch_bounds__(64 * 2 * ND) void down_a8_kernel(
         acc[1][s] = f32x16{};
     }
     if (ND == 4 && n_sub == 4)
-        da8_main<ND, (ND >= 4 ? 4 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
+        da8_main<ND, W, (ND >= 4 ? 4 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
                                            lane, has_rows, acc);
     else if (ND >= 3 && n_sub == 3)
-        da8_main<ND, (ND >= 3 ? 3 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
+        da8_main<ND, W, (ND >= 3 ? 3 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
                                            lane, has_rows, acc);
     else if (ND >= 2 && n_sub == 2)
-        da8_main<ND, (ND >= 2 ? 2 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
+        da8_main<ND, W, (ND >= 2 ? 2 : 1), S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv,
                                            lane, has_rows, acc);
     else
-        da8_main<ND, 1, S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv, lane,
+        da8_main<ND, W, 1, S>(ring, hsrc, hk, ssrc, codes0, scales0, t1c, t1s, sc_shift, n_slabs, I, wv, lane,
                            has_rows, acc);
 
     if (!has_rows) return;
@@ -1106,9 +1131,13 @@ hipError_t launch_gemms_a8(const moedec_moe_weights& w, const PrefillLayout& lay
     uint8_t* h8 = base + lay.h8_off;
     uint8_t* hs = base + lay.hs_off;
 
+    // One wave per 1 KB piece of the activation slab: 8-wave blocks for 128-token
+    // tiles (one block per CU).  Two 4-wave blocks per CU instead, whose waves
+    // would run out of step, measured 20 % slower: the tile's x is read by twice
+    // as many row blocks.
     constexpr int WG = 2 * NS, SG = NS >= 2 ? 4 : 3;
     const size_t gu_items = (size_t)lay.max_tiles * ((w.I + 32 * WG - 1) / (32 * WG));
-    hipLaunchKernelGGL((gateup_a8_kernel<NS, SG>), dim3((unsigned)(kXcds * ((gu_items + kXcds - 1) / kXcds))),
+    hipLaunchKernelGGL((gateup_a8_kernel<NS, WG, SG>), dim3((unsigned)(kXcds * ((gu_items + kXcds - 1) / kXcds))),
                        dim3(64 * WG), 0, s, static_cast<const uint8_t*>(w.gu_codes),
                        static_cast<const uint8_t*>(w.gu_scales), sz.gu_codes, sz.gu_scales,
                        static_cast<const uint8_t*>(w.sh_gu_codes), static_cast<const uint8_t*>(w.sh_gu_scales),
@@ -1119,7 +1148,7 @@ hipError_t launch_gemms_a8(const moedec_moe_weights& w, const PrefillLayout& lay
     constexpr int ND = NS;
     constexpr int WD = 2 * ND, SD = ND >= 2 ? 4 : 3;
     const size_t dn_items = (size_t)lay.max_tiles * (NS / ND) * ((w.H + 64 * WD - 1) / (64 * WD));
-    hipLaunchKernelGGL((down_a8_kernel<ND, SD>), dim3((unsigned)(kXcds * ((dn_items + kXcds - 1) / kXcds))),
+    hipLaunchKernelGGL((down_a8_kernel<ND, WD, SD>), dim3((unsigned)(kXcds * ((dn_items + kXcds - 1) / kXcds))),
                        dim3(64 * WD), 0, s, static_cast<const uint8_t*>(w.dn_codes),
                        static_cast<const uint8_t*>(w.dn_scales), sz.dn_codes, sz.dn_scales,
                        static_cast<const uint8_t*>(w.sh_dn_codes), static_cast<const uint8_t*>(w.sh_dn_scales), h8,
