@@ -102,6 +102,17 @@ def test_prefill_skewed_routing_and_idle_experts(m):
     _check(m, W, xb, lg, shape.k, fn, sh, "prefill skewed")
 
 
+def test_prefill_max_tokens(m):
+    """T = MOEDEC_MAX_PREFILL_T (65,536) on the tiny shape: 8,192 tokens per
+    expert on average; routing and counts on every token, outputs sampled."""
+    shape = synth.TINY
+    W, fn, sh = _small_layer(m, shape)
+    T = m._lib.MOEDEC_MAX_PREFILL_T
+    xb = synth.activations_bf16(9, 0, T, shape.H)
+    tokens = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(9).choice(T, 30, replace=False)]))
+    _check(m, W, xb, synth.logits_f32(9, 0, T, shape.E), shape.k, fn, sh, f"prefill tiny T={T}", tokens=tokens)
+
+
 def test_prefill_zero_input(m):
     shape = synth.TINY
     W, fn, sh = _small_layer(m, shape)
@@ -141,11 +152,11 @@ def _ling_expert(e):
                          synth.mxfp4_expert(0, 0, e, synth.LING).items()}, 0)
 
 
-@pytest.mark.parametrize("T,n_sample", [(64, 4), (256, 4), (4096, 3)])
+@pytest.mark.parametrize("T,n_sample", [(64, 4), (256, 4), (4096, 3), (32768, 3)])
 def test_prefill_ling(m, ling_layer, T, n_sample):
     """Ling-shaped layer (hidden 2560, 512 experts top-8 + shared, I 768):
     routing and counts on every token, outputs on the first, last and a few
-    seeded tokens."""
+    seeded tokens; T = 32,768 is the largest token count the bench times."""
     xb = synth.activations_bf16(7, 0, T, synth.LING.H)
     lg = synth.logits_f32(7, 0, T, synth.LING.E)
     rng = np.random.default_rng(T)

@@ -159,14 +159,17 @@ def _check(m, W, x_bits, logits, k, expert_fn, shared, what, tokens=None):
     groups = oracle.expert_groups(ref_ids, W.E)
     np.testing.assert_array_equal(counts, [len(g) for g in groups], err_msg=f"{what}: group counts")
 
-    # x: bit-exact MXFP8
-    x = synth.bf16_values(x_bits).astype(np.float64)
-    xc, xsb = w4a8.mxfp8_quantize(x)
-    np.testing.assert_array_equal(it["xs"], xsb, err_msg=f"{what}: x scale bytes")
-    np.testing.assert_array_equal(it["x8"], xc, err_msg=f"{what}: x codes")
-    x_q = w4a8.mxfp8_dequant(xc, xsb)
-
     sel = np.arange(T) if tokens is None else np.asarray(tokens)
+    # x: bit-exact MXFP8 on every token (on the sampled tokens and the first
+    # 2,048 beyond 20 M values, to bound the oracle's time)
+    rows_x = (np.arange(T) if T * W.H <= 20_000_000
+              else np.unique(np.concatenate([sel, np.arange(min(T, 2048))])))
+    x = synth.bf16_values(x_bits[rows_x]).astype(np.float64)
+    xc, xsb = w4a8.mxfp8_quantize(x)
+    np.testing.assert_array_equal(it["xs"][rows_x], xsb, err_msg=f"{what}: x scale bytes")
+    np.testing.assert_array_equal(it["x8"][rows_x], xc, err_msg=f"{what}: x codes")
+    x_q_rows = w4a8.mxfp8_dequant(xc, xsb)
+    row_of = {int(t): i for i, t in enumerate(rows_x)}
     # h of every pair of the selected tokens, then y from the kernel's own h
     flips = rescaled = n_el = n_blk = 0
     y_ref = np.zeros((len(sel), W.H))
@@ -180,7 +183,7 @@ def _check(m, W, x_bits, logits, k, expert_fn, shared, what, tokens=None):
         wg, wu, wd = expert_fn(e) if e < W.E else shared
         rows = np.array([p for _, _, _, p in items])
         toks = np.array([t for _, t, _, _ in items])
-        xq = x_q[toks]
+        xq = x_q_rows[[row_of[int(t)] for t in toks]]
         g, u = xq @ wg.T, xq @ wu.T
         with np.errstate(over="ignore"):
             silu = g / (1.0 + np.exp(-g))
@@ -272,6 +275,16 @@ def test_prefill_a8_wide_range(m):
     _check(m, W, xb, synth.logits_f32(8, 0, T, shape.E), shape.k, fn, sh, "a8 wide range")
 
 
+def test_prefill_a8_max_tokens(m):
+    """T = MOEDEC_MAX_PREFILL_T (65,536) on the tiny shape; h and y sampled."""
+    shape = synth.TINY
+    W, fn, sh = _small_layer(m, shape)
+    T = m._lib.MOEDEC_MAX_PREFILL_T
+    xb = synth.activations_bf16(9, 0, T, shape.H)
+    tokens = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(9).choice(T, 30, replace=False)]))
+    _check(m, W, xb, synth.logits_f32(9, 0, T, shape.E), shape.k, fn, sh, f"a8 tiny T={T}", tokens=tokens)
+
+
 def test_prefill_a8_repeatable(m):
     W, fn, sh = _small_layer(m, MID, seed=6)
     xb = synth.activations_bf16(6, 0, 700, MID.H)
@@ -298,11 +311,12 @@ def _ling_expert(e):
                          synth.mxfp4_expert(0, 0, e, synth.LING).items()}, 0)
 
 
-@pytest.mark.parametrize("T,n_sample", [(64, 3), (4096, 3)])
+@pytest.mark.parametrize("T,n_sample", [(64, 3), (4096, 3), (32768, 3)])
 def test_prefill_a8_ling(m, ling_layer, T, n_sample):
     """Ling-shaped layer (hidden 2560, 512 experts top-8 + shared, I 768):
     routing, counts and x's MXFP8 on every token; h and y on the first, last
-    and a few seeded tokens."""
+    and a few seeded tokens; T = 32,768 is the largest token count the bench
+    times."""
     xb = synth.activations_bf16(7, 0, T, synth.LING.H)
     lg = synth.logits_f32(7, 0, T, synth.LING.E)
     rng = np.random.default_rng(T)
