@@ -47,6 +47,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kSub = 32;             // tokens per MFMA column block
@@ -1043,37 +1044,57 @@ __global__ __launch_bounds__(64 * W) void down_a8_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// combine: one thread per 4 consecutive outputs of one token.
+// combine: one wave per 256 consecutive outputs of one token (4 per lane), so
+// the token's pair rows and weights are wave-uniform and every lane's k + 1
+// row reads are in flight together.  y[t] = sum_j w[t][j] * y_pair[pos(t, j)]
+// (fmaf, j ascending) + y_pair[shared row], then one RNE to bf16.
 
+template <int KMAX>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y_pair,
                                                            const int32_t* __restrict__ pos,
                                                            const float* __restrict__ wts, int T, int k, int H,
                                                            int shared_row0, uint16_t* __restrict__ y_bf16,
                                                            float* __restrict__ y_f32) {
-    const int q = H / 4;
-    for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < (size_t)T * q;
-         i += (size_t)gridDim.x * kThreads) {
-        const int t = (int)(i / q), n = (int)(i - (size_t)t * q) * 4;
-        float4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j) {
-            const float wj = wts[(size_t)t * k + j];
-            const float4 v = *reinterpret_cast<const float4*>(y_pair + (size_t)pos[(size_t)t * k + j] * H + n);
-            acc.x = fmaf(wj, v.x, acc.x);
-            acc.y = fmaf(wj, v.y, acc.y);
-            acc.z = fmaf(wj, v.z, acc.z);
-            acc.w = fmaf(wj, v.w, acc.w);
-        }
-        const float4 v = *reinterpret_cast<const float4*>(y_pair + (size_t)(shared_row0 + t) * H + n);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
-        const size_t o = (size_t)t * H + n;
-        if (y_f32) *reinterpret_cast<float4*>(y_f32 + o) = acc;
-        const uint32_t b0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-        const uint32_t b1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
-        *reinterpret_cast<u32x2*>(y_bf16 + o) = u32x2{b0, b1};
+    const int per_tok = (H + 255) / 256;
+    const int piece = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6));
+    if (piece >= T * per_tok) return;
+    const int t = piece / per_tok;
+    const int n = (piece - t * per_tok) * 256 + lane_id() * 4;
+    if (n >= H) return;
+    f32x4 v[KMAX], vs;
+    float w[KMAX];
+    // choices past k repeat the last one (loads without branches, all in
+    // flight at once); they are not added
+    int pj[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const size_t jj = (size_t)t * k + min(j, k - 1);
+        pj[j] = pos[jj];
+        w[j] = wts[jj];
     }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y_pair + (size_t)pj[j] * H + n));
+    vs = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y_pair + (size_t)(shared_row0 + t) * H + n));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+            acc[0] = fmaf(w[j], v[j][0], acc[0]);
+            acc[1] = fmaf(w[j], v[j][1], acc[1]);
+            acc[2] = fmaf(w[j], v[j][2], acc[2]);
+            acc[3] = fmaf(w[j], v[j][3], acc[3]);
+        }
+    }
+    acc[0] += vs[0];
+    acc[1] += vs[1];
+    acc[2] += vs[2];
+    acc[3] += vs[3];
+    const size_t o = (size_t)t * H + n;
+    if (y_f32) *reinterpret_cast<f32x4*>(y_f32 + o) = acc;
+    const uint32_t b0 = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+    const uint32_t b1 = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    *reinterpret_cast<u32x2*>(y_bf16 + o) = u32x2{b0, b1};
 }
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1241,7 +1262,10 @@ hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const 
         }
     }
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(combine_kernel, dim3(grid_cap((size_t)T * (w.H / 4), 8192)), dim3(kThreads), 0, s,
+    const size_t pieces = (size_t)T * ((w.H + 255) / 256);
+    const dim3 cgrid((unsigned)((pieces + kThreads / kWave - 1) / (kThreads / kWave)));
+    auto combine = k <= 8 ? combine_kernel<8> : (k <= 16 ? combine_kernel<16> : combine_kernel<MOEDEC_MAX_K>);
+    hipLaunchKernelGGL(combine, cgrid, dim3(kThreads), 0, s,
                        reinterpret_cast<const float*>(base + lay.y_pair_off), pos, wts, T, k, w.H, T * k, y_bf16,
                        y_f32);
     return hipGetLastError();
