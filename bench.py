@@ -150,9 +150,10 @@ def capture(torch, fn):
 # MoE layer measurements
 
 def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
-    """Time K layer steps three ways: the fused layer call (routing + FFN in
+    """Time K layer steps four ways: the fused layer call (routing + FFN in
     one launch; the headline), the two-call path (moe_route_topk then
-    moe_expert_ffn_mxfp4) and the FFN call alone on precomputed tables."""
+    moe_expert_ffn_mxfp4), the FFN call alone on precomputed tables, and the
+    fused layer with MXFP8 activations (moe_layer_mxfp4_a8, W4A8)."""
     n_layers = len(layers)
     shape = synth.LING
     k = shape.k
@@ -176,9 +177,14 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
         L = i % n_layers
         m.expert_ffn(layers[L], xs[L], disp[L], k, ws, y=ys[L], want_f32=False)
 
+    def fused_a8(i):
+        L = i % n_layers
+        m.moe_layer(layers[L], xs[L], lgs[L], k, ws, y=ys[L], want_f32=False, act8=True)
+
     # one eager pass of each path: fills every layer's dispatch table, checks the calls work
     for i in range(n_layers):
         two_call_step(i)
+        fused_a8(i)
         fused_step(i)
     torch.cuda.synchronize()
     n_slots = [m.decode_dispatch(d)["n_slots"] for d in disp]
@@ -192,16 +198,19 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
     g_main = capture(torch, lambda: [fused_step(i) for i in range(steps)])
     g_two = capture(torch, lambda: [two_call_step(i) for i in range(steps)])
     g_ffn = capture(torch, lambda: [ffn_only(i) for i in range(steps)])
+    g_a8 = capture(torch, lambda: [fused_a8(i) for i in range(steps)])
     if g_warm is not None:
         g_warm.replay()
     g_two.replay()
     g_ffn.replay()
+    g_a8.replay()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ms = t.run(g_main.replay)
     wall1 = time.perf_counter()
     ms_two = t.run(g_two.replay)
     ms_ffn = t.run(g_ffn.replay)
+    ms_a8 = t.run(g_a8.replay)
     m.check_ffn_workspace(ws)              # raises if a cross-block wait gave up
     ffn_bytes = step_bytes - M * shape.E * 4                   # no logits read
     res = {
@@ -218,13 +227,14 @@ def moe_bench(m, torch, synth, layers, M, steps, warmup, dev):
         "ffn_us": 1e3 * ms_ffn / steps,
         "ffn_bytes": ffn_bytes,
         "ffn_gbs": ffn_bytes / (1e6 * ms_ffn / steps),
+        "a8_us_per_layer": 1e3 * ms_a8 / steps,
         "mean_active_experts": sum(s - 1 for s in n_slots) / n_layers,
         "max_active_experts": max(s - 1 for s in n_slots),
     }
     res["frac_of_peak"] = res["gbs"] / PEAK_HBM_GBS
     res["two_call_frac_of_peak"] = res["two_call_gbs"] / PEAK_HBM_GBS
     res["ffn_frac_of_peak"] = res["ffn_gbs"] / PEAK_HBM_GBS
-    del g_warm, g_main, g_two, g_ffn
+    del g_warm, g_main, g_two, g_ffn, g_a8
     return res
 
 
@@ -918,7 +928,9 @@ def main(argv=None):
     if router is not None:
         line["router_us_m1"] = round(router["us_m1"], 3)
         line["router_plus_layer_us_m1"] = round(router["router_plus_layer_us_m1"], 3)
+    line["a8_us_per_layer_m1"] = round(r1["a8_us_per_layer"], 3)
     if r4 is not None:
+        line["a8_us_per_layer_m4"] = round(r4["a8_us_per_layer"], 3)
         line["us_per_layer_m4"] = round(r4["us_per_layer"], 3)
         line["gbs_m4"] = round(r4["gbs"], 1)
         line["frac_of_peak_m4"] = round(r4["frac_of_peak"], 4)

@@ -240,10 +240,11 @@ def expert_ffn(weights, x, dispatch, k_max, workspace, y=None, y_f32=None, want_
 
 
 def moe_layer(weights, x, logits, k, workspace, y=None, y_f32=None, want_f32=True,
-              ids=None, topk_w=None, dispatch=None):
+              ids=None, topk_w=None, dispatch=None, act8=False):
     """Routing and expert FFN in one launch.  x: [M][H] bfloat16, logits [M][E]
     float32.  Returns (y bf16, y_f32 or None); ids / topk_w / dispatch are
-    filled when given (device tensors as route_topk returns them)."""
+    filled when given (device tensors as route_topk returns them).  act8 =
+    True runs the W4A8 variant (moe_layer_mxfp4_a8: MXFP8 x and h)."""
     _need(x, torch.bfloat16, "x", 2)
     _need(logits, torch.float32, "logits", 2)
     _need(workspace, torch.uint8, "workspace", 1)
@@ -258,9 +259,9 @@ def moe_layer(weights, x, logits, k, workspace, y=None, y_f32=None, want_f32=Tru
         y = torch.empty((m_tokens, hidden), dtype=torch.bfloat16, device=x.device)
     if y_f32 is None and want_f32:
         y_f32 = torch.empty((m_tokens, hidden), dtype=torch.float32, device=x.device)
-    _check(lib.moe_layer_mxfp4(ctypes.byref(weights.desc), _ptr(x), _ptr(logits), m_tokens, k,
-                               _ptr(ids), _ptr(topk_w), _ptr(dispatch), _ptr(y), _ptr(y_f32),
-                               _ptr(workspace), workspace.numel(), _stream(x)))
+    fn = lib.moe_layer_mxfp4_a8 if act8 else lib.moe_layer_mxfp4
+    _check(fn(ctypes.byref(weights.desc), _ptr(x), _ptr(logits), m_tokens, k, _ptr(ids), _ptr(topk_w),
+              _ptr(dispatch), _ptr(y), _ptr(y_f32), _ptr(workspace), workspace.numel(), _stream(x)))
     return y, y_f32
 
 
@@ -274,6 +275,17 @@ def prefill_workspace_bytes(T, E, k, H, I):
 def make_prefill_workspace(T, E, k, H, I, device):
     """Workspace of moe_layer_prefill (no initial contents needed)."""
     return torch.empty(prefill_workspace_bytes(T, E, k, H, I), dtype=torch.uint8, device=device)
+
+
+def ffn_workspace_h(workspace, M, k, H, I):
+    """float32 h [M * k + 1][M][I] (slot-major, the call's dispatch order)
+    that the last FFN / fused-layer call left in `workspace`
+    (moe_ffn_workspace_layout); valid for each slot's own tokens."""
+    out = _lib.FfnLayout()
+    _check(lib.moe_ffn_workspace_layout(M, k, H, I, ctypes.byref(out)))
+    n = out.max_slots * M * I
+    words = workspace[out.h_words:out.h_words + 8 * n].view(torch.int32).reshape(n, 2)[:, 0]
+    return words.view(torch.float32).reshape(out.max_slots, M, I)
 
 
 def prefill_workspace_layout(T, E, k, H, I):

@@ -70,6 +70,12 @@ class MoEWeights(ctypes.Structure):
     ]
 
 
+class FfnLayout(ctypes.Structure):
+    """moedec_ffn_layout: where an FFN call leaves each (slot, token)'s h."""
+    _fields_ = [("total_bytes", ctypes.c_uint64), ("h_words", ctypes.c_uint64), ("max_slots", ctypes.c_int32),
+                ("M", ctypes.c_int32)]
+
+
 class PrefillLayout(ctypes.Structure):
     """moedec_prefill_layout: byte offsets of the many-token intermediates."""
     _fields_ = [("total_bytes", ctypes.c_uint64), ("pos", ctypes.c_uint64), ("y_pair", ctypes.c_uint64),
@@ -107,10 +113,13 @@ SIGNATURES = {
     "moe_pack_shared_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p]),
     "moe_ffn_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "moe_ffn_workspace_layout": (c_int, [c_int, c_int, c_int, c_int, ctypes.POINTER(FfnLayout)]),
     "moe_expert_ffn_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_int, c_void_p, c_int,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_layer_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_layer_mxfp4_a8": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_layer_rmsnorm_mxfp4": (c_int, [ctypes.POINTER(MoEWeights), c_void_p, c_void_p, c_int, c_int,
                                         ctypes.c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]),

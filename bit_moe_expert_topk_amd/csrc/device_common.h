@@ -214,6 +214,28 @@ __device__ __forceinline__ uint32_t e4m3_mag_code(float q) {
     return c;
 }
 
+// MXFP8 (E4M3 elements sharing one power-of-two scale per 32 values): a
+// block whose largest magnitude is amax (float32 bits, sign cleared) has
+// scale X = 2^(floor(log2 amax) - 8), clamped at 2^-127 (also for an
+// all-zero block); mx8_scale returns X and its exact reciprocal.
+__device__ __forceinline__ void mx8_scale(uint32_t amax_bits, float& X, float& inv) {
+    const uint32_t b = (uint32_t)max((int)((amax_bits >> 23) & 0xFFu) - 8, 0);
+    X = b ? __uint_as_float(b << 23) : 0x1p-127f;
+    inv = __uint_as_float((254u - b) << 23);
+}
+
+// v rounded to its MXFP8 value e4m3(v / X) * X: the quotient (exact) keeps 3
+// mantissa bits at and above 2^-6 and becomes a multiple of 2^-9 below,
+// nearest-even either way, and saturates at 448; the sign is kept.
+__device__ __forceinline__ float mx8_round(float v, float X, float inv) {
+    const float q = fabsf(v * inv);
+    const uint32_t b = __float_as_uint(q);
+    float r = b >= 0x3C800000u ? __uint_as_float((b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u)
+                               : (q + 16384.0f) - 16384.0f;
+    r = fminf(r, 448.0f);
+    return copysignf(r * X, v);
+}
+
 // RMSNorm factors inv[m] = 1 / sqrt(mean(r_m^2) + eps) of M_T tokens of H
 // float32 values, by a block of 256 threads that holds the residual as
 // 16-byte pieces: piece p = threadIdx.x + 256 i (held in xv[i], p <

@@ -132,6 +132,7 @@ struct FfnArgs {
     int n_gu, n_units;
     int writer;                      // the block that writes routing outputs and x_out (runs a gate/up unit)
     int pair_bytes, red_off;         // LDS layout
+    int a8;                          // nonzero: MXFP8 activations (x into gate/up, h into down)
     const uint16_t* x;               // [M][H] bf16 (null when r_in is given)
     const float* r_in;               // [M][H] residual: x = bf16(RMSNorm(r_in)), or null
     float* r_out;                    // [M][H] r_in + y, or null
@@ -634,7 +635,7 @@ __device__ void gateup_fp8_unit(const FfnArgs& a, const SlotTable& T, uint8_t* l
 // ---------------------------------------------------------------------------
 // down unit
 
-template <int M_T, bool ONE, bool SH8 = false>
+template <int M_T, bool ONE, bool SH8 = false, bool A8 = false>
 __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, uint32_t gen) {
     const int n_nc = (a.max_groups - 1) * a.dn_units;    // units of groups 1.. come first
     int grp, g;
@@ -804,7 +805,7 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
                     if (!((done >> q) & 1u) && raw[q][1] == gen && raw[q][3] == gen) {
                         const int p = pf[q] >> 16, k = pf[q] & 0xFFFF;
                         const int src = T.pair[p];
-                        const float wt = T.weight[src >> 8][src & 0xFF];
+                        const float wt = A8 ? 1.f : T.weight[src >> 8][src & 0xFF];   // A8: weighted below
                         *reinterpret_cast<float2*>(lds + p * a.pair_bytes + (k >> 5) * kHBlock + (k & 31) * 4) =
                             make_float2(__uint_as_float(raw[q][0]) * wt, __uint_as_float(raw[q][2]) * wt);
                         done |= 1u << q;
@@ -816,6 +817,33 @@ __device__ void down_unit(const FfnArgs& a, SlotTable& T, uint8_t* lds, int d, u
                     break;
                 }
                 __builtin_amdgcn_s_sleep(4);                 // not there yet: pause before re-reading
+            }
+        }
+    }
+    if constexpr (A8) {
+        // MXFP8 of each pair's h (blocks of 32 along I, 8 lanes per block,
+        // four values each; padding blocks are zero), then the routing weight
+        const int per_pair_blk = a.kbi4 * 4, n_blk = n_pairs * per_pair_blk;
+        for (int b0 = 0; b0 < n_blk; b0 += kThreads / 8) {
+            const int b = b0 + (tid >> 3);
+            const bool valid = b < n_blk;
+            const int p = valid ? b / per_pair_blk : 0;
+            float4* hp =
+                reinterpret_cast<float4*>(lds + p * a.pair_bytes + (valid ? b - p * per_pair_blk : 0) * kHBlock) +
+                (tid & 7);
+            const float4 v = valid ? *hp : make_float4(0.f, 0.f, 0.f, 0.f);
+            uint32_t am = max(max(__float_as_uint(v.x) & 0x7FFFFFFFu, __float_as_uint(v.y) & 0x7FFFFFFFu),
+                              max(__float_as_uint(v.z) & 0x7FFFFFFFu, __float_as_uint(v.w) & 0x7FFFFFFFu));
+            am = max(am, dpp_u32<kQuadSwap1>(am));
+            am = max(am, dpp_u32<kQuadSwap2>(am));
+            am = max(am, dpp_u32<kRowHalfMirror>(am));
+            float X, inv;
+            mx8_scale(am, X, inv);
+            if (valid) {
+                const int src = T.pair[p];
+                const float wt = T.weight[src >> 8][src & 0xFF];
+                *hp = make_float4(mx8_round(v.x, X, inv) * wt, mx8_round(v.y, X, inv) * wt,
+                                  mx8_round(v.z, X, inv) * wt, mx8_round(v.w, X, inv) * wt);
             }
         }
     }
@@ -1069,6 +1097,38 @@ __device__ void x_stage(const FfnArgs& a, const u32x4 (&xv)[x_pieces<M_T, NORM>(
     }
 }
 
+// MXFP8 of the staged x in place (W4A8): each 32-value block of each token
+// (64 bytes in the x area) by 4 lanes, 8 values each; the block's largest
+// magnitude by two lane swaps, then every value rounded to its MXFP8 value
+// (exact in bf16).  Runs while the first unit's weight loads are in flight;
+// the caller's barrier publishes the stores.
+template <int M_T>
+__device__ void x_quant_lds(const FfnArgs& a, uint8_t* lds) {
+    const int tid = threadIdx.x;
+    const int xtok = a.kbh4 * 4 * kXBlock, n_blk = M_T * a.kbh;
+    for (int b0 = 0; b0 < n_blk; b0 += kThreads / 4) {
+        const int b = b0 + (tid >> 2);
+        const bool valid = b < n_blk;
+        const int m = valid ? b / a.kbh : 0;
+        u32x4* p = reinterpret_cast<u32x4*>(lds + m * xtok + (valid ? b - m * a.kbh : 0) * kXBlock + (tid & 3) * 16);
+        u32x4 v = valid ? *p : u32x4{0u, 0u, 0u, 0u};
+        uint32_t am = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) am = max(am, max(v[e] & 0x7FFFu, (v[e] >> 16) & 0x7FFFu));
+        am = max(am, dpp_u32<kQuadSwap1>(am));
+        am = max(am, dpp_u32<kQuadSwap2>(am));
+        float X, inv;
+        mx8_scale(am << 16, X, inv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = mx8_round(bf16_to_f32(v[e] & 0xFFFFu), X, inv);
+            const float hi = mx8_round(bf16_to_f32(v[e] >> 16), X, inv);
+            v[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+        }
+        if (valid) *p = v;
+    }
+}
+
 // The launch count on the workspace: every one of the kMaxGrid words advances
 // once per launch (block b takes b, b + grid, ...), so all blocks agree
 // whatever the grid of earlier launches.  One thread per block.
@@ -1089,7 +1149,7 @@ __device__ __forceinline__ void gateup_run(const FfnArgs& a, const SlotTable& T,
         gateup_compute<M_T, NB>(a, T, lds, u, gen, L);
 }
 
-template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE, bool SH8>
+template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE, bool SH8, bool A8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(blocks_per_cu<ONE>())))
 void moe_ffn_kernel(FfnArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -1121,6 +1181,10 @@ void moe_ffn_kernel(FfnArgs a) {
             }
             x_stage<M_T, NORM>(a, xv, lds);
             __syncthreads();
+            if constexpr (A8) {
+                x_quant_lds<M_T>(a, lds);
+                __syncthreads();
+            }
             gateup_run<M_T, NB, SH8>(a, T, lds, unit0, s_gen, cur);
             return;
         }
@@ -1172,6 +1236,12 @@ void moe_ffn_kernel(FfnArgs a) {
         for (; u < a.n_gu; u += gridDim.x) {
             GuLoads<NB> cur;
             gateup_issue<M_T, NB, SH8>(a, T, u, cur);
+            if constexpr (A8) {
+                if (u == unit0) {
+                    x_quant_lds<M_T>(a, lds);
+                    __syncthreads();
+                }
+            }
             gateup_run<M_T, NB, SH8>(a, T, lds, u, gen, cur);
             __syncthreads();
         }
@@ -1181,6 +1251,10 @@ void moe_ffn_kernel(FfnArgs a) {
         // with the gate/up stream that every down unit waits for.)
         GuLoads<NB> cur, nxt;
         gateup_issue<M_T, NB, SH8>(a, T, u, cur);
+        if constexpr (A8) {
+            x_quant_lds<M_T>(a, lds);
+            __syncthreads();
+        }
         bool groups_pending = groups_late;
         for (; u < a.n_gu; u += gridDim.x) {
             const int un = u + gridDim.x;
@@ -1195,7 +1269,7 @@ void moe_ffn_kernel(FfnArgs a) {
         }
     }
     for (; u < a.n_units; u += gridDim.x) {
-        down_unit<M_T, ONE, SH8>(a, T, lds, u - a.n_gu, gen);
+        down_unit<M_T, ONE, SH8, A8>(a, T, lds, u - a.n_gu, gen);
         __syncthreads();
     }
 }
@@ -1226,7 +1300,7 @@ int device_cus() {
     return d.cus;
 }
 
-template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE, bool SH8>
+template <int M_T, int NB, bool ROUTE, bool NORM, bool ONE, bool SH8, bool A8>
 hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) {
     constexpr int kBlocksPerCU = blocks_per_cu<ONE>();
     // ONE: a block per unit (the host picks ONE only when they all fit)
@@ -1238,30 +1312,30 @@ hipError_t launch_variant(const FfnArgs& a, int cus, size_t lds, hipStream_t s) 
     if (v == 0) {
         int blocks = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE, SH8>), kThreads, lds);
+            &blocks, reinterpret_cast<const void*>(&moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE, SH8, A8>), kThreads, lds);
         if (e != hipSuccess) return e;
         v = (blocks >= kBlocksPerCU) ? 1 : 2;
         occ_ok[cls].store(v, std::memory_order_relaxed);
     }
     if (v != 1) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE, SH8>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((moe_ffn_kernel<M_T, NB, ROUTE, NORM, ONE, SH8, A8>), dim3(grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
-template <int M_T, bool ROUTE, bool NORM, bool ONE, bool SH8>
+template <int M_T, bool ROUTE, bool NORM, bool ONE, bool SH8, bool A8>
 hipError_t launch_nb(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     switch (nb) {
-        case 1: return launch_variant<M_T, 1, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
-        case 2: return launch_variant<M_T, 2, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
-        case 4: return launch_variant<M_T, 4, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
-        case 5: return launch_variant<M_T, 5, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
-        default: return launch_variant<M_T, 8, ROUTE, NORM, ONE, SH8>(a, cus, lds, s);
+        case 1: return launch_variant<M_T, 1, ROUTE, NORM, ONE, SH8, A8>(a, cus, lds, s);
+        case 2: return launch_variant<M_T, 2, ROUTE, NORM, ONE, SH8, A8>(a, cus, lds, s);
+        case 4: return launch_variant<M_T, 4, ROUTE, NORM, ONE, SH8, A8>(a, cus, lds, s);
+        case 5: return launch_variant<M_T, 5, ROUTE, NORM, ONE, SH8, A8>(a, cus, lds, s);
+        default: return launch_variant<M_T, 8, ROUTE, NORM, ONE, SH8, A8>(a, cus, lds, s);
     }
 }
 
 // One token: a block per unit when the units fit four blocks per CU (and the
 // variant's occupancy allows it), else the general three-block grid.
-template <int M_T, bool ROUTE, bool NORM, bool SH8>
+template <int M_T, bool ROUTE, bool NORM, bool SH8, bool A8 = false>
 hipError_t launch_one(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     if constexpr (M_T == 1) {
         FfnArgs b = a;                                  // the down units of the ONE form
@@ -1269,11 +1343,11 @@ hipError_t launch_one(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t
         b.n_units = b.n_gu + b.max_groups * b.dn_units;
         b.writer = b.gu_units;                          // slot 1's first gate/up block routes; slot 0's do not
         if (b.n_units <= std::min(kMaxGrid, blocks_per_cu<true>() * cus)) {
-            const hipError_t e = launch_nb<M_T, ROUTE, NORM, true, SH8>(b, nb, cus, lds, s);
+            const hipError_t e = launch_nb<M_T, ROUTE, NORM, true, SH8, A8>(b, nb, cus, lds, s);
             if (e != hipErrorInvalidConfiguration) return e;
         }
     }
-    return launch_nb<M_T, ROUTE, NORM, false, SH8>(a, nb, cus, lds, s);
+    return launch_nb<M_T, ROUTE, NORM, false, SH8, A8>(a, nb, cus, lds, s);
 }
 
 // routing from logits with or without the residual stream, or from a table
@@ -1281,6 +1355,10 @@ hipError_t launch_one(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t
 template <int M_T, bool SH8>
 hipError_t launch_m(const FfnArgs& a, int nb, int cus, size_t lds, hipStream_t s) {
     if (a.r_in) return launch_one<M_T, true, true, SH8>(a, nb, cus, lds, s);
+    if (a.a8) {                                      // W4A8: routed from logits, MXFP4 shared expert
+        if constexpr (SH8) return hipErrorInvalidValue;
+        else return launch_one<M_T, true, false, false, true>(a, nb, cus, lds, s);
+    }
     if (a.logits) return launch_one<M_T, true, false, SH8>(a, nb, cus, lds, s);
     if constexpr (SH8)
         return hipErrorInvalidValue;
@@ -1337,7 +1415,7 @@ FfnLayout ffn_layout(int M, int k_max, int H, int I) {
 hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int k_max,
                       const moedec_dispatch* disp, const float* logits, int32_t* ids_out,
                       float* w_out, moedec_dispatch* disp_out, uint16_t* y_bf16, float* y_f32,
-                      void* ws, hipStream_t s, const ResidualArgs* res) {
+                      void* ws, hipStream_t s, const ResidualArgs* res, bool a8) {
     const FfnLayout L = ffn_layout(M, k_max, w.H, w.I);
     const int cus = device_cus();
     if (cus <= 0) return hipErrorInvalidDevice;
@@ -1375,6 +1453,7 @@ hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int
     a.n_units = a.n_gu + L.max_groups * a.dn_units;
     a.pair_bytes = L.pair_bytes;
     a.red_off = L.red_off;
+    a.a8 = a8 ? 1 : 0;
     a.writer = 0;
     a.x = x;
     a.disp = disp;

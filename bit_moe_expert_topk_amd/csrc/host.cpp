@@ -176,6 +176,18 @@ size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I) {
     return moedec::ffn_layout(M, k_max, H, I).total;
 }
 
+int moe_ffn_workspace_layout(int M, int k_max, int H, int I, moedec_ffn_layout* out) {
+    if (!out) return fail(MOEDEC_ERR_NULL, "out is NULL");
+    if (!moe_ffn_workspace_bytes(M, k_max, H, I))
+        return fail(MOEDEC_ERR_SHAPE, "M=%d k_max=%d H=%d I=%d out of range", M, k_max, H, I);
+    const moedec::FfnLayout L = moedec::ffn_layout(M, k_max, H, I);
+    out->total_bytes = L.total;
+    out->h_words = L.h_off;
+    out->max_slots = L.max_slots;
+    out->M = M;
+    return MOEDEC_OK;
+}
+
 // Checks of a MoE call's weights, activations and sizes (not its workspace).
 static int check_moe_core(const moedec_moe_weights* w, const uint16_t* x_bf16, int M, int k,
                           uint16_t* y_bf16, float* y_f32, bool residual) {
@@ -231,19 +243,37 @@ int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, in
                     "moe_expert_ffn_mxfp4");
 }
 
-int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int M,
-                    int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
-                    uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
-                    moedec_stream_t stream) {
+static int fused_layer(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int M, int k,
+                       int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch, uint16_t* y_bf16,
+                       float* y_f32, void* workspace, size_t workspace_bytes, moedec_stream_t stream, bool a8,
+                       const char* name) {
     if (int st = check_moe_args(w, x_bf16, M, k, y_bf16, y_f32, workspace, workspace_bytes)) return st;
+    if (a8 && w->magic == MOEDEC_MOE_MAGIC_SHARED_FP8)
+        return fail(MOEDEC_ERR_FORMAT, "the W4A8 layer takes an MXFP4 shared expert");
     if (!logits) return fail(MOEDEC_ERR_NULL, "logits is NULL");
     if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
         return fail(MOEDEC_ERR_ALIGN, "logits/topk_ids/topk_w must be 4-byte aligned");
     if (!aligned(dispatch, 16)) return fail(MOEDEC_ERR_ALIGN, "dispatch must be 16-byte aligned");
     if (int st = check_device()) return st;
     return launched(moedec::launch_moe(*w, x_bf16, M, k, nullptr, logits, topk_ids, topk_w, dispatch,
-                                       y_bf16, y_f32, workspace, static_cast<hipStream_t>(stream)),
-                    "moe_layer_mxfp4");
+                                       y_bf16, y_f32, workspace, static_cast<hipStream_t>(stream), nullptr, a8),
+                    name);
+}
+
+int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int M,
+                    int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
+                    uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
+                    moedec_stream_t stream) {
+    return fused_layer(w, x_bf16, logits, M, k, topk_ids, topk_w, dispatch, y_bf16, y_f32, workspace,
+                       workspace_bytes, stream, false, "moe_layer_mxfp4");
+}
+
+int moe_layer_mxfp4_a8(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits, int M,
+                       int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
+                       uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
+                       moedec_stream_t stream) {
+    return fused_layer(w, x_bf16, logits, M, k, topk_ids, topk_w, dispatch, y_bf16, y_f32, workspace,
+                       workspace_bytes, stream, true, "moe_layer_mxfp4_a8");
 }
 
 int moe_ffn_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* flags_out,

@@ -65,7 +65,7 @@ struct ResidualArgs {
 hipError_t launch_moe(const moedec_moe_weights& w, const uint16_t* x, int M, int k_max,
                       const moedec_dispatch* disp, const float* logits, int32_t* ids_out,
                       float* w_out, moedec_dispatch* disp_out, uint16_t* y_bf16, float* y_f32,
-                      void* ws, hipStream_t s, const ResidualArgs* res = nullptr);
+                      void* ws, hipStream_t s, const ResidualArgs* res = nullptr, bool a8 = false);
 
 hipError_t launch_expert_ffn(const moedec_moe_weights& w, const uint16_t* x, int M,
                              const moedec_dispatch* disp, int k_max, uint16_t* y_bf16,

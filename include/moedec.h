@@ -229,6 +229,24 @@ typedef struct {
  */
 size_t moe_ffn_workspace_bytes(int M, int k_max, int H, int I);
 
+/* Where an FFN / fused-layer call leaves each (slot, token)'s h in its
+ * workspace, for inspecting a finished call (stream synchronised): h_words
+ * is the byte offset of [M * k_max + 1][M][I] 64-bit words, slot-major: slot
+ * 0 the shared expert, slot s >= 1 the routed entry s - 1 of the call's
+ * dispatch table (the table's valid entries in its order); the low 32
+ * bits of a word are the float32 h = silu(g) * u (before any MXFP8 rounding),
+ * valid for the tokens in the slot's token mask.  Same argument ranges as
+ * moe_ffn_workspace_bytes; returns MOEDEC_OK, or MOEDEC_ERR_NULL /
+ * MOEDEC_ERR_SHAPE with *out untouched.
+ */
+typedef struct moedec_ffn_layout {
+    uint64_t total_bytes;
+    uint64_t h_words;
+    int32_t max_slots, M;
+} moedec_ffn_layout;
+
+int moe_ffn_workspace_layout(int M, int k_max, int H, int I, moedec_ffn_layout* out);
+
 int moe_expert_ffn_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, int M,
                          const moedec_dispatch* dispatch, int k_max,
                          uint16_t* y_bf16, float* y_f32,
@@ -260,6 +278,28 @@ int moe_layer_mxfp4(const moedec_moe_weights* w, const uint16_t* x_bf16, const f
                     int M, int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
                     uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
                     moedec_stream_t stream);
+
+/* The fused layer with 8-bit activations (W4A8), M = 1..4.  [news
+ * "boundary": the measured baseline serves the model in its W4A8
+ * configuration; MX Specification v1.0 §5.2 and §6.3: MXFP8 = E4M3 elements
+ * sharing one E8M0 scale per 32 values]
+ *
+ * As moe_layer_mxfp4 with both products taking MXFP8 activations along their
+ * reduction axis: x_q = MXFP8(x) per token over H, h = silu(W_gate x_q) *
+ * (W_up x_q), h_q = MXFP8(h) per (token, expert) over I, y = sum_j w_j W_down
+ * h_q_j + W_down,s h_q_s.  Scale and rounding as moe_layer_mxfp4_prefill_a8.
+ * Each block quantises the values it reads (x as it stages it, h as it
+ * stages a pair's h), so the products see exactly the MXFP8 values; the
+ * weights' bytes, which bound the layer at these token counts, are the same.
+ * Domain: blocks of x whose largest magnitude is 0 or at least 2^-110 (below
+ * that an MXFP8 value may be a bf16 subnormal).  An FP8 shared-expert
+ * descriptor is refused (MOEDEC_ERR_FORMAT).  Arguments, workspace and errors
+ * as moe_layer_mxfp4.
+ */
+int moe_layer_mxfp4_a8(const moedec_moe_weights* w, const uint16_t* x_bf16, const float* logits,
+                       int M, int k, int32_t* topk_ids, float* topk_w, moedec_dispatch* dispatch,
+                       uint16_t* y_bf16, float* y_f32, void* workspace, size_t workspace_bytes,
+                       moedec_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Health of an FFN workspace.  The FFN calls above (and the residual-stream

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
                  "moe_layer_mxfp4_noalloc", "moe_layer_rmsnorm_router_mxfp4",
                  "moe_pack_shared_fp8", "moedec_shared_fp8_packed_sizes",
                  "moe_layer_mxfp4_prefill", "moe_prefill_workspace_bytes", "moe_layer_mxfp4_prefill_a8",
-                 "moe_prefill_workspace_layout"):
+                 "moe_prefill_workspace_layout", "moe_layer_mxfp4_a8", "moe_ffn_workspace_layout"):
         assert want in names
 
 
@@ -362,6 +362,20 @@ def test_prefill_workspace_and_argument_checks(m):
         _prefill_argument_checks(m, fn, ws)
 
 
+def test_a8_layer_argument_checks(m):
+    """moe_layer_mxfp4_a8 checks as moe_layer_mxfp4 and refuses an FP8 shared
+    expert (before touching the device)."""
+    L = m.lib
+    ws = m.ffn_workspace_bytes(1, 8, 2560, 768)
+    call = lambda w, lg=FAKE, k=8, n=ws: L.moe_layer_mxfp4_a8(
+        ctypes.byref(w), FAKE, lg, 1, k, None, None, None, FAKE, None, FAKE, n, None)
+    assert call(_weights(m, magic=m._lib.MOE_MAGIC_SHARED_FP8)) == -4
+    assert call(_weights(m, magic=0x12345678)) == -4
+    assert call(_weights(m), lg=None) == -1
+    assert call(_weights(m), k=33) == -3
+    assert call(_weights(m), n=ws - 1) == -5
+
+
 def _prefill_argument_checks(m, fn, ws):
     call = lambda w, lg=FAKE, T=64, k=8, n=ws, work=FAKE, y32=None: fn(
         ctypes.byref(w), FAKE, lg, T, k, None, None, None, FAKE, y32, work, n, None)
@@ -400,3 +414,16 @@ def test_prefill_workspace_layout(m):
             assert a + n <= b
         assert regions[-1][0] + regions[-1][1] <= lay["total_bytes"]
         assert all(off % 256 == 0 for off, _ in regions)
+
+
+def test_ffn_workspace_layout(m):
+    L = m.lib
+    out = m._lib.FfnLayout()
+    assert L.moe_ffn_workspace_layout(1, 8, 2560, 768, None) == -1
+    assert L.moe_ffn_workspace_layout(5, 8, 2560, 768, ctypes.byref(out)) == -3
+    for M, k, H, I in ((1, 8, 2560, 768), (4, 8, 2560, 768), (4, 32, 4096, 2048), (2, 3, 320, 96)):
+        assert L.moe_ffn_workspace_layout(M, k, H, I, ctypes.byref(out)) == 0
+        assert out.total_bytes == L.moe_ffn_workspace_bytes(M, k, H, I)
+        assert out.max_slots == M * k + 1 and out.M == M
+        assert out.h_words % 256 == 0
+        assert out.h_words + 8 * out.max_slots * M * I <= out.total_bytes
