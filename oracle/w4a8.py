@@ -73,7 +73,8 @@ def w4a8_h(wg, wu, x_q):
     dequantised MXFP8 activations), float64 [n][I], before its own MXFP8."""
     g = x_q @ wg.T
     u = x_q @ wu.T
-    return g / (1.0 + np.exp(-g)) * u
+    with np.errstate(over="ignore"):        # exp(-g) = inf for g << 0 gives silu = -0, as it should
+        return g / (1.0 + np.exp(-g)) * u
 
 
 def moe_layer_w4a8(x, ids, w, expert_weights, shared_weights, tokens=None):
