@@ -99,6 +99,16 @@ def test_a8_ragged(m, H, I, E, k, M):
     _check(m, W, xb, lg, k, fn, sh, f"a8 ragged H={H} I={I} M={M}")
 
 
+@pytest.mark.parametrize("H,I,E,k,M", [(1024, 64, 8, 2, 3), (2048, 128, 8, 3, 2), (4096, 64, 16, 4, 4),
+                                       (4096, 2048, 4, 2, 1)])
+def test_a8_wide_hidden(m, H, I, E, k, M):
+    """Hidden sizes that select the other chunk-pair counts per wave (2, 4, 8)
+    and the largest intermediate size."""
+    shape = synth.MoEShape(H=H, I=I, E=E, k=k, scale_lo=127 - 9, scale_hi=127 - 5)
+    W, xb, lg, fn, sh = _host_case(m, shape, M, seed=4)
+    _check(m, W, xb, lg, k, fn, sh, f"a8 H={H} I={I} M={M}")
+
+
 def test_a8_zero_and_wide_blocks(m):
     """A token of zeros (every block scale 2^-127) and a token whose blocks
     span 2^+-10 (E4M3 subnormals and zeros after quantisation)."""
