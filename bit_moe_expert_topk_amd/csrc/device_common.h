@@ -214,14 +214,24 @@ __device__ __forceinline__ uint32_t e4m3_mag_code(float q) {
     return c;
 }
 
-// MXFP8 (E4M3 elements sharing one power-of-two scale per 32 values): a
-// block whose largest magnitude is amax (float32 bits, sign cleared) has
-// scale X = 2^(floor(log2 amax) - 8), clamped at 2^-127 (also for an
-// all-zero block); mx8_scale returns X and its exact reciprocal.
+// MXFP8 (E4M3 elements sharing one power-of-two scale per 32 values).  A
+// block whose largest magnitude has float32 bits amax_bits (sign clear) has
+// scale X = 2^(floor(log2 amax) - 8), clamped at 2^-127 (also for an all-zero
+// block): E8M0 byte mx8_scale_byte, exact reciprocal mx8_inv (byte <= 246).
+__device__ __forceinline__ uint32_t mx8_scale_byte(uint32_t amax_bits) {
+    return (uint32_t)max((int)((amax_bits >> 23) & 0xFFu) - 8, 0);
+}
+__device__ __forceinline__ float mx8_inv(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
 __device__ __forceinline__ void mx8_scale(uint32_t amax_bits, float& X, float& inv) {
-    const uint32_t b = (uint32_t)max((int)((amax_bits >> 23) & 0xFFu) - 8, 0);
+    const uint32_t b = mx8_scale_byte(amax_bits);
     X = b ? __uint_as_float(b << 23) : 0x1p-127f;
-    inv = __uint_as_float((254u - b) << 23);
+    inv = mx8_inv(b);
+}
+
+// E4M3 code of v / X (an exact product), nearest-even, saturating, sign kept.
+__device__ __forceinline__ uint32_t mx8_code(float v, float inv) {
+    const float q = v * inv;
+    return e4m3_mag_code<true>(fabsf(q)) | ((__float_as_uint(q) >> 24) & 0x80u);
 }
 
 // v rounded to its MXFP8 value e4m3(v / X) * X: the quotient (exact) keeps 3

@@ -611,18 +611,8 @@ __global__ __launch_bounds__(64 * W) void down_kernel(
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// E8M0 byte of a block whose largest magnitude is amax: 2^(floor(log2 amax) - 8),
-// the exponent clamped at -127 (byte 0, also for an all-zero block).
-__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
-    return (uint32_t)max((int)((__float_as_uint(amax) >> 23) & 0xFFu) - 8, 0);
-}
-// 2^(127 - byte): the exact reciprocal of the block scale (byte <= 246).
-__device__ __forceinline__ float mx8_inv(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
-// E4M3 code of v / X (an exact product), nearest-even, saturating, sign kept.
-__device__ __forceinline__ uint32_t mx8_code(float v, float inv) {
-    const float q = v * inv;
-    return e4m3_mag_code<true>(fabsf(q)) | ((__float_as_uint(q) >> 24) & 0x80u);
-}
+// The MXFP8 scale rule and encoder (mx8_scale_byte, mx8_inv, mx8_code) are in
+// device_common.h, shared with the decode layer.
 
 __device__ __forceinline__ f32x16 mfma_a4b8(const u32x4& a, const i32x8& b, uint32_t sa, uint32_t sb, f32x16 c) {
     const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
@@ -649,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void quant_x8_kernel(const uint16_t* __re
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) am = max(am, max(d[q][e] & 0x7FFFu, (d[q][e] >> 16) & 0x7FFFu));
-        const uint32_t sbyte = mx8_scale_byte(bf16_to_f32(am));
+        const uint32_t sbyte = mx8_scale_byte(am << 16);
         const float inv = mx8_inv(sbyte);
         u32x4 o[2];
 #pragma unroll
@@ -862,7 +852,7 @@ __global__ __launch_bounds__(64 * W) void gateup_a8_kernel(
             am = max(am, __float_as_uint(hv[e]) & 0x7FFFFFFFu);
         }
         const u32x2 pr = swap32(am);
-        const uint32_t sbyte = mx8_scale_byte(__uint_as_float(max(pr[0], pr[1])));
+        const uint32_t sbyte = mx8_scale_byte(max(pr[0], pr[1]));
         const float inv = mx8_inv(sbyte);
         const int row = s * kSub + r;
         if (row >= it.rows) continue;
