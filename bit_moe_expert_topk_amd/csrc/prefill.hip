@@ -33,6 +33,11 @@
 // (a token), each supplying 8 consecutive k of its half (l / 32); D register
 // r of lane l = row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 //
+// The W4A8 variant (moe_layer_mxfp4_prefill_a8) runs the same steps with
+// MXFP8 activations: x quantised once (quant_x8), gate/up and down on the
+// block-scaled fp4 x fp8 matrix instruction, h quantised in the gate/up
+// epilogue; see the W4A8 section below.
+//
 // Block -> work mapping is XCD-aware: block b runs on XCD b % 8, and each XCD
 // takes a contiguous range of (tile, row block) items, so the row blocks of
 // one token tile (which share its activations) and the tiles of one expert
@@ -605,9 +610,9 @@ __global__ __launch_bounds__(64 * W) void down_kernel(
 // ceil(H/128), padding blocks 127); h by the gate/up epilogue ([P][I] codes,
 // [P][SBI] scale bytes): the 32 rows of a wave's MFMA tile are one MX block of
 // h for each token, split over lanes l and l ^ 32.  Per slab the ring carries
-// the activation codes (64 B per token row, one 1 KB load per wave: a block
-// of W waves holds 16 W tokens) and each wave's weights; the activation scales
-// of the whole reduction are loaded into LDS once per block.
+// the activation codes (64 B per token row, in 1 KB pieces of 16 rows spread
+// over the waves), the rows' scale dwords of the slab's 128-k chunk, and each
+// wave's weights (A8Ring below).
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
