@@ -247,6 +247,14 @@ def test_prefill_a8_odd_shape(m):
     _check(m, W, xb, synth.logits_f32(3, 0, 129, ODD.E), ODD.k, fn, sh, "a8 odd H=320 I=96 T=129")
 
 
+def test_prefill_a8_max_k(m):
+    """k = 32 of 64 experts (the largest k): 33 pairs per token."""
+    shape = synth.MoEShape(H=256, I=64, E=64, k=32, scale_lo=127 - 8, scale_hi=127 - 5)
+    W, fn, sh = _small_layer(m, shape, seed=11)
+    xb = synth.activations_bf16(11, 0, 100, shape.H)
+    _check(m, W, xb, synth.logits_f32(11, 0, 100, shape.E), shape.k, fn, sh, "a8 k=32 of 64")
+
+
 def test_prefill_a8_skewed_and_zero_blocks(m):
     """Every token picks experts 3 and 5 (1000 rows each); some tokens have
     all-zero MX blocks of x (scale byte 0) and one token is zero throughout."""
