@@ -101,7 +101,7 @@ hipError_t launch_norm_router_bf16(const uint16_t* w, int E, int H, const float*
 struct PrefillLayout {
     int ns;             // 32-token column blocks per tile
     int max_tiles;      // tiles at most: (T*k + T) / (32*ns) + E + 1
-    size_t counts_off, cursor_off, off_off, n_tiles_off, tiles_off, ids_off, w_off, pos_off, tok_of_off,
+    size_t counts_off, hist_off, base_off, off_off, n_tiles_off, tiles_off, ids_off, w_off, pos_off, tok_of_off,
         h_hi_off, h_lo_off, y_pair_off, total;
     // MXFP8-activation variant: scale bytes per token row of x (sb) and of h
     // (sbi), x's codes and scales, h's codes and scales (inside h_hi / h_lo)

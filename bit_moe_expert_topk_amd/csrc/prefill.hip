@@ -10,8 +10,11 @@
 // method point 3); the shared expert multiplies all T.
 //
 // Steps (one stream, in order):
-//   route    one wave per token: top-k of its logits (route_device.h), the
-//            routing weights, and per-expert token counts
+//   route    one wave per token: top-k of its logits (route_device.h) and
+//            the routing weights
+//   count    the routed pairs in chunks: per-chunk expert counts in LDS, then
+//            a column scan into per-expert totals and each chunk's first row
+//            inside every expert's group
 //   plan     one block: exclusive scan of the counts into pair offsets, and
 //            the tile list (group, first row) in units of 32*NS tokens
 //   scatter  each (token, choice) pair gets a row in its expert's group; the
@@ -98,18 +101,9 @@ __device__ __forceinline__ bool block_item(const int32_t* n_tiles_p, const int2*
 // ----------------------------------------------------------------------------
 // Routing, counting, plan and scatter.
 
-__global__ __launch_bounds__(kThreads) void zero_counts_kernel(int32_t* counts, int32_t* cursor, int n) {
-    for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) {
-        counts[i] = 0;
-        cursor[i] = 0;
-    }
-}
-
 template <int KPL>
-__global__ __launch_bounds__(kThreads) void route_count_kernel(const float* __restrict__ logits, int T, int E,
-                                                               int k, int32_t* __restrict__ ids,
-                                                               float* __restrict__ wts,
-                                                               int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ wts) {
     __shared__ uint64_t s_buf[kThreads / kWave][kTopkBufWords];
     const int wv = threadIdx.x >> 6, lane = lane_id();
     const int t = blockIdx.x * (kThreads / kWave) + wv;
@@ -117,14 +111,53 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(const float* __re
     float w;
     const uint64_t key = wave_topk<KPL>(logits + (size_t)t * E, E, k, w, s_buf[wv]);
     if (lane < k) {
-        const int id = key_to_index(key);
-        ids[(size_t)t * k + lane] = id;
+        ids[(size_t)t * k + lane] = key_to_index(key);
         wts[(size_t)t * k + lane] = w;
-        atomicAdd(&counts[id], 1);
     }
 }
 
-// One block.  counts[0..E) from the route kernel; the shared group E gets T.
+// Counting without device-scope atomics.  Those serialise per address: with
+// E counters each one takes T*k/E atomics in a row, which made this step
+// grow linearly with T (about 140 us for the routing of 32,768 tokens over
+// 512 experts).  Instead the T*k routed pairs (token-major) are cut into
+// n_chunks chunks of `chunk` pairs; block c counts its chunk's experts with
+// LDS atomics and writes the row hist[c][0..E); a column scan gives every
+// expert's total (counts) and each chunk's first row inside every group
+// (base[c][e]); the scatter block of chunk c ranks its pairs in LDS again.
+constexpr int kCountThreads = 1024;
+constexpr int kMaxChunks = 64;
+constexpr int kChunkMin = 2048;
+
+__global__ __launch_bounds__(kCountThreads) void count_kernel(const int32_t* __restrict__ ids, int n_routed,
+                                                              int chunk, int E, int32_t* __restrict__ hist) {
+    __shared__ int s_cnt[MOEDEC_MAX_E];
+    for (int e = threadIdx.x; e < E; e += kCountThreads) s_cnt[e] = 0;
+    __syncthreads();
+    const int first = blockIdx.x * chunk, last = min(n_routed, first + chunk);
+    for (int i = first + threadIdx.x; i < last; i += kCountThreads) atomicAdd(&s_cnt[ids[i]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kCountThreads) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// One thread per expert: all of its column's chunk counts in flight at once.
+__global__ __launch_bounds__(kWave) void chunk_scan_kernel(const int32_t* __restrict__ hist, int n_chunks, int E,
+                                                           int32_t* __restrict__ base,
+                                                           int32_t* __restrict__ counts) {
+    const int e = blockIdx.x * kWave + threadIdx.x;
+    if (e >= E) return;
+    int v[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) v[c] = c < n_chunks ? hist[(size_t)c * E + e] : 0;
+    int run = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        if (c < n_chunks) base[(size_t)c * E + e] = run;
+        run += v[c];
+    }
+    counts[e] = run;
+}
+
+// One block.  counts[0..E) from the column scan; the shared group E gets T.
 // off[g] = first pair row of group g (off[E + 1] = total); tiles list every
 // (group, first row) in steps of tile_tokens; *n_tiles their number.
 constexpr int kPlanPerThread = (MOEDEC_MAX_E + 1 + kThreads - 1) / kThreads;
@@ -173,27 +206,30 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t* __restrict__ co
     }
 }
 
-// One thread per routed pair, then one per token for the shared group.  The
-// row a pair gets inside its group depends on atomic arrival order; no value
-// depends on it (each row of the products is computed on its own).
-__global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __restrict__ ids, int T, int k,
-                                                           const int32_t* __restrict__ off,
-                                                           int32_t* __restrict__ cursor,
-                                                           int32_t* __restrict__ tok_of,
-                                                           int32_t* __restrict__ pos, int E) {
-    const size_t n_routed = (size_t)T * k;
-    for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < n_routed + T;
-         i += (size_t)gridDim.x * kThreads) {
-        if (i < n_routed) {
-            const int e = ids[i];
-            const int row = off[e] + atomicAdd(&cursor[e], 1);
-            tok_of[row] = (int)(i / k);
-            pos[i] = row;
-        } else {
-            const int t = (int)(i - n_routed);
-            tok_of[off[E] + t] = t;
-        }
+// Block c places the pairs of chunk c: row = off[e] + base[c][e] + its rank
+// among the chunk's pairs of expert e (LDS atomic, in arrival order; no value
+// depends on the order of rows inside a group, each row of the products is
+// computed on its own).  The blocks also write the shared group's rows.
+__global__ __launch_bounds__(kCountThreads) void scatter_kernel(const int32_t* __restrict__ ids, int T, int k,
+                                                                int chunk, const int32_t* __restrict__ off,
+                                                                const int32_t* __restrict__ base,
+                                                                int32_t* __restrict__ tok_of,
+                                                                int32_t* __restrict__ pos, int E) {
+    __shared__ int s_cnt[MOEDEC_MAX_E];
+    for (int e = threadIdx.x; e < E; e += kCountThreads) s_cnt[e] = 0;
+    __syncthreads();
+    const int n_routed = T * k;
+    const int first = blockIdx.x * chunk, last = min(n_routed, first + chunk);
+    const int32_t* b = base + (size_t)blockIdx.x * E;
+    for (int i = first + threadIdx.x; i < last; i += kCountThreads) {
+        const int e = ids[i];
+        const int row = off[e] + b[e] + atomicAdd(&s_cnt[e], 1);
+        tok_of[row] = i / k;
+        pos[i] = row;
     }
+    const int shared0 = off[E];
+    for (int t = blockIdx.x * kCountThreads + threadIdx.x; t < T; t += gridDim.x * kCountThreads)
+        tok_of[shared0 + t] = t;
 }
 
 // ----------------------------------------------------------------------------
@@ -1188,7 +1224,8 @@ PrefillLayout prefill_layout(int T, int E, int k, int H, int I) {
     l.max_tiles = (int)(P / tile_tokens + G);
     size_t o = 0;
     l.counts_off = o;   o = align256(o + (G + 1) * 4);
-    l.cursor_off = o;   o = align256(o + (G + 1) * 4);
+    l.hist_off = o;     o = align256(o + (size_t)kMaxChunks * E * 4);
+    l.base_off = o;     o = align256(o + (size_t)kMaxChunks * E * 4);
     l.off_off = o;      o = align256(o + (G + 1) * 4);
     l.n_tiles_off = o;  o = align256(o + 4);
     l.tiles_off = o;    o = align256(o + (size_t)l.max_tiles * 8);
@@ -1216,28 +1253,34 @@ hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const 
     const PrefillLayout lay = prefill_layout(T, w.E, k, w.H, w.I);
     uint8_t* base = static_cast<uint8_t*>(ws);
     int32_t* counts = reinterpret_cast<int32_t*>(base + lay.counts_off);
-    int32_t* cursor = reinterpret_cast<int32_t*>(base + lay.cursor_off);
+    int32_t* hist = reinterpret_cast<int32_t*>(base + lay.hist_off);
+    int32_t* chunk_base = reinterpret_cast<int32_t*>(base + lay.base_off);
     int32_t* off = reinterpret_cast<int32_t*>(base + lay.off_off);
     int32_t* ids = ids_out ? ids_out : reinterpret_cast<int32_t*>(base + lay.ids_off);
     float* wts = w_out ? w_out : reinterpret_cast<float*>(base + lay.w_off);
-    const int G = w.E + 1;
 
-    hipLaunchKernelGGL(zero_counts_kernel, dim3(grid_cap(G + 1, 8)), dim3(kThreads), 0, s, counts, cursor, G + 1);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    const int n_routed = T * k;
+    const int chunk = std::max(kChunkMin, (n_routed + kMaxChunks - 1) / kMaxChunks);
+    const int n_chunks = (n_routed + chunk - 1) / chunk;
     const dim3 rgrid((T + kThreads / kWave - 1) / (kThreads / kWave));
     if (w.E <= 512)
-        hipLaunchKernelGGL(route_count_kernel<8>, rgrid, dim3(kThreads), 0, s, logits, T, w.E, k, ids, wts, counts);
+        hipLaunchKernelGGL(route_kernel<8>, rgrid, dim3(kThreads), 0, s, logits, T, w.E, k, ids, wts);
     else
-        hipLaunchKernelGGL(route_count_kernel<16>, rgrid, dim3(kThreads), 0, s, logits, T, w.E, k, ids, wts, counts);
+        hipLaunchKernelGGL(route_kernel<16>, rgrid, dim3(kThreads), 0, s, logits, T, w.E, k, ids, wts);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(count_kernel, dim3(n_chunks), dim3(kCountThreads), 0, s, ids, n_routed, chunk, w.E, hist);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(chunk_scan_kernel, dim3((w.E + kWave - 1) / kWave), dim3(kWave), 0, s, hist, n_chunks, w.E,
+                       chunk_base, counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, counts, w.E, T, lay.ns * kSub, off,
                        reinterpret_cast<int2*>(base + lay.tiles_off),
                        reinterpret_cast<int32_t*>(base + lay.n_tiles_off), counts_out);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     int32_t* pos = reinterpret_cast<int32_t*>(base + lay.pos_off);
-    hipLaunchKernelGGL(scatter_kernel, dim3(grid_cap((size_t)T * (k + 1), 4096)), dim3(kThreads), 0, s, ids, T, k,
-                       off, cursor, reinterpret_cast<int32_t*>(base + lay.tok_of_off), pos, w.E);
+    hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks), dim3(kCountThreads), 0, s, ids, T, k, chunk, off, chunk_base,
+                       reinterpret_cast<int32_t*>(base + lay.tok_of_off), pos, w.E);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     if (a8) {

@@ -351,8 +351,9 @@ def test_prefill_workspace_and_argument_checks(m):
         pairs = T * (k + 1)
         body = pairs * (4 * H + 4 * I)                    # y_pair float32 + h as two bf16
         x8 = T * H + T * (H // 32 + 4)                     # MXFP8 x of the W4A8 call
-        assert body <= n <= (body + pairs * 4 + 3 * T * k * 4 + (3 * (E + 2) * 4) + ((pairs // 32 + E + 1) * 8)
-                             + x8 + 4096)
+        chunks = 2 * 64 * E * 4                            # per-chunk expert counts and first rows
+        assert body <= n <= (body + pairs * 4 + 3 * T * k * 4 + (2 * (E + 2) * 4) + ((pairs // 32 + E + 1) * 8)
+                             + x8 + chunks + 4096)
     assert L.moe_prefill_workspace_bytes(0, 512, 8, 2560, 768) == 0
     assert L.moe_prefill_workspace_bytes(m._lib.MOEDEC_MAX_PREFILL_T + 1, 512, 8, 2560, 768) == 0
     assert L.moe_prefill_workspace_bytes(64, 512, 33, 2560, 768) == 0
