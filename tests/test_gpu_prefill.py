@@ -121,6 +121,30 @@ def test_prefill_max_tokens(m):
     _check(m, W, xb, synth.logits_f32(9, 0, T, shape.E), shape.k, fn, sh, f"prefill tiny T={T}", tokens=tokens)
 
 
+def test_prefill_chunk_tails_and_reuse(m):
+    """Counting runs over chunks of the token-major routed pairs (at most 64
+    chunks of at least 2,048 pairs).  T = 65,535 on the tiny shape (k = 2):
+    64 chunks of 2,048 pairs, the last one 2,046; the first 30,000 tokens all
+    pick experts 3 and 5, so the early chunks' counts differ from the late
+    ones'.  Tokens at chunk edges (1,024 tokens per chunk) are sampled.  Then
+    T = 3,001 (three chunks, a ragged last) on the same workspace, in full."""
+    shape = synth.TINY
+    W, fn, sh = _small_layer(m, shape)
+    T = 65535
+    ws = m.make_prefill_workspace(T, shape.E, shape.k, shape.H, shape.I, "cuda")
+    xb = synth.activations_bf16(12, 0, T, shape.H)
+    lg = synth.logits_f32(12, 0, T, shape.E).copy()
+    lg[:30000, 3] += 50.0
+    lg[:30000, 5] += 40.0
+    edges = [c * 1024 + d for c in (1, 2, 29, 30, 63) for d in (-1, 0)]
+    tokens = np.unique(np.concatenate([[0, 29999, 30000, T - 2, T - 1], edges,
+                                       np.random.default_rng(12).choice(T, 20, replace=False)]))
+    _check(m, W, xb, lg, shape.k, fn, sh, f"prefill chunk tails T={T}", tokens=tokens, workspace=ws)
+    xb2 = synth.activations_bf16(13, 0, 3001, shape.H)
+    _check(m, W, xb2, synth.logits_f32(13, 0, 3001, shape.E), shape.k, fn, sh, "prefill T=3001 after T=65535",
+           workspace=ws)
+
+
 def test_prefill_zero_input(m):
     shape = synth.TINY
     W, fn, sh = _small_layer(m, shape)
@@ -130,8 +154,8 @@ def test_prefill_zero_input(m):
 
 
 def test_prefill_repeatable_and_workspace_reuse(m):
-    """Rows inside an expert's group follow atomic arrival order; the outputs
-    must not depend on it: two calls on one workspace give identical bits, and
+    """Rows inside an expert's group follow LDS-atomic arrival order; the
+    outputs must not depend on it: two calls on one workspace give identical bits, and
     a smaller call after a larger one on the same workspace is still correct."""
     W, fn, sh = _small_layer(m, MID, seed=6)
     ws = m.make_prefill_workspace(700, MID.E, MID.k, MID.H, MID.I, "cuda")
