@@ -12,11 +12,11 @@
 // Steps (one stream, in order):
 //   route    one wave per token: top-k of its logits (route_device.h) and
 //            the routing weights
-//   count    the routed pairs in chunks: per-chunk expert counts in LDS, then
-//            a column scan into per-expert totals and each chunk's first row
-//            inside every expert's group
-//   plan     one block: exclusive scan of the counts into pair offsets, and
-//            the tile list (group, first row) in units of 32*NS tokens
+//   count    the routed pairs in chunks: per-chunk expert counts in LDS
+//   plan     one block: a column scan of the chunk counts into per-expert
+//            totals and each chunk's first row inside every expert's group,
+//            then an exclusive scan of the totals into pair offsets, and the
+//            tile list (group, first row) in units of 32*NS tokens
 //   scatter  each (token, choice) pair gets a row in its expert's group; the
 //            shared group holds token t at row T*k + t
 //   gate/up  per (tile, 128 intermediate rows): g = W_gate x, u = W_up x on
@@ -139,70 +139,75 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(const int32_t* __r
     for (int e = threadIdx.x; e < E; e += kCountThreads) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-// One thread per expert: all of its column's chunk counts in flight at once.
-__global__ __launch_bounds__(kWave) void chunk_scan_kernel(const int32_t* __restrict__ hist, int n_chunks, int E,
-                                                           int32_t* __restrict__ base,
-                                                           int32_t* __restrict__ counts) {
-    const int e = blockIdx.x * kWave + threadIdx.x;
-    if (e >= E) return;
-    int v[kMaxChunks];
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) v[c] = c < n_chunks ? hist[(size_t)c * E + e] : 0;
-    int run = 0;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-        if (c < n_chunks) base[(size_t)c * E + e] = run;
-        run += v[c];
-    }
-    counts[e] = run;
-}
+// One block, thread e for routed expert e.  The column scan of the per-chunk
+// counts (all of a column's loads in flight at once) gives each chunk's first
+// row inside group e (base[c][e]) and the group's total; an exclusive scan
+// over experts of the totals and of their tile counts (inside each wave by
+// lane shifts, then over the wave totals) gives off[e], the group's first pair
+// row, and its place in the tile list (group, first row) in steps of
+// tile_tokens.  The shared group E holds T rows after every routed pair and
+// its tiles come last; *n_tiles is the list's length.
+static_assert(MOEDEC_MAX_E <= kCountThreads, "one plan thread per routed expert");
 
-// One block.  counts[0..E) from the column scan; the shared group E gets T.
-// off[g] = first pair row of group g (off[E + 1] = total); tiles list every
-// (group, first row) in steps of tile_tokens; *n_tiles their number.
-constexpr int kPlanPerThread = (MOEDEC_MAX_E + 1 + kThreads - 1) / kThreads;
-
-__global__ __launch_bounds__(kThreads) void plan_kernel(int32_t* __restrict__ counts, int E, int T,
-                                                        int tile_tokens, int32_t* __restrict__ off,
-                                                        int2* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-                                                        int32_t* __restrict__ counts_out) {
-    __shared__ int s_pairs[kThreads], s_tiles[kThreads];
-    const int tid = threadIdx.x, G = E + 1;
-    if (tid == 0) counts[E] = T;
-    __syncthreads();
-    int c[kPlanPerThread];
-    int my_pairs = 0, my_tiles = 0;
+__global__ __launch_bounds__(kCountThreads) void plan_kernel(const int32_t* __restrict__ hist, int n_chunks, int E,
+                                                             int T, int tile_tokens, int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ off, int2* __restrict__ tiles,
+                                                             int32_t* __restrict__ n_tiles,
+                                                             int32_t* __restrict__ counts_out) {
+    constexpr int kWaves = kCountThreads / kWave;
+    __shared__ int s_pairs[kWaves], s_tiles[kWaves];
+    const int e = threadIdx.x, lane = lane_id(), wv = e / kWave;
+    int cnt = 0;
+    if (e < E) {
+        int v[kMaxChunks];
 #pragma unroll
-    for (int i = 0; i < kPlanPerThread; ++i) {
-        const int g = tid * kPlanPerThread + i;
-        c[i] = g < G ? counts[g] : 0;
-        my_pairs += c[i];
-        my_tiles += (c[i] + tile_tokens - 1) / tile_tokens;
-    }
-    s_pairs[tid] = my_pairs;
-    s_tiles[tid] = my_tiles;
-    __syncthreads();
-    for (int d = 1; d < kThreads; d <<= 1) {    // inclusive scan (Hillis-Steele)
-        const int a = tid >= d ? s_pairs[tid - d] : 0, b = tid >= d ? s_tiles[tid - d] : 0;
-        __syncthreads();
-        s_pairs[tid] += a;
-        s_tiles[tid] += b;
-        __syncthreads();
-    }
-    int p = s_pairs[tid] - my_pairs, q = s_tiles[tid] - my_tiles;
+        for (int c = 0; c < kMaxChunks; ++c) v[c] = c < n_chunks ? hist[(size_t)c * E + e] : 0;
 #pragma unroll
-    for (int i = 0; i < kPlanPerThread; ++i) {
-        const int g = tid * kPlanPerThread + i;
-        if (g < G) {
-            off[g] = p;
-            if (counts_out) counts_out[g] = c[i];
-            for (int s = 0; s < c[i]; s += tile_tokens) tiles[q++] = int2{g, s};
-            p += c[i];
+        for (int c = 0; c < kMaxChunks; ++c) {
+            if (c < n_chunks) base[(size_t)c * E + e] = cnt;
+            cnt += v[c];
         }
     }
-    if (tid == kThreads - 1) {
-        off[G] = s_pairs[tid];
-        *n_tiles = s_tiles[tid];
+    const int nt = (cnt + tile_tokens - 1) / tile_tokens;
+    int ip = cnt, it = nt;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int a = __shfl_up(ip, d), b = __shfl_up(it, d);
+        if (lane >= d) {
+            ip += a;
+            it += b;
+        }
+    }
+    if (lane == kWave - 1) {
+        s_pairs[wv] = ip;
+        s_tiles[wv] = it;
+    }
+    __syncthreads();
+    int below_p = 0, below_t = 0, all_p = 0, all_t = 0;
+    for (int i = 0; i < kWaves; ++i) {
+        if (i < wv) {
+            below_p += s_pairs[i];
+            below_t += s_tiles[i];
+        }
+        all_p += s_pairs[i];
+        all_t += s_tiles[i];
+    }
+    if (e < E) {
+        counts[e] = cnt;
+        off[e] = below_p + ip - cnt;
+        if (counts_out) counts_out[e] = cnt;
+        int q = below_t + it - nt;
+        for (int r = 0; r < cnt; r += tile_tokens) tiles[q++] = int2{e, r};
+    }
+    const int shared_tiles = (T + tile_tokens - 1) / tile_tokens;
+    for (int i = e; i < shared_tiles; i += kCountThreads) tiles[all_t + i] = int2{E, i * tile_tokens};
+    if (e == 0) {
+        counts[E] = T;
+        off[E] = all_p;
+        off[E + 1] = all_p + T;
+        if (counts_out) counts_out[E] = T;
+        *n_tiles = all_t + shared_tiles;
     }
 }
 
@@ -1271,11 +1276,8 @@ hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const 
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(count_kernel, dim3(n_chunks), dim3(kCountThreads), 0, s, ids, n_routed, chunk, w.E, hist);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(chunk_scan_kernel, dim3((w.E + kWave - 1) / kWave), dim3(kWave), 0, s, hist, n_chunks, w.E,
-                       chunk_base, counts);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, counts, w.E, T, lay.ns * kSub, off,
-                       reinterpret_cast<int2*>(base + lay.tiles_off),
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kCountThreads), 0, s, hist, n_chunks, w.E, T, lay.ns * kSub,
+                       chunk_base, counts, off, reinterpret_cast<int2*>(base + lay.tiles_off),
                        reinterpret_cast<int32_t*>(base + lay.n_tiles_off), counts_out);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     int32_t* pos = reinterpret_cast<int32_t*>(base + lay.pos_off);

@@ -412,8 +412,9 @@ int moe_layer_rmsnorm_router_mxfp4(const moedec_moe_weights* w, const uint16_t* 
  * Results do not depend on scheduling: every output is formed from its own
  * row and column only, in a fixed order.
  *
- * Eight launches on `stream`: routing, per-chunk expert counts, their column
- * scan, plan (one block), scatter, gate/up, down, combine.
+ * Seven launches on `stream`: routing, per-chunk expert counts, plan (one
+ * block: the scans of the counts and the tile list), scatter, gate/up, down,
+ * combine.
  * w             MOEDEC_MOE_MAGIC weights (an FP8 shared expert is refused
  *               with MOEDEC_ERR_FORMAT); the four scale arrays 4-byte
  *               aligned (they are read as 32-bit words)
@@ -456,7 +457,7 @@ int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16,
  * then the combine of moe_layer_mxfp4_prefill.  A block's scale is
  * 2^(floor(log2 max|v|) - 8), 2^-127 for an all-zero block; each element is
  * v / scale rounded to the nearest E4M3 value, ties to even, saturating at
- * +-448.  Nine launches: the eight above plus the quantisation of x.
+ * +-448.  Eight launches: the seven above plus the quantisation of x.
  * Arguments, alignment, errors and workspace (moe_prefill_workspace_bytes,
  * the same size) as for moe_layer_mxfp4_prefill.
  */
