@@ -37,9 +37,9 @@
 // r of lane l = row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 //
 // The W4A8 variant (moe_layer_mxfp4_prefill_a8) runs the same steps with
-// MXFP8 activations: x quantised once (quant_x8), gate/up and down on the
-// block-scaled fp4 x fp8 matrix instruction, h quantised in the gate/up
-// epilogue; see the W4A8 section below.
+// MXFP8 activations: x quantised once (in the routing launch), gate/up and
+// down on the block-scaled fp4 x fp8 matrix instruction, h quantised in the
+// gate/up epilogue; see the W4A8 section below.
 //
 // Block -> work mapping is XCD-aware: block b runs on XCD b % 8, and each XCD
 // takes a contiguous range of (tile, row block) items, so the row blocks of
@@ -101,12 +101,13 @@ __device__ __forceinline__ bool block_item(const int32_t* n_tiles_p, const int2*
 // ----------------------------------------------------------------------------
 // Routing, counting, plan and scatter.
 
+// One wave per token (block `blk` takes tokens 4 blk .. 4 blk + 3).
 template <int KPL>
-__global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                         int32_t* __restrict__ ids, float* __restrict__ wts) {
+__device__ __forceinline__ void route_body(const float* __restrict__ logits, int T, int E, int k,
+                                           int32_t* __restrict__ ids, float* __restrict__ wts, int blk) {
     __shared__ uint64_t s_buf[kThreads / kWave][kTopkBufWords];
     const int wv = threadIdx.x >> 6, lane = lane_id();
-    const int t = blockIdx.x * (kThreads / kWave) + wv;
+    const int t = blk * (kThreads / kWave) + wv;
     if (t >= T) return;
     float w;
     const uint64_t key = wave_topk<KPL>(logits + (size_t)t * E, E, k, w, s_buf[wv]);
@@ -114,6 +115,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
         ids[(size_t)t * k + lane] = key_to_index(key);
         wts[(size_t)t * k + lane] = w;
     }
+}
+
+template <int KPL>
+__global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ wts) {
+    route_body<KPL>(logits, T, E, k, ids, wts, blockIdx.x);
 }
 
 // Counting without device-scope atomics.  Those serialise per address: with
@@ -647,7 +654,7 @@ __global__ __launch_bounds__(64 * W) void down_kernel(
 // l % 32 with k 16 (l/32) .. +15 and 32 + 16 (l/32) .. +15, and the scale of
 // block l / 32.  D as for the bf16 MFMA.
 //
-// x is quantised by quant_x8 ([T][H] codes, [T][SB] scale bytes, SB = 4 *
+// x is quantised by quant_x8_body ([T][H] codes, [T][SB] scale bytes, SB = 4 *
 // ceil(H/128), padding blocks 127); h by the gate/up epilogue ([P][I] codes,
 // [P][SBI] scale bytes): the 32 rows of a wave's MFMA tile are one MX block of
 // h for each token, split over lanes l and l ^ 32.  Per slab the ring carries
@@ -665,12 +672,13 @@ __device__ __forceinline__ f32x16 mfma_a4b8(const u32x4& a, const i32x8& b, uint
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, b, c, 4, 0, 0, (int)sa, 0, (int)sb);
 }
 
-// One thread per 32-value block of one token.
-__global__ __launch_bounds__(kThreads) void quant_x8_kernel(const uint16_t* __restrict__ x, int T, int H, int sb,
-                                                           uint8_t* __restrict__ x8, uint8_t* __restrict__ xs) {
+// One thread per 32-value block of one token; blocks blk = 0 .. nblk - 1 of
+// the launch stride over them.
+__device__ __forceinline__ void quant_x8_body(const uint16_t* __restrict__ x, int T, int H, int sb,
+                                              uint8_t* __restrict__ x8, uint8_t* __restrict__ xs, int blk,
+                                              int nblk) {
     const int nb = H / 32;
-    for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < (size_t)T * sb;
-         i += (size_t)gridDim.x * kThreads) {
+    for (size_t i = blk * (size_t)kThreads + threadIdx.x; i < (size_t)T * sb; i += (size_t)nblk * kThreads) {
         const int t = (int)(i / sb), b = (int)(i - (size_t)t * sb);
         if (b >= nb) {
             xs[i] = 127;
@@ -704,6 +712,22 @@ __global__ __launch_bounds__(kThreads) void quant_x8_kernel(const uint16_t* __re
         dst[1] = o[1];
         xs[i] = (uint8_t)sbyte;
     }
+}
+
+// The W4A8 call's first launch: blocks [0, route_blocks) route (route_body),
+// the others quantise x (quant_x8_body).  The two read different inputs, so
+// the routing's latency-bound waves and the quantisation's streaming share
+// one grid instead of following each other.
+template <int KPL>
+__global__ __launch_bounds__(kThreads) void route_quant_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                               int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                               int route_blocks, const uint16_t* __restrict__ x,
+                                                               int H, int sb, uint8_t* __restrict__ x8,
+                                                               uint8_t* __restrict__ xs) {
+    if ((int)blockIdx.x < route_blocks)
+        route_body<KPL>(logits, T, E, k, ids, wts, blockIdx.x);
+    else
+        quant_x8_body(x, T, H, sb, x8, xs, blockIdx.x - route_blocks, gridDim.x - route_blocks);
 }
 
 // Activation rows in a ring slot: 64 B per row, 16-byte unit u at u ^ ((row >> 2) & 3).
@@ -1267,11 +1291,16 @@ hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const 
     const int n_routed = T * k;
     const int chunk = std::max(kChunkMin, (n_routed + kMaxChunks - 1) / kMaxChunks);
     const int n_chunks = (n_routed + chunk - 1) / chunk;
-    const dim3 rgrid((T + kThreads / kWave - 1) / (kThreads / kWave));
-    if (w.E <= 512)
-        hipLaunchKernelGGL(route_kernel<8>, rgrid, dim3(kThreads), 0, s, logits, T, w.E, k, ids, wts);
-    else
-        hipLaunchKernelGGL(route_kernel<16>, rgrid, dim3(kThreads), 0, s, logits, T, w.E, k, ids, wts);
+    const int route_blocks = (T + kThreads / kWave - 1) / (kThreads / kWave);
+    if (a8) {
+        const int qblocks = grid_cap((size_t)T * lay.sb, 8192);
+        auto rq = w.E <= 512 ? route_quant_kernel<8> : route_quant_kernel<16>;
+        hipLaunchKernelGGL(rq, dim3(route_blocks + qblocks), dim3(kThreads), 0, s, logits, T, w.E, k, ids, wts,
+                           route_blocks, x, w.H, lay.sb, base + lay.x8_off, base + lay.xs_off);
+    } else {
+        auto r = w.E <= 512 ? route_kernel<8> : route_kernel<16>;
+        hipLaunchKernelGGL(r, dim3(route_blocks), dim3(kThreads), 0, s, logits, T, w.E, k, ids, wts);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(count_kernel, dim3(n_chunks), dim3(kCountThreads), 0, s, ids, n_routed, chunk, w.E, hist);
@@ -1286,9 +1315,6 @@ hipError_t launch_prefill(const moedec_moe_weights& w, const uint16_t* x, const 
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     if (a8) {
-        hipLaunchKernelGGL(quant_x8_kernel, dim3(grid_cap((size_t)T * lay.sb, 8192)), dim3(kThreads), 0, s, x, T,
-                           w.H, lay.sb, base + lay.x8_off, base + lay.xs_off);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
         switch (lay.ns) {
             case 4: err = launch_gemms_a8<4>(w, lay, base, s); break;
             case 2: err = launch_gemms_a8<2>(w, lay, base, s); break;

@@ -457,7 +457,7 @@ int moe_layer_mxfp4_prefill(const moedec_moe_weights* w, const uint16_t* x_bf16,
  * then the combine of moe_layer_mxfp4_prefill.  A block's scale is
  * 2^(floor(log2 max|v|) - 8), 2^-127 for an all-zero block; each element is
  * v / scale rounded to the nearest E4M3 value, ties to even, saturating at
- * +-448.  Eight launches: the seven above plus the quantisation of x.
+ * +-448.  Seven launches, as above; the routing launch also quantises x.
  * Arguments, alignment, errors and workspace (moe_prefill_workspace_bytes,
  * the same size) as for moe_layer_mxfp4_prefill.
  */
